@@ -1,0 +1,110 @@
+"""Pure-Python brute-force HSA forward layer for tiny inputs.
+
+TEST INFRASTRUCTURE ONLY.  Written independently of ``hsa_oracle`` (no numpy,
+no shared helpers) so that the two pin each other.  Inputs are nested Python
+lists of floats holding the stored values exactly.
+
+Follows the skill card "Every Token Counts 16m Context", sections "Core
+Technique" and "Implementation", one query at a time:
+landmark = exact mean of the chunk's keys (Fraction arithmetic) rounded once,
+half-to-even, to the storage precision; scores = exact dot products (the
+common positive 1/sqrt(D) factor cannot change the order, so the selection is
+decided on exact rationals); top-k under (score desc, index asc); softmax
+attention inside each kept chunk; softmax fusion over the kept scores.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+PRECISION_BITS = {"bf16": 8, "fp32": 24}
+
+
+def round_fraction(x: Fraction, bits: int) -> Fraction:
+    """Round a rational to the nearest binary float with ``bits`` significant
+    bits, ties to even (normal range only)."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = -x if x < 0 else x
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    # adjust so that 2**e <= a < 2**(e+1)
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (e - bits + 1)
+    q = a / ulp
+    fl = q.numerator // q.denominator
+    rem = q - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * ulp
+
+
+def landmark(chunk_keys, dtype: str):
+    """Mean of a chunk's keys, rounded once to the storage precision."""
+    S = len(chunk_keys)
+    D = len(chunk_keys[0])
+    out = []
+    for d in range(D):
+        tot = sum((Fraction(row[d]) for row in chunk_keys), Fraction(0))
+        out.append(float(round_fraction(tot / S, PRECISION_BITS[dtype])))
+    return out
+
+
+def _softmax(xs):
+    mx = max(xs)
+    es = [math.exp(x - mx) for x in xs]
+    tot = sum(es)
+    return [e / tot for e in es]
+
+
+def hsa_query(q, p: int, K, V, S: int, k: int, dtype: str):
+    """Output, selected chunks (in order) and their scores for the query row q
+    at position p, against one KV head (K, V: lists of T rows)."""
+    D = len(q)
+    T = len(K)
+    Nc = T // S
+    n = min(p // S, Nc)
+    if n == 0:
+        return [0.0] * D, [], []
+    lms = [landmark(K[c * S:(c + 1) * S], dtype) for c in range(n)]
+    exact = [sum((Fraction(q[d]) * Fraction(lm[d]) for d in range(D)), Fraction(0)) for lm in lms]
+    order = sorted(range(n), key=lambda c: (-exact[c], c))
+    sel = order[:min(k, n)]
+    scale = 1.0 / math.sqrt(D)
+    scores = [float(exact[c]) * scale for c in sel]
+    outs = []
+    for c in sel:
+        logits = [sum(q[d] * K[t][d] for d in range(D)) * scale for t in range(c * S, c * S + S)]
+        a = _softmax(logits)
+        outs.append([sum(a[i] * V[c * S + i][d] for i in range(S)) for d in range(D)])
+    w = _softmax(scores)
+    out = [sum(w[j] * outs[j][d] for j in range(len(sel))) for d in range(D)]
+    return out, sel, scores
+
+
+def prefill(Q, K, V, S: int, k: int, dtype: str):
+    """Q: [B][Hq][T][D]; K, V: [B][Hkv][T][D] nested lists.
+    Returns (out, sel, scores) nested as [B][Hq][T]."""
+    B, Hq, T = len(Q), len(Q[0]), len(Q[0][0])
+    Hkv = len(K[0])
+    outs, sels, scs = [], [], []
+    for b in range(B):
+        ob, sb, cb = [], [], []
+        for h in range(Hq):
+            g = (h * Hkv) // Hq
+            oh, sh, ch = [], [], []
+            for p in range(T):
+                o, s, c = hsa_query(Q[b][h][p], p, K[b][g], V[b][g], S, k, dtype)
+                oh.append(o)
+                sh.append(s)
+                ch.append(c)
+            ob.append(oh)
+            sb.append(sh)
+            cb.append(ch)
+        outs.append(ob)
+        sels.append(sb)
+        scs.append(cb)
+    return outs, sels, scs

@@ -1,0 +1,352 @@
+"""numpy float64 oracle of the Hierarchical Sparse Attention (HSA) forward layer.
+
+TEST INFRASTRUCTURE ONLY -- imported by tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.
+
+What HSA computes (skill card "Every Token Counts 16m Context", sections
+"Core Technique" and "Implementation"; abstract page "Every Token Counts:
+Generalizing 16M Ultra-Long Context in Large Language Models"):
+
+  1. split the keys into non-overlapping chunks of a fixed length S;
+  2. give every chunk a landmark, read here as the plain mean of the chunk's
+     keys (the card's learned encoder needs trained weights, so this layer
+     fixes the mean pool);
+  3. score every earlier landmark against the query (scaled dot product);
+  4. keep the top-k chunks;
+  5. attend inside each kept chunk with ordinary softmax attention;
+  6. fuse the per-chunk outputs with weights taken from the retrieval scores
+     (read as a softmax over the kept scores).
+
+Readings of points the pages leave open (each is listed in the design doc):
+
+* candidates of a query at position p are the complete chunks strictly before
+  the query's own chunk: c < n_p = min(floor(p / S), Nc); a decode query sits at
+  position T (just after its cache).  A query with no candidate outputs zero.
+* GQA: query head h reads KV head g(h) = floor(h * Hkv / Hq) (contiguous groups);
+  every query head scores and selects on its own.
+* ties in the top-k go to the lower chunk index (total order: score
+  descending, then index ascending); -0.0 and +0.0 compare equal.
+* landmarks are rounded once, round-to-nearest-even, to the storage dtype.
+* the in-chunk softmax and the fusion softmax both use the 1/sqrt(D) scale;
+  each chunk output is normalised on its own.
+* the output is float (fp64 here; fp32 on the GPU) even for bf16 inputs.
+
+Every input array handed to this module holds the exact values of the stored
+tensors as float64 (bf16 and fp32 upcast exactly).  Parity unpinned: nothing.
+Every function below is pinned by the CPU tests (brute force, closed forms,
+special cases, invariants and a library-routine cross-check).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64", "f32_to_bf16_bits", "round_to_bf16", "round_to_f32",
+    "round_to_dtype", "landmarks", "num_candidates", "scores_for_rows",
+    "select_topk", "chunk_attention", "fuse", "hsa_rows", "prefill", "decode",
+    "near_tie_info", "check_selection", "HSARowsResult",
+]
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact value of bf16 bit patterns: the 16 bits are the top half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value, ties to even, in ONE step.
+
+    bf16 keeps 8 significant bits; float64 keeps 53.  The low 45 significand
+    bits of the float64 are rounded away with round-half-even directly (no
+    intermediate fp32, which would round twice).  Only the normal bf16 range
+    is supported (|x| >= 2**-126 or x == 0, no overflow); anything else raises.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    if np.any((ax != 0) & (ax < 2.0 ** -126)) or np.any(ax >= 3.3895313892515355e38):
+        raise ValueError("round_to_bf16: value outside the normal bf16 range")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("round_to_bf16: non-finite input")
+    u = x.view(np.uint64)
+    drop = np.uint64(45)
+    lsb = (u >> drop) & np.uint64(1)
+    u = u + (np.uint64((1 << 44) - 1) + lsb)
+    u = u & ~np.uint64((1 << 45) - 1)
+    return u.view(np.float64)
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """bf16 bit pattern of values that are already exactly representable in bf16."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if not np.array_equal(f.astype(np.float64), np.asarray(x, dtype=np.float64)):
+        raise ValueError("f32_to_bf16_bits: value not representable")
+    bits = f.view(np.uint32)
+    if np.any(bits & np.uint32(0xFFFF)):
+        raise ValueError("f32_to_bf16_bits: value not representable in bf16")
+    return (bits >> np.uint32(16)).astype(np.uint16)
+
+
+def round_to_f32(x) -> np.ndarray:
+    """Round float64 to the nearest fp32 value (numpy's cast is one RNE step)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def round_to_dtype(x, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "fp32":
+        return round_to_f32(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# step 1-2: chunks and landmarks
+# ---------------------------------------------------------------------------
+
+def landmarks(K: np.ndarray, S: int, dtype: str) -> np.ndarray:
+    """Mean-pooled landmark of every complete chunk of S keys.
+
+    Skill card "Every Token Counts 16m Context", section "Implementation"
+    (landmark from mean pooling of the chunk's tokens) and "Core Technique"
+    (non-overlapping fixed-length chunks).  K: [..., T, D] float64 holding the
+    stored key values.  Returns [..., floor(T/S), D] float64 whose values are
+    exactly representable in ``dtype``.  A trailing partial chunk gets no
+    landmark.  The chunk sum is taken in float64 (exact for bf16 inputs of the
+    magnitudes used here), divided by S and rounded once to ``dtype``.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    T, D = K.shape[-2], K.shape[-1]
+    Nc = T // S
+    chunks = K[..., : Nc * S, :].reshape(K.shape[:-2] + (Nc, S, D))
+    mean = chunks.sum(axis=-2) / S
+    return round_to_dtype(mean, dtype)
+
+
+def num_candidates(p, S: int, Nc: int):
+    """n_p = min(floor(p/S), Nc): complete chunks strictly before position p's chunk."""
+    return np.minimum(np.asarray(p) // S, Nc)
+
+
+# ---------------------------------------------------------------------------
+# step 3-4: scoring and selection
+# ---------------------------------------------------------------------------
+
+def scores_for_rows(q: np.ndarray, L: np.ndarray, n: int) -> np.ndarray:
+    """s[r, c] = (q[r] . L[c]) / sqrt(D) for c < n (card, "Implementation":
+    similarity of the query with every landmark; read as the scaled dot product)."""
+    D = q.shape[-1]
+    return (q @ L[:n].T) * (1.0 / math.sqrt(D))
+
+
+def select_topk(s: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the top-min(k, n) entries of each row of s under the order
+    (score descending, chunk index ascending); rows of s are [R, n].
+
+    Card "Implementation": keep the k best-scoring chunks.  The card's argsort
+    expression leaves ties open; this layer breaks them toward the lower index.
+    Returned in that order, shape [R, min(k, n)].
+    """
+    R, n = s.shape
+    m = min(k, n)
+    if m == 0:
+        return np.zeros((R, 0), dtype=np.int64)
+    s0 = s + 0.0  # -0.0 -> +0.0, so the two zeros tie
+    idx = np.broadcast_to(np.arange(n), (R, n))
+    order = np.lexsort((idx, -s0), axis=-1)
+    return order[:, :m]
+
+
+# ---------------------------------------------------------------------------
+# step 5-6: in-chunk attention and fusion
+# ---------------------------------------------------------------------------
+
+def chunk_attention(q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray) -> np.ndarray:
+    """Softmax attention of query rows over the S tokens of one chunk each.
+
+    Card "Implementation": attend to each selected chunk with standard
+    attention.  q: [R, D]; Kc, Vc: [R, m, S, D] (the m chunks of each row).
+    Returns o: [R, m, D]; each chunk output is normalised on its own, with the
+    1/sqrt(D) scale and no mask (every token of a candidate chunk precedes q).
+    """
+    D = q.shape[-1]
+    logits = np.einsum("rd,rmtd->rmt", q, Kc) * (1.0 / math.sqrt(D))
+    logits = logits - logits.max(axis=-1, keepdims=True)
+    a = np.exp(logits)
+    a = a / a.sum(axis=-1, keepdims=True)
+    return np.einsum("rmt,rmtd->rmd", a, Vc)
+
+
+def fuse(s_sel: np.ndarray, o: np.ndarray) -> np.ndarray:
+    """out = sum_c w_c o_c with w = softmax of the kept retrieval scores.
+
+    Card "Core Technique" / "Implementation": results are fused with the
+    retrieval scores as weights; read as a softmax over the kept scores (the
+    scores already carry 1/sqrt(D)).  s_sel: [R, m]; o: [R, m, D].
+    Rows with m == 0 give zeros.
+    """
+    R, m = s_sel.shape
+    if m == 0:
+        return np.zeros((R, o.shape[-1]))
+    z = s_sel - s_sel.max(axis=-1, keepdims=True)
+    w = np.exp(z)
+    w = w / w.sum(axis=-1, keepdims=True)
+    return np.einsum("rm,rmd->rd", w, o)
+
+
+# ---------------------------------------------------------------------------
+# the layer over a set of query rows sharing one KV head
+# ---------------------------------------------------------------------------
+
+@dataclass
+class HSARowsResult:
+    out: np.ndarray        # [R, D] float64
+    sel_idx: np.ndarray    # [R, k] int64, -1 padded
+    sel_score: np.ndarray  # [R, k] float64, -inf padded
+    n: np.ndarray          # [R] number of candidates
+
+
+def hsa_rows(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.ndarray,
+             Lg: np.ndarray, S: int, k: int, sel_override=None) -> HSARowsResult:
+    """HSA output of query rows q[r] at positions pos[r] against one KV head.
+
+    q: [R, D]; Kg, Vg: [T, D]; Lg: [Nc', D] (landmarks of at least the needed
+    chunks).  ``sel_override`` (list of index arrays, one per row) replaces the
+    selection step, for checking a different but equally valid selection.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    R, D = q.shape
+    T = Kg.shape[0]
+    Nc = T // S
+    n_all = num_candidates(pos, S, Nc)
+    out = np.zeros((R, D))
+    sel_idx = np.full((R, k), -1, dtype=np.int64)
+    sel_score = np.full((R, k), -np.inf)
+    # rows with the same candidate count share the whole candidate set
+    for n in np.unique(n_all):
+        rows = np.nonzero(n_all == n)[0]
+        if n == 0:
+            continue
+        s = scores_for_rows(q[rows], Lg, int(n))
+        if sel_override is None:
+            sel = select_topk(s, k)
+        else:
+            sel = np.stack([np.asarray(sel_override[r], dtype=np.int64) for r in rows])
+        m = sel.shape[1]
+        s_sel = np.take_along_axis(s, sel, axis=1)
+        tok = sel[:, :, None] * S + np.arange(S)[None, None, :]  # [r, m, S]
+        o = chunk_attention(q[rows], Kg[tok], Vg[tok])
+        out[rows] = fuse(s_sel, o)
+        sel_idx[rows, :m] = sel
+        sel_score[rows, :m] = s_sel
+    return HSARowsResult(out, sel_idx, sel_score, n_all)
+
+
+def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
+    """Contiguous GQA grouping: g(h) = floor(h * Hkv / Hq)."""
+    return (h * Hkv) // Hq
+
+
+def prefill(Q, K, V, S: int, k: int, dtype: str, L=None, rows=None):
+    """Causal HSA over a whole sequence.  Q: [B, Hq, T, D]; K, V: [B, Hkv, T, D].
+
+    Query row p uses chunks strictly before its own.  ``rows`` optionally
+    restricts the computation to a subset of positions (same for every head).
+    Returns (out [B,Hq,R,D], sel_idx, sel_score, L).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    B, Hq, T, D = Q.shape
+    Hkv = K.shape[1]
+    if L is None:
+        L = landmarks(K, S, dtype)
+    pos = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = pos.shape[0]
+    out = np.zeros((B, Hq, R, D))
+    sel_idx = np.full((B, Hq, R, k), -1, dtype=np.int64)
+    sel_score = np.full((B, Hq, R, k), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            r = hsa_rows(Q[b, h, pos], pos, K[b, g], V[b, g], L[b, g], S, k)
+            out[b, h], sel_idx[b, h], sel_score[b, h] = r.out, r.sel_idx, r.sel_score
+    return out, sel_idx, sel_score, L
+
+
+def decode(q, Kc, Vc, L, S: int, k: int):
+    """Single-token queries after their caches.  q: [B, Hq, D]; Kc, Vc: [B, Hkv, T, D];
+    L: [B, Hkv, >= floor(T/S), D].  The query sits at position T."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv, T = Kc.shape[1], Kc.shape[2]
+    out = np.zeros((B, Hq, D))
+    sel_idx = np.full((B, Hq, k), -1, dtype=np.int64)
+    sel_score = np.full((B, Hq, k), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            r = hsa_rows(q[b, h][None], np.array([T]), Kc[b, g], Vc[b, g], L[b, g], S, k)
+            out[b, h], sel_idx[b, h], sel_score[b, h] = r.out[0], r.sel_idx[0], r.sel_score[0]
+    return out, sel_idx, sel_score
+
+
+# ---------------------------------------------------------------------------
+# near-tie acceptance for a selection computed in lower precision
+# ---------------------------------------------------------------------------
+
+def near_tie_info(q: np.ndarray, Lg: np.ndarray, n: int, k: int, rel: float = 1e-5):
+    """For one query row: (is_near_tie, band, s) where s are the fp64 scores of
+    the n candidates.
+
+    The cut between the m-th and (m+1)-th best (m = min(k, n)) is a near tie
+    when their gap is below rel * mu, mu = max(|s_m|, |s_m+1|, A_m, A_m+1) and
+    A_c = sum_d |q_d| |L_cd| / sqrt(D) bounds the rounding error of a
+    lower-precision dot product (a plain relative test is ill-posed near 0).
+    The block-sparse router page (value-of-information router abstract) names
+    this k-th versus (k+1)-th gap.
+    """
+    D = q.shape[-1]
+    s = (Lg[:n] @ q) / math.sqrt(D)
+    m = min(k, n)
+    if m >= n:
+        return False, 0.0, s
+    order = np.lexsort((np.arange(n), -(s + 0.0)))
+    a, b = order[m - 1], order[m]
+    A = (np.abs(Lg[:n]) @ np.abs(q)) / math.sqrt(D)
+    mu = max(abs(s[a]), abs(s[b]), A[a], A[b])
+    band = rel * mu
+    return bool(s[a] - s[b] < band), band, s
+
+
+def check_selection(gpu_sel, q, Lg, n: int, k: int, rel: float = 1e-5):
+    """Accept or reject a GPU selection for one row (indices, -1 padded).
+
+    Returns (ok, exact_match, message).  Non-near-tie rows must match the
+    oracle's set exactly; near-tie rows must be a top-m set up to the band.
+    """
+    g = [int(c) for c in gpu_sel if int(c) >= 0]
+    m = min(k, n)
+    pad = [int(c) for c in gpu_sel[len(g):]]
+    if len(g) != m or any(c != -1 for c in pad):
+        return False, False, f"expected {m} indices then -1 padding, got {list(gpu_sel)}"
+    if len(set(g)) != m or any(c < 0 or c >= n for c in g):
+        return False, False, f"invalid indices {g} for n={n}"
+    if m == 0:
+        return True, True, ""
+    tie, band, s = near_tie_info(q, Lg, n, k, rel)
+    ref = select_topk(s[None, :], k)[0]
+    if set(ref.tolist()) == set(g):
+        return True, True, ""
+    if not tie:
+        return False, False, f"selection {sorted(g)} != oracle {sorted(ref.tolist())}"
+    inside = min(s[c] for c in g)
+    outside = [s[c] for c in range(n) if c not in set(g)]
+    ok = (not outside) or inside >= max(outside) - band
+    return ok, False, "" if ok else "near-tie selection outside the band"
