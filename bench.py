@@ -1,0 +1,341 @@
+"""Benchmark of the HSA forward layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME|all] [--no-cpu-baseline]
+
+Workloads (seeded, synthetic, shapes of the layer's published use: 1M- and
+16M-token decode, 256K-token prefill; see hierarchical_sparse_attention_hsa_amd/workloads.py):
+  decode_1m_bf16     step = hsa_forward_decode over 64 queries (landmarks
+                     precomputed, as the workload defines), metric queries/s
+  prefill_256k_bf16  step = hsa_build_landmarks + hsa_forward_prefill over
+                     the 262144-token sequence, metric tokens/s
+  decode_16m_bf16, prefill_32k_bf16, prefill_4k_fp32 on request.
+
+The default (`all`) times prefill_256k_bf16 and then decode_1m_bf16 and prints
+ONE JSON line: `value` is the 1M decode throughput (queries/s); the prefill
+result rides along under "prefill".  Each timed region: W warm-up steps, then
+K steps bracketed by torch.cuda.synchronize(); inputs are resident in HBM.
+Per-kernel durations come from HIP events the library records around each of
+its launches on the same stream (hsa_attn_set_timing_events).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "HSA layer queries/s + achieved HBM GB/s (1M decode); tokens/s + MFMA% (256K prefill)"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- HIP events
+class HipEvents:
+    """Raw hipEvent_t handles (created with the HIP runtime) so that the
+    library can record them on its own launch stream."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pool = []
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            out.append(e.value)
+        self.pool += out
+        return out
+
+    def ms(self, a, b):
+        t = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(t.value)
+
+
+def timed_steps(step, steps, warmup, n_launch, events):
+    """Run warm-up, then `steps` timed steps; returns (total seconds,
+    per-launch mean durations in ms)."""
+    import torch
+    import hierarchical_sparse_attention_hsa_amd as hsa
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    evs = [events.create(2 * n_launch) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    hsa.hsa_attn_set_timing_events(None)
+    per = np.zeros(n_launch)
+    for i in range(steps):
+        for j in range(n_launch):
+            per[j] += events.ms(evs[i][2 * j], evs[i][2 * j + 1])
+    return t1 - t0, per / steps
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+# ---------------------------------------------------------------- decode
+def bench_decode(wname, steps, warmup, cpu_baseline):
+    import torch
+    import hierarchical_sparse_attention_hsa_amd as hsa
+    from hierarchical_sparse_attention_hsa_amd.workloads import WORKLOADS, decode_inputs
+
+    w = WORKLOADS[wname]
+    G = w.Hq // w.Hkv
+    esz = 2 if w.dtype == "bf16" else 4
+    Nc = w.T // w.S
+    kv_bytes = 2 * w.B * w.Hkv * w.T * w.D * esz
+    lm_bytes = w.B * w.Hkv * Nc * w.D * esz
+    free, total = torch.cuda.mem_get_info()
+    log(f"[{wname}] device memory free {free / 2**30:.1f} GiB of {total / 2**30:.1f} GiB; "
+        f"needs {(kv_bytes + lm_bytes) / 2**30:.1f} GiB")
+    if kv_bytes + lm_bytes + (2 << 30) > free:
+        raise SystemExit(f"{wname}: inputs ({(kv_bytes + lm_bytes) / 2**30:.1f} GiB) do not fit in free device "
+                         f"memory ({free / 2**30:.1f} GiB)")
+    t0 = time.perf_counter()
+    q, k, v = decode_inputs(w, "cuda")
+    torch.cuda.synchronize()
+    log(f"[{wname}] generated inputs in {time.perf_counter() - t0:.1f} s")
+    L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
+    hsa.hsa_build_landmarks(k, L, w.S)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, w.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, w.k), dtype=torch.float32, device="cuda")
+    dims = hsa.make_dims(w.B, w.Hq, w.Hkv, w.D, w.S, w.k, w.T, hsa.HSA_ATTN_BF16 if esz == 2 else hsa.HSA_ATTN_FP32)
+    ws = torch.empty(hsa.hsa_attn_workspace_size(dims, True), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if ev is not None:
+            hsa.hsa_attn_set_timing_events(ev)
+        hsa.hsa_forward_decode(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc, workspace=ws)
+
+    secs, per = timed_steps(step, steps, warmup, 4, HipEvents())
+    ms_step = 1e3 * secs / steps
+    # distinct selected (b, g, chunk) tiles
+    s = sel.view(w.B, w.Hkv, G * w.k).cpu().numpy()
+    distinct = sum(len(set(s[b, g][s[b, g] >= 0].tolist())) for b in range(w.B) for g in range(w.Hkv))
+    tile_bytes = 2 * w.S * w.D * esz
+    alg_bytes = lm_bytes + distinct * tile_bytes
+    names = ["decode_scan", "decode_merge", "decode_attn", "decode_fuse"]
+    res = {
+        "workload": wname, "value": w.B / (ms_step / 1e3), "unit": "queries/s", "ms_per_step": ms_step,
+        "kernel_ms": {n: float(x) for n, x in zip(names, per)},
+        "step_alg_bytes": alg_bytes, "step_alg_GBps": alg_bytes / (ms_step / 1e3) / 1e9,
+        "config": {"workload": wname, "batch_queries": w.B, "cache_tokens": w.T, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.D, "chunk": w.S, "top_k": w.k, "needles": w.needles},
+        "dtype": w.dtype,
+        "roofline": {"kernel": "decode_scan_kernel", "bound": "hbm",
+                     "achieved": lm_bytes / (per[0] / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": lm_bytes / (per[0] / 1e3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                     "alg_bytes_per_launch": lm_bytes},
+    }
+    # needle recall (semantic sanity of the synthetic retrieval task)
+    from hierarchical_sparse_attention_hsa_amd.workloads import needle_chunks
+    sh = sel.cpu().numpy()
+    hit = tot = 0
+    for b in range(w.B):
+        nd = set(needle_chunks(w, b).tolist())
+        for h in range(w.Hq):
+            got = set(sh[b, h].tolist())
+            hit += len(nd & got)
+            tot += len(nd)
+    res["needle_recall"] = hit / max(tot, 1)
+    log(f"[{wname}] {ms_step:.3f} ms/step, kernels {dict(zip(names, np.round(per, 4)))}, "
+        f"scan {res['roofline']['achieved']:.0f} GB/s, needle recall {res['needle_recall']:.4f}")
+    if cpu_baseline:
+        res["cpu_baseline"] = decode_cpu_baseline(w, q, k, v)
+    del q, k, v, L, out, sel, sc, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_cpu_baseline(w, q, k, v, n_queries=2):
+    """The oracle on a bounded sample: the first n_queries queries, all heads.
+    Host copies and the oracle's own landmark build are untimed (landmarks are
+    precomputed in this workload); scoring, top-k, chunk attention and fusion
+    are timed."""
+    from oracle import hsa_oracle as O
+    G = w.Hq // w.Hkv
+    total = 0.0
+    for b in range(n_queries):
+        qb = q[b].float().cpu().double().numpy()
+        for g in range(w.Hkv):
+            Kg = k[b, g].float().cpu().double().numpy()
+            Vg = v[b, g].float().cpu().double().numpy()
+            Lg = O.landmarks(Kg, w.S, w.dtype)
+            t0 = time.perf_counter()
+            O.hsa_rows(qb[g * G:(g + 1) * G], np.full(G, w.T), Kg, Vg, Lg, w.S, w.k)
+            total += time.perf_counter() - t0
+            del Kg, Vg
+    return {"value": n_queries / total, "unit": "queries/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{n_queries} of {w.B} queries (all {w.Hq} heads); oracle landmark build and host "
+                      f"copies untimed"}
+
+
+# ---------------------------------------------------------------- prefill
+def bench_prefill(wname, steps, warmup, cpu_baseline):
+    import torch
+    import hierarchical_sparse_attention_hsa_amd as hsa
+    from hierarchical_sparse_attention_hsa_amd.workloads import WORKLOADS, prefill_inputs
+
+    w = WORKLOADS[wname]
+    esz = 2 if w.dtype == "bf16" else 4
+    Nc = w.T // w.S
+    t0 = time.perf_counter()
+    q, k, v = prefill_inputs(w, "cuda")
+    torch.cuda.synchronize()
+    log(f"[{wname}] generated inputs in {time.perf_counter() - t0:.1f} s")
+    L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
+    out = torch.empty((w.B, w.Hq, w.T, w.D), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.float32, device="cuda")
+    events = HipEvents()
+
+    def step(ev):
+        if ev is not None:
+            hsa.hsa_attn_set_timing_events(ev[:2])
+        hsa.hsa_build_landmarks(k, L, w.S)
+        if ev is not None:
+            hsa.hsa_attn_set_timing_events(ev[2:])
+        hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
+
+    secs, per = timed_steps(step, steps, warmup, 3, events)
+    ms_step = 1e3 * secs / steps
+    # exact algorithmic work
+    p = np.arange(w.T)
+    n_p = np.minimum(p // w.S, Nc)
+    m_p = np.minimum(n_p, w.k)
+    score_flops = 2.0 * w.B * w.Hq * w.D * n_p.sum()
+    attn_flops = 4.0 * w.S * w.D * w.B * w.Hq * m_p.sum()
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    names = ["landmarks", "prefill_select", "prefill_attn"]
+    sel_tf = score_flops / (per[1] / 1e3) / 1e12
+    att_tf = attn_flops / (per[2] / 1e3) / 1e12
+    dom = 1 if per[1] >= per[2] else 2
+    dom_name = ["", "prefill_select_kernel", "prefill_attn_kernel"][dom]
+    dom_tf = sel_tf if dom == 1 else att_tf
+    res = {
+        "workload": wname, "value": w.B * w.T / (ms_step / 1e3), "unit": "tokens/s", "ms_per_step": ms_step,
+        "kernel_ms": {n: float(x) for n, x in zip(names, per)},
+        "scoring_tflops": sel_tf, "scoring_mfma_frac": sel_tf / peak,
+        "attention_tflops": att_tf, "attention_mfma_frac": att_tf / peak,
+        "landmark_GBps": (w.B * w.Hkv * Nc * w.S * w.D * esz) / (per[0] / 1e3) / 1e9,
+        "config": {"workload": wname, "batch": w.B, "seq_len": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "chunk": w.S, "top_k": w.k, "lowrank": w.lowrank},
+        "dtype": w.dtype,
+        "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": dom_tf, "peak": peak, "unit": "TFLOP/s",
+                     "frac": dom_tf / peak, "traffic": None,
+                     "alg_flops_per_launch": score_flops if dom == 1 else attn_flops},
+    }
+    log(f"[{wname}] {ms_step:.3f} ms/step, kernels {dict(zip(names, np.round(per, 4)))}, "
+        f"scoring {sel_tf:.1f} TFLOP/s, attention {att_tf:.1f} TFLOP/s")
+    if cpu_baseline:
+        res["cpu_baseline"] = prefill_cpu_baseline(w, q, k, v)
+    del q, k, v, L, out, sel, sc
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_cpu_baseline(w, q, k, v, chunks=(1000, 3000)):
+    """The oracle on a bounded sample: all heads of the query chunks listed
+    (64 tokens each).  Host copies and landmark building are untimed."""
+    from oracle import hsa_oracle as O
+    G = w.Hq // w.Hkv
+    chunks = [c for c in chunks if c * w.S < w.T] or [w.T // w.S - 1]
+    total = 0.0
+    for g in range(w.Hkv):
+        Kg = k[0, g].float().cpu().double().numpy()
+        Vg = v[0, g].float().cpu().double().numpy()
+        Lg = O.landmarks(Kg, w.S, w.dtype)
+        for c in chunks:
+            pos = np.arange(c * w.S, min(w.T, (c + 1) * w.S))
+            qq = q[0, g * G:(g + 1) * G, c * w.S:(c + 1) * w.S].float().cpu().double().numpy()
+            t0 = time.perf_counter()
+            for hh in range(G):
+                O.hsa_rows(qq[hh], pos, Kg, Vg, Lg, w.S, w.k)
+            total += time.perf_counter() - t0
+    tokens = len(chunks) * w.S
+    return {"value": tokens / total, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"query chunks {list(chunks)} ({tokens} tokens, all {w.Hq} heads); host copies and "
+                      f"oracle landmark build untimed"}
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this layer is measured on one GPU; the multi-GPU sharding is a design only "
+              "(see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import hierarchical_sparse_attention_hsa_amd as hsa
+    hsa.load_library()
+    cpu = not args.no_cpu_baseline
+    results = {}
+    if args.workload == "all":
+        results["prefill"] = bench_prefill("prefill_256k_bf16", args.steps, args.warmup, cpu)
+        main_res = bench_decode("decode_1m_bf16", args.steps, args.warmup, cpu)
+    elif args.workload.startswith("decode"):
+        main_res = bench_decode(args.workload, args.steps, args.warmup, cpu)
+    else:
+        main_res = bench_prefill(args.workload, args.steps, args.warmup, cpu)
+    line = {
+        "metric": METRIC, "value": main_res["value"], "unit": main_res["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": main_res["dtype"],
+        "data": "synthetic", "config": main_res["config"], "roofline": main_res["roofline"],
+    }
+    if "cpu_baseline" in main_res:
+        line["cpu_baseline"] = main_res["cpu_baseline"]
+    for key in ("kernel_ms", "step_alg_GBps", "needle_recall"):
+        if key in main_res:
+            line[key] = main_res[key]
+    if "prefill" in results:
+        line["prefill"] = results["prefill"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

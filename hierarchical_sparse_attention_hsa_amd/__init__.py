@@ -1,0 +1,224 @@
+"""Hierarchical Sparse Attention (HSA) forward layer for AMD MI355X (gfx950).
+
+Thin Python binding of the C ABI in ``include/hsa_attn.h`` (libhsa_attn.so,
+built in-tree by ``hierarchical_sparse_attention_hsa_amd.build``).  The
+binding only marshals arguments: torch tensors supply device pointers and the
+current HIP stream, and every step of the layer runs in the library's HIP
+kernels.  There is no fallback: if the library is missing or a call fails,
+an exception is raised.
+
+Functions carry the C names:
+
+    hsa_build_landmarks(k, landmarks, chunk_size, chunk_begin=0, chunk_end=None)
+    hsa_forward_prefill(q, k, v, landmarks, chunk_size, top_k, out=None, sel_idx=None, sel_score=None, workspace=None)
+    hsa_forward_decode(q, k_cache, v_cache, landmarks, chunk_size, top_k, out=None, sel_idx=None, sel_score=None, workspace=None)
+    hsa_attn_workspace_size(...)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "library_path", "load_library", "Dims", "HSAError", "EXPORTED_SYMBOLS",
+    "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_decode",
+    "hsa_attn_set_timing_events", "hsa_attn_workspace_size", "hsa_attn_status_string",
+    "hsa_attn_last_error", "landmarks_shape",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+EXPORTED_SYMBOLS = (
+    "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_decode",
+    "hsa_attn_set_timing_events", "hsa_attn_workspace_size", "hsa_attn_status_string",
+    "hsa_attn_last_error",
+)
+
+HSA_ATTN_OK = 0
+HSA_ATTN_INVALID_ARGUMENT = 1
+HSA_ATTN_UNSUPPORTED = 2
+HSA_ATTN_WORKSPACE_TOO_SMALL = 3
+HSA_ATTN_HIP_ERROR = 4
+HSA_ATTN_FP32 = 0
+HSA_ATTN_BF16 = 1
+
+
+class Dims(ctypes.Structure):
+    """Mirror of hsa_attn_dims_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("seq_len", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class HSAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libhsa_attn.so")
+
+
+_LIB = None
+
+
+def load_library():
+    """Load libhsa_attn.so (built in-tree); raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m hierarchical_sparse_attention_hsa_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    dims = ctypes.POINTER(Dims)
+    lib.hsa_build_landmarks.argtypes = [dims, P, P, I64, I64, P]
+    lib.hsa_forward_prefill.argtypes = [dims, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_forward_decode.argtypes = [dims, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_attn_workspace_size.argtypes = [dims, ctypes.c_int, ctypes.POINTER(SZ)]
+    lib.hsa_attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    lib.hsa_attn_status_string.argtypes = [ctypes.c_int]
+    lib.hsa_attn_status_string.restype = ctypes.c_char_p
+    lib.hsa_attn_last_error.argtypes = []
+    lib.hsa_attn_last_error.restype = ctypes.c_char_p
+    for f in ("hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_decode", "hsa_attn_workspace_size",
+              "hsa_attn_set_timing_events"):
+        getattr(lib, f).restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def hsa_attn_status_string(status: int) -> str:
+    return load_library().hsa_attn_status_string(status).decode()
+
+
+def hsa_attn_last_error() -> str:
+    return load_library().hsa_attn_last_error().decode()
+
+
+def _check(status: int, what: str):
+    if status != HSA_ATTN_OK:
+        raise HSAError(status, f"{what}: {hsa_attn_status_string(status)}: {hsa_attn_last_error()}")
+
+
+# ---------------------------------------------------------------- tensor marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return HSA_ATTN_BF16
+    if t.dtype == torch.float32:
+        return HSA_ATTN_FP32
+    raise TypeError(f"unsupported storage dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_dims(batch, num_q_heads, num_kv_heads, head_dim, chunk_size, top_k, seq_len, dtype) -> Dims:
+    return Dims(batch, num_q_heads, num_kv_heads, head_dim, chunk_size, top_k, seq_len, dtype, 0)
+
+
+def landmarks_shape(k_shape, chunk_size):
+    B, Hkv, T, D = k_shape
+    return (B, Hkv, T // chunk_size, D)
+
+
+def hsa_attn_set_timing_events(events) -> None:
+    """Record caller-created hipEvent_t handles (ints) around each kernel
+    launch of the following calls on this thread: events[2i] before and
+    events[2i+1] after launch i.  Pass None or [] to switch off."""
+    global _EVENT_ARRAY
+    if not events:
+        _EVENT_ARRAY = None
+        _check(load_library().hsa_attn_set_timing_events(None, 0), "hsa_attn_set_timing_events")
+        return
+    if len(events) % 2:
+        raise ValueError("events come in (before, after) pairs")
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _EVENT_ARRAY = arr  # keep alive while the library holds the pointer
+    _check(load_library().hsa_attn_set_timing_events(arr, len(events) // 2), "hsa_attn_set_timing_events")
+
+
+_EVENT_ARRAY = None
+
+
+def hsa_attn_workspace_size(dims: Dims, is_decode: bool) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().hsa_attn_workspace_size(ctypes.byref(dims), int(bool(is_decode)), ctypes.byref(n)),
+           "hsa_attn_workspace_size")
+    return n.value
+
+
+def hsa_build_landmarks(k, landmarks, chunk_size: int, chunk_begin: int = 0, chunk_end=None):
+    """Mean-pool chunks [chunk_begin, chunk_end) of k [B, Hkv, T, D] into
+    landmarks [B, Hkv, T // chunk_size, D] (same dtype), asynchronously."""
+    B, Hkv, T, D = k.shape
+    if tuple(landmarks.shape) != landmarks_shape(k.shape, chunk_size) or landmarks.dtype != k.dtype:
+        raise ValueError("landmarks must be [B, Hkv, T // chunk_size, D] with the dtype of k")
+    if chunk_end is None:
+        chunk_end = T // chunk_size
+    dims = make_dims(B, Hkv, Hkv, D, chunk_size, 1, T, _dtype_code(k))
+    _check(load_library().hsa_build_landmarks(ctypes.byref(dims), _ptr(k), _ptr(landmarks), int(chunk_begin),
+                                              int(chunk_end), _stream(k.device)), "hsa_build_landmarks")
+    return landmarks
+
+
+def _forward(is_decode, q, k, v, landmarks, chunk_size, top_k, out, sel_idx, sel_score, workspace):
+    torch = _torch()
+    B, Hkv, T, D = k.shape
+    Hq = q.shape[1]
+    if v.shape != k.shape or v.dtype != k.dtype or q.dtype != k.dtype:
+        raise ValueError("q, k and v must share dtype; v must match k's shape")
+    expect_q = (B, Hq, D) if is_decode else (B, Hq, T, D)
+    if tuple(q.shape) != expect_q:
+        raise ValueError(f"q must be {expect_q}, got {tuple(q.shape)}")
+    if tuple(landmarks.shape) != landmarks_shape(k.shape, chunk_size) or landmarks.dtype != k.dtype:
+        raise ValueError("landmarks must be [B, Hkv, T // chunk_size, D] with the dtype of k")
+    dims = make_dims(B, Hq, Hkv, D, chunk_size, top_k, T, _dtype_code(k))
+    if out is None:
+        out = torch.empty(expect_q, dtype=torch.float32, device=q.device)
+    if (sel_idx is None) != (sel_score is None):
+        raise ValueError("give both sel_idx and sel_score or neither")
+    if workspace is None:
+        need = hsa_attn_workspace_size(dims, is_decode)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    fn = load_library().hsa_forward_decode if is_decode else load_library().hsa_forward_prefill
+    st = fn(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(landmarks), _ptr(out), _ptr(sel_idx),
+            _ptr(sel_score), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(st, "hsa_forward_decode" if is_decode else "hsa_forward_prefill")
+    return out
+
+
+def hsa_forward_prefill(q, k, v, landmarks, chunk_size: int, top_k: int, out=None, sel_idx=None, sel_score=None,
+                        workspace=None):
+    """Causal HSA over a sequence: q [B,Hq,T,D], k/v [B,Hkv,T,D] -> out [B,Hq,T,D] fp32."""
+    return _forward(False, q, k, v, landmarks, chunk_size, top_k, out, sel_idx, sel_score, workspace)
+
+
+def hsa_forward_decode(q, k_cache, v_cache, landmarks, chunk_size: int, top_k: int, out=None, sel_idx=None,
+                       sel_score=None, workspace=None):
+    """HSA for single-token queries q [B,Hq,D] after caches k/v [B,Hkv,T,D] -> out [B,Hq,D] fp32."""
+    return _forward(True, q, k_cache, v_cache, landmarks, chunk_size, top_k, out, sel_idx, sel_score, workspace)

@@ -1,0 +1,94 @@
+"""Builds libhsa_attn.so (all HIP sources, gfx950) in-tree next to this file.
+
+    python -m hierarchical_sparse_attention_hsa_amd.build
+
+Compiles every csrc/*.hip with hipcc for gfx950 and links one shared
+library.  No fast-math and no denormal flushing; packed fp32 VALU ops are
+disabled for device code.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libhsa_attn.so")
+ARCH = "gfx950"
+
+CXXFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(os.path.dirname(HERE), "include"),
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def sources():
+    """All HIP sources, minus prefill instantiation units left out by
+    HSA_ATTN_PREFILL_VARIANTS (comma list such as "bf16_d128_k16"; default:
+    all).  A left-out variant makes the matching prefill call return
+    HSA_ATTN_HIP_ERROR (not supported); the full build has every variant."""
+    want = os.environ.get("HSA_ATTN_PREFILL_VARIANTS", "").strip()
+    keep = {w.strip() for w in want.split(",") if w.strip()}
+    out = []
+    for f in sorted(os.listdir(CSRC)):
+        if not f.endswith(".hip"):
+            continue
+        if f.startswith("prefill_inst_") and keep and f[len("prefill_inst_"):-4] not in keep:
+            continue
+        out.append(os.path.join(CSRC, f))
+    return out
+
+
+def _variant_defines(srcs):
+    defs = []
+    for s in srcs:
+        f = os.path.basename(s)
+        if f.startswith("prefill_inst_"):
+            defs.append("-DHSA_ATTN_HAVE_" + f[len("prefill_inst_"):-4].upper() + "=1")
+    return defs
+
+
+def _compile(src: str, defines=()) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    cmd = [hipcc(), *CXXFLAGS, *defines, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    defines = _variant_defines(srcs)
+    # slowest units first so the pool stays busy
+    order = sorted(srcs, key=lambda s: not os.path.basename(s).startswith("prefill_inst_"))
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, defines), order))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

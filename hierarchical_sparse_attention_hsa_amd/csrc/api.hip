@@ -1,0 +1,225 @@
+// C ABI of libhsa_attn: host-side validation, workspace sizing and dispatch.
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing.  No C++ exception crosses the ABI.
+#include <cstdarg>
+#include <cstdio>
+#include <exception>
+
+#include "../../include/hsa_attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+thread_local void** g_events = nullptr;
+thread_local int g_event_pairs = 0;
+thread_local int g_event_next = 0;
+
+void restart_timing() { g_event_next = 0; }
+
+hsa_attn_status_t fail(hsa_attn_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+hsa_attn_status_t ok() {
+  g_last_error[0] = '\0';
+  return HSA_ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+enum class Call { kLandmarks, kPrefill, kDecode };
+
+// Validates the dimension block and fills a Geometry.
+hsa_attn_status_t check_dims(const hsa_attn_dims_t* d, Call call, hsa_attn::Geometry* g) {
+  if (!d) return fail(HSA_ATTN_INVALID_ARGUMENT, "dims is NULL");
+  if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return fail(HSA_ATTN_INVALID_ARGUMENT, "batch and head counts must be >= 1");
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(HSA_ATTN_INVALID_ARGUMENT, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)", d->num_q_heads,
+                d->num_kv_heads);
+  if (d->head_dim < 1 || d->chunk_size < 1 || d->top_k < 1)
+    return fail(HSA_ATTN_INVALID_ARGUMENT, "head_dim, chunk_size and top_k must be >= 1");
+  if (d->seq_len < 0) return fail(HSA_ATTN_INVALID_ARGUMENT, "seq_len must be >= 0");
+  if (d->dtype != HSA_ATTN_FP32 && d->dtype != HSA_ATTN_BF16)
+    return fail(HSA_ATTN_INVALID_ARGUMENT, "unknown dtype %d", d->dtype);
+  if (d->reserved != 0) return fail(HSA_ATTN_INVALID_ARGUMENT, "reserved field must be 0");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(HSA_ATTN_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", d->head_dim);
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (call != Call::kLandmarks) {
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+      return fail(HSA_ATTN_UNSUPPORTED, "query heads per KV head %d unsupported (1, 2, 4, 8)", G);
+    if (d->chunk_size != 64) return fail(HSA_ATTN_UNSUPPORTED, "chunk_size %d unsupported (64)", d->chunk_size);
+    const int kmax = call == Call::kDecode ? 64 : 32;
+    if (d->top_k > kmax) return fail(HSA_ATTN_UNSUPPORTED, "top_k %d unsupported (<= %d)", d->top_k, kmax);
+  }
+  const int64_t Nc = d->seq_len / d->chunk_size;
+  if (call == Call::kPrefill) {
+    if (Nc > 65536) return fail(HSA_ATTN_UNSUPPORTED, "prefill supports at most 65536 chunks");
+    if ((d->seq_len + 63) / 64 * (int64_t)d->batch * d->num_kv_heads * 2 > 0x7fffffffLL)
+      return fail(HSA_ATTN_UNSUPPORTED, "prefill grid too large");
+  }
+  if (call == Call::kDecode && Nc > 0x7fffffffLL) return fail(HSA_ATTN_UNSUPPORTED, "cache too long");
+  g->B = d->batch;
+  g->Hq = d->num_q_heads;
+  g->Hkv = d->num_kv_heads;
+  g->G = G;
+  g->D = d->head_dim;
+  g->S = d->chunk_size;
+  g->k = d->top_k;
+  g->T = d->seq_len;
+  g->Nc = Nc;
+  g->bf16 = d->dtype == HSA_ATTN_BF16;
+  return HSA_ATTN_OK;
+}
+
+hsa_attn_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(HSA_ATTN_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+void hsa_attn::mark_launch(hipStream_t st) {
+  if (g_events && g_event_next < 2 * g_event_pairs) {
+    (void)hipEventRecord(static_cast<hipEvent_t>(g_events[g_event_next]), st);
+    ++g_event_next;
+  }
+}
+
+extern "C" {
+
+hsa_attn_status_t hsa_attn_set_timing_events(void** events, int n_pairs) {
+  if (n_pairs < 0) return fail(HSA_ATTN_INVALID_ARGUMENT, "n_pairs must be >= 0");
+  if (n_pairs > 0 && !events) return fail(HSA_ATTN_INVALID_ARGUMENT, "events is NULL");
+  g_events = n_pairs > 0 ? events : nullptr;
+  g_event_pairs = n_pairs;
+  g_event_next = 0;
+  return ok();
+}
+
+
+const char* hsa_attn_status_string(hsa_attn_status_t s) {
+  switch (s) {
+    case HSA_ATTN_OK: return "ok";
+    case HSA_ATTN_INVALID_ARGUMENT: return "invalid argument";
+    case HSA_ATTN_UNSUPPORTED: return "unsupported shape or type";
+    case HSA_ATTN_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case HSA_ATTN_HIP_ERROR: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* hsa_attn_last_error(void) { return g_last_error; }
+
+hsa_attn_status_t hsa_attn_workspace_size(const hsa_attn_dims_t* d, int is_decode, size_t* bytes) {
+  try {
+    if (!bytes) return fail(HSA_ATTN_INVALID_ARGUMENT, "bytes is NULL");
+    hsa_attn::Geometry g;
+    const hsa_attn_status_t st = check_dims(d, is_decode ? Call::kDecode : Call::kPrefill, &g);
+    if (st != HSA_ATTN_OK) return st;
+    // the size assumes the library keeps the selection itself (sel outputs NULL)
+    *bytes = is_decode ? hsa_attn::plan_decode(g, true).bytes : hsa_attn::plan_prefill(g, true).bytes;
+    return ok();
+  } catch (const std::exception& e) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error");
+  }
+}
+
+hsa_attn_status_t hsa_build_landmarks(const hsa_attn_dims_t* d, const void* k, void* landmarks, int64_t chunk_begin,
+                                      int64_t chunk_end, void* stream) {
+  try {
+    hsa_attn::Geometry g;
+    hsa_attn_status_t st = check_dims(d, Call::kLandmarks, &g);
+    if (st != HSA_ATTN_OK) return st;
+    if (chunk_begin < 0 || chunk_begin > chunk_end || chunk_end > g.Nc)
+      return fail(HSA_ATTN_INVALID_ARGUMENT, "chunk range [%lld, %lld) outside [0, %lld]", (long long)chunk_begin,
+                  (long long)chunk_end, (long long)g.Nc);
+    if (chunk_begin == chunk_end) return ok();  // nothing to build; pointers may be NULL
+    if (!k || !landmarks) return fail(HSA_ATTN_INVALID_ARGUMENT, "k and landmarks must be non-NULL");
+    if (!aligned16(k) || !aligned16(landmarks)) return fail(HSA_ATTN_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    restart_timing();
+    hsa_attn::LandmarkArgs a{k, landmarks, (int64_t)g.B * g.Hkv, g.T, g.Nc, chunk_begin, chunk_end, g.S, g.D, g.bf16};
+    return hip_status(hsa_attn::launch_landmarks(a, static_cast<hipStream_t>(stream)), "landmark launch");
+  } catch (const std::exception& e) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error");
+  }
+}
+
+hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, const void* k, const void* v,
+                                      const void* landmarks, float* out, int32_t* sel_idx, float* sel_score,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    hsa_attn::Geometry g;
+    hsa_attn_status_t st = check_dims(d, Call::kPrefill, &g);
+    if (st != HSA_ATTN_OK) return st;
+    if (!q || !k || !v || !out || (!landmarks && g.Nc > 0))
+      return fail(HSA_ATTN_INVALID_ARGUMENT, "q, k, v, landmarks and out must be non-NULL");
+    if ((sel_idx == nullptr) != (sel_score == nullptr))
+      return fail(HSA_ATTN_INVALID_ARGUMENT, "sel_idx and sel_score must both be given or both be NULL");
+    for (const void* p : {q, k, v, landmarks, (const void*)out, (const void*)sel_idx, (const void*)sel_score,
+                          (const void*)workspace})
+      if (p && !aligned16(p)) return fail(HSA_ATTN_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    const bool own = sel_idx == nullptr;
+    const hsa_attn::PrefillPlan plan = hsa_attn::plan_prefill(g, own);
+    if (workspace_bytes < plan.bytes)
+      return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes, workspace_bytes);
+    if (plan.bytes > 0 && !workspace) return fail(HSA_ATTN_INVALID_ARGUMENT, "workspace is NULL");
+    if (g.T == 0) return ok();
+    if (own) {
+      sel_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.off_sel_idx);
+      sel_score = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.off_sel_score);
+    }
+    restart_timing();
+    hsa_attn::PrefillArgs a{g, q, k, v, landmarks, out, sel_idx, sel_score};
+    return hip_status(hsa_attn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
+  } catch (const std::exception& e) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error");
+  }
+}
+
+hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, const void* k_cache,
+                                     const void* v_cache, const void* landmarks, float* out, int32_t* sel_idx,
+                                     float* sel_score, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    hsa_attn::Geometry g;
+    hsa_attn_status_t st = check_dims(d, Call::kDecode, &g);
+    if (st != HSA_ATTN_OK) return st;
+    if (!q || !out || (g.Nc > 0 && (!k_cache || !v_cache || !landmarks)))
+      return fail(HSA_ATTN_INVALID_ARGUMENT, "q, k_cache, v_cache, landmarks and out must be non-NULL");
+    if ((sel_idx == nullptr) != (sel_score == nullptr))
+      return fail(HSA_ATTN_INVALID_ARGUMENT, "sel_idx and sel_score must both be given or both be NULL");
+    for (const void* p : {q, k_cache, v_cache, landmarks, (const void*)out, (const void*)sel_idx,
+                          (const void*)sel_score, (const void*)workspace})
+      if (p && !aligned16(p)) return fail(HSA_ATTN_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    const bool own = sel_idx == nullptr;
+    const hsa_attn::DecodePlan plan = hsa_attn::plan_decode(g, own);
+    if (workspace_bytes < plan.bytes)
+      return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes, workspace_bytes);
+    if (!workspace) return fail(HSA_ATTN_INVALID_ARGUMENT, "workspace is NULL");
+    if (own) {
+      sel_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.off_sel_idx);
+      sel_score = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.off_sel_score);
+    }
+    restart_timing();
+    hsa_attn::DecodeArgs a{g, q, k_cache, v_cache, landmarks, out, sel_idx, sel_score, workspace};
+    return hip_status(hsa_attn::launch_decode(a, plan, static_cast<hipStream_t>(stream)), "decode launch");
+  } catch (const std::exception& e) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Host-side launch interfaces of the HSA kernels (internal to libhsa_attn).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hsa_attn {
+
+// Records the next caller-provided timing event on `st` when per-launch
+// timing is enabled on this thread (hsa_attn_set_timing_events); no-op otherwise.
+void mark_launch(hipStream_t st);
+
+struct LandmarkArgs {
+  const void* k;
+  void* lm;
+  int64_t bh;      // B * Hkv
+  int64_t T;       // tokens per (b, g) in k
+  int64_t Nc;      // landmark rows per (b, g)
+  int64_t c0, c1;  // chunk range to build
+  int S, D;
+  bool bf16;
+};
+hipError_t launch_landmarks(const LandmarkArgs& a, hipStream_t st);
+
+// Geometry shared by the forward passes.
+struct Geometry {
+  int B, Hq, Hkv, G, D, S, k;
+  int64_t T;    // prefill: sequence length; decode: cache length
+  int64_t Nc;   // floor(T / S)
+  bool bf16;
+};
+
+// ---------------------------------------------------------------- decode
+struct DecodePlan {
+  int splits;          // landmark-scan workgroups per (b, g)
+  int rows_per_split;  // landmarks per split (multiple of 64)
+  size_t off_cand, off_sel_idx, off_sel_score, off_partial, bytes;
+};
+DecodePlan plan_decode(const Geometry& g, bool own_sel);
+
+struct DecodeArgs {
+  Geometry g;
+  const void *q, *k, *v, *lm;
+  float* out;
+  int32_t* sel_idx;
+  float* sel_score;
+  void* ws;
+};
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t st);
+
+// ---------------------------------------------------------------- prefill
+struct PrefillPlan {
+  size_t off_sel_idx, off_sel_score, bytes;
+};
+PrefillPlan plan_prefill(const Geometry& g, bool own_sel);
+
+struct PrefillArgs {
+  Geometry g;
+  const void *q, *k, *v, *lm;
+  float* out;
+  int32_t* sel_idx;
+  float* sel_score;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+
+}  // namespace hsa_attn

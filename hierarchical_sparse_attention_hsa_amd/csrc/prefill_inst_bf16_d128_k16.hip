@@ -1,0 +1,7 @@
+// Instantiation of the prefill kernels for storage BF16, head dim 128,
+// top-k register list of 16 entries (all query-group sizes).
+#include "prefill_kernels.hpp"
+
+namespace hsa_attn {
+template hipError_t launch_prefill_g<BF16, 128, 16>(const PrefillArgs&, hipStream_t);
+}  // namespace hsa_attn

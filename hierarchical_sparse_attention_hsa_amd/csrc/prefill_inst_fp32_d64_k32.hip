@@ -1,0 +1,7 @@
+// Instantiation of the prefill kernels for storage FP32, head dim 64,
+// top-k register list of 32 entries (all query-group sizes).
+#include "prefill_kernels.hpp"
+
+namespace hsa_attn {
+template hipError_t launch_prefill_g<FP32, 64, 32>(const PrefillArgs&, hipStream_t);
+}  // namespace hsa_attn

@@ -1,0 +1,566 @@
+// HSA prefill: causal HSA over a whole sequence (skill card "Every Token
+// Counts 16m Context", sections "Core Technique" and "Implementation").
+//
+// Two kernels on one stream:
+//
+// prefill_select  one workgroup per (b, g, query chunk j), one wave per query
+//   head of the group, 64 query rows per wave.  Landmark tiles of 32 rows are
+//   staged in LDS (shared by the G waves) and contracted with the wave's
+//   queries on MFMA (bf16 in, fp32 accumulate): the causal-block GEMM
+//   Q . L^T restricted to the j earlier chunks.  Tiles run from the newest
+//   chunk to the oldest.  After every tile the two lane halves swap
+//   accumulator halves (v_permlane32_swap) so that each lane holds the 32
+//   scores of one query row; the lane keeps that row's top-k in registers
+//   (descending order, so a new candidate always has the lowest index so far
+//   and wins ties, which realises "ties toward the lower chunk index").  The
+//   score matrix never reaches memory.
+//
+// prefill_attn  one workgroup per (b, g, query chunk j, 32-token half), one
+//   wave per query head.  The union of the rows' selected chunks is walked in
+//   ascending order; each chunk's K and V tiles are staged in LDS once for all
+//   the workgroup's rows.  S^T = K_c Q^T on MFMA, an fp32 softmax per row,
+//   and O^T += V_c^T P'^T on MFMA, where P' is the in-chunk probability
+//   already multiplied by the row's fusion weight (softmax of its kept
+//   retrieval scores); rows that did not select the chunk have weight 0.
+//   P' is fed to the bf16 MFMA as a hi + lo pair so it keeps ~16 bits.
+#pragma once
+
+#include <climits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma.hpp"
+
+namespace hsa_attn {
+
+constexpr int kChunk = 64;
+
+template <typename T>
+__device__ __forceinline__ void load_frag_lds(Frag<T>& f, const char* row, int slot_xor, int kch, int half);
+
+// bf16: 8 elements of one half k-chunk = one 16-byte slot (2*kch + half)
+template <>
+__device__ __forceinline__ void load_frag_lds<BF16>(Frag<BF16>& f, const char* row, int slot_xor, int kch,
+                                                    int half) {
+  const int slot = (2 * kch + half) ^ slot_xor;
+  f.load16(row + slot * 16);
+}
+// fp32: 8 elements = two 16-byte slots (4*kch + 2*half, +1)
+template <>
+__device__ __forceinline__ void load_frag_lds<FP32>(Frag<FP32>& f, const char* row, int slot_xor, int kch,
+                                                    int half) {
+  const int s0 = (4 * kch + 2 * half) ^ slot_xor;
+  const int s1 = (4 * kch + 2 * half + 1) ^ slot_xor;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(row + s0 * 16);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(row + s1 * 16);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = a[e];
+    f.v[4 + e] = b[e];
+  }
+}
+
+// 8 consecutive elements of a global row (zero when !ok)
+__device__ __forceinline__ void load_frag_global(Frag<BF16>& f, const uint16_t* p, bool ok) {
+  const u32x4 z = ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u};
+  f.v = as_bf16x8(z);
+}
+__device__ __forceinline__ void load_frag_global(Frag<FP32>& f, const float* p, bool ok) {
+  const f32x4 z{0.f, 0.f, 0.f, 0.f};
+  const f32x4 a = ok ? reinterpret_cast<const f32x4*>(p)[0] : z;
+  const f32x4 b = ok ? reinterpret_cast<const f32x4*>(p)[1] : z;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = a[e];
+    f.v[4 + e] = b[e];
+  }
+}
+
+// Insert x (index xi) into a descending register list; the new element wins
+// ties (callers offer candidates in descending index order).
+template <int K>
+__device__ __forceinline__ void list_insert(float (&s)[K], int (&id)[K], float x, int xi) {
+  bool c[K];
+#pragma unroll
+  for (int p = 0; p < K; ++p) c[p] = x >= s[p];
+#pragma unroll
+  for (int p = K - 1; p >= 1; --p) {
+    id[p] = c[p - 1] ? id[p - 1] : (c[p] ? xi : id[p]);
+    s[p] = __builtin_amdgcn_fmed3f(s[p - 1], x, s[p]);
+  }
+  id[0] = c[0] ? xi : id[0];
+  s[0] = c[0] ? x : s[0];
+}
+
+// ---------------------------------------------------------------- select
+template <typename T, int D, int G, int KSEL>
+__global__ __launch_bounds__(kWave* G) void prefill_select_kernel(const typename T::storage* __restrict__ q,
+                                                                  const typename T::storage* __restrict__ lm,
+                                                                  int32_t* __restrict__ sel_idx,
+                                                                  float* __restrict__ sel_score, int B, int Hkv,
+                                                                  int64_t T_len, int64_t Nc, int nqc, int k,
+                                                                  float scale) {
+  using st = typename T::storage;
+  constexpr int NTH = kWave * G;
+  constexpr int EPS = 16 / T::kBytes;       // elements per 16-byte slot
+  constexpr int ROWB = D * T::kBytes;       // bytes per landmark row
+  constexpr int NSL = ROWB / 16;            // slots per row
+  constexpr int TILE_SLOTS = 32 * NSL;
+  constexpr int LPT = (TILE_SLOTS + NTH - 1) / NTH;
+  constexpr int KCH = D / 16;
+  __shared__ __align__(16) char tile[2][32 * ROWB];
+
+  const int bid = blockIdx.x;
+  const int g = bid % Hkv;
+  const int rest = bid / Hkv;
+  const int b = rest % B;
+  const int j = nqc - 1 - rest / B;  // heaviest query chunks first
+  const int tid = threadIdx.x, lane = tid & 63, hh = tid >> 6, half = lane >> 5;
+  const int Hq = Hkv * G, h = g * G + hh;
+  const int64_t n = min((int64_t)j, Nc);
+
+  float ls[KSEL];
+  int li[KSEL];
+#pragma unroll
+  for (int e = 0; e < KSEL; ++e) {
+    ls[e] = -__builtin_inff();
+    li[e] = INT_MAX;
+  }
+
+  if (n > 0) {
+    Frag<T> qf[2][KCH];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int64_t tok = (int64_t)j * kChunk + 32 * nb + (lane & 31);
+      const bool ok = tok < T_len;
+      const st* qp = q + (((int64_t)b * Hq + h) * T_len + (ok ? tok : 0)) * D + 8 * half;
+#pragma unroll
+      for (int s = 0; s < KCH; ++s) load_frag_global(qf[nb][s], qp + 16 * s, ok);
+    }
+    const st* lmg = lm + ((int64_t)b * Hkv + g) * Nc * D;
+    const int ntiles = (int)((n + 31) / 32);
+    u32x4 pre[LPT];
+    auto fetch = [&](int ti) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int slot = tid + i * NTH;
+        const int r = slot / NSL, sl = slot % NSL;
+        const int64_t c = (int64_t)ti * 32 + r;
+        pre[i] = (slot < TILE_SLOTS && c < n) ? *reinterpret_cast<const u32x4*>(lmg + c * D + sl * EPS)
+                                              : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int slot = tid + i * NTH;
+        if (slot < TILE_SLOTS) {
+          const int r = slot / NSL, sl = slot % NSL;
+          *reinterpret_cast<u32x4*>(tile[buf] + r * ROWB + ((sl ^ (r & 7)) * 16)) = pre[i];
+        }
+      }
+    };
+    fetch(ntiles - 1);
+    stash(0);
+    __syncthreads();
+    for (int ti = ntiles - 1, it = 0; ti >= 0; --ti, ++it) {
+      const int cur = it & 1;
+      if (ti > 0) fetch(ti - 1);
+      f32x16 acc0 = {}, acc1 = {};
+      const char* trow = tile[cur] + (lane & 31) * ROWB;
+#pragma unroll
+      for (int s = 0; s < KCH; ++s) {
+        Frag<T> a;
+        load_frag_lds<T>(a, trow, lane & 7, s, half);
+        mfma(acc0, a, qf[0][s]);
+        mfma(acc1, a, qf[1][s]);
+      }
+      // lane l now holds scores of tile rows tile_row(r, half) for query
+      // rows (l%32) and 32 + (l%32); swap halves so that lane l owns query
+      // row l: lo[r] -> tile row tile_row(r, 0), hi[r] -> tile_row(r, 1)
+      float lo[16], hi[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0[r]), __float_as_uint(acc1[r]),
+                                                        false, false);
+        lo[r] = __uint_as_float(p[0]);
+        hi[r] = __uint_as_float(p[1]);
+      }
+      const int cbase = ti * 32;
+      const bool top = (int64_t)cbase + 32 > n;
+      // Candidates come in 4 groups of 8 tile rows (group gg = rows
+      // 8gg..8gg+7 = lo/hi[4gg..4gg+3]).  A group is skipped when no lane's
+      // group maximum reaches that lane's threshold at the start of the tile
+      // (thresholds only grow, so such a group cannot contribute).
+      const float thr0 = ls[KSEL - 1];
+      uint32_t gmask = 0u;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const float m = fmaxf(fmaxf(fmaxf(lo[4 * gg], lo[4 * gg + 1]), fmaxf(lo[4 * gg + 2], lo[4 * gg + 3])),
+                              fmaxf(fmaxf(hi[4 * gg], hi[4 * gg + 1]), fmaxf(hi[4 * gg + 2], hi[4 * gg + 3])));
+        if (__ballot(m >= thr0)) gmask |= 1u << gg;
+      }
+#pragma unroll 1
+      for (int gg = 3; gg >= 0; --gg) {
+        if (!((gmask >> gg) & 1u)) continue;
+        // the group's 8 candidates in descending tile-row order 8gg+7 .. 8gg
+        float xs[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = (e < 4) ? 3 - e : 7 - e;  // register inside the group
+          const float a0 = (e < 4) ? hi[r] : lo[r];
+          const float a1 = (e < 4) ? hi[4 + r] : lo[4 + r];
+          const float a2 = (e < 4) ? hi[8 + r] : lo[8 + r];
+          const float a3 = (e < 4) ? hi[12 + r] : lo[12 + r];
+          xs[e] = gg == 0 ? a0 : (gg == 1 ? a1 : (gg == 2 ? a2 : a3));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ii = 8 * gg + 7 - e;
+          bool pass = xs[e] >= ls[KSEL - 1];
+          if (top) pass = pass && (int64_t)(cbase + ii) < n;
+          if (pass) list_insert<KSEL>(ls, li, xs[e], cbase + ii);
+        }
+      }
+      if (ti > 0) stash(cur ^ 1);
+      __syncthreads();
+    }
+  }
+  const int64_t t_row = (int64_t)j * kChunk + lane;
+  if (t_row < T_len) {
+    const int64_t base = (((int64_t)b * Hq + h) * T_len + t_row) * k;
+#pragma unroll
+    for (int e = 0; e < KSEL; ++e) {
+      if (e < k) {
+        const bool ok = li[e] != INT_MAX;
+        sel_idx[base + e] = ok ? li[e] : -1;
+        sel_score[base + e] = ok ? ls[e] * scale + 0.0f : -__builtin_inff();
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- attention
+struct AttnLds {
+  // byte offsets inside the dynamic LDS block
+  int k_off, vt_off, tab_off, bm_off, bytes;
+};
+
+template <typename T, int D, int G>
+__host__ __device__ constexpr int attn_fixed_bytes() {
+  return 2 * kChunk * D * T::kBytes;  // K tile + V^T tile
+}
+
+// V^T element position of token t inside the 64-token row of column d, in
+// the order the P' fragments present tokens: k-step t/16, lane half
+// (t%8)/4, element 4*((t%16)/8) + t%4.
+__device__ __forceinline__ int vt_pos(int t) {
+  return (t / 16) * 16 + ((t % 8) / 4) * 8 + 4 * ((t % 16) / 8) + (t % 4);
+}
+
+template <typename T, int D, int G, int KSEL>
+__global__ __launch_bounds__(kWave* G) void prefill_attn_kernel(
+    const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ kk,
+    const typename T::storage* __restrict__ vv, const int32_t* __restrict__ sel_idx,
+    const float* __restrict__ sel_score, float* __restrict__ out, int B, int Hkv, int64_t T_len, int64_t Nc,
+    int nqc, int k, float scale) {
+  using st = typename T::storage;
+  constexpr int NTH = kWave * G;
+  constexpr int EPS = 16 / T::kBytes;
+  constexpr int ROWB = D * T::kBytes;        // bytes per K row
+  constexpr int NSL = ROWB / 16;             // slots per K row
+  constexpr int KV_SLOTS = kChunk * NSL;     // slots per K (or V) tile
+  constexpr int LPT = KV_SLOTS / NTH;        // slots per thread per tile
+  constexpr int VTB = kChunk * T::kBytes;    // bytes per V^T row (one column d)
+  constexpr int KCH = D / 16;
+  constexpr int DM = D / 32;
+  static_assert(KV_SLOTS % NTH == 0, "tile slots must divide evenly");
+  extern __shared__ __align__(16) char smem[];
+  char* ks = smem;
+  char* vt = smem + kChunk * ROWB;
+  int2* tab = reinterpret_cast<int2*>(smem + 2 * kChunk * ROWB);  // [32*G rows][k]
+  uint32_t* bm = reinterpret_cast<uint32_t*>(tab + 32 * G * k);
+
+  const int bid = blockIdx.x;
+  const int g = bid % Hkv;
+  int rest = bid / Hkv;
+  const int b = rest % B;
+  rest /= B;
+  const int hc = rest & 1;
+  const int j = nqc - 1 - (rest >> 1);
+  const int tid = threadIdx.x, lane = tid & 63, hh = tid >> 6, half = lane >> 5;
+  const int Hq = Hkv * G, h = g * G + hh;
+  const int64_t n = min((int64_t)j, Nc);
+  const int nwords = (int)((n + 31) / 32);
+  const int row = hh * 32 + (lane & 31);                       // row inside the workgroup
+  const int64_t tok = (int64_t)j * kChunk + 32 * hc + (lane & 31);
+  const bool tok_ok = tok < T_len;
+
+  for (int i = tid; i < nwords; i += NTH) bm[i] = 0u;
+  __syncthreads();
+
+  // ---- per-row table: selected chunks ascending with their fusion weights
+  int m = 0;
+  if (lane < 32 && tok_ok && n > 0) {
+    const int64_t base = (((int64_t)b * Hq + h) * T_len + tok) * k;
+    int ci[KSEL];
+    float sc[KSEL];
+#pragma unroll
+    for (int e = 0; e < KSEL; ++e) {
+      ci[e] = (e < k) ? sel_idx[base + e] : -1;
+      sc[e] = (e < k && ci[e] >= 0) ? sel_score[base + e] : -__builtin_inff();
+      m += ci[e] >= 0;
+    }
+    const float smax = sc[0];
+    float w[KSEL], den = 0.0f;
+#pragma unroll
+    for (int e = 0; e < KSEL; ++e) {
+      w[e] = ci[e] >= 0 ? expf(sc[e] - smax) : 0.0f;
+      den += w[e];
+    }
+    const float inv = 1.0f / den;
+#pragma unroll
+    for (int e = 0; e < KSEL; ++e) {
+      if (ci[e] >= 0) {
+        int rank = 0;
+#pragma unroll
+        for (int f = 0; f < KSEL; ++f) rank += (ci[f] >= 0 && ci[f] < ci[e]);
+        tab[row * k + rank] = make_int2(ci[e], __float_as_int(w[e] * inv));
+        atomicOr(&bm[ci[e] >> 5], 1u << (ci[e] & 31));
+      }
+    }
+  }
+  m = __shfl(m, lane & 31);  // the partner lane of the row learns the count
+  __syncthreads();
+
+  // ---- queries as the B operand (rows = tokens of this half chunk)
+  Frag<T> qf[KCH];
+  {
+    const st* qp = q + (((int64_t)b * Hq + h) * T_len + (tok_ok ? tok : 0)) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < KCH; ++s) load_frag_global(qf[s], qp + 16 * s, tok_ok);
+  }
+  f32x16 oacc[DM];
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
+
+  // walk the union of selected chunks in ascending order
+  int word = 0;
+  uint32_t bits = nwords > 0 ? bm[0] : 0u;
+  auto next_chunk = [&]() -> int {
+    while (bits == 0u) {
+      if (++word >= nwords) return -1;
+      bits = bm[word];
+    }
+    const int c = word * 32 + __builtin_ctz(bits);
+    bits &= bits - 1u;
+    return c;
+  };
+  const st* kg = kk + ((int64_t)b * Hkv + g) * T_len * D;
+  const st* vg = vv + ((int64_t)b * Hkv + g) * T_len * D;
+  // K/V staging: NP slots of each tile per thread per pass; with a single
+  // pass the next chunk's tiles are fetched into registers while the current
+  // one is computed.
+  constexpr int NP = LPT < 4 ? LPT : 4;
+  constexpr int PASSES = LPT / NP;
+  static_assert(LPT % NP == 0, "staging passes must divide evenly");
+  u32x4 kpre[NP], vpre[NP];
+  auto fetch = [&](int c, int pass) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int slot = tid + (pass * NP + i) * NTH;
+      const int64_t off = ((int64_t)c * kChunk + slot / NSL) * D + (slot % NSL) * EPS;
+      kpre[i] = *reinterpret_cast<const u32x4*>(kg + off);
+      vpre[i] = *reinterpret_cast<const u32x4*>(vg + off);
+    }
+  };
+  auto stash = [&](int pass) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int slot = tid + (pass * NP + i) * NTH;
+      const int t = slot / NSL, sl = slot % NSL;
+      *reinterpret_cast<u32x4*>(ks + t * ROWB + ((sl ^ (t & 7)) * 16)) = kpre[i];
+      const int p = vt_pos(t);
+      if constexpr (T::kBytes == 2) {
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) {
+          const int d = sl * EPS + e;
+          const int pp = (((p / 8) ^ (d & 7)) * 8) + (p % 8);
+          const uint32_t w32 = vpre[i][e / 2];
+          reinterpret_cast<uint16_t*>(vt + d * VTB)[pp] = (uint16_t)((e & 1) ? (w32 >> 16) : (w32 & 0xffffu));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) {
+          const int d = sl * EPS + e;
+          const int pp = (((p / 4) ^ (d & 7)) * 4) + (p % 4);
+          reinterpret_cast<uint32_t*>(vt + d * VTB)[pp] = vpre[i][e];
+        }
+      }
+    }
+  };
+
+  const float cexp = scale * 1.4426950408889634f;  // softmax in base 2
+  int ptr = 0;
+  int c = next_chunk();
+  if (PASSES == 1 && c >= 0) fetch(c, 0);
+  while (c >= 0) {
+    __syncthreads();  // everyone is done with the previous tile
+    if constexpr (PASSES == 1) {
+      stash(0);
+    } else {
+#pragma unroll 1
+      for (int ps = 0; ps < PASSES; ++ps) {
+        fetch(c, ps);
+        stash(ps);
+      }
+    }
+    __syncthreads();
+    const int cn = next_chunk();
+    if (PASSES == 1 && cn >= 0) fetch(cn, 0);
+    float wgt = 0.0f;
+    bool mine = false;
+    if (ptr < m) {
+      const int2 e = tab[row * k + ptr];
+      mine = e.x == c;
+      if (mine) {
+        wgt = __int_as_float(e.y);
+        ++ptr;
+      }
+    }
+    if (__ballot(mine)) {
+      // S^T = K_c Q^T: two 32-token blocks
+      f32x16 s0 = {}, s1 = {};
+      const char* k0 = ks + (lane & 31) * ROWB;
+      const char* k1 = ks + (32 + (lane & 31)) * ROWB;
+#pragma unroll
+      for (int s = 0; s < KCH; ++s) {
+        Frag<T> a0, a1;
+        load_frag_lds<T>(a0, k0, lane & 7, s, half);
+        load_frag_lds<T>(a1, k1, lane & 7, s, half);
+        mfma(s0, a0, qf[s]);
+        mfma(s1, a1, qf[s]);
+      }
+      // softmax over the 64 tokens of row (lane & 31); lane l and l^32 split them
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float sum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = __builtin_amdgcn_exp2f((s0[r] - mx) * cexp);
+        s1[r] = __builtin_amdgcn_exp2f((s1[r] - mx) * cexp);
+        sum += s0[r] + s1[r];
+      }
+      sum += __shfl_xor(sum, 32);
+      const float f = wgt / sum;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] *= f;
+        s1[r] *= f;
+      }
+      // O^T += V^T P'^T over four 16-token k-steps
+#pragma unroll
+      for (int ks_ = 0; ks_ < 4; ++ks_) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = (ks_ < 2) ? s0[8 * (ks_ & 1) + e] : s1[8 * (ks_ & 1) + e];
+        if constexpr (T::kBytes == 2) {
+          Frag<BF16> phi, plo;
+          phi.from_f32(pv);
+          float rem[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rem[e] = pv[e] - static_cast<float>(phi.v[e]);
+          plo.from_f32(rem);
+#pragma unroll
+          for (int dm = 0; dm < DM; ++dm) {
+            Frag<BF16> a;
+            const int d = 32 * dm + (lane & 31);
+            const int slot = (2 * ks_ + half) ^ (d & 7);
+            a.load16(vt + d * VTB + slot * 16);
+            mfma(oacc[dm], a, phi);
+            mfma(oacc[dm], a, plo);
+          }
+        } else {
+          Frag<FP32> pf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf.v[e] = pv[e];
+#pragma unroll
+          for (int dm = 0; dm < DM; ++dm) {
+            Frag<FP32> a;
+            const int d = 32 * dm + (lane & 31);
+            const int s0i = (4 * ks_ + 2 * half) ^ (d & 7);
+            const int s1i = (4 * ks_ + 2 * half + 1) ^ (d & 7);
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(vt + d * VTB + s0i * 16);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(vt + d * VTB + s1i * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a.v[e] = x0[e];
+              a.v[4 + e] = x1[e];
+            }
+            mfma(oacc[dm], a, pf);
+          }
+        }
+      }
+    }
+    c = cn;
+  }
+  if (tok_ok) {
+    float* op = out + (((int64_t)b * Hq + h) * T_len + tok) * D;
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * dm + 8 * q4 + 4 * half;
+        f32x4 o{oacc[dm][4 * q4], oacc[dm][4 * q4 + 1], oacc[dm][4 * q4 + 2], oacc[dm][4 * q4 + 3]};
+        *reinterpret_cast<f32x4*>(op + d0) = o;
+      }
+    }
+  }
+}
+
+size_t prefill_attn_lds_bytes(const Geometry& g);
+
+template <typename T, int D, int G, int KSEL>
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
+  const Geometry& g = a.g;
+  using stg = typename T::storage;
+  const int nqc = (int)((g.T + kChunk - 1) / kChunk);
+  const float scale = 1.0f / sqrtf((float)D);
+  const unsigned blocks = (unsigned)((int64_t)nqc * g.B * g.Hkv);
+  mark_launch(st);
+  hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(blocks), dim3(kWave * G), 0, st,
+                     static_cast<const stg*>(a.q), static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, g.B,
+                     g.Hkv, g.T, g.Nc, nqc, g.k, scale);
+  mark_launch(st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = prefill_attn_lds_bytes(g);
+  auto kern = prefill_attn_kernel<T, D, G, KSEL>;
+  if (lds > 65536) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  mark_launch(st);
+  hipLaunchKernelGGL(kern, dim3(2 * blocks), dim3(kWave * G), lds, st, static_cast<const stg*>(a.q),
+                     static_cast<const stg*>(a.k), static_cast<const stg*>(a.v), a.sel_idx, a.sel_score, a.out,
+                     g.B, g.Hkv, g.T, g.Nc, nqc, g.k, scale);
+  mark_launch(st);
+  return hipGetLastError();
+}
+
+// Dispatch over the query-group size; instantiated once per (dtype, D, list
+// size) in its own translation unit so the build parallelises.
+template <typename T, int D, int KSEL>
+hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t st) {
+  switch (a.g.G) {
+    case 1: return launch_prefill_t<T, D, 1, KSEL>(a, st);
+    case 2: return launch_prefill_t<T, D, 2, KSEL>(a, st);
+    case 4: return launch_prefill_t<T, D, 4, KSEL>(a, st);
+    default: return launch_prefill_t<T, D, 8, KSEL>(a, st);
+  }
+}
+
+}  // namespace hsa_attn

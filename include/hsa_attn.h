@@ -1,0 +1,147 @@
+/*
+ * hsa_attn.h -- C ABI of the Hierarchical Sparse Attention (HSA) forward layer
+ * for AMD MI355X (gfx950).  Library: libhsa_attn.so.
+ *
+ * What the layer computes (skill card "Every Token Counts 16m Context",
+ * sections "Core Technique" and "Implementation"; abstract page "Every Token
+ * Counts: Generalizing 16M Ultra-Long Context in Large Language Models"):
+ * the keys are cut into chunks of S tokens, every chunk gets a landmark (the
+ * mean of its keys), each query scores the landmarks of the complete chunks
+ * before its own chunk with q.L/sqrt(D), keeps the k best (ties to the lower
+ * chunk index), runs softmax attention inside every kept chunk, and fuses the
+ * per-chunk outputs with a softmax over the kept scores.  A query with no
+ * earlier complete chunk outputs zeros.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensors are dense, contiguous and head-major:
+ *      prefill  Q [B, Hq, T, D]      K, V [B, Hkv, T, D]
+ *      decode   Q [B, Hq, D]         K, V [B, Hkv, T, D]  (the caches)
+ *      landmarks  [B, Hkv, floor(T/S), D]   (same storage dtype as K)
+ *      out      fp32, shaped like Q
+ *      sel_idx  int32 [..., k]  (-1 padding)   sel_score fp32 [..., k] (-inf padding)
+ *    Query head h reads KV head floor(h * Hkv / Hq).
+ *  - Q, K, V and landmarks are stored as bf16 or fp32 (hsa_attn_dims_t.dtype);
+ *    arithmetic accumulates in fp32 (landmark sums in fp64); out is fp32.
+ *  - Every pointer is a device pointer, owned by the caller, 16-byte aligned.
+ *    The library allocates no memory and keeps no state between calls.
+ *  - Calls are asynchronous: they validate on the host, enqueue kernels on
+ *    `stream` (a hipStream_t; NULL means the default stream) and return.
+ *    HSA_ATTN_OK means "enqueued".  Validation happens before any HIP call,
+ *    so a rejected call enqueues nothing.
+ *  - Inputs must be finite; NaN or Inf inputs give undefined results.
+ *  - Errors: HSA_ATTN_INVALID_ARGUMENT (null or misaligned pointer, bad
+ *    sizes), HSA_ATTN_UNSUPPORTED (sizes outside the supported envelope:
+ *    D in {64,128}, S == 64 for the forward calls, Hq/Hkv in {1,2,4,8},
+ *    k <= 64 for decode and k <= 32 for prefill), HSA_ATTN_WORKSPACE_TOO_SMALL,
+ *    HSA_ATTN_HIP_ERROR (a launch failed).  hsa_attn_last_error() returns a
+ *    thread-local message about the last failure.
+ */
+#ifndef HSA_ATTN_H_
+#define HSA_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSA_ATTN_OK = 0,
+  HSA_ATTN_INVALID_ARGUMENT = 1,
+  HSA_ATTN_UNSUPPORTED = 2,
+  HSA_ATTN_WORKSPACE_TOO_SMALL = 3,
+  HSA_ATTN_HIP_ERROR = 4
+} hsa_attn_status_t;
+
+typedef enum { HSA_ATTN_FP32 = 0, HSA_ATTN_BF16 = 1 } hsa_attn_dtype_t;
+
+typedef struct {
+  int32_t batch;        /* B */
+  int32_t num_q_heads;  /* Hq */
+  int32_t num_kv_heads; /* Hkv, divides Hq */
+  int32_t head_dim;     /* D */
+  int32_t chunk_size;   /* S */
+  int32_t top_k;        /* k */
+  int64_t seq_len;      /* prefill: T (queries = keys); decode: cache length T,
+                           the query sits at position T */
+  int32_t dtype;        /* hsa_attn_dtype_t: storage of Q, K, V, landmarks */
+  int32_t reserved;     /* must be 0 */
+} hsa_attn_dims_t;
+
+/*
+ * Landmark builder (card, "Implementation": a landmark per chunk from mean
+ * pooling of the chunk's tokens; read as the plain mean of the keys).
+ *
+ * For every (b, g) and every chunk c in [chunk_begin, chunk_end):
+ *   landmarks[b, g, c, :] = round_to_dtype( (sum_{t=cS}^{cS+S-1} K[b, g, t, :]) / S )
+ * The sum is exact (fp64), the division is one fp64 operation and the result
+ * is rounded once, to nearest even, to the storage dtype.  For bf16 keys the
+ * result is bit-identical to the exact mean rounded to bf16.
+ * k: K or K cache [B, Hkv, T, D]; landmarks: [B, Hkv, floor(T/S), D].
+ * Requires 0 <= chunk_begin <= chunk_end <= floor(T/S) and S >= 1; only D in
+ * {64, 128} is supported.  chunk_begin == chunk_end enqueues nothing (and then
+ * k and landmarks may be NULL).
+ */
+hsa_attn_status_t hsa_build_landmarks(const hsa_attn_dims_t* d, const void* k, void* landmarks,
+                                      int64_t chunk_begin, int64_t chunk_end, void* stream);
+
+/*
+ * Causal HSA forward over a whole sequence (card, "Core Technique" and
+ * "Implementation").  Query row p of head h uses the complete chunks
+ * c < min(floor(p/S), floor(T/S)) of KV head g(h).
+ * q [B,Hq,T,D], k/v [B,Hkv,T,D], landmarks [B,Hkv,floor(T/S),D] (from
+ * hsa_build_landmarks), out [B,Hq,T,D] fp32.  sel_idx / sel_score
+ * [B,Hq,T,k] are optional outputs (NULL: kept in the workspace); slots are
+ * ordered by score descending, then index ascending.
+ * workspace: device scratch of at least hsa_attn_workspace_size(d, 0) bytes
+ * (may be NULL when that size is 0).
+ */
+hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, const void* k,
+                                      const void* v, const void* landmarks, float* out,
+                                      int32_t* sel_idx, float* sel_score, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
+ * HSA forward for B independent single-token queries, each after its own
+ * cache of T tokens (card, "Core Technique": scoring is O(n/S) per query and
+ * attention O(k*S)).  The query sits at position T, so its candidates are
+ * all floor(T/S) complete chunks of its cache.
+ * q [B,Hq,D], k_cache/v_cache [B,Hkv,T,D], landmarks [B,Hkv,floor(T/S),D],
+ * out [B,Hq,D] fp32, sel_idx/sel_score [B,Hq,k] optional (NULL allowed).
+ * workspace: at least hsa_attn_workspace_size(d, 1) bytes.
+ */
+hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, const void* k_cache,
+                                     const void* v_cache, const void* landmarks, float* out,
+                                     int32_t* sel_idx, float* sel_score, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
+ * Diagnostics: per-launch timing.  After this call, every subsequent
+ * hsa_build_landmarks / hsa_forward_prefill / hsa_forward_decode call made on
+ * the calling thread records events[2*i] (hipEvent_t, created by the caller)
+ * on its stream just before its i-th kernel launch and events[2*i+1] just
+ * after it, for i < n_pairs; the index restarts at 0 with each call.
+ * Launch order: landmarks: 1 kernel; prefill: select, attention; decode:
+ * scan, merge, attention, fusion (scan and attention are skipped when the
+ * cache has no complete chunk).  events == NULL or n_pairs == 0 turns
+ * recording off.  The setting is thread-local; the events stay owned by the
+ * caller and must outlive the calls that record them.
+ */
+hsa_attn_status_t hsa_attn_set_timing_events(void** events, int n_pairs);
+
+/* Bytes of device workspace a forward call needs (is_decode: 0 prefill, 1 decode). */
+hsa_attn_status_t hsa_attn_workspace_size(const hsa_attn_dims_t* d, int is_decode, size_t* bytes);
+
+/* Static description of a status code. */
+const char* hsa_attn_status_string(hsa_attn_status_t status);
+
+/* Thread-local detail about the last failed call on this thread ("" if none). */
+const char* hsa_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSA_ATTN_H_ */

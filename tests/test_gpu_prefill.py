@@ -1,0 +1,87 @@
+"""GPU parity of hsa_forward_prefill against the oracle, through the C-ABI
+binding: selected chunk indices exact except near ties, outputs within
+2e-3 (bf16) / 1e-5 (fp32) max-abs.  Covers several tiles, ragged tails, all
+supported query-group sizes and both top-k list sizes."""
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_hsa_amd as hsa
+from hierarchical_sparse_attention_hsa_amd.workloads import small_inputs
+from oracle import hsa_oracle as O
+from tests.gpu_util import TOL, check_rows, f64, new_stats
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(q, k, v, S, topk):
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    B, Hkv, T, D = k.shape
+    L = torch.empty((B, Hkv, T // S, D), dtype=k.dtype, device="cuda")
+    hsa.hsa_build_landmarks(kd, L, S)
+    Hq = q.shape[1]
+    sel = torch.full((B, Hq, T, topk), -7, dtype=torch.int32, device="cuda")
+    score = torch.full((B, Hq, T, topk), 7.0, dtype=torch.float32, device="cuda")
+    out = torch.full((B, Hq, T, D), 3.0, dtype=torch.float32, device="cuda")
+    hsa.hsa_forward_prefill(qd, kd, vd, L, S, topk, out=out, sel_idx=sel, sel_score=score)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy(), sel.cpu().numpy(), score.cpu().double().numpy()
+
+
+def compare(q, k, v, S, topk, dtype, out, sel, score, rows=None):
+    Q, K, V = f64(q), f64(k), f64(v)
+    B, Hq, T, D = Q.shape
+    Hkv = K.shape[1]
+    L = O.landmarks(K, S, dtype)
+    pos = np.arange(T) if rows is None else np.asarray(rows)
+    stats = new_stats()
+    for b in range(B):
+        for h in range(Hq):
+            g = O.kv_head_of(h, Hq, Hkv)
+            check_rows(Q[b, h, pos], pos, K[b, g], V[b, g], L[b, g], S, topk, out[b, h, pos], sel[b, h, pos],
+                       score[b, h, pos], TOL[dtype], stats)
+    return stats
+
+
+CASES = [
+    # B, Hq, Hkv, T, D, k, dtype
+    (1, 4, 1, 64 * 12 + 30, 128, 4, "bf16"),
+    (1, 8, 2, 64 * 40, 128, 16, "bf16"),
+    (2, 2, 2, 64 * 20 + 1, 64, 8, "fp32"),
+    (1, 2, 1, 64 * 70 + 40, 128, 32, "bf16"),    # G = 2, k = 32
+    (1, 8, 1, 64 * 18, 64, 16, "bf16"),          # G = 8
+    (1, 4, 4, 64 * 33 + 63, 64, 8, "fp32"),      # cfg1-like: G = 1
+    (1, 4, 1, 50, 128, 4, "bf16"),               # no complete chunk
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_prefill_matches_oracle(case):
+    B, Hq, Hkv, T, D, topk, dtype = case
+    print(f"prefill case {case}", flush=True)
+    q, k, v = small_inputs(B, Hq, Hkv, T, D, dtype, seed=hash(case) % 10000)
+    out, sel, score = run_prefill(q, k, v, 64, topk)
+    stats = compare(q, k, v, 64, topk, dtype, out, sel, score)
+    print(stats)
+
+
+def test_prefill_row_equals_decode():
+    q, k, v = small_inputs(1, 8, 2, 64 * 30, 128, "bf16", seed=21)
+    out, sel, score = run_prefill(q, k, v, 64, 8)
+    for p in (64, 65, 64 * 7 + 3, 64 * 29 + 63):
+        qd = q[:, :, p].contiguous()
+        kd, vd = k[:, :, :p].contiguous(), v[:, :, :p].contiguous()
+        L = torch.empty((1, 2, p // 64, 128), dtype=torch.bfloat16, device="cuda")
+        hsa.hsa_build_landmarks(kd.cuda(), L, 64)
+        o2 = hsa.hsa_forward_decode(qd.cuda(), kd.cuda(), vd.cuda(), L, 64, 8)
+        torch.cuda.synchronize()
+        # both paths are checked against the oracle; here they must agree closely too
+        np.testing.assert_allclose(o2.cpu().double().numpy(), out[:, :, p], atol=2e-3)
+
+
+def test_prefill_is_deterministic():
+    q, k, v = small_inputs(1, 8, 2, 64 * 50 + 9, 128, "bf16", seed=22)
+    a = run_prefill(q, k, v, 64, 16)
+    b = run_prefill(q, k, v, 64, 16)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
