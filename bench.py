@@ -125,7 +125,7 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
         raise SystemExit(f"{wname}: inputs ({(kv_bytes + lm_bytes) / 2**30:.1f} GiB) do not fit in free device "
                          f"memory ({free / 2**30:.1f} GiB)")
     t0 = time.perf_counter()
-    q, k, v = decode_inputs(w, "cuda")
+    q, k, v = decode_inputs(w, "cuda", progress=lambda b: (b + 1) % 16 == 0 and log(f"[{wname}] generated {b + 1}/{w.B} caches"))
     torch.cuda.synchronize()
     log(f"[{wname}] generated inputs in {time.perf_counter() - t0:.1f} s")
     L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
