@@ -107,6 +107,16 @@ __device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
   return sa > sb || (sa == sb && ia < ib);
 }
 
+// Wave-uniform broadcast of lane `src` (src must be uniform).
+__device__ __forceinline__ float bcast_f(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+__device__ __forceinline__ int bcast_i(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+
+// Whole-wave shift by one lane toward higher lanes (DPP wave_shr:1); lane 0
+// keeps its own value.
+__device__ __forceinline__ int wave_shr1(int v) { return __builtin_amdgcn_update_dpp(v, v, 0x138, 0xf, 0xf, false); }
+
 // A wave-resident sorted list of up to 64 candidates: lane i holds the i-th
 // best.  Empty slots hold (-inf, INT_MAX).
 struct WaveTopK {
@@ -124,15 +134,21 @@ struct WaveTopK {
     const uint64_t m = __ballot(keep) & ((k >= 64) ? ~0ull : ((1ull << k) - 1));
     const int pos = __popcll(m);
     if (pos >= k) return;
-    const float ps = __shfl_up(s, 1);
-    const int pi = __shfl_up(i, 1);
-    if (lane > pos) { s = ps; i = pi; }
-    if (lane == pos) { s = cs; i = ci; }
+    const float ps = __int_as_float(wave_shr1(__float_as_int(s)));
+    const int pi = wave_shr1(i);
+    if (lane > pos) {
+      s = ps;
+      i = pi;
+    }
+    if (lane == pos) {
+      s = cs;
+      i = ci;
+    }
   }
   // Current k-th best (the admission threshold), wave-uniform.
   __device__ __forceinline__ void kth(int k, float& ts, int& ti) const {
-    ts = __shfl(s, k - 1);
-    ti = __shfl(i, k - 1);
+    ts = bcast_f(s, k - 1);
+    ti = bcast_i(i, k - 1);
   }
 };
 
@@ -146,8 +162,8 @@ __device__ __forceinline__ void offer_wave(WaveTopK& list, int k, float cs, int 
   while (m) {
     const int src = __builtin_ctzll(m);
     m &= m - 1;
-    const float s = __shfl(cs, src);
-    const int i = __shfl(ci, src);
+    const float s = bcast_f(cs, src);
+    const int i = bcast_i(ci, src);
     list.kth(k, ts, ti);
     if (better(s, i, ts, ti)) list.insert(s, i, k);
   }

@@ -18,11 +18,27 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mfma.hpp"
 
 namespace hsa_attn {
 
+// Tuning knobs of the landmark scan (compile-time; defaults are the measured
+// best on MI355X): loads in flight per lane, register double-buffering,
+// largest landmark range per workgroup, non-temporal loads.
+#ifndef HSA_ATTN_SCAN_UNROLL
+#define HSA_ATTN_SCAN_UNROLL 8
+#endif
+#ifndef HSA_ATTN_SCAN_PREFETCH
+#define HSA_ATTN_SCAN_PREFETCH 0
+#endif
+#ifndef HSA_ATTN_SCAN_MAX_ROWS
+#define HSA_ATTN_SCAN_MAX_ROWS 1024
+#endif
+#ifndef HSA_ATTN_SCAN_NT
+#define HSA_ATTN_SCAN_NT 1
+#endif
 constexpr int kScanThreads = 256;
-constexpr int kScanUnroll = 4;
+constexpr int kScanUnroll = HSA_ATTN_SCAN_UNROLL;
 
 // dot product of a 16-byte slice of a bf16 landmark row with the matching
 // slice of a bf16 query (both as packed pairs), fp32 accumulation
@@ -66,14 +82,25 @@ __global__ __launch_bounds__(kScanThreads) void decode_scan_kernel(const typenam
     qv[h] = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * Hkv * G + (int64_t)g * G + h) * D + col);
 
   const typename T::storage* base = lm + (((int64_t)b * Hkv + g) * Nc + r_begin) * D + col;
-  for (int it = 0; it < n; it += ROWS_PER_ITER) {
-    u32x4 v[kScanUnroll];
+  // with HSA_ATTN_SCAN_PREFETCH the next iteration's rows are in flight while
+  // the current ones are scored (register double buffer)
+  u32x4 nxt[kScanUnroll];
+  auto fetch = [&](int it) {
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
       const int r = it + (wave * kScanUnroll + u) * RPI + lane / LPR;
-      if (r < n) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)r * D));
-      else v[u] = u32x4{0u, 0u, 0u, 0u};
+      const u32x4* src = reinterpret_cast<const u32x4*>(base + (int64_t)r * D);
+      if (r < n) nxt[u] = HSA_ATTN_SCAN_NT ? __builtin_nontemporal_load(src) : *src;
+      else nxt[u] = u32x4{0u, 0u, 0u, 0u};
     }
+  };
+  if (HSA_ATTN_SCAN_PREFETCH) fetch(0);
+  for (int it = 0; it < n; it += ROWS_PER_ITER) {
+    if (!HSA_ATTN_SCAN_PREFETCH) fetch(it);
+    u32x4 v[kScanUnroll];
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) v[u] = nxt[u];
+    if (HSA_ATTN_SCAN_PREFETCH && it + ROWS_PER_ITER < n) fetch(it + ROWS_PER_ITER);
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
       const int r = it + (wave * kScanUnroll + u) * RPI + lane / LPR;
@@ -105,23 +132,35 @@ __global__ __launch_bounds__(kScanThreads) void decode_scan_kernel(const typenam
 }
 
 // ---------------------------------------------------------------- 2. merge
-__global__ __launch_bounds__(kWave) void decode_merge_kernel(const float2* __restrict__ cand,
-                                                             int32_t* __restrict__ sel_idx,
-                                                             float* __restrict__ sel_score, int Hq, int Hkv,
-                                                             int G, int splits, int k) {
-  const int bh = blockIdx.x;
-  const int b = bh / Hq, h = bh % Hq, g = h / G, hh = h % G;
-  const int lane = __lane_id();
+// One workgroup per (b, g), one wave per query head of the group: merge the
+// split candidates of the head into its global top-k (total order: score
+// desc, index asc), then list the group's distinct selected chunks once,
+// each with the slot it holds in every head's selection (0xff = not
+// selected).  The list order is deterministic (first occurrence in head-major
+// slot order).
+template <int G>
+__global__ __launch_bounds__(kWave* G) void decode_merge_kernel(const float2* __restrict__ cand,
+                                                                int32_t* __restrict__ sel_idx,
+                                                                float* __restrict__ sel_score,
+                                                                int4* __restrict__ ulist, int* __restrict__ ucount,
+                                                                int Hkv, int splits, int k) {
+  __shared__ int ls[G * 64];
+  __shared__ int wave_cnt[G];
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int lane = __lane_id(), hh = threadIdx.x / kWave;
+  const int64_t bh = (int64_t)b * Hkv * G + (int64_t)g * G + hh;
   WaveTopK list;
   list.init();
   const int total = splits * k;
+  // rank-major order: every split's best first, so the list fills with
+  // strong candidates early and later ranks rarely get in
   for (int i0 = 0; i0 < total; i0 += kWave) {
     const int j = i0 + lane;
     bool valid = j < total;
     float s = -__builtin_inff();
     int ci = INT_MAX;
     if (valid) {
-      const int sp = j / k, e = j % k;
+      const int e = j / splits, sp = j % splits;
       const float2 c = cand[((((int64_t)b * Hkv + g) * splits + sp) * G + hh) * k + e];
       s = c.x;
       ci = __float_as_int(c.y);
@@ -129,120 +168,194 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(const float2* __res
     }
     offer_wave(list, k, s, ci, valid);
   }
+  const bool ok = list.i != INT_MAX;
   if (lane < k) {
-    const bool ok = list.i != INT_MAX;
-    sel_idx[(int64_t)bh * k + lane] = ok ? list.i : -1;
-    sel_score[(int64_t)bh * k + lane] = ok ? list.s : -__builtin_inff();
+    sel_idx[bh * k + lane] = ok ? list.i : -1;
+    sel_score[bh * k + lane] = ok ? list.s : -__builtin_inff();
+    ls[hh * k + lane] = ok ? list.i : -1;
+  }
+  __syncthreads();
+  // entry e = hh * k + lane owns its chunk when no earlier entry names it;
+  // every entry of the group is compared through uniform LDS reads
+  const int e = hh * k + lane;
+  const int c = lane < k ? ls[e] : -1;
+  bool owner = c >= 0;
+  uint32_t slots[2] = {0xffffffffu, 0xffffffffu};
+  for (int h2 = 0; h2 < G; ++h2) {
+    for (int s2 = 0; s2 < k; ++s2) {
+      const int f = h2 * k + s2;
+      if (ls[f] == c) {
+        if (f < e) owner = false;
+        slots[h2 / 4] = (slots[h2 / 4] & ~(0xffu << (8 * (h2 % 4)))) | ((uint32_t)s2 << (8 * (h2 % 4)));
+      }
+    }
+  }
+  const uint64_t om = __ballot(owner);
+  if (lane == 0) wave_cnt[hh] = __popcll(om);
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < hh; ++w) base += wave_cnt[w];
+  if (owner) {
+    const int pos = base + __popcll(om & ((1ull << lane) - 1));
+    ulist[((int64_t)b * Hkv + g) * (G * k) + pos] = make_int4(c, (int)slots[0], (int)slots[1], 0);
+  }
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int w = 0; w < G; ++w) n += wave_cnt[w];
+    ucount[(int64_t)b * Hkv + g] = n;
   }
 }
 
 // ---------------------------------------------------------------- 3. chunk attention
-// One workgroup per (b, g, j) where j enumerates the G*k (head, slot) pairs of
-// the group; the pair that first names a chunk owns it, so every distinct
-// selected chunk of the group is read from HBM once.
+// One wave per distinct selected chunk of a (b, g) group; waves are
+// independent (no LDS, no barriers).  Logits of all G heads on MFMA:
+// S^T[token][head] = K_c . q_head (A = the chunk's keys, B = the group's
+// queries padded to 32 columns); each head's softmax stays in the two lanes
+// that hold its column.  P.V on the VALU: lane l owns key rows l/LPR + RPI*i
+// and a 16-byte column slice; the probabilities reach it by v_readlane from
+// the owning lanes; a cross-lane sum finishes each output column.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void decode_attn_kernel(const typename T::storage* __restrict__ q,
                                                           const typename T::storage* __restrict__ kc,
                                                           const typename T::storage* __restrict__ vc,
-                                                          const int32_t* __restrict__ sel_idx,
+                                                          const int4* __restrict__ ulist,
+                                                          const int* __restrict__ ucount,
                                                           float* __restrict__ partial, int Hkv, int64_t T_len,
                                                           int k, float scale) {
-  constexpr int S = 64;                 // tokens per chunk (4 threads per token)
-  constexpr int EPT = D / 4;            // key elements per thread
-  constexpr int LOADS = EPT * T::kBytes / 16;
-  constexpr int NT = 256 / D;           // threads per output column in P.V
-  constexpr int TPT = S / NT;           // tokens per thread in P.V
   using st = typename T::storage;
-  __shared__ int sel[G * 64];
-  __shared__ int slot_of[G];
-  __shared__ float qs[G][D];
-  __shared__ float red[256];
-  __shared__ st vs[S * D];
+  constexpr int S = 64;
+  constexpr int KCH = D / 16;
+  constexpr int EPS = 16 / T::kBytes;          // elements per 16-byte slice
+  constexpr int LPR = D / EPS;                 // lanes per V row
+  constexpr int RPI = kWave / LPR;             // V rows per load instruction
+  constexpr int VL = S / RPI;                  // V loads per lane (whole tile)
+  constexpr int VPASS = VL > 16 ? 2 : 1;       // fp32 D=128 loads V in two passes
+  constexpr int VLP = VL / VPASS;
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int lane = __lane_id(), wave = threadIdx.x / kWave;
+  const int e = blockIdx.x * 4 + wave;
+  const int64_t grp = (int64_t)b * Hkv + g;
+  if (e >= ucount[grp]) return;
+  const int4 ent = ulist[grp * (G * k) + e];
+  const int c = ent.x;
+  const uint32_t slots[2] = {(uint32_t)ent.y, (uint32_t)ent.z};
+  const int half = lane >> 5;
+  const st* ktile = kc + (grp * T_len + (int64_t)c * S) * D;
+  const st* vtile = vc + (grp * T_len + (int64_t)c * S) * D;
 
-  const int b = blockIdx.z, g = blockIdx.y, j = blockIdx.x;
-  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-  const int Hq = Hkv * G;
-  for (int i = tid; i < G * k; i += 256) sel[i] = sel_idx[((int64_t)b * Hq + (int64_t)g * G + i / k) * k + i % k];
-  __syncthreads();
-  const int c = sel[j];
-  if (c < 0) return;
-  bool dup = false;
-  for (int i = tid; i < j; i += 256) dup |= sel[i] == c;
-  if (__syncthreads_or(dup)) return;
+  // queries of the group as the B operand: column j = head (lane % 32 < G)
+  Frag<T> qf[KCH];
+  {
+    const int j = lane & 31;
+    const bool okq = j < G;
+    const st* qp = q + (grp * G + (okq ? j : 0)) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < KCH; ++s) load_frag_global(qf[s], qp + 16 * s, okq);
+  }
+  // every load of the tile is issued before any use: keys as A operands of
+  // both 32-token blocks, and the first pass of V slices (lane owns rows
+  // RPI*i + lane/LPR, elements (lane%LPR)*EPS..)
+  Frag<T> ka[2][KCH];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const st* kp = ktile + (int64_t)(32 * tb + (lane & 31)) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < KCH; ++s) load_frag_global(ka[tb][s], kp + 16 * s, true);
+  }
+  u32x4 vr[VLP];
+  const int vcol = (lane % LPR) * EPS;
+  const int vrow0 = lane / LPR;
+#pragma unroll
+  for (int i = 0; i < VLP; ++i)
+    vr[i] = *reinterpret_cast<const u32x4*>(vtile + (int64_t)(RPI * i + vrow0) * D + vcol);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int s = 0; s < KCH; ++s) mfma(sacc[tb], ka[tb][s], qf[s]);
 
-  // K slice of this thread into registers, V tile into LDS, queries into LDS
-  const int t = tid / 4, qd = tid % 4;
-  const int64_t tile = (((int64_t)b * Hkv + g) * T_len + (int64_t)c * S) * D;
-  u32x4 kr[LOADS];
+  // softmax per head column: lane l (l%32 = head) holds tokens
+  // 32*tb + tile_row(r, half); its partner l^32 holds the rest
+  float mx = -__builtin_inff();
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i)
-    kr[i] = *reinterpret_cast<const u32x4*>(kc + tile + (int64_t)t * D + qd * EPT + i * (16 / T::kBytes));
-  for (int i = tid; i < S * D * T::kBytes / 16; i += 256)
-    reinterpret_cast<u32x4*>(vs)[i] = reinterpret_cast<const u32x4*>(vc + tile)[i];
-  for (int i = tid; i < G * D; i += 256) {
-    const st x = q[((int64_t)b * Hq + (int64_t)g * G) * D + i];
-    if constexpr (T::kBytes == 2) qs[i / D][i % D] = __uint_as_float((uint32_t)x << 16);
-    else qs[i / D][i % D] = x;
-  }
-  if (wave < G && lane < k) {
-    const uint64_t m = __ballot(sel[wave * k + lane] == c);
-    if (lane == 0) slot_of[wave] = m ? __builtin_ctzll(m) : -1;
-  }
-  for (int hh = 4 + wave; hh < G; hh += 4) {  // G == 8: waves cover two heads each
-    const uint64_t m = __ballot(lane < k && sel[hh * k + lane] == c);
-    if (lane == 0) slot_of[hh] = m ? __builtin_ctzll(m) : -1;
-  }
-  __syncthreads();
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[tb][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float cexp = scale * 1.4426950408889634f;
+  float den = 0.0f;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sacc[tb][r] = exp2f((sacc[tb][r] - mx) * cexp);
+      den += sacc[tb][r];
+    }
+  den += __shfl_xor(den, 32);
+  const float inv = 1.0f / den;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[tb][r] *= inv;
 
-  for (int hh = 0; hh < G; ++hh) {
-    const int slot = slot_of[hh];
-    if (slot < 0) continue;
-    // logits: 4 threads per token
-    float acc = 0.0f;
+  float o[G][EPS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
+  for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int e = qd * EPT + i * (16 / T::kBytes);
+    for (int x = 0; x < EPS; ++x) o[hh][x] = 0.0f;
+#pragma unroll
+  for (int ps = 0; ps < VPASS; ++ps) {
+    if (ps > 0) {
+#pragma unroll
+      for (int i = 0; i < VLP; ++i)
+        vr[i] = *reinterpret_cast<const u32x4*>(vtile + (int64_t)(RPI * (ps * VLP + i) + vrow0) * D + vcol);
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const uint32_t sl = (slots[hh / 4] >> (8 * (hh % 4))) & 0xffu;
+      if (sl == 0xffu) continue;  // this head did not select the chunk (wave-uniform)
+#pragma unroll
+      for (int i = 0; i < VLP; ++i) {
+        // probability of the token this lane holds in load i
+        float p = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < RPI; ++jj) {
+          const int t = RPI * (ps * VLP + i) + jj;
+          const int tb = t / 32, tt = t % 32;
+          const int src_lane = hh + 32 * ((tt / 4) % 2);
+          const int r = 4 * (tt / 8) + (tt % 4);
+          const float pt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sacc[tb][r]), src_lane));
+          p = (vrow0 == jj) ? pt : p;
+        }
         if constexpr (T::kBytes == 2) {
-          acc = fmaf(bf16_lo(kr[i][w]), qs[hh][e + 2 * w], acc);
-          acc = fmaf(bf16_hi(kr[i][w]), qs[hh][e + 2 * w + 1], acc);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            o[hh][2 * w] = fmaf(p, bf16_lo(vr[i][w]), o[hh][2 * w]);
+            o[hh][2 * w + 1] = fmaf(p, bf16_hi(vr[i][w]), o[hh][2 * w + 1]);
+          }
         } else {
-          acc = fmaf(__uint_as_float(kr[i][w]), qs[hh][e + w], acc);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) o[hh][w] = fmaf(p, __uint_as_float(vr[i][w]), o[hh][w]);
         }
       }
     }
-    acc = group_sum<4>(acc) * scale;
-    if (qd == 0) red[t] = acc;
-    __syncthreads();
-    // softmax over the 64 tokens, computed redundantly by every wave (lane = token)
-    const float l = red[lane];
-    const float mx = group_max<64>(l);
-    const float p = __expf(l - mx);
-    const float den = group_sum<64>(p);
-    const float pn = p / den;
-    __syncthreads();  // red[] is reused below
-    // P.V: thread -> output column d, token range
-    const int d = tid % D, tr = tid / D;
-    float o = 0.0f;
+  }
+  // sum over the RPI row groups (lanes that share lane % LPR), then write
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int tok = tr * TPT + i;
-      const float pt = __shfl(pn, tok);
-      float vv;
-      if constexpr (T::kBytes == 2) vv = __uint_as_float((uint32_t)vs[tok * D + d] << 16);
-      else vv = vs[tok * D + d];
-      o = fmaf(pt, vv, o);
-    }
-    red[tid] = o;
-    __syncthreads();
-    if (tid < D) {
-      float sum = 0.0f;
+  for (int hh = 0; hh < G; ++hh) {
+    const uint32_t sl = (slots[hh / 4] >> (8 * (hh % 4))) & 0xffu;
+    if (sl == 0xffu) continue;
 #pragma unroll
-      for (int r = 0; r < NT; ++r) sum += red[r * D + tid];
-      partial[(((int64_t)b * Hq + (int64_t)g * G + hh) * k + slot) * D + tid] = sum;
+    for (int x = 0; x < EPS; ++x)
+#pragma unroll
+      for (int off = LPR; off < kWave; off <<= 1) o[hh][x] += __shfl_xor(o[hh][x], off);
+    if (lane < LPR) {
+      float* dst = partial + ((grp * G + hh) * k + sl) * D + vcol;
+#pragma unroll
+      for (int x = 0; x < EPS; x += 4)
+        *reinterpret_cast<f32x4*>(dst + x) = f32x4{o[hh][x], o[hh][x + 1], o[hh][x + 2], o[hh][x + 3]};
     }
-    __syncthreads();
   }
 }
 
@@ -268,9 +381,11 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 DecodePlan plan_decode(const Geometry& g, bool own_sel) {
   DecodePlan p{};
   const int64_t bh = (int64_t)g.B * g.Hkv;
-  int64_t rows = (g.Nc * bh + 2047) / 2048;
+  // aim for ~8K scan workgroups in total (many rounds over the 256 CUs keep the
+  // tail short), 256..1024 landmark rows each
+  int64_t rows = (g.Nc * bh + 8191) / 8192;
   rows = (rows + 63) / 64 * 64;
-  rows = rows < 256 ? 256 : (rows > 2048 ? 2048 : rows);
+  rows = rows < 256 ? 256 : (rows > HSA_ATTN_SCAN_MAX_ROWS ? HSA_ATTN_SCAN_MAX_ROWS : rows);
   p.rows_per_split = (int)rows;
   p.splits = g.Nc > 0 ? (int)((g.Nc + rows - 1) / rows) : 0;
   size_t off = 0;
@@ -285,6 +400,10 @@ DecodePlan plan_decode(const Geometry& g, bool own_sel) {
   }
   p.off_partial = off;
   off = align_up(off + rows_q * g.k * g.D * sizeof(float), 256);
+  p.off_ulist = off;
+  off = align_up(off + (size_t)bh * g.G * g.k * sizeof(int4), 256);
+  p.off_ucount = off;
+  off = align_up(off + (size_t)bh * sizeof(int), 256);
   p.bytes = off;
   return p;
 }
@@ -295,6 +414,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipS
   char* ws = static_cast<char*>(a.ws);
   float2* cand = reinterpret_cast<float2*>(ws + p.off_cand);
   float* partial = reinterpret_cast<float*>(ws + p.off_partial);
+  int4* ulist = reinterpret_cast<int4*>(ws + p.off_ulist);
+  int* ucount = reinterpret_cast<int*>(ws + p.off_ucount);
   const float scale = 1.0f / sqrtf((float)D);
   using stg = typename T::storage;
   if (p.splits > 0) {
@@ -306,14 +427,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipS
     mark_launch(st);
   }
   mark_launch(st);
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(g.B * g.Hq), dim3(kWave), 0, st, cand, a.sel_idx, a.sel_score,
-                     g.Hq, g.Hkv, G, p.splits, g.k);
+  hipLaunchKernelGGL((decode_merge_kernel<G>), dim3(g.Hkv, g.B), dim3(kWave * G), 0, st, cand, a.sel_idx,
+                     a.sel_score, ulist, ucount, g.Hkv, p.splits, g.k);
   mark_launch(st);
   if (p.splits > 0) {
     mark_launch(st);
-    hipLaunchKernelGGL((decode_attn_kernel<T, D, G>), dim3(G * g.k, g.Hkv, g.B), dim3(256), 0, st,
+    hipLaunchKernelGGL((decode_attn_kernel<T, D, G>), dim3((G * g.k + 3) / 4, g.Hkv, g.B), dim3(256), 0, st,
                        static_cast<const stg*>(a.q), static_cast<const stg*>(a.k), static_cast<const stg*>(a.v),
-                       a.sel_idx, partial, g.Hkv, g.T, g.k, scale);
+                       ulist, ucount, partial, g.Hkv, g.T, g.k, scale);
     mark_launch(st);
   }
   mark_launch(st);

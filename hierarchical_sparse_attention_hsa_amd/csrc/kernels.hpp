@@ -35,7 +35,7 @@ struct Geometry {
 struct DecodePlan {
   int splits;          // landmark-scan workgroups per (b, g)
   int rows_per_split;  // landmarks per split (multiple of 64)
-  size_t off_cand, off_sel_idx, off_sel_score, off_partial, bytes;
+  size_t off_cand, off_sel_idx, off_sel_score, off_partial, off_ulist, off_ucount, bytes;
 };
 DecodePlan plan_decode(const Geometry& g, bool own_sel);
 

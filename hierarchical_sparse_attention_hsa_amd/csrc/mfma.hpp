@@ -44,6 +44,22 @@ __device__ __forceinline__ void mfma(f32x16& acc, const Frag<FP32>& a, const Fra
   for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[e], b.v[e], acc, 0, 0, 0);
 }
 
+// 8 consecutive elements of a global row (zero when !ok)
+__device__ __forceinline__ void load_frag_global(Frag<BF16>& f, const uint16_t* p, bool ok) {
+  const u32x4 z = ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u};
+  f.v = as_bf16x8(z);
+}
+__device__ __forceinline__ void load_frag_global(Frag<FP32>& f, const float* p, bool ok) {
+  const f32x4 z{0.f, 0.f, 0.f, 0.f};
+  const f32x4 a = ok ? reinterpret_cast<const f32x4*>(p)[0] : z;
+  const f32x4 b = ok ? reinterpret_cast<const f32x4*>(p)[1] : z;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = a[e];
+    f.v[4 + e] = b[e];
+  }
+}
+
 // C-tile row of accumulator register r for a lane in half h (= lane / 32).
 __device__ __forceinline__ constexpr int tile_row(int r, int h) { return 8 * (r / 4) + 4 * h + (r % 4); }
 

@@ -60,22 +60,6 @@ __device__ __forceinline__ void load_frag_lds<FP32>(Frag<FP32>& f, const char* r
   }
 }
 
-// 8 consecutive elements of a global row (zero when !ok)
-__device__ __forceinline__ void load_frag_global(Frag<BF16>& f, const uint16_t* p, bool ok) {
-  const u32x4 z = ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u};
-  f.v = as_bf16x8(z);
-}
-__device__ __forceinline__ void load_frag_global(Frag<FP32>& f, const float* p, bool ok) {
-  const f32x4 z{0.f, 0.f, 0.f, 0.f};
-  const f32x4 a = ok ? reinterpret_cast<const f32x4*>(p)[0] : z;
-  const f32x4 b = ok ? reinterpret_cast<const f32x4*>(p)[1] : z;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f.v[e] = a[e];
-    f.v[4 + e] = b[e];
-  }
-}
-
 // Insert x (index xi) into a descending register list; the new element wins
 // ties (callers offer candidates in descending index order).
 template <int K>
