@@ -76,88 +76,127 @@ __device__ __forceinline__ void list_insert(float (&s)[K], int (&id)[K], float x
   s[0] = c[0] ? x : s[0];
 }
 
+// Insert x into a descending list of scores (ties are equal values, so no
+// index is needed): one v_med3 per position.
+template <int K>
+__device__ __forceinline__ void score_insert(float (&s)[K], float x) {
+#pragma unroll
+  for (int p = K - 1; p >= 1; --p) s[p] = __builtin_amdgcn_fmed3f(s[p - 1], x, s[p]);
+  s[0] = fmaxf(s[0], x);
+}
+
 // ---------------------------------------------------------------- select
 template <typename T, int D, int G, int KSEL>
-__global__ __launch_bounds__(kWave* G) void prefill_select_kernel(const typename T::storage* __restrict__ q,
+__global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(const typename T::storage* __restrict__ q,
                                                                   const typename T::storage* __restrict__ lm,
                                                                   int32_t* __restrict__ sel_idx,
                                                                   float* __restrict__ sel_score, int B, int Hkv,
                                                                   int64_t T_len, int64_t Nc, int nqc, int k,
                                                                   float scale) {
   using st = typename T::storage;
-  constexpr int NTH = kWave * G;
-  constexpr int EPS = 16 / T::kBytes;       // elements per 16-byte slot
-  constexpr int ROWB = D * T::kBytes;       // bytes per landmark row
-  constexpr int NSL = ROWB / 16;            // slots per row
-  constexpr int TILE_SLOTS = 32 * NSL;
-  constexpr int LPT = (TILE_SLOTS + NTH - 1) / NTH;
+  constexpr int HPW = G < 4 ? G : 4;        // query heads (waves) per workgroup
+  constexpr int HS = G / HPW;               // workgroups per (b, g, query chunk)
   constexpr int KCH = D / 16;
-  __shared__ __align__(16) char tile[2][32 * ROWB];
+  // per-lane buffer of admitted candidates, layout [wave][entry][lane] so that
+  // a wave's accesses are consecutive words; room for the kept top set (a
+  // compaction leaves at most KSEL entries) plus two groups of 8 new ones
+  constexpr int CAP = KSEL + 16;
+  __shared__ float2 cbuf[HPW][CAP][kWave];
 
   const int bid = blockIdx.x;
-  const int g = bid % Hkv;
-  const int rest = bid / Hkv;
+  const int g = bid % Hkv;  // consecutive workgroups on different XCDs share nothing
+  int rest = bid / Hkv;
+  const int hs = rest % HS;
+  rest /= HS;
   const int b = rest % B;
   const int j = nqc - 1 - rest / B;  // heaviest query chunks first
   const int tid = threadIdx.x, lane = tid & 63, hh = tid >> 6, half = lane >> 5;
-  const int Hq = Hkv * G, h = g * G + hh;
+  const int Hq = Hkv * G, h = g * G + hs * HPW + hh;
   const int64_t n = min((int64_t)j, Nc);
 
+  // Per lane (= query row): ls holds the KSEL best scores seen so far in
+  // descending order (seeded with -FLT_MAX so that a masked -inf candidate
+  // never passes) and is updated at once on every admission; the LDS buffer
+  // keeps (score, index) of every admitted candidate.  Candidates are offered
+  // in descending chunk index, so among equal scores the later entry has the
+  // lower index and wins.  When a buffer could overflow it is compacted to
+  // the exact current top set.
   float ls[KSEL];
-  int li[KSEL];
 #pragma unroll
-  for (int e = 0; e < KSEL; ++e) {
-    ls[e] = -__builtin_inff();
-    li[e] = INT_MAX;
-  }
-
+  for (int e = 0; e < KSEL; ++e) ls[e] = -3.402823466e38f;
+  int cnt = 0;
+  auto wave_max = [&](int v) {
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
+    return __builtin_amdgcn_readfirstlane(v);  // the same in every lane
+  };
+  auto compact = [&]() {
+    const int mx = wave_max(cnt);
+    const float tau = ls[KSEL - 1];
+    int gt = 0, eq = 0;
+    for (int e = 0; e < mx; ++e) {
+      if (e < cnt) {
+        const float x = cbuf[hh][e][lane].x;
+        gt += x > tau;
+        eq += x == tau;
+      }
+    }
+    // of the entries equal to the threshold only the latest (lowest index)
+    // ones fit next to the gt strictly better ones
+    const int skip_eq = max(0, eq - (KSEL - gt));
+    int w = 0, seen_eq = 0;
+    for (int e = 0; e < mx; ++e) {
+      if (e < cnt) {
+        const float2 c = cbuf[hh][e][lane];
+        bool keep = c.x > tau;
+        if (c.x == tau) {
+          keep = seen_eq >= skip_eq;
+          ++seen_eq;
+        }
+        if (keep) {
+          cbuf[hh][w][lane] = c;
+          ++w;
+        }
+      }
+    }
+    cnt = w;
+  };
   if (n > 0) {
+    // Contraction index assignment (shared by both operands): in k-step s,
+    // lane half h supplies dims D/2*h + 8*s .. +8, so each lane reads one
+    // contiguous run of its row.
+    constexpr int HALF_D = D / 2;
     Frag<T> qf[2][KCH];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int64_t tok = (int64_t)j * kChunk + 32 * nb + (lane & 31);
       const bool ok = tok < T_len;
-      const st* qp = q + (((int64_t)b * Hq + h) * T_len + (ok ? tok : 0)) * D + 8 * half;
+      const st* qp = q + (((int64_t)b * Hq + h) * T_len + (ok ? tok : 0)) * D + HALF_D * half;
 #pragma unroll
-      for (int s = 0; s < KCH; ++s) load_frag_global(qf[nb][s], qp + 16 * s, ok);
+      for (int s = 0; s < KCH; ++s) load_frag_global(qf[nb][s], qp + 8 * s, ok);
     }
-    const st* lmg = lm + ((int64_t)b * Hkv + g) * Nc * D;
+    const st* lmg = lm + ((int64_t)b * Hkv + g) * Nc * D + HALF_D * half;
     const int ntiles = (int)((n + 31) / 32);
-    u32x4 pre[LPT];
+    // each wave streams its own landmark fragments (A operand) from L2, one
+    // tile ahead; waves never wait for each other
+    Frag<T> an[KCH];
     auto fetch = [&](int ti) {
+      const int64_t c = (int64_t)ti * 32 + (lane & 31);
+      const bool ok = c < n;
+      const st* p = lmg + (ok ? c : 0) * D;
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) {
-        const int slot = tid + i * NTH;
-        const int r = slot / NSL, sl = slot % NSL;
-        const int64_t c = (int64_t)ti * 32 + r;
-        pre[i] = (slot < TILE_SLOTS && c < n) ? *reinterpret_cast<const u32x4*>(lmg + c * D + sl * EPS)
-                                              : u32x4{0u, 0u, 0u, 0u};
-      }
-    };
-    auto stash = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < LPT; ++i) {
-        const int slot = tid + i * NTH;
-        if (slot < TILE_SLOTS) {
-          const int r = slot / NSL, sl = slot % NSL;
-          *reinterpret_cast<u32x4*>(tile[buf] + r * ROWB + ((sl ^ (r & 7)) * 16)) = pre[i];
-        }
-      }
+      for (int s = 0; s < KCH; ++s) load_frag_global(an[s], p + 8 * s, ok);
     };
     fetch(ntiles - 1);
-    stash(0);
-    __syncthreads();
-    for (int ti = ntiles - 1, it = 0; ti >= 0; --ti, ++it) {
-      const int cur = it & 1;
+    for (int ti = ntiles - 1; ti >= 0; --ti) {
+      Frag<T> a[KCH];
+#pragma unroll
+      for (int s = 0; s < KCH; ++s) a[s] = an[s];
       if (ti > 0) fetch(ti - 1);
       f32x16 acc0 = {}, acc1 = {};
-      const char* trow = tile[cur] + (lane & 31) * ROWB;
 #pragma unroll
       for (int s = 0; s < KCH; ++s) {
-        Frag<T> a;
-        load_frag_lds<T>(a, trow, lane & 7, s, half);
-        mfma(acc0, a, qf[0][s]);
-        mfma(acc1, a, qf[1][s]);
+        mfma(acc0, a[s], qf[0][s]);
+        mfma(acc1, a[s], qf[1][s]);
       }
       // lane l now holds scores of tile rows tile_row(r, half) for query
       // rows (l%32) and 32 + (l%32); swap halves so that lane l owns query
@@ -171,54 +210,62 @@ __global__ __launch_bounds__(kWave* G) void prefill_select_kernel(const typename
         hi[r] = __uint_as_float(p[1]);
       }
       const int cbase = ti * 32;
-      const bool top = (int64_t)cbase + 32 > n;
-      // Candidates come in 4 groups of 8 tile rows (group gg = rows
-      // 8gg..8gg+7 = lo/hi[4gg..4gg+3]).  A group is skipped when no lane's
-      // group maximum reaches that lane's threshold at the start of the tile
-      // (thresholds only grow, so such a group cannot contribute).
-      const float thr0 = ls[KSEL - 1];
-      uint32_t gmask = 0u;
+      if ((int64_t)cbase + 32 > n) {
+        // rows of the top tile past the candidate range can never be chosen
+        const int nv = (int)(n - cbase);
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const float m = fmaxf(fmaxf(fmaxf(lo[4 * gg], lo[4 * gg + 1]), fmaxf(lo[4 * gg + 2], lo[4 * gg + 3])),
-                              fmaxf(fmaxf(hi[4 * gg], hi[4 * gg + 1]), fmaxf(hi[4 * gg + 2], hi[4 * gg + 3])));
-        if (__ballot(m >= thr0)) gmask |= 1u << gg;
-      }
-#pragma unroll 1
-      for (int gg = 3; gg >= 0; --gg) {
-        if (!((gmask >> gg) & 1u)) continue;
-        // the group's 8 candidates in descending tile-row order 8gg+7 .. 8gg
-        float xs[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = (e < 4) ? 3 - e : 7 - e;  // register inside the group
-          const float a0 = (e < 4) ? hi[r] : lo[r];
-          const float a1 = (e < 4) ? hi[4 + r] : lo[4 + r];
-          const float a2 = (e < 4) ? hi[8 + r] : lo[8 + r];
-          const float a3 = (e < 4) ? hi[12 + r] : lo[12 + r];
-          xs[e] = gg == 0 ? a0 : (gg == 1 ? a1 : (gg == 2 ? a2 : a3));
+        for (int r = 0; r < 16; ++r) {
+          if (tile_row(r, 0) >= nv) lo[r] = -__builtin_inff();
+          if (tile_row(r, 1) >= nv) hi[r] = -__builtin_inff();
         }
+      }
+      // Offer the tile's 32 candidates in descending index order: an
+      // admitted candidate updates the score list and is appended to the
+      // lane's buffer (exec-masked, so lanes pay only for their own events).
+#pragma unroll
+      for (int gg = 3; gg >= 0; --gg) {
+        if (__ballot(cnt > CAP - 8)) compact();
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int ii = 8 * gg + 7 - e;
-          bool pass = xs[e] >= ls[KSEL - 1];
-          if (top) pass = pass && (int64_t)(cbase + ii) < n;
-          if (pass) list_insert<KSEL>(ls, li, xs[e], cbase + ii);
+          const int r = (ii / 8) * 4 + (ii % 4);
+          const float x = ((ii / 4) & 1) ? hi[r] : lo[r];
+          if (x >= ls[KSEL - 1]) {
+            score_insert<KSEL>(ls, x);
+            cbuf[hh][cnt][lane] = make_float2(x, __int_as_float(cbase + ii));
+            ++cnt;
+          }
         }
       }
-      if (ti > 0) stash(cur ^ 1);
-      __syncthreads();
     }
+    compact();
   }
   const int64_t t_row = (int64_t)j * kChunk + lane;
+  // order the final top set by (score desc, index asc)
+  float os[KSEL];
+  int oi[KSEL];
+#pragma unroll
+  for (int e = 0; e < KSEL; ++e) {
+    os[e] = -__builtin_inff();
+    oi[e] = INT_MAX;
+  }
+  {
+    const int mx = wave_max(cnt);
+    for (int e = 0; e < mx; ++e) {
+      if (e < cnt) {
+        const float2 c = cbuf[hh][e][lane];
+        list_insert<KSEL>(os, oi, c.x, __float_as_int(c.y));
+      }
+    }
+  }
   if (t_row < T_len) {
     const int64_t base = (((int64_t)b * Hq + h) * T_len + t_row) * k;
 #pragma unroll
     for (int e = 0; e < KSEL; ++e) {
       if (e < k) {
-        const bool ok = li[e] != INT_MAX;
-        sel_idx[base + e] = ok ? li[e] : -1;
-        sel_score[base + e] = ok ? ls[e] * scale + 0.0f : -__builtin_inff();
+        const bool ok = oi[e] != INT_MAX;
+        sel_idx[base + e] = ok ? oi[e] : -1;
+        sel_score[base + e] = ok ? os[e] * scale + 0.0f : -__builtin_inff();
       }
     }
   }
@@ -514,7 +561,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)D);
   const unsigned blocks = (unsigned)((int64_t)nqc * g.B * g.Hkv);
   mark_launch(st);
-  hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(blocks), dim3(kWave * G), 0, st,
+  constexpr int HPW = G < 4 ? G : 4;
+  hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(blocks * (G / HPW)), dim3(kWave * HPW), 0, st,
                      static_cast<const stg*>(a.q), static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, g.B,
                      g.Hkv, g.T, g.Nc, nqc, g.k, scale);
   mark_launch(st);
