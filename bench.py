@@ -97,6 +97,25 @@ def timed_steps(step, steps, warmup, n_launch, events):
     return t1 - t0, per / steps
 
 
+def profiled_traffic(workload, kernel_prefix):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    record (profiles/<workload>.traffic.json: FETCH_SIZE and WRITE_SIZE scaled
+    by a 1 GiB copy), or None when the kernel sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = b"".join(open(os.path.join(ROOT, "hierarchical_sparse_attention_hsa_amd", f), "rb").read()
+                   for f in rec["sources"])
+    if hashlib.sha256(src).hexdigest()[:16] != rec["source_sha256_16"]:
+        return None
+    for name, b in rec["traffic_bytes_per_launch"].items():
+        if kernel_prefix in name:
+            return b
+    return None
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -159,7 +178,8 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
         "dtype": w.dtype,
         "roofline": {"kernel": "decode_scan_kernel", "bound": "hbm",
                      "achieved": lm_bytes / (per[0] / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": lm_bytes / (per[0] / 1e3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                     "frac": lm_bytes / (per[0] / 1e3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": profiled_traffic(wname, "decode_scan_kernel"),
                      "alg_bytes_per_launch": lm_bytes},
     }
     # needle recall (semantic sanity of the synthetic retrieval task)
@@ -301,6 +321,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one device copy of exactly 1 GiB (the reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this layer is measured on one GPU; the multi-GPU sharding is a design only "
@@ -313,6 +335,14 @@ def main():
     import hierarchical_sparse_attention_hsa_amd as hsa
     hsa.load_library()
     cpu = not args.no_cpu_baseline
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 1 GiB read + 1 GiB written")
+        del src, dst
     results = {}
     if args.workload == "all":
         results["prefill"] = bench_prefill("prefill_256k_bf16", args.steps, args.warmup, cpu)
