@@ -252,7 +252,9 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
             hsa.hsa_attn_set_timing_events(ev[2:])
         hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
 
-    secs, per = timed_steps(step, steps, warmup, 3, events)
+    names = ["landmarks", "prefill_select", "prefill_zero", "prefill_count", "prefill_scan", "prefill_scatter",
+             "prefill_remote", "prefill_local"]
+    secs, per = timed_steps(step, steps, warmup, len(names), events)
     ms_step = 1e3 * secs / steps
     # exact algorithmic work
     p = np.arange(w.T)
@@ -260,28 +262,39 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
     m_p = np.minimum(n_p, w.k)
     score_flops = 2.0 * w.B * w.Hq * w.D * n_p.sum()
     attn_flops = 4.0 * w.S * w.D * w.B * w.Hq * m_p.sum()
+    # split of the selected pairs into remote (chunk before the query's
+    # 64-chunk window) and local ones, counted from this run's selection
+    win0 = torch.div(torch.arange(w.T, device="cuda") // w.S, 64, rounding_mode="floor") * 64
+    n_remote = int(((sel >= 0) & (sel < win0[None, None, :, None])).sum().item())
+    n_pairs = int(m_p.sum()) * w.B * w.Hq
+    remote_flops = 4.0 * w.S * w.D * n_remote
+    local_flops = 4.0 * w.S * w.D * (n_pairs - n_remote)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    names = ["landmarks", "prefill_select", "prefill_attn"]
+    attn_ms = float(per[2:].sum())
     sel_tf = score_flops / (per[1] / 1e3) / 1e12
-    att_tf = attn_flops / (per[2] / 1e3) / 1e12
-    dom = 1 if per[1] >= per[2] else 2
-    dom_name = ["", "prefill_select_kernel", "prefill_attn_kernel"][dom]
-    dom_tf = sel_tf if dom == 1 else att_tf
+    att_tf = attn_flops / (attn_ms / 1e3) / 1e12
+    kern = {1: ("prefill_select_kernel", score_flops), 6: ("prefill_remote_kernel", remote_flops),
+            7: ("prefill_local_kernel", local_flops)}
+    dom = max(kern, key=lambda i: per[i])
+    dom_name, dom_flops = kern[dom]
+    dom_tf = dom_flops / (per[dom] / 1e3) / 1e12
     res = {
         "workload": wname, "value": w.B * w.T / (ms_step / 1e3), "unit": "tokens/s", "ms_per_step": ms_step,
         "kernel_ms": {n: float(x) for n, x in zip(names, per)},
         "scoring_tflops": sel_tf, "scoring_mfma_frac": sel_tf / peak,
-        "attention_tflops": att_tf, "attention_mfma_frac": att_tf / peak,
+        "attention_ms": attn_ms, "attention_tflops": att_tf, "attention_mfma_frac": att_tf / peak,
+        "remote_pair_frac": n_remote / max(n_pairs, 1),
+        "remote_tflops": remote_flops / (per[6] / 1e3) / 1e12,
+        "local_tflops": local_flops / (per[7] / 1e3) / 1e12,
         "landmark_GBps": (w.B * w.Hkv * Nc * w.S * w.D * esz) / (per[0] / 1e3) / 1e9,
         "config": {"workload": wname, "batch": w.B, "seq_len": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "chunk": w.S, "top_k": w.k, "lowrank": w.lowrank},
         "dtype": w.dtype,
         "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": dom_tf, "peak": peak, "unit": "TFLOP/s",
-                     "frac": dom_tf / peak, "traffic": None,
-                     "alg_flops_per_launch": score_flops if dom == 1 else attn_flops},
+                     "frac": dom_tf / peak, "traffic": None, "alg_flops_per_launch": dom_flops},
     }
     log(f"[{wname}] {ms_step:.3f} ms/step, kernels {dict(zip(names, np.round(per, 4)))}, "
-        f"scoring {sel_tf:.1f} TFLOP/s, attention {att_tf:.1f} TFLOP/s")
+        f"scoring {sel_tf:.1f} TFLOP/s, attention {att_tf:.1f} TFLOP/s, remote pairs {n_remote / max(n_pairs, 1):.3f}")
     if cpu_baseline:
         res["cpu_baseline"] = prefill_cpu_baseline(w, q, k, v)
     del q, k, v, L, out, sel, sc

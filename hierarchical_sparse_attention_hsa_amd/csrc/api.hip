@@ -173,14 +173,18 @@ hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, c
     const hsa_attn::PrefillPlan plan = hsa_attn::plan_prefill(g, own);
     if (workspace_bytes < plan.bytes)
       return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes, workspace_bytes);
-    if (plan.bytes > 0 && !workspace) return fail(HSA_ATTN_INVALID_ARGUMENT, "workspace is NULL");
     if (g.T == 0) return ok();
+    if (!workspace) return fail(HSA_ATTN_INVALID_ARGUMENT, "workspace is NULL");
+    char* ws = static_cast<char*>(workspace);
     if (own) {
-      sel_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.off_sel_idx);
-      sel_score = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.off_sel_score);
+      sel_idx = reinterpret_cast<int32_t*>(ws + plan.off_sel_idx);
+      sel_score = reinterpret_cast<float*>(ws + plan.off_sel_score);
     }
     restart_timing();
-    hsa_attn::PrefillArgs a{g, q, k, v, landmarks, out, sel_idx, sel_score};
+    hsa_attn::PrefillArgs a{g, q, k, v, landmarks, out, sel_idx, sel_score,
+                            reinterpret_cast<int32_t*>(ws + plan.off_pair_pos), reinterpret_cast<int*>(ws + plan.off_cnt),
+                            reinterpret_cast<int*>(ws + plan.off_off), reinterpret_cast<int32_t*>(ws + plan.off_pairs),
+                            reinterpret_cast<float*>(ws + plan.off_partial)};
     return hip_status(hsa_attn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
   } catch (const std::exception& e) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());

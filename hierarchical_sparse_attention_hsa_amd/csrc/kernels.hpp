@@ -51,7 +51,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s
 
 // ---------------------------------------------------------------- prefill
 struct PrefillPlan {
-  size_t off_sel_idx, off_sel_score, bytes;
+  size_t off_sel_idx, off_sel_score, off_pair_pos, off_cnt, off_off, off_pairs, off_partial, bytes;
 };
 PrefillPlan plan_prefill(const Geometry& g, bool own_sel);
 
@@ -61,6 +61,12 @@ struct PrefillArgs {
   float* out;
   int32_t* sel_idx;
   float* sel_score;
+  // workspace: remote-pair bucketing and the remote pairs' outputs
+  int32_t* pair_pos;  // [B, Hq, T, k]
+  int* cnt;           // [B * Hkv * Nc]
+  int* off;           // [B * Hkv * Nc + 1]
+  int32_t* pairs;     // [B * Hq * T * k] (worst case)
+  float* partial;     // [B * Hq * T * k, D] (worst case)
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 

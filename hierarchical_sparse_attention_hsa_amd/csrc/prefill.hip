@@ -27,50 +27,136 @@ HSA_ATTN_PREFILL_EXTERN(FP32, 64, 32)
 // ---------------------------------------------------------------- host side
 static size_t align_up_p(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// ---- remote-pair bucketing (chunk-major lists of the scattered pairs)
+__global__ void prefill_zero_kernel(int* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+// pair_pos[i] = position of remote pair i inside its (b, g, chunk) bucket
+// (arbitrary order), -1 for local or empty slots; cnt[bucket] counts them.
+__global__ void prefill_count_kernel(const int32_t* __restrict__ sel_idx, int* __restrict__ cnt,
+                                     int32_t* __restrict__ pair_pos, int Hq, int G, int64_t T_len, int64_t Nc,
+                                     int k, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t row = i / k;
+  const int64_t t = row % T_len;
+  const int64_t bh = row / T_len;
+  const int h = (int)(bh % Hq);
+  const int64_t b = bh / Hq;
+  const int c = sel_idx[i];
+  const int64_t j = t / kChunk;
+  const int64_t ws = (j / kLocalWindow) * kLocalWindow;
+  int pos = -1;
+  if (c >= 0 && c < ws) {
+    const int64_t bucket = (b * (Hq / G) + h / G) * Nc + c;
+    pos = atomicAdd(&cnt[bucket], 1);
+  }
+  pair_pos[i] = pos;
+}
+
+// exclusive prefix sum of n counts into off[0..n] (off[n] = total), one
+// workgroup of 1024 threads
+__global__ __launch_bounds__(1024) void prefill_scan_kernel(const int* __restrict__ cnt, int* __restrict__ off,
+                                                            int64_t n) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t lo = tid * per, hi = min(n, lo + per);
+  int s = 0;
+  for (int64_t i = lo; i < hi; ++i) s += cnt[i];
+  part[tid] = s;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int v = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = tid > 0 ? part[tid - 1] : 0;
+  for (int64_t i = lo; i < hi; ++i) {
+    off[i] = run;
+    run += cnt[i];
+  }
+  if (tid == 1023) off[n] = part[1023];
+}
+
+// pairs[pos] = row of each remote pair; pair_pos becomes the global position
+__global__ void prefill_scatter_kernel(const int32_t* __restrict__ sel_idx, const int* __restrict__ off,
+                                       int32_t* __restrict__ pair_pos, int32_t* __restrict__ pairs, int Hq, int G,
+                                       int64_t T_len, int64_t Nc, int k, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int32_t inb = pair_pos[i];
+  if (inb < 0) return;
+  const int64_t row = i / k;
+  const int64_t bh = row / T_len;
+  const int h = (int)(bh % Hq);
+  const int64_t b = bh / Hq;
+  const int64_t bucket = (b * (Hq / G) + h / G) * Nc + sel_idx[i];
+  const int32_t pos = off[bucket] + inb;
+  pairs[pos] = (int32_t)row;
+  pair_pos[i] = pos;
+}
+
+
+hipError_t launch_prefill_bucketing(const PrefillArgs& a, hipStream_t st) {
+  const Geometry& g = a.g;
+  const int64_t total = (int64_t)g.B * g.Hq * g.T * g.k;
+  const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;
+  const unsigned pb = (unsigned)((total + 255) / 256);
+  mark_launch(st);
+  hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)std::min<int64_t>((nb + 255) / 256, 4096)), dim3(256), 0,
+                     st, a.cnt, nb);
+  mark_launch(st);
+  if (pb > 0) {
+    mark_launch(st);
+    hipLaunchKernelGGL(prefill_count_kernel, dim3(pb), dim3(256), 0, st, a.sel_idx, a.cnt, a.pair_pos, g.Hq, g.G,
+                       g.T, g.Nc, g.k, total);
+    mark_launch(st);
+  }
+  mark_launch(st);
+  hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, a.cnt, a.off, nb);
+  mark_launch(st);
+  if (pb > 0) {
+    mark_launch(st);
+    hipLaunchKernelGGL(prefill_scatter_kernel, dim3(pb), dim3(256), 0, st, a.sel_idx, a.off, a.pair_pos, a.pairs,
+                       g.Hq, g.G, g.T, g.Nc, g.k, total);
+    mark_launch(st);
+  }
+  return hipGetLastError();
+}
+
 PrefillPlan plan_prefill(const Geometry& g, bool own_sel) {
   PrefillPlan p{};
   size_t off = 0;
+  const size_t pairs = (size_t)g.B * g.Hq * (size_t)g.T * g.k;
+  const size_t nb = (size_t)g.B * g.Hkv * (size_t)g.Nc;
   if (own_sel) {
-    const size_t rows = (size_t)g.B * g.Hq * (size_t)g.T;
     p.off_sel_idx = off;
-    off = align_up_p(off + rows * g.k * sizeof(int32_t), 256);
+    off = align_up_p(off + pairs * sizeof(int32_t), 256);
     p.off_sel_score = off;
-    off = align_up_p(off + rows * g.k * sizeof(float), 256);
+    off = align_up_p(off + pairs * sizeof(float), 256);
   }
+  p.off_pair_pos = off;
+  off = align_up_p(off + pairs * sizeof(int32_t), 256);
+  p.off_cnt = off;
+  off = align_up_p(off + nb * sizeof(int), 256);
+  p.off_off = off;
+  off = align_up_p(off + (nb + 1) * sizeof(int), 256);
+  p.off_pairs = off;
+  off = align_up_p(off + pairs * sizeof(int32_t), 256);
+  p.off_partial = off;
+  off = align_up_p(off + pairs * g.D * sizeof(float), 256);
   p.bytes = off;
   return p;
 }
 
 size_t prefill_attn_lds_bytes(const Geometry& g) {
   const size_t esz = g.bf16 ? 2 : 4;
-  const size_t nwords = (size_t)((g.Nc + 31) / 32);
-  return 2 * (size_t)kChunk * g.D * esz + (size_t)32 * g.G * g.k * 8 + nwords * 4;
+  return 2 * (size_t)kChunk * g.D * esz + (size_t)32 * g.G * g.k * 8;
 }
-
-#ifndef HSA_ATTN_HAVE_BF16_D128_K16
-#define HSA_ATTN_HAVE_BF16_D128_K16 0
-#endif
-#ifndef HSA_ATTN_HAVE_BF16_D128_K32
-#define HSA_ATTN_HAVE_BF16_D128_K32 0
-#endif
-#ifndef HSA_ATTN_HAVE_BF16_D64_K16
-#define HSA_ATTN_HAVE_BF16_D64_K16 0
-#endif
-#ifndef HSA_ATTN_HAVE_BF16_D64_K32
-#define HSA_ATTN_HAVE_BF16_D64_K32 0
-#endif
-#ifndef HSA_ATTN_HAVE_FP32_D128_K16
-#define HSA_ATTN_HAVE_FP32_D128_K16 0
-#endif
-#ifndef HSA_ATTN_HAVE_FP32_D128_K32
-#define HSA_ATTN_HAVE_FP32_D128_K32 0
-#endif
-#ifndef HSA_ATTN_HAVE_FP32_D64_K16
-#define HSA_ATTN_HAVE_FP32_D64_K16 0
-#endif
-#ifndef HSA_ATTN_HAVE_FP32_D64_K32
-#define HSA_ATTN_HAVE_FP32_D64_K32 0
-#endif
 
 // the register top-k list holds 16 or 32 entries; k <= 16 uses the short list
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {

@@ -272,15 +272,19 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(c
 }
 
 // ---------------------------------------------------------------- attention
-struct AttnLds {
-  // byte offsets inside the dynamic LDS block
-  int k_off, vt_off, tab_off, bm_off, bytes;
-};
-
-template <typename T, int D, int G>
-__host__ __device__ constexpr int attn_fixed_bytes() {
-  return 2 * kChunk * D * T::kBytes;  // K tile + V^T tile
-}
+//
+// A selected (row, chunk) pair is "local" when the chunk lies in the query's
+// aligned window of kLocalWindow chunks and "remote" otherwise.  Local pairs
+// are shared by many rows of a query block (measured: most selections fall
+// in the query's own window), so prefill_local_kernel walks the union of a
+// block's local selections and runs every row of the block through each
+// chunk on MFMA (rows that did not select it get weight 0).  Remote pairs
+// are scattered, so they are processed chunk-major: they are bucketed by
+// (b, g, chunk), prefill_remote_kernel loads each chunk's K/V tile once and
+// gathers its selecting rows 32 at a time into full MFMA tiles, and writes
+// each pair's normalised in-chunk output; the local kernel then adds the
+// weighted remote outputs of its rows.
+constexpr int kLocalWindow = 64;
 
 // V^T element position of token t inside the 64-token row of column d, in
 // the order the P' fragments present tokens: k-step t/16, lane half
@@ -289,123 +293,34 @@ __device__ __forceinline__ int vt_pos(int t) {
   return (t / 16) * 16 + ((t % 8) / 4) * 8 + 4 * ((t % 16) / 8) + (t % 4);
 }
 
-template <typename T, int D, int G, int KSEL>
-__global__ __launch_bounds__(kWave* G) void prefill_attn_kernel(
-    const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ kk,
-    const typename T::storage* __restrict__ vv, const int32_t* __restrict__ sel_idx,
-    const float* __restrict__ sel_score, float* __restrict__ out, int B, int Hkv, int64_t T_len, int64_t Nc,
-    int nqc, int k, float scale) {
+// Stages one chunk's K tile (row-major, 16-byte slots XOR-swizzled by row)
+// and V^T tile (column-major with the token order of vt_pos, slots swizzled
+// by column) into LDS.  NTH threads cooperate; NP slots per thread per pass.
+template <typename T, int D, int NTH>
+struct KVStage {
   using st = typename T::storage;
-  constexpr int NTH = kWave * G;
-  constexpr int EPS = 16 / T::kBytes;
-  constexpr int ROWB = D * T::kBytes;        // bytes per K row
-  constexpr int NSL = ROWB / 16;             // slots per K row
-  constexpr int KV_SLOTS = kChunk * NSL;     // slots per K (or V) tile
-  constexpr int LPT = KV_SLOTS / NTH;        // slots per thread per tile
-  constexpr int VTB = kChunk * T::kBytes;    // bytes per V^T row (one column d)
-  constexpr int KCH = D / 16;
-  constexpr int DM = D / 32;
-  static_assert(KV_SLOTS % NTH == 0, "tile slots must divide evenly");
-  extern __shared__ __align__(16) char smem[];
-  char* ks = smem;
-  char* vt = smem + kChunk * ROWB;
-  int2* tab = reinterpret_cast<int2*>(smem + 2 * kChunk * ROWB);  // [32*G rows][k]
-  uint32_t* bm = reinterpret_cast<uint32_t*>(tab + 32 * G * k);
-
-  const int bid = blockIdx.x;
-  const int g = bid % Hkv;
-  int rest = bid / Hkv;
-  const int b = rest % B;
-  rest /= B;
-  const int hc = rest & 1;
-  const int j = nqc - 1 - (rest >> 1);
-  const int tid = threadIdx.x, lane = tid & 63, hh = tid >> 6, half = lane >> 5;
-  const int Hq = Hkv * G, h = g * G + hh;
-  const int64_t n = min((int64_t)j, Nc);
-  const int nwords = (int)((n + 31) / 32);
-  const int row = hh * 32 + (lane & 31);                       // row inside the workgroup
-  const int64_t tok = (int64_t)j * kChunk + 32 * hc + (lane & 31);
-  const bool tok_ok = tok < T_len;
-
-  for (int i = tid; i < nwords; i += NTH) bm[i] = 0u;
-  __syncthreads();
-
-  // ---- per-row table: selected chunks ascending with their fusion weights
-  int m = 0;
-  if (lane < 32 && tok_ok && n > 0) {
-    const int64_t base = (((int64_t)b * Hq + h) * T_len + tok) * k;
-    int ci[KSEL];
-    float sc[KSEL];
-#pragma unroll
-    for (int e = 0; e < KSEL; ++e) {
-      ci[e] = (e < k) ? sel_idx[base + e] : -1;
-      sc[e] = (e < k && ci[e] >= 0) ? sel_score[base + e] : -__builtin_inff();
-      m += ci[e] >= 0;
-    }
-    const float smax = sc[0];
-    float w[KSEL], den = 0.0f;
-#pragma unroll
-    for (int e = 0; e < KSEL; ++e) {
-      w[e] = ci[e] >= 0 ? expf(sc[e] - smax) : 0.0f;
-      den += w[e];
-    }
-    const float inv = 1.0f / den;
-#pragma unroll
-    for (int e = 0; e < KSEL; ++e) {
-      if (ci[e] >= 0) {
-        int rank = 0;
-#pragma unroll
-        for (int f = 0; f < KSEL; ++f) rank += (ci[f] >= 0 && ci[f] < ci[e]);
-        tab[row * k + rank] = make_int2(ci[e], __float_as_int(w[e] * inv));
-        atomicOr(&bm[ci[e] >> 5], 1u << (ci[e] & 31));
-      }
-    }
-  }
-  m = __shfl(m, lane & 31);  // the partner lane of the row learns the count
-  __syncthreads();
-
-  // ---- queries as the B operand (rows = tokens of this half chunk)
-  Frag<T> qf[KCH];
-  {
-    const st* qp = q + (((int64_t)b * Hq + h) * T_len + (tok_ok ? tok : 0)) * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < KCH; ++s) load_frag_global(qf[s], qp + 16 * s, tok_ok);
-  }
-  f32x16 oacc[DM];
-#pragma unroll
-  for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
-
-  // walk the union of selected chunks in ascending order
-  int word = 0;
-  uint32_t bits = nwords > 0 ? bm[0] : 0u;
-  auto next_chunk = [&]() -> int {
-    while (bits == 0u) {
-      if (++word >= nwords) return -1;
-      bits = bm[word];
-    }
-    const int c = word * 32 + __builtin_ctz(bits);
-    bits &= bits - 1u;
-    return c;
-  };
-  const st* kg = kk + ((int64_t)b * Hkv + g) * T_len * D;
-  const st* vg = vv + ((int64_t)b * Hkv + g) * T_len * D;
-  // K/V staging: NP slots of each tile per thread per pass; with a single
-  // pass the next chunk's tiles are fetched into registers while the current
-  // one is computed.
-  constexpr int NP = LPT < 4 ? LPT : 4;
-  constexpr int PASSES = LPT / NP;
-  static_assert(LPT % NP == 0, "staging passes must divide evenly");
+  static constexpr int EPS = 16 / T::kBytes;
+  static constexpr int ROWB = D * T::kBytes;
+  static constexpr int NSL = ROWB / 16;
+  static constexpr int KV_SLOTS = kChunk * NSL;
+  static constexpr int LPT = KV_SLOTS / NTH;
+  static constexpr int NP = LPT < 4 ? LPT : 4;
+  static constexpr int PASSES = LPT / NP;
+  static constexpr int VTB = kChunk * T::kBytes;
+  static constexpr int BYTES = 2 * kChunk * ROWB;
+  static_assert(KV_SLOTS % NTH == 0 && LPT % NP == 0, "tile slots must divide evenly");
   u32x4 kpre[NP], vpre[NP];
-  auto fetch = [&](int c, int pass) {
+
+  __device__ __forceinline__ void fetch(const st* kg, const st* vg, int64_t c, int pass, int tid) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int slot = tid + (pass * NP + i) * NTH;
-      const int64_t off = ((int64_t)c * kChunk + slot / NSL) * D + (slot % NSL) * EPS;
+      const int64_t off = (c * kChunk + slot / NSL) * D + (slot % NSL) * EPS;
       kpre[i] = *reinterpret_cast<const u32x4*>(kg + off);
       vpre[i] = *reinterpret_cast<const u32x4*>(vg + off);
     }
-  };
-  auto stash = [&](int pass) {
+  }
+  __device__ __forceinline__ void stash(char* ks, char* vt, int pass, int tid) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int slot = tid + (pass * NP + i) * NTH;
@@ -429,26 +344,280 @@ __global__ __launch_bounds__(kWave* G) void prefill_attn_kernel(
         }
       }
     }
-  };
+  }
+  // whole tile, fetch and stash pass by pass (caller synchronises)
+  __device__ __forceinline__ void load(const st* kg, const st* vg, int64_t c, char* ks, char* vt, int tid) {
+#pragma unroll 1
+    for (int ps = 0; ps < PASSES; ++ps) {
+      fetch(kg, vg, c, ps, tid);
+      stash(ks, vt, ps, tid);
+    }
+  }
+};
 
-  const float cexp = scale * 1.4426950408889634f;  // softmax in base 2
+// One wave, 32 query rows (B operand qf, row = lane % 32; lanes l and l^32
+// hold the two halves of each row): softmax attention over the 64 tokens of
+// the staged chunk, accumulated into the O^T tiles as factor * o_c.
+template <typename T, int D>
+__device__ __forceinline__ void attend_block(const Frag<T> (&qf)[D / 16], const char* ks, const char* vt,
+                                             float factor, float cexp, f32x16 (&oacc)[D / 32], int lane) {
+  constexpr int ROWB = D * T::kBytes;
+  constexpr int VTB = kChunk * T::kBytes;
+  constexpr int KCH = D / 16;
+  constexpr int DM = D / 32;
+  const int half = lane >> 5;
+  // S^T = K_c Q^T: two 32-token blocks
+  f32x16 s0 = {}, s1 = {};
+  const char* k0 = ks + (lane & 31) * ROWB;
+  const char* k1 = ks + (32 + (lane & 31)) * ROWB;
+#pragma unroll
+  for (int s = 0; s < KCH; ++s) {
+    Frag<T> a0, a1;
+    load_frag_lds<T>(a0, k0, lane & 7, s, half);
+    load_frag_lds<T>(a1, k1, lane & 7, s, half);
+    mfma(s0, a0, qf[s]);
+    mfma(s1, a1, qf[s]);
+  }
+  // softmax over the row's 64 tokens; lane l and l^32 split them
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float sum = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = __builtin_amdgcn_exp2f((s0[r] - mx) * cexp);
+    s1[r] = __builtin_amdgcn_exp2f((s1[r] - mx) * cexp);
+    sum += s0[r] + s1[r];
+  }
+  sum += __shfl_xor(sum, 32);
+  const float f = factor / sum;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] *= f;
+    s1[r] *= f;
+  }
+  // O^T += V^T P'^T over four 16-token k-steps
+#pragma unroll
+  for (int ks_ = 0; ks_ < 4; ++ks_) {
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pv[e] = (ks_ < 2) ? s0[8 * (ks_ & 1) + e] : s1[8 * (ks_ & 1) + e];
+    if constexpr (T::kBytes == 2) {
+      Frag<BF16> phi, plo;
+      phi.from_f32(pv);
+      float rem[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rem[e] = pv[e] - static_cast<float>(phi.v[e]);
+      plo.from_f32(rem);
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm) {
+        Frag<BF16> a;
+        const int d = 32 * dm + (lane & 31);
+        const int slot = (2 * ks_ + half) ^ (d & 7);
+        a.load16(vt + d * VTB + slot * 16);
+        mfma(oacc[dm], a, phi);
+        mfma(oacc[dm], a, plo);
+      }
+    } else {
+      Frag<FP32> pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf.v[e] = pv[e];
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm) {
+        Frag<FP32> a;
+        const int d = 32 * dm + (lane & 31);
+        const int s0i = (4 * ks_ + 2 * half) ^ (d & 7);
+        const int s1i = (4 * ks_ + 2 * half + 1) ^ (d & 7);
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(vt + d * VTB + s0i * 16);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(vt + d * VTB + s1i * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a.v[e] = x0[e];
+          a.v[4 + e] = x1[e];
+        }
+        mfma(oacc[dm], a, pf);
+      }
+    }
+  }
+}
+
+// Output columns held by a lane in the O^T accumulators: for tile dm and
+// register group q4, four consecutive columns starting at out_col(dm, q4).
+__device__ __forceinline__ int out_col(int dm, int q4, int half) { return 32 * dm + 8 * q4 + 4 * half; }
+
+// Buckets the remote pairs by (b, g, chunk): pair_pos[i] = position of
+// pair i in `pairs` (-1 when local or empty), off[] = bucket offsets,
+// pairs[] = query row of each pair.  Four launches (prefill.hip).
+hipError_t launch_prefill_bucketing(const PrefillArgs& a, hipStream_t st);
+
+// ---- chunk-major attention of the remote pairs
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void prefill_remote_kernel(const typename T::storage* __restrict__ q,
+                                                             const typename T::storage* __restrict__ kk,
+                                                             const typename T::storage* __restrict__ vv,
+                                                             const int* __restrict__ off,
+                                                             const int32_t* __restrict__ pairs,
+                                                             float* __restrict__ partial, int Hkv, int64_t T_len,
+                                                             int64_t Nc, float scale) {
+  using st = typename T::storage;
+  using Stage = KVStage<T, D, 256>;
+  constexpr int KCH = D / 16;
+  constexpr int DM = D / 32;
+  __shared__ __align__(16) char smem[Stage::BYTES];
+  char* ks = smem;
+  char* vt = smem + kChunk * Stage::ROWB;
+  const int64_t bucket = blockIdx.x;
+  const int begin = off[bucket], end = off[bucket + 1];
+  if (begin == end) return;
+  const int64_t c = bucket % Nc;
+  const int64_t bg = bucket / Nc;  // b * Hkv + g
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  Stage stage;
+  stage.load(kk + bg * T_len * D, vv + bg * T_len * D, c, ks, vt, tid);
+  __syncthreads();
+  const float cexp = scale * 1.4426950408889634f;
+  for (int blk = wave; begin + 32 * blk < end; blk += 4) {
+    const int p = begin + 32 * blk + (lane & 31);
+    const bool ok = p < end;
+    const int64_t row = ok ? pairs[p] : 0;
+    Frag<T> qf[KCH];
+    const st* qp = q + row * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < KCH; ++s) load_frag_global(qf[s], qp + 16 * s, ok);
+    f32x16 oacc[DM];
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
+    attend_block<T, D>(qf, ks, vt, 1.0f, cexp, oacc, lane);
+    if (ok) {
+      float* op = partial + (int64_t)p * D;
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(op + out_col(dm, q4, half)) =
+              f32x4{oacc[dm][4 * q4], oacc[dm][4 * q4 + 1], oacc[dm][4 * q4 + 2], oacc[dm][4 * q4 + 3]};
+    }
+  }
+}
+
+// ---- local pairs and fusion
+template <typename T, int D, int G, int KSEL>
+__global__ __launch_bounds__(kWave* G) void prefill_local_kernel(
+    const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ kk,
+    const typename T::storage* __restrict__ vv, const int32_t* __restrict__ sel_idx,
+    const float* __restrict__ sel_score, const int32_t* __restrict__ pair_pos, const float* __restrict__ partial,
+    float* __restrict__ out, int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int k, float scale) {
+  using st = typename T::storage;
+  constexpr int NTH = kWave * G;
+  using Stage = KVStage<T, D, NTH>;
+  constexpr int KCH = D / 16;
+  constexpr int DM = D / 32;
+  constexpr int NW = kLocalWindow / 32;  // bitmap words of one window
+  extern __shared__ __align__(16) char smem[];
+  char* ks = smem;
+  char* vt = smem + kChunk * Stage::ROWB;
+  // per row k entries: local (chunk, weight) ascending from the front,
+  // remote (pair position, weight) from the back
+  int2* tab = reinterpret_cast<int2*>(smem + Stage::BYTES);
+  __shared__ uint32_t bm[NW];
+
+  const int bid = blockIdx.x;
+  const int g = bid % Hkv;
+  int rest = bid / Hkv;
+  const int b = rest % B;
+  rest /= B;
+  const int hc = rest & 1;
+  const int j = nqc - 1 - (rest >> 1);
+  const int tid = threadIdx.x, lane = tid & 63, hh = tid >> 6, half = lane >> 5;
+  const int Hq = Hkv * G, h = g * G + hh;
+  const int64_t n = min((int64_t)j, Nc);
+  const int ws = (j / kLocalWindow) * kLocalWindow;  // first chunk of the query's window
+  const int row = hh * 32 + (lane & 31);
+  const int64_t tok = (int64_t)j * kChunk + 32 * hc + (lane & 31);
+  const bool tok_ok = tok < T_len;
+
+  if (tid < NW) bm[tid] = 0u;
+  __syncthreads();
+
+  // ---- per-row tables: fusion weights of all kept chunks, local ones in
+  // ascending chunk order, remote ones with their pair positions
+  int m = 0, rc = 0;
+  if (lane < 32 && tok_ok && n > 0) {
+    const int64_t base = (((int64_t)b * Hq + h) * T_len + tok) * k;
+    int ci[KSEL];
+    float sc[KSEL];
+#pragma unroll
+    for (int e = 0; e < KSEL; ++e) {
+      ci[e] = (e < k) ? sel_idx[base + e] : -1;
+      sc[e] = (e < k && ci[e] >= 0) ? sel_score[base + e] : -__builtin_inff();
+    }
+    const float smax = sc[0];
+    float w[KSEL], den = 0.0f;
+#pragma unroll
+    for (int e = 0; e < KSEL; ++e) {
+      w[e] = ci[e] >= 0 ? expf(sc[e] - smax) : 0.0f;
+      den += w[e];
+    }
+    const float inv = 1.0f / den;
+#pragma unroll
+    for (int e = 0; e < KSEL; ++e) {
+      if (ci[e] >= ws) {
+        int rank = 0;
+#pragma unroll
+        for (int f = 0; f < KSEL; ++f) rank += (ci[f] >= ws && ci[f] < ci[e]);
+        tab[row * k + rank] = make_int2(ci[e], __float_as_int(w[e] * inv));
+        atomicOr(&bm[(ci[e] - ws) >> 5], 1u << ((ci[e] - ws) & 31));
+        ++m;
+      } else if (ci[e] >= 0) {
+        ++rc;
+        tab[row * k + k - rc] = make_int2(pair_pos[base + e], __float_as_int(w[e] * inv));
+      }
+    }
+  }
+  m = __shfl(m, lane & 31);  // the partner lane of the row learns the counts
+  rc = __shfl(rc, lane & 31);
+  __syncthreads();
+
+  Frag<T> qf[KCH];
+  {
+    const st* qp = q + (((int64_t)b * Hq + h) * T_len + (tok_ok ? tok : 0)) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < KCH; ++s) load_frag_global(qf[s], qp + 16 * s, tok_ok);
+  }
+  f32x16 oacc[DM];
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
+
+  // walk the union of the block's local selections in ascending order
+  int word = 0;
+  uint32_t bits = bm[0];
+  auto next_chunk = [&]() -> int {
+    while (bits == 0u) {
+      if (++word >= NW) return -1;
+      bits = bm[word];
+    }
+    const int c = ws + word * 32 + __builtin_ctz(bits);
+    bits &= bits - 1u;
+    return c;
+  };
+  const st* kg = kk + ((int64_t)b * Hkv + g) * T_len * D;
+  const st* vg = vv + ((int64_t)b * Hkv + g) * T_len * D;
+  const float cexp = scale * 1.4426950408889634f;
+  Stage stage;
   int ptr = 0;
   int c = next_chunk();
-  if (PASSES == 1 && c >= 0) fetch(c, 0);
+  if (Stage::PASSES == 1 && c >= 0) stage.fetch(kg, vg, c, 0, tid);
   while (c >= 0) {
     __syncthreads();  // everyone is done with the previous tile
-    if constexpr (PASSES == 1) {
-      stash(0);
+    if constexpr (Stage::PASSES == 1) {
+      stage.stash(ks, vt, 0, tid);
     } else {
-#pragma unroll 1
-      for (int ps = 0; ps < PASSES; ++ps) {
-        fetch(c, ps);
-        stash(ps);
-      }
+      stage.load(kg, vg, c, ks, vt, tid);
     }
     __syncthreads();
     const int cn = next_chunk();
-    if (PASSES == 1 && cn >= 0) fetch(cn, 0);
+    if (Stage::PASSES == 1 && cn >= 0) stage.fetch(kg, vg, cn, 0, tid);
     float wgt = 0.0f;
     bool mine = false;
     if (ptr < m) {
@@ -459,95 +628,35 @@ __global__ __launch_bounds__(kWave* G) void prefill_attn_kernel(
         ++ptr;
       }
     }
-    if (__ballot(mine)) {
-      // S^T = K_c Q^T: two 32-token blocks
-      f32x16 s0 = {}, s1 = {};
-      const char* k0 = ks + (lane & 31) * ROWB;
-      const char* k1 = ks + (32 + (lane & 31)) * ROWB;
-#pragma unroll
-      for (int s = 0; s < KCH; ++s) {
-        Frag<T> a0, a1;
-        load_frag_lds<T>(a0, k0, lane & 7, s, half);
-        load_frag_lds<T>(a1, k1, lane & 7, s, half);
-        mfma(s0, a0, qf[s]);
-        mfma(s1, a1, qf[s]);
-      }
-      // softmax over the 64 tokens of row (lane & 31); lane l and l^32 split them
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      float sum = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = __builtin_amdgcn_exp2f((s0[r] - mx) * cexp);
-        s1[r] = __builtin_amdgcn_exp2f((s1[r] - mx) * cexp);
-        sum += s0[r] + s1[r];
-      }
-      sum += __shfl_xor(sum, 32);
-      const float f = wgt / sum;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] *= f;
-        s1[r] *= f;
-      }
-      // O^T += V^T P'^T over four 16-token k-steps
-#pragma unroll
-      for (int ks_ = 0; ks_ < 4; ++ks_) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = (ks_ < 2) ? s0[8 * (ks_ & 1) + e] : s1[8 * (ks_ & 1) + e];
-        if constexpr (T::kBytes == 2) {
-          Frag<BF16> phi, plo;
-          phi.from_f32(pv);
-          float rem[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) rem[e] = pv[e] - static_cast<float>(phi.v[e]);
-          plo.from_f32(rem);
-#pragma unroll
-          for (int dm = 0; dm < DM; ++dm) {
-            Frag<BF16> a;
-            const int d = 32 * dm + (lane & 31);
-            const int slot = (2 * ks_ + half) ^ (d & 7);
-            a.load16(vt + d * VTB + slot * 16);
-            mfma(oacc[dm], a, phi);
-            mfma(oacc[dm], a, plo);
-          }
-        } else {
-          Frag<FP32> pf;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf.v[e] = pv[e];
-#pragma unroll
-          for (int dm = 0; dm < DM; ++dm) {
-            Frag<FP32> a;
-            const int d = 32 * dm + (lane & 31);
-            const int s0i = (4 * ks_ + 2 * half) ^ (d & 7);
-            const int s1i = (4 * ks_ + 2 * half + 1) ^ (d & 7);
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(vt + d * VTB + s0i * 16);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(vt + d * VTB + s1i * 16);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              a.v[e] = x0[e];
-              a.v[4 + e] = x1[e];
-            }
-            mfma(oacc[dm], a, pf);
-          }
-        }
-      }
-    }
+    if (__ballot(mine)) attend_block<T, D>(qf, ks, vt, wgt, cexp, oacc, lane);
     c = cn;
+  }
+  // add the weighted outputs of the row's remote pairs
+  int rmax = rc;
+  for (int off = 32; off >= 1; off >>= 1) rmax = max(rmax, __shfl_xor(rmax, off));
+  for (int r = 0; r < rmax; ++r) {
+    if (r < rc) {
+      const int2 e = tab[row * k + k - 1 - r];
+      const float w = __int_as_float(e.y);
+      const float* pp = partial + (int64_t)e.x * D;
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(pp + out_col(dm, q4, half));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[dm][4 * q4 + i] = fmaf(w, x[i], oacc[dm][4 * q4 + i]);
+        }
+    }
   }
   if (tok_ok) {
     float* op = out + (((int64_t)b * Hq + h) * T_len + tok) * D;
 #pragma unroll
-    for (int dm = 0; dm < DM; ++dm) {
+    for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * dm + 8 * q4 + 4 * half;
-        f32x4 o{oacc[dm][4 * q4], oacc[dm][4 * q4 + 1], oacc[dm][4 * q4 + 2], oacc[dm][4 * q4 + 3]};
-        *reinterpret_cast<f32x4*>(op + d0) = o;
-      }
-    }
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(op + out_col(dm, q4, half)) =
+            f32x4{oacc[dm][4 * q4], oacc[dm][4 * q4 + 1], oacc[dm][4 * q4 + 2], oacc[dm][4 * q4 + 3]};
   }
 }
 
@@ -560,25 +669,35 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   const int nqc = (int)((g.T + kChunk - 1) / kChunk);
   const float scale = 1.0f / sqrtf((float)D);
   const unsigned blocks = (unsigned)((int64_t)nqc * g.B * g.Hkv);
-  mark_launch(st);
+  const stg* q = static_cast<const stg*>(a.q);
+  const stg* k = static_cast<const stg*>(a.k);
+  const stg* v = static_cast<const stg*>(a.v);
   constexpr int HPW = G < 4 ? G : 4;
-  hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(blocks * (G / HPW)), dim3(kWave * HPW), 0, st,
-                     static_cast<const stg*>(a.q), static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, g.B,
-                     g.Hkv, g.T, g.Nc, nqc, g.k, scale);
   mark_launch(st);
+  hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(blocks * (G / HPW)), dim3(kWave * HPW), 0, st, q,
+                     static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, g.B, g.Hkv, g.T, g.Nc, nqc, g.k, scale);
+  mark_launch(st);
+  const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;  // remote-pair buckets
+  if (nb > 0) {
+    hipError_t e = launch_prefill_bucketing(a, st);
+    if (e != hipSuccess) return e;
+    mark_launch(st);
+    hipLaunchKernelGGL((prefill_remote_kernel<T, D, G>), dim3((unsigned)nb), dim3(256), 0, st, q, k, v, a.off,
+                       a.pairs, a.partial, g.Hkv, g.T, g.Nc, scale);
+    mark_launch(st);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = prefill_attn_lds_bytes(g);
-  auto kern = prefill_attn_kernel<T, D, G, KSEL>;
+  auto kern = prefill_local_kernel<T, D, G, KSEL>;
   if (lds > 65536) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds);
     if (e != hipSuccess) return e;
   }
   mark_launch(st);
-  hipLaunchKernelGGL(kern, dim3(2 * blocks), dim3(kWave * G), lds, st, static_cast<const stg*>(a.q),
-                     static_cast<const stg*>(a.k), static_cast<const stg*>(a.v), a.sel_idx, a.sel_score, a.out,
-                     g.B, g.Hkv, g.T, g.Nc, nqc, g.k, scale);
+  hipLaunchKernelGGL(kern, dim3(2 * blocks), dim3(kWave * G), lds, st, q, k, v, a.sel_idx, a.sel_score, a.pair_pos,
+                     a.partial, a.out, g.B, g.Hkv, g.T, g.Nc, nqc, g.k, scale);
   mark_launch(st);
   return hipGetLastError();
 }

@@ -1,6 +1,8 @@
 """GPU parity of hsa_forward_decode against the oracle, through the C-ABI
 binding: selected chunk indices exact except near ties, outputs within
 2e-3 (bf16) / 1e-5 (fp32) max-abs."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -58,7 +60,7 @@ CASES = [
 def test_decode_matches_oracle(case):
     B, Hq, Hkv, T, D, topk, dtype = case
     print(f"decode case {case}", flush=True)
-    q, k, v = small_inputs(B, Hq, Hkv, T, D, dtype, seed=hash(case) % 10000, decode=True)
+    q, k, v = small_inputs(B, Hq, Hkv, T, D, dtype, seed=zlib.crc32(repr(case).encode()) % 10000, decode=True)
     out, sel, score = run_decode(q, k, v, 64, topk)
     stats = compare(q, k, v, 64, topk, dtype, out, sel, score)
     print(stats)

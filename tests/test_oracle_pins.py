@@ -7,6 +7,7 @@ mutation tests at the end plant plausible mistakes in the oracle and check
 that these pins catch them.
 """
 import math
+import zlib
 
 import numpy as np
 import pytest
@@ -120,7 +121,7 @@ CASES = [
 @pytest.mark.parametrize("case", CASES)
 def test_oracle_matches_brute_force(case):
     B, Hq, Hkv, T, D, S, k, dtype = case
-    Q, K, V = rand_qkv(hash(case) % 1000, B, Hq, Hkv, T, D, dtype)
+    Q, K, V = rand_qkv(zlib.crc32(repr(case).encode()) % 1000, B, Hq, Hkv, T, D, dtype)
     out, sel, sc, L = O.prefill(Q, K, V, S, k, dtype)
     bo, bs, bc = brute.prefill(Q.tolist(), K.tolist(), V.tolist(), S, k, dtype)
     for b in range(B):
