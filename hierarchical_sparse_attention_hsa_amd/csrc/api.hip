@@ -63,6 +63,9 @@ hsa_attn_status_t check_dims(const hsa_attn_dims_t* d, Call call, hsa_attn::Geom
     if (Nc > 65536) return fail(HSA_ATTN_UNSUPPORTED, "prefill supports at most 65536 chunks");
     if ((d->seq_len + 63) / 64 * (int64_t)d->batch * d->num_kv_heads * 2 > 0x7fffffffLL)
       return fail(HSA_ATTN_UNSUPPORTED, "prefill grid too large");
+    // remote-pair positions and row indices are int32
+    if ((int64_t)d->batch * d->num_q_heads * d->seq_len * d->top_k > 0x7fffffffLL)
+      return fail(HSA_ATTN_UNSUPPORTED, "prefill: batch * q_heads * seq_len * top_k must stay below 2^31");
   }
   if (call == Call::kDecode && Nc > 0x7fffffffLL) return fail(HSA_ATTN_UNSUPPORTED, "cache too long");
   g->B = d->batch;

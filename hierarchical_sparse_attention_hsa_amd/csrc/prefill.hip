@@ -35,25 +35,46 @@ __global__ void prefill_zero_kernel(int* __restrict__ p, int64_t n) {
 
 // pair_pos[i] = position of remote pair i inside its (b, g, chunk) bucket
 // (arbitrary order), -1 for local or empty slots; cnt[bucket] counts them.
+// Lanes of a wave that hit the same bucket share one atomic (neighbouring
+// rows select largely the same chunks, and popular chunks would otherwise
+// serialise on their counter).
 __global__ void prefill_count_kernel(const int32_t* __restrict__ sel_idx, int* __restrict__ cnt,
                                      int32_t* __restrict__ pair_pos, int Hq, int G, int64_t T_len, int64_t Nc,
                                      int k, int64_t total) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  const int64_t row = i / k;
-  const int64_t t = row % T_len;
-  const int64_t bh = row / T_len;
-  const int h = (int)(bh % Hq);
-  const int64_t b = bh / Hq;
-  const int c = sel_idx[i];
-  const int64_t j = t / kChunk;
-  const int64_t ws = (j / kLocalWindow) * kLocalWindow;
-  int pos = -1;
-  if (c >= 0 && c < ws) {
-    const int64_t bucket = (b * (Hq / G) + h / G) * Nc + c;
-    pos = atomicAdd(&cnt[bucket], 1);
+  // the host guarantees total < 2^31, so 32-bit index arithmetic suffices
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  const int lane = threadIdx.x & 63;
+  int bucket = -1;
+  if (i < total) {
+    const int row = i / k;
+    const int t = row % (int)T_len;
+    const int bh = row / (int)T_len;
+    const int h = bh % Hq;
+    const int b = bh / Hq;
+    const int c = sel_idx[i];
+    const int ws = (t / (kChunk * kLocalWindow)) * kLocalWindow;
+    if (c >= 0 && c < ws) bucket = (int)(((int64_t)b * (Hq / G) + h / G) * Nc + c);
   }
-  pair_pos[i] = pos;
+  // group the lanes by bucket (no memory traffic), then one atomic per group
+  // from its lowest lane, all groups at once
+  int leader = -1, rank = 0, group = 0;
+  uint64_t todo = __ballot(bucket >= 0);
+  while (todo) {
+    const int l = __builtin_ctzll(todo);
+    const int lb = __builtin_amdgcn_readlane(bucket, l);
+    const uint64_t same = __ballot(bucket == lb);
+    if (bucket == lb) {
+      leader = l;
+      rank = __popcll(same & ((1ull << lane) - 1ull));
+    }
+    if (lane == l) group = __popcll(same);
+    todo &= ~same;
+  }
+  int base = 0;
+  if (group > 0) base = atomicAdd(&cnt[bucket], group);
+  base = __shfl(base, leader < 0 ? lane : leader);
+  const int pos = leader < 0 ? -1 : base + rank;
+  if (i < total) pair_pos[i] = pos;
 }
 
 // exclusive prefix sum of n counts into off[0..n] (off[n] = total), one
@@ -86,15 +107,15 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(const int* __restric
 __global__ void prefill_scatter_kernel(const int32_t* __restrict__ sel_idx, const int* __restrict__ off,
                                        int32_t* __restrict__ pair_pos, int32_t* __restrict__ pairs, int Hq, int G,
                                        int64_t T_len, int64_t Nc, int k, int64_t total) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
   if (i >= total) return;
   const int32_t inb = pair_pos[i];
   if (inb < 0) return;
-  const int64_t row = i / k;
-  const int64_t bh = row / T_len;
-  const int h = (int)(bh % Hq);
-  const int64_t b = bh / Hq;
-  const int64_t bucket = (b * (Hq / G) + h / G) * Nc + sel_idx[i];
+  const int row = i / k;
+  const int bh = row / (int)T_len;
+  const int h = bh % Hq;
+  const int b = bh / Hq;
+  const int64_t bucket = ((int64_t)b * (Hq / G) + h / G) * Nc + sel_idx[i];
   const int32_t pos = off[bucket] + inb;
   pairs[pos] = (int32_t)row;
   pair_pos[i] = pos;

@@ -86,22 +86,33 @@ __device__ __forceinline__ void score_insert(float (&s)[K], float x) {
 }
 
 // ---------------------------------------------------------------- select
+//
+// One workgroup per (b, g, query chunk j) and group of up to four query
+// heads; one wave per head, 64 query rows per wave (lane = row).  Each wave
+// streams the landmark tiles (32 chunks) of its KV head from L2 and
+// contracts them with its queries on MFMA; the scores stay in registers.
+//
+// Pass 1 runs the tiles from the newest chunk down and keeps, per row, only
+// the multiset of the k best scores (one v_med3 per list position per
+// admitted candidate), which yields the row's k-th best score tau and how
+// many of the k best are strictly above it.  Pass 2 recomputes the same
+// tiles (bit-identical: same operands, same instruction sequence) in
+// ascending chunk order and collects every candidate above tau plus the
+// lowest-index candidates equal to tau until k are kept: exactly the first
+// k in the order (score desc, index asc).  Tiles whose maximum cannot reach
+// a row's threshold are skipped in both passes.
 template <typename T, int D, int G, int KSEL>
-__global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(const typename T::storage* __restrict__ q,
-                                                                  const typename T::storage* __restrict__ lm,
-                                                                  int32_t* __restrict__ sel_idx,
-                                                                  float* __restrict__ sel_score, int B, int Hkv,
-                                                                  int64_t T_len, int64_t Nc, int nqc, int k,
-                                                                  float scale) {
+__global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
+    const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ lm,
+    int32_t* __restrict__ sel_idx, float* __restrict__ sel_score, int B, int Hkv, int64_t T_len, int64_t Nc, int nqc,
+    int k, float scale) {
   using st = typename T::storage;
-  constexpr int HPW = G < 4 ? G : 4;        // query heads (waves) per workgroup
-  constexpr int HS = G / HPW;               // workgroups per (b, g, query chunk)
+  constexpr int HPW = G < 4 ? G : 4;  // query heads (waves) per workgroup
+  constexpr int HS = G / HPW;         // workgroups per (b, g, query chunk)
   constexpr int KCH = D / 16;
-  // per-lane buffer of admitted candidates, layout [wave][entry][lane] so that
-  // a wave's accesses are consecutive words; room for the kept top set (a
-  // compaction leaves at most KSEL entries) plus two groups of 8 new ones
-  constexpr int CAP = KSEL + 16;
-  __shared__ float2 cbuf[HPW][CAP][kWave];
+  constexpr int MAXT = 2048;          // tiles with a recorded pass-1 skip
+  __shared__ float2 cbuf[HPW][KSEL][kWave];
+  __shared__ uint8_t tskip[HPW][MAXT];
 
   const int bid = blockIdx.x;
   const int g = bid % Hkv;  // consecutive workgroups on different XCDs share nothing
@@ -114,104 +125,71 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(c
   const int Hq = Hkv * G, h = g * G + hs * HPW + hh;
   const int64_t n = min((int64_t)j, Nc);
 
-  // Per lane (= query row): ls holds the KSEL best scores seen so far in
-  // descending order (seeded with -FLT_MAX so that a masked -inf candidate
-  // never passes) and is updated at once on every admission; the LDS buffer
-  // keeps (score, index) of every admitted candidate.  Candidates are offered
-  // in descending chunk index, so among equal scores the later entry has the
-  // lower index and wins.  When a buffer could overflow it is compacted to
-  // the exact current top set.
-  float ls[KSEL];
-#pragma unroll
-  for (int e = 0; e < KSEL; ++e) ls[e] = -3.402823466e38f;
-  int cnt = 0;
-  auto wave_max = [&](int v) {
+  auto wave_max_i = [&](int v) {
     for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
-    return __builtin_amdgcn_readfirstlane(v);  // the same in every lane
+    return __builtin_amdgcn_readfirstlane(v);
   };
-  auto compact = [&]() {
-    const int mx = wave_max(cnt);
-    const float tau = ls[KSEL - 1];
-    int gt = 0, eq = 0;
-    for (int e = 0; e < mx; ++e) {
-      if (e < cnt) {
-        const float x = cbuf[hh][e][lane].x;
-        gt += x > tau;
-        eq += x == tau;
-      }
-    }
-    // of the entries equal to the threshold only the latest (lowest index)
-    // ones fit next to the gt strictly better ones
-    const int skip_eq = max(0, eq - (KSEL - gt));
-    int w = 0, seen_eq = 0;
-    for (int e = 0; e < mx; ++e) {
-      if (e < cnt) {
-        const float2 c = cbuf[hh][e][lane];
-        bool keep = c.x > tau;
-        if (c.x == tau) {
-          keep = seen_eq >= skip_eq;
-          ++seen_eq;
-        }
-        if (keep) {
-          cbuf[hh][w][lane] = c;
-          ++w;
-        }
-      }
-    }
-    cnt = w;
-  };
+
+  int cnt = 0;
   if (n > 0) {
     // Contraction index assignment (shared by both operands): in k-step s,
-    // lane half h supplies dims D/2*h + 8*s .. +8, so each lane reads one
-    // contiguous run of its row.
-    constexpr int HALF_D = D / 2;
+    // lane half h supplies dims 16*s + 8*h .. +8, so the two lanes of a row
+    // read adjacent 16-byte pieces of one cache line.  Rows past the end of
+    // the sequence or of the candidate range read a valid row instead; their
+    // results are never used (query rows) or masked to -inf (landmarks).
     Frag<T> qf[2][KCH];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int64_t tok = (int64_t)j * kChunk + 32 * nb + (lane & 31);
-      const bool ok = tok < T_len;
-      const st* qp = q + (((int64_t)b * Hq + h) * T_len + (ok ? tok : 0)) * D + HALF_D * half;
+      const int64_t tok = min((int64_t)j * kChunk + 32 * nb + (lane & 31), T_len - 1);
+      const st* qp = q + (((int64_t)b * Hq + h) * T_len + tok) * D + 8 * half;
 #pragma unroll
-      for (int s = 0; s < KCH; ++s) load_frag_global(qf[nb][s], qp + 8 * s, ok);
+      for (int s = 0; s < KCH; ++s) load_frag_global(qf[nb][s], qp + 16 * s, true);
     }
-    const st* lmg = lm + ((int64_t)b * Hkv + g) * Nc * D + HALF_D * half;
+    const st* lmg = lm + ((int64_t)b * Hkv + g) * Nc * D + 8 * half;
     const int ntiles = (int)((n + 31) / 32);
-    // each wave streams its own landmark fragments (A operand) from L2, one
-    // tile ahead; waves never wait for each other
-    Frag<T> an[KCH];
-    auto fetch = [&](int ti) {
-      const int64_t c = (int64_t)ti * 32 + (lane & 31);
-      const bool ok = c < n;
-      const st* p = lmg + (ok ? c : 0) * D;
+    // landmark fragments (A operand) of one tile, double-buffered
+    Frag<T> fa[KCH], fb[KCH];
+    auto fetch = [&](Frag<T>(&f)[KCH], int ti) {
+      const int64_t c = min((int64_t)ti * 32 + (lane & 31), n - 1);
+      const st* p = lmg + c * D;
 #pragma unroll
-      for (int s = 0; s < KCH; ++s) load_frag_global(an[s], p + 8 * s, ok);
+      for (int s = 0; s < KCH; ++s) load_frag_global(f[s], p + 16 * s, true);
     };
-    fetch(ntiles - 1);
-    for (int ti = ntiles - 1; ti >= 0; --ti) {
-      Frag<T> a[KCH];
-#pragma unroll
-      for (int s = 0; s < KCH; ++s) a[s] = an[s];
-      if (ti > 0) fetch(ti - 1);
-      f32x16 acc0 = {}, acc1 = {};
+    // scores of a tile: lane l gets them for query rows (l%32) and
+    // 32 + (l%32) at tile rows tile_row(r, l/32)
+    auto contract = [&](const Frag<T>(&f)[KCH], f32x16& acc0, f32x16& acc1) {
+      acc0 = f32x16{};
+      acc1 = f32x16{};
 #pragma unroll
       for (int s = 0; s < KCH; ++s) {
-        mfma(acc0, a[s], qf[0][s]);
-        mfma(acc1, a[s], qf[1][s]);
+        mfma(acc0, f[s], qf[0][s]);
+        mfma(acc1, f[s], qf[1][s]);
       }
-      // lane l now holds scores of tile rows tile_row(r, half) for query
-      // rows (l%32) and 32 + (l%32); swap halves so that lane l owns query
-      // row l: lo[r] -> tile row tile_row(r, 0), hi[r] -> tile_row(r, 1)
-      float lo[16], hi[16];
+    };
+    // per-row tile maximum: the per-lane maxima of acc0/acc1, swapped like
+    // the scores, combine into the maximum over the row's 32 candidates
+    auto row_max = [&](const f32x16& acc0, const f32x16& acc1) {
+      float m0 = acc0[0], m1 = acc1[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+        m0 = fmaxf(m0, acc0[r]);
+        m1 = fmaxf(m1, acc1[r]);
+      }
+      const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m1), false, false);
+      return fmaxf(__uint_as_float(pm[0]), __uint_as_float(pm[1]));
+    };
+    // lane l takes query row l: lo[r] -> tile row tile_row(r, 0), hi[r] ->
+    // tile_row(r, 1); rows of the top tile past the candidate range get -inf
+    auto to_rows = [&](const f32x16& acc0, const f32x16& acc1, int ti, float (&lo)[16], float (&hi)[16]) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0[r]), __float_as_uint(acc1[r]),
-                                                        false, false);
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0[r]), __float_as_uint(acc1[r]), false,
+                                                        false);
         lo[r] = __uint_as_float(p[0]);
         hi[r] = __uint_as_float(p[1]);
       }
       const int cbase = ti * 32;
       if ((int64_t)cbase + 32 > n) {
-        // rows of the top tile past the candidate range can never be chosen
         const int nv = (int)(n - cbase);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -219,29 +197,91 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(c
           if (tile_row(r, 1) >= nv) hi[r] = -__builtin_inff();
         }
       }
-      // Offer the tile's 32 candidates in descending index order: an
-      // admitted candidate updates the score list and is appended to the
-      // lane's buffer (exec-masked, so lanes pay only for their own events).
+    };
+    // candidate ii of the tile (chunk 32*ti + ii) in the lo/hi registers
+    auto cand = [](const float (&lo)[16], const float (&hi)[16], int ii) {
+      const int r = (ii / 8) * 4 + (ii % 4);
+      return ((ii / 4) & 1) ? hi[r] : lo[r];
+    };
+
+    // ---- pass 1: the multiset of the k best scores.  List positions above
+    // k hold +inf, so ls[KSEL-1] is the k-th best once k are seen; until
+    // then the -FLT_MAX seeds keep masked (-inf) candidates out.  A tile in
+    // which no row reaches its running threshold is marked: the threshold
+    // only grows, so pass 2 can skip it too.
+    float ls[KSEL];
 #pragma unroll
-      for (int gg = 3; gg >= 0; --gg) {
-        if (__ballot(cnt > CAP - 8)) compact();
+    for (int e = 0; e < KSEL; ++e) ls[e] = (e < KSEL - k) ? __builtin_inff() : -3.402823466e38f;
+    auto pass1 = [&](const Frag<T>(&f)[KCH], int ti) {
+      f32x16 acc0, acc1;
+      contract(f, acc0, acc1);
+      const bool top = (int64_t)ti * 32 + 32 > n;
+      if (!top && !__ballot(row_max(acc0, acc1) >= ls[KSEL - 1])) {
+        if (ti < MAXT && lane == 0) tskip[hh][ti] = 1;
+        return;
+      }
+      if (ti < MAXT && lane == 0) tskip[hh][ti] = 0;
+      float lo[16], hi[16];
+      to_rows(acc0, acc1, ti, lo, hi);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ii = 8 * gg + 7 - e;
-          const int r = (ii / 8) * 4 + (ii % 4);
-          const float x = ((ii / 4) & 1) ? hi[r] : lo[r];
-          if (x >= ls[KSEL - 1]) {
-            score_insert<KSEL>(ls, x);
-            cbuf[hh][cnt][lane] = make_float2(x, __int_as_float(cbase + ii));
+      for (int ii = 31; ii >= 0; --ii) {
+        const float x = cand(lo, hi, ii);
+        if (x >= ls[KSEL - 1]) score_insert<KSEL>(ls, x);
+      }
+    };
+    fetch(fa, ntiles - 1);
+    for (int ti = ntiles - 1; ti >= 0; ti -= 2) {
+      if (ti >= 1) fetch(fb, ti - 1);
+      pass1(fa, ti);
+      if (ti < 1) break;
+      if (ti >= 2) fetch(fa, ti - 2);
+      pass1(fb, ti - 1);
+    }
+
+    // ---- pass 2: collect the k best in ascending chunk order
+    const float tau = ls[KSEL - 1];
+    int quota = KSEL;  // entries equal to tau that still fit
+#pragma unroll
+    for (int e = 0; e < KSEL; ++e) quota -= ls[e] > tau;
+    auto next_tile = [&](int ti) {
+      while (ti < ntiles && ti < MAXT && tskip[hh][ti]) ++ti;
+      return ti;
+    };
+    auto pass2 = [&](const Frag<T>(&f)[KCH], int ti) {
+      f32x16 acc0, acc1;
+      contract(f, acc0, acc1);
+      const bool top = (int64_t)ti * 32 + 32 > n;
+      if (!top && !__ballot(row_max(acc0, acc1) >= tau)) return;
+      float lo[16], hi[16];
+      to_rows(acc0, acc1, ti, lo, hi);
+#pragma unroll
+      for (int ii = 0; ii < 32; ++ii) {
+        const float x = cand(lo, hi, ii);
+        if (x >= tau) {
+          const bool take = x > tau || quota > 0;
+          if (x == tau) --quota;
+          if (take && cnt < KSEL) {
+            cbuf[hh][cnt][lane] = make_float2(x, __int_as_float(ti * 32 + ii));
             ++cnt;
           }
         }
       }
+    };
+    int ti = next_tile(0);
+    if (ti < ntiles) fetch(fa, ti);
+    while (ti < ntiles) {
+      const int t1 = next_tile(ti + 1);
+      if (t1 < ntiles) fetch(fb, t1);
+      pass2(fa, ti);
+      if (t1 >= ntiles) break;
+      const int t2 = next_tile(t1 + 1);
+      if (t2 < ntiles) fetch(fa, t2);
+      pass2(fb, t1);
+      ti = t2;
     }
-    compact();
   }
   const int64_t t_row = (int64_t)j * kChunk + lane;
-  // order the final top set by (score desc, index asc)
+  // order the kept set by (score desc, index asc)
   float os[KSEL];
   int oi[KSEL];
 #pragma unroll
@@ -250,7 +290,7 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(c
     oi[e] = INT_MAX;
   }
   {
-    const int mx = wave_max(cnt);
+    const int mx = wave_max_i(cnt);
     for (int e = 0; e < mx; ++e) {
       if (e < cnt) {
         const float2 c = cbuf[hh][e][lane];
@@ -293,55 +333,66 @@ __device__ __forceinline__ int vt_pos(int t) {
   return (t / 16) * 16 + ((t % 8) / 4) * 8 + 4 * ((t % 16) / 8) + (t % 4);
 }
 
+// XOR swizzle of the 16-byte slots of V^T column d.  Reads take eight
+// consecutive columns at once (d & 7 varies); stash writes take columns
+// eight apart (d >> 3 varies): both sets land on distinct slots.
+__device__ __forceinline__ int vt_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
+
 // Stages one chunk's K tile (row-major, 16-byte slots XOR-swizzled by row)
 // and V^T tile (column-major with the token order of vt_pos, slots swizzled
-// by column) into LDS.  NTH threads cooperate; NP slots per thread per pass.
+// by vt_swz) into LDS.  NTH threads cooperate; a unit of work is one
+// 16-byte column slot of four consecutive tokens, so each thread writes the
+// four tokens of a V^T column as one contiguous 8-byte (bf16) or 16-byte
+// (fp32) piece.
 template <typename T, int D, int NTH>
 struct KVStage {
   using st = typename T::storage;
-  static constexpr int EPS = 16 / T::kBytes;
+  static constexpr int EPS = 16 / T::kBytes;  // elements per 16-byte slot
   static constexpr int ROWB = D * T::kBytes;
   static constexpr int NSL = ROWB / 16;
-  static constexpr int KV_SLOTS = kChunk * NSL;
-  static constexpr int LPT = KV_SLOTS / NTH;
-  static constexpr int NP = LPT < 4 ? LPT : 4;
-  static constexpr int PASSES = LPT / NP;
+  static constexpr int UNITS = NSL * (kChunk / 4);
+  static constexpr int PASSES = (UNITS + NTH - 1) / NTH;
   static constexpr int VTB = kChunk * T::kBytes;
   static constexpr int BYTES = 2 * kChunk * ROWB;
-  static_assert(KV_SLOTS % NTH == 0 && LPT % NP == 0, "tile slots must divide evenly");
-  u32x4 kpre[NP], vpre[NP];
+  u32x4 kpre[4], vpre[4];
 
   __device__ __forceinline__ void fetch(const st* kg, const st* vg, int64_t c, int pass, int tid) {
+    const int u = tid + pass * NTH;
+    if (UNITS % NTH != 0 && u >= UNITS) return;
+    const int sl = u % NSL, t0 = 4 * (u / NSL);
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int slot = tid + (pass * NP + i) * NTH;
-      const int64_t off = (c * kChunk + slot / NSL) * D + (slot % NSL) * EPS;
+    for (int i = 0; i < 4; ++i) {
+      const int64_t off = (c * kChunk + t0 + i) * D + sl * EPS;
       kpre[i] = *reinterpret_cast<const u32x4*>(kg + off);
       vpre[i] = *reinterpret_cast<const u32x4*>(vg + off);
     }
   }
   __device__ __forceinline__ void stash(char* ks, char* vt, int pass, int tid) {
+    const int u = tid + pass * NTH;
+    if (UNITS % NTH != 0 && u >= UNITS) return;
+    const int sl = u % NSL, t0 = 4 * (u / NSL);
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int slot = tid + (pass * NP + i) * NTH;
-      const int t = slot / NSL, sl = slot % NSL;
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + i;
       *reinterpret_cast<u32x4*>(ks + t * ROWB + ((sl ^ (t & 7)) * 16)) = kpre[i];
-      const int p = vt_pos(t);
-      if constexpr (T::kBytes == 2) {
+    }
+    const int p = vt_pos(t0);  // the four tokens sit at p .. p+3
+    if constexpr (T::kBytes == 2) {
 #pragma unroll
-        for (int e = 0; e < EPS; ++e) {
-          const int d = sl * EPS + e;
-          const int pp = (((p / 8) ^ (d & 7)) * 8) + (p % 8);
-          const uint32_t w32 = vpre[i][e / 2];
-          reinterpret_cast<uint16_t*>(vt + d * VTB)[pp] = (uint16_t)((e & 1) ? (w32 >> 16) : (w32 & 0xffffu));
-        }
-      } else {
+      for (int e = 0; e < EPS; ++e) {
+        const int d = sl * EPS + e;
+        const int w = e / 2, sh = (e & 1) * 16;
+        const uint32_t lo = ((vpre[0][w] >> sh) & 0xffffu) | (((vpre[1][w] >> sh) & 0xffffu) << 16);
+        const uint32_t hi = ((vpre[2][w] >> sh) & 0xffffu) | (((vpre[3][w] >> sh) & 0xffffu) << 16);
+        const int pp = (((p / 8) ^ vt_swz(d)) * 8) + (p % 8);
+        *reinterpret_cast<u32x2*>(vt + d * VTB + pp * 2) = u32x2{lo, hi};
+      }
+    } else {
 #pragma unroll
-        for (int e = 0; e < EPS; ++e) {
-          const int d = sl * EPS + e;
-          const int pp = (((p / 4) ^ (d & 7)) * 4) + (p % 4);
-          reinterpret_cast<uint32_t*>(vt + d * VTB)[pp] = vpre[i][e];
-        }
+      for (int e = 0; e < EPS; ++e) {
+        const int d = sl * EPS + e;
+        const int pp = ((p / 4) ^ vt_swz(d)) * 4;
+        *reinterpret_cast<u32x4*>(vt + d * VTB + pp * 4) = u32x4{vpre[0][e], vpre[1][e], vpre[2][e], vpre[3][e]};
       }
     }
   }
@@ -414,7 +465,7 @@ __device__ __forceinline__ void attend_block(const Frag<T> (&qf)[D / 16], const 
       for (int dm = 0; dm < DM; ++dm) {
         Frag<BF16> a;
         const int d = 32 * dm + (lane & 31);
-        const int slot = (2 * ks_ + half) ^ (d & 7);
+        const int slot = (2 * ks_ + half) ^ vt_swz(d);
         a.load16(vt + d * VTB + slot * 16);
         mfma(oacc[dm], a, phi);
         mfma(oacc[dm], a, plo);
@@ -427,8 +478,8 @@ __device__ __forceinline__ void attend_block(const Frag<T> (&qf)[D / 16], const 
       for (int dm = 0; dm < DM; ++dm) {
         Frag<FP32> a;
         const int d = 32 * dm + (lane & 31);
-        const int s0i = (4 * ks_ + 2 * half) ^ (d & 7);
-        const int s1i = (4 * ks_ + 2 * half + 1) ^ (d & 7);
+        const int s0i = (4 * ks_ + 2 * half) ^ vt_swz(d);
+        const int s1i = (4 * ks_ + 2 * half + 1) ^ vt_swz(d);
         const f32x4 x0 = *reinterpret_cast<const f32x4*>(vt + d * VTB + s0i * 16);
         const f32x4 x1 = *reinterpret_cast<const f32x4*>(vt + d * VTB + s1i * 16);
 #pragma unroll
@@ -503,7 +554,11 @@ __global__ __launch_bounds__(256) void prefill_remote_kernel(const typename T::s
 
 // ---- local pairs and fusion
 template <typename T, int D, int G, int KSEL>
-__global__ __launch_bounds__(kWave* G) void prefill_local_kernel(
+#ifndef HSA_ATTN_LOCAL_WAVES_PER_EU
+#define HSA_ATTN_LOCAL_WAVES_PER_EU 2
+#endif
+__global__ __launch_bounds__(kWave* G)
+    __attribute__((amdgpu_waves_per_eu(HSA_ATTN_LOCAL_WAVES_PER_EU))) void prefill_local_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ kk,
     const typename T::storage* __restrict__ vv, const int32_t* __restrict__ sel_idx,
     const float* __restrict__ sel_score, const int32_t* __restrict__ pair_pos, const float* __restrict__ partial,

@@ -33,7 +33,8 @@
  *  - Errors: HSA_ATTN_INVALID_ARGUMENT (null or misaligned pointer, bad
  *    sizes), HSA_ATTN_UNSUPPORTED (sizes outside the supported envelope:
  *    D in {64,128}, S == 64 for the forward calls, Hq/Hkv in {1,2,4,8},
- *    k <= 64 for decode and k <= 32 for prefill), HSA_ATTN_WORKSPACE_TOO_SMALL,
+ *    k <= 64 for decode and k <= 32 for prefill; prefill also needs
+ *    floor(T/S) <= 65536 and B*Hq*T*k < 2^31), HSA_ATTN_WORKSPACE_TOO_SMALL,
  *    HSA_ATTN_HIP_ERROR (a launch failed).  hsa_attn_last_error() returns a
  *    thread-local message about the last failure.
  */
@@ -96,7 +97,12 @@ hsa_attn_status_t hsa_build_landmarks(const hsa_attn_dims_t* d, const void* k, v
  * [B,Hq,T,k] are optional outputs (NULL: kept in the workspace); slots are
  * ordered by score descending, then index ascending.
  * workspace: device scratch of at least hsa_attn_workspace_size(d, 0) bytes
- * (may be NULL when that size is 0).
+ * (never NULL when T > 0).  It holds the selection when sel_idx is NULL,
+ * the bucketing of selected chunks that lie before the query's aligned
+ * window of 64 chunks, and one fp32 [D] attention output per such pair.
+ * The size covers the worst case, every selected pair outside the window:
+ * about B*Hq*T*k*(4*D + 16) bytes (69 GB at B=1, Hq=32, T=2^18, k=16,
+ * D=128).
  */
 hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, const void* k,
                                       const void* v, const void* landmarks, float* out,
@@ -123,7 +129,8 @@ hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, co
  * the calling thread records events[2*i] (hipEvent_t, created by the caller)
  * on its stream just before its i-th kernel launch and events[2*i+1] just
  * after it, for i < n_pairs; the index restarts at 0 with each call.
- * Launch order: landmarks: 1 kernel; prefill: select, attention; decode:
+ * Launch order: landmarks: 1 kernel; prefill: select, then (when T >= S)
+ * zero, count, scan, scatter, remote attention, then local attention; decode:
  * scan, merge, attention, fusion (scan and attention are skipped when the
  * cache has no complete chunk).  events == NULL or n_pairs == 0 turns
  * recording off.  The setting is thread-local; the events stay owned by the
