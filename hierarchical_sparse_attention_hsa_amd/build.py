@@ -23,6 +23,9 @@ ARCH = "gfx950"
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the scores and outputs feed VALU
+    # code directly, without v_accvgpr_read copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(os.path.dirname(HERE), "include"),
 ]
 

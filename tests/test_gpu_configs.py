@@ -1,0 +1,146 @@
+"""GPU parity at the five full workload sizes, in the launch configuration the
+benchmark times: the whole layer runs at full size and sampled rows (all
+rows for the 4K prefill) are checked against the oracle under the layer's
+acceptance rule.  Landmarks of the sampled KV heads are checked bit for bit
+(bf16) or to within one ulp (fp32).
+
+Inputs come from the seeded generators in workloads.py; the oracle reads
+them from the device (the same values the kernels read), never any output of
+the HIP path."""
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_hsa_amd as hsa
+from hierarchical_sparse_attention_hsa_amd.workloads import WORKLOADS, decode_inputs, prefill_inputs
+from oracle import hsa_oracle as O
+from tests.gpu_util import TOL, check_rows, new_stats
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+
+def host64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+class DeviceRows:
+    """[T, D] view of a device tensor for the oracle: fancy indexing fetches
+    just the indexed rows as float64 (the caches are too large to copy)."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, idx):
+        idx = np.asarray(idx)
+        rows = self.t[torch.as_tensor(idx.reshape(-1), device=self.t.device)]
+        return host64(rows).reshape(idx.shape + (self.shape[-1],))
+
+
+def oracle_landmarks(kg, S, dtype, slab=1 << 20):
+    """Oracle landmarks of one KV head [T, D] on the device, slab by slab."""
+    T = kg.shape[0]
+    Nc = T // S
+    parts = []
+    for t0 in range(0, Nc * S, slab):
+        t1 = min(Nc * S, t0 + slab)
+        parts.append(O.landmarks(host64(kg[t0:t1]), S, dtype))
+    return np.concatenate(parts, axis=0) if parts else np.zeros((0, kg.shape[1]))
+
+
+def check_landmarks(L_gpu, L_ref, dtype):
+    got = host64(L_gpu)
+    if dtype == "bf16":
+        assert np.array_equal(got, L_ref), "bf16 landmarks must match the oracle bit for bit"
+    else:
+        ulp = np.spacing(np.abs(L_ref).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got - L_ref) <= ulp), "fp32 landmarks must be within one ulp"
+
+
+def run_prefill_workload(name, chunks, heads=None):
+    w = WORKLOADS[name]
+    print(f"workload {name}: sampled query chunks {chunks}", flush=True)
+    q, k, v = prefill_inputs(w, "cuda")
+    Nc = w.T // w.S
+    L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
+    out = torch.empty((w.B, w.Hq, w.T, w.D), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.float32, device="cuda")
+    hsa.hsa_build_landmarks(k, L, w.S)
+    hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
+    torch.cuda.synchronize()
+    pos = np.concatenate([np.arange(c * w.S, min(w.T, (c + 1) * w.S)) for c in chunks]) if chunks is not None \
+        else np.arange(w.T)
+    pos_t = torch.as_tensor(pos, device="cuda")
+    G = w.Hq // w.Hkv
+    stats = new_stats()
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            Kg, Vg = host64(k[b, g]), host64(v[b, g])
+            Lg = O.landmarks(Kg, w.S, w.dtype)
+            check_landmarks(L[b, g], Lg, w.dtype)
+            for h in range(g * G, (g + 1) * G):
+                if heads is not None and h not in heads:
+                    continue
+                check_rows(host64(q[b, h, pos_t]), pos, Kg, Vg, Lg, w.S, w.k, host64(out[b, h, pos_t]),
+                           sel[b, h, pos_t].cpu().numpy(), host64(sc[b, h, pos_t]), TOL[w.dtype], stats)
+    print(name, stats, flush=True)
+    del q, k, v, L, out, sel, sc
+    torch.cuda.empty_cache()
+    return stats
+
+
+def test_prefill_4k_fp32_every_row():
+    stats = run_prefill_workload("prefill_4k_fp32", None)
+    assert stats["rows"] == 4 * 4096
+
+
+def test_prefill_32k_bf16_sampled():
+    # no candidate, one candidate, exactly k, k + 1, and spread chunks to the last
+    run_prefill_workload("prefill_32k_bf16", [0, 1, 16, 17, 100, 255, 400, 511])
+
+
+def test_prefill_256k_bf16_sampled():
+    # the special chunks, chunks around window and segment edges, and chunks
+    # spread over the sequence
+    run_prefill_workload("prefill_256k_bf16", [0, 1, 16, 17, 63, 64, 65, 1000, 2047, 3333, 4095])
+
+
+def run_decode_workload(name, queries):
+    w = WORKLOADS[name]
+    esz = 2 if w.dtype == "bf16" else 4
+    Nc = w.T // w.S
+    need = 2 * w.B * w.Hkv * w.T * w.D * esz + w.B * w.Hkv * Nc * w.D * esz
+    free, _ = torch.cuda.mem_get_info()
+    if need + (2 << 30) > free:
+        pytest.skip(f"{name} needs {need / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} GiB free")
+    print(f"workload {name}: sampled queries {queries}", flush=True)
+    q, k, v = decode_inputs(w, "cuda")
+    L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
+    hsa.hsa_build_landmarks(k, L, w.S)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, w.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, w.k), dtype=torch.float32, device="cuda")
+    hsa.hsa_forward_decode(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    stats = new_stats()
+    for b in queries:
+        for g in range(w.Hkv):
+            Lg = oracle_landmarks(k[b, g], w.S, w.dtype)
+            check_landmarks(L[b, g], Lg, w.dtype)
+            hs = slice(g * G, (g + 1) * G)
+            check_rows(host64(q[b, hs]), np.full(G, w.T), DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lg, w.S, w.k,
+                       host64(out[b, hs]), sel[b, hs].cpu().numpy(), host64(sc[b, hs]), TOL[w.dtype], stats)
+        print(name, "query", b, stats, flush=True)
+    del q, k, v, L, out, sel, sc
+    torch.cuda.empty_cache()
+    return stats
+
+
+def test_decode_1m_bf16_sampled():
+    run_decode_workload("decode_1m_bf16", [0, 41])
+
+
+def test_decode_16m_bf16_sampled():
+    run_decode_workload("decode_16m_bf16", [2])
