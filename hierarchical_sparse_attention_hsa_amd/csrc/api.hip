@@ -187,7 +187,7 @@ hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, c
     hsa_attn::PrefillArgs a{g, q, k, v, landmarks, out, sel_idx, sel_score,
                             reinterpret_cast<int32_t*>(ws + plan.off_pair_pos), reinterpret_cast<int*>(ws + plan.off_cnt),
                             reinterpret_cast<int*>(ws + plan.off_off), reinterpret_cast<int32_t*>(ws + plan.off_pairs),
-                            reinterpret_cast<float*>(ws + plan.off_partial)};
+                            reinterpret_cast<float*>(ws + plan.off_partial), ws + plan.off_vt};
     return hip_status(hsa_attn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
   } catch (const std::exception& e) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());

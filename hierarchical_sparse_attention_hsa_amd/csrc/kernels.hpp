@@ -51,7 +51,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s
 
 // ---------------------------------------------------------------- prefill
 struct PrefillPlan {
-  size_t off_sel_idx, off_sel_score, off_pair_pos, off_cnt, off_off, off_pairs, off_partial, bytes;
+  size_t off_sel_idx, off_sel_score, off_pair_pos, off_cnt, off_off, off_pairs, off_partial, off_vt, bytes;
 };
 PrefillPlan plan_prefill(const Geometry& g, bool own_sel);
 
@@ -67,6 +67,7 @@ struct PrefillArgs {
   int* off;           // [B * Hkv * Nc + 1]
   int32_t* pairs;     // [B * Hq * T * k] (worst case)
   float* partial;     // [B * Hq * T * k, D] (worst case)
+  void* vt;           // [B, Hkv, Nc, D, 64] transposed V tiles (storage dtype)
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 

@@ -170,14 +170,19 @@ PrefillPlan plan_prefill(const Geometry& g, bool own_sel) {
   off = align_up_p(off + pairs * sizeof(int32_t), 256);
   p.off_partial = off;
   off = align_up_p(off + pairs * g.D * sizeof(float), 256);
+  p.off_vt = off;
+  off = align_up_p(off + nb * kChunk * g.D * (g.bf16 ? 2 : 4), 256);
   p.bytes = off;
   return p;
 }
 
-size_t prefill_attn_lds_bytes(const Geometry& g) {
+size_t prefill_local_lds_bytes(const Geometry& g, int nbuf) {
   const size_t esz = g.bf16 ? 2 : 4;
-  return 2 * (size_t)kChunk * g.D * esz + (size_t)32 * g.G * g.k * 8;
+  return (size_t)nbuf * 2 * kChunk * g.D * esz + (size_t)32 * g.G * g.k * 8;
 }
+
+// two chunk images when they fit next to the tables in the 160 KiB of LDS
+int prefill_local_buffers(const Geometry& g) { return prefill_local_lds_bytes(g, 2) <= 160 * 1024 ? 2 : 1; }
 
 // the register top-k list holds 16 or 32 entries; k <= 16 uses the short list
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {

@@ -338,73 +338,131 @@ __device__ __forceinline__ int vt_pos(int t) {
 // eight apart (d >> 3 varies): both sets land on distinct slots.
 __device__ __forceinline__ int vt_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
 
-// Stages one chunk's K tile (row-major, 16-byte slots XOR-swizzled by row)
-// and V^T tile (column-major with the token order of vt_pos, slots swizzled
-// by vt_swz) into LDS.  NTH threads cooperate; a unit of work is one
-// 16-byte column slot of four consecutive tokens, so each thread writes the
-// four tokens of a V^T column as one contiguous 8-byte (bf16) or 16-byte
-// (fp32) piece.
-template <typename T, int D, int NTH>
-struct KVStage {
-  using st = typename T::storage;
-  static constexpr int EPS = 16 / T::kBytes;  // elements per 16-byte slot
-  static constexpr int ROWB = D * T::kBytes;
-  static constexpr int NSL = ROWB / 16;
-  static constexpr int UNITS = NSL * (kChunk / 4);
-  static constexpr int PASSES = (UNITS + NTH - 1) / NTH;
-  static constexpr int VTB = kChunk * T::kBytes;
-  static constexpr int BYTES = 2 * kChunk * ROWB;
-  u32x4 kpre[4], vpre[4];
+// LDS image of one chunk (both attention kernels): the K tile, 64 rows of
+// D elements whose 16-byte slots are XOR-swizzled by (row & 7), then the
+// V^T tile, D rows of 64 tokens in vt_pos order whose 16-byte slots are
+// swizzled by vt_swz(d).  Both are filled by direct global->LDS loads
+// (global_load_lds_dwordx4: lane i of an instruction writes LDS bytes
+// base + 16 i), the swizzle being applied on the global side; V^T comes from
+// the transposed copy written by prefill_vt_kernel.
+template <typename T, int D>
+struct Tile {
+  static constexpr int ROWB = D * T::kBytes;       // K row bytes
+  static constexpr int NSL = ROWB / 16;            // 16-byte slots per K row
+  static constexpr int VTB = kChunk * T::kBytes;   // V^T row bytes
+  static constexpr int NSLV = VTB / 16;            // 16-byte slots per V^T row
+  static constexpr int KBYTES = kChunk * ROWB;
+  static constexpr int BYTES = 2 * KBYTES;         // K tile + V^T tile
+  static constexpr int NK = kChunk * NSL / kWave;  // load instructions for K
+  static constexpr int NV = D * NSLV / kWave;      // load instructions for V^T
+  static_assert(NSL >= 8 && NSLV >= 8, "swizzles need 8 slots per row");
 
-  __device__ __forceinline__ void fetch(const st* kg, const st* vg, int64_t c, int pass, int tid) {
-    const int u = tid + pass * NTH;
-    if (UNITS % NTH != 0 && u >= UNITS) return;
-    const int sl = u % NSL, t0 = 4 * (u / NSL);
+  // Issue this wave's share (instructions w, w + NW, ...) of the loads of a
+  // chunk: kb = the chunk's K rows, vtb = its V^T tile, lds = the buffer.
+  template <int NW>
+  static __device__ __forceinline__ void issue(const char* kb, const char* vtb, char* lds, int w, int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t off = (c * kChunk + t0 + i) * D + sl * EPS;
-      kpre[i] = *reinterpret_cast<const u32x4*>(kg + off);
-      vpre[i] = *reinterpret_cast<const u32x4*>(vg + off);
+    for (int ii = 0; ii < NK + NV; ++ii) {
+      if (ii % NW != w) continue;
+      const char* src;
+      if (ii < NK) {
+        const int L = ii * kWave + lane;
+        const int t = L / NSL, sp = L % NSL;
+        src = kb + t * ROWB + ((sp ^ (t & 7)) * 16);
+      } else {
+        const int L = (ii - NK) * kWave + lane;
+        const int d = L / NSLV, sp = L % NSLV;
+        src = vtb + d * VTB + ((sp ^ vt_swz(d)) * 16);
+      }
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds + ii * kWave * 16), 16, 0,
+                                       0);
     }
   }
-  __device__ __forceinline__ void stash(char* ks, char* vt, int pass, int tid) {
-    const int u = tid + pass * NTH;
-    if (UNITS % NTH != 0 && u >= UNITS) return;
-    const int sl = u % NSL, t0 = 4 * (u / NSL);
+};
+
+// wait for this wave's direct-to-LDS loads
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposed copy of V for the attention kernels: for every complete chunk,
+// D rows of its 64 values of dimension d, tokens in vt_pos order, so that a
+// chunk's V^T tile is one contiguous block.  One workgroup per chunk: a
+// thread loads 16 bytes of 4 consecutive tokens, writes them transposed into
+// LDS (4 tokens of one column form one contiguous piece), and the tile then
+// leaves LDS in 16-byte slots.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prefill_vt_kernel(const typename T::storage* __restrict__ vv,
+                                                         typename T::storage* __restrict__ vt_g, int64_t T_len,
+                                                         int64_t Nc) {
+  using st = typename T::storage;
+  using TL = Tile<T, D>;
+  constexpr int EPS = 16 / T::kBytes;
+  constexpr int UNITS = TL::NSL * (kChunk / 4);
+  __shared__ __align__(16) char vt[D * TL::VTB];
+  const int64_t bc = blockIdx.x;  // (b * Hkv + g) * Nc + c
+  const int64_t c = bc % Nc, bg = bc / Nc;
+  const st* vb = vv + (bg * T_len + c * kChunk) * D;
+  const int tid = threadIdx.x;
+  for (int u = tid; u < UNITS; u += 256) {
+    const int sl = u % TL::NSL, t0 = 4 * (u / TL::NSL);
+    u32x4 v4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + i;
-      *reinterpret_cast<u32x4*>(ks + t * ROWB + ((sl ^ (t & 7)) * 16)) = kpre[i];
-    }
+    for (int i = 0; i < 4; ++i) v4[i] = *reinterpret_cast<const u32x4*>(vb + (t0 + i) * D + sl * EPS);
     const int p = vt_pos(t0);  // the four tokens sit at p .. p+3
     if constexpr (T::kBytes == 2) {
 #pragma unroll
       for (int e = 0; e < EPS; ++e) {
         const int d = sl * EPS + e;
         const int w = e / 2, sh = (e & 1) * 16;
-        const uint32_t lo = ((vpre[0][w] >> sh) & 0xffffu) | (((vpre[1][w] >> sh) & 0xffffu) << 16);
-        const uint32_t hi = ((vpre[2][w] >> sh) & 0xffffu) | (((vpre[3][w] >> sh) & 0xffffu) << 16);
+        const uint32_t lo = ((v4[0][w] >> sh) & 0xffffu) | (((v4[1][w] >> sh) & 0xffffu) << 16);
+        const uint32_t hi = ((v4[2][w] >> sh) & 0xffffu) | (((v4[3][w] >> sh) & 0xffffu) << 16);
         const int pp = (((p / 8) ^ vt_swz(d)) * 8) + (p % 8);
-        *reinterpret_cast<u32x2*>(vt + d * VTB + pp * 2) = u32x2{lo, hi};
+        *reinterpret_cast<u32x2*>(vt + d * TL::VTB + pp * 2) = u32x2{lo, hi};
       }
     } else {
 #pragma unroll
       for (int e = 0; e < EPS; ++e) {
         const int d = sl * EPS + e;
         const int pp = ((p / 4) ^ vt_swz(d)) * 4;
-        *reinterpret_cast<u32x4*>(vt + d * VTB + pp * 4) = u32x4{vpre[0][e], vpre[1][e], vpre[2][e], vpre[3][e]};
+        *reinterpret_cast<u32x4*>(vt + d * TL::VTB + pp * 4) = u32x4{v4[0][e], v4[1][e], v4[2][e], v4[3][e]};
       }
     }
   }
-  // whole tile, fetch and stash pass by pass (caller synchronises)
-  __device__ __forceinline__ void load(const st* kg, const st* vg, int64_t c, char* ks, char* vt, int tid) {
-#pragma unroll 1
-    for (int ps = 0; ps < PASSES; ++ps) {
-      fetch(kg, vg, c, ps, tid);
-      stash(ks, vt, ps, tid);
-    }
+  __syncthreads();
+  char* out = reinterpret_cast<char*>(vt_g) + bc * (int64_t)(D * TL::VTB);
+  for (int L = tid; L < D * TL::NSLV; L += 256) {
+    const int d = L / TL::NSLV, sl = L % TL::NSLV;  // logical slot sl of row d
+    *reinterpret_cast<u32x4*>(out + d * TL::VTB + sl * 16) =
+        *reinterpret_cast<const u32x4*>(vt + d * TL::VTB + ((sl ^ vt_swz(d)) * 16));
   }
-};
+}
+
+// max / sum of a value over the lane pair (l, l ^ 32)
+__device__ __forceinline__ float pair_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// x = head + tail with head = x truncated to bf16 and tail = the exact
+// remainder rounded to bf16 (relative error of head + tail below 2^-16)
+__device__ __forceinline__ void split_bf16(const float (&x)[8], Frag<BF16>& head, Frag<BF16>& tail) {
+  u32x4 hw, tw;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = __float_as_uint(x[2 * i]), b = __float_as_uint(x[2 * i + 1]);
+    hw[i] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // upper halves of a (low) and b (high)
+    const f32x2 r{x[2 * i] - __uint_as_float(a & 0xffff0000u), x[2 * i + 1] - __uint_as_float(b & 0xffff0000u)};
+    const bf16x2 t = __builtin_convertvector(r, bf16x2);
+    uint32_t tw32;
+    __builtin_memcpy(&tw32, &t, 4);
+    tw[i] = tw32;
+  }
+  head.v = as_bf16x8(hw);
+  tail.v = as_bf16x8(tw);
+}
 
 // One wave, 32 query rows (B operand qf, row = lane % 32; lanes l and l^32
 // hold the two halves of each row): softmax attention over the 64 tokens of
@@ -429,38 +487,34 @@ __device__ __forceinline__ void attend_block(const Frag<T> (&qf)[D / 16], const 
     mfma(s0, a0, qf[s]);
     mfma(s1, a1, qf[s]);
   }
-  // softmax over the row's 64 tokens; lane l and l^32 split them
+  // softmax over the row's 64 tokens; lane l and l^32 split them (the
+  // permlane32 swap hands each lane its partner's value)
   float mx = -__builtin_inff();
 #pragma unroll
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = pair_max(mx);
+  const float mb = mx * cexp;
   float sum = 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    s0[r] = __builtin_amdgcn_exp2f((s0[r] - mx) * cexp);
-    s1[r] = __builtin_amdgcn_exp2f((s1[r] - mx) * cexp);
+    s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], cexp, -mb));
+    s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], cexp, -mb));
     sum += s0[r] + s1[r];
   }
-  sum += __shfl_xor(sum, 32);
+  sum = pair_sum(sum);
   const float f = factor / sum;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s0[r] *= f;
-    s1[r] *= f;
-  }
   // O^T += V^T P'^T over four 16-token k-steps
 #pragma unroll
   for (int ks_ = 0; ks_ < 4; ++ks_) {
     float pv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = (ks_ < 2) ? s0[8 * (ks_ & 1) + e] : s1[8 * (ks_ & 1) + e];
+    for (int e = 0; e < 8; ++e) pv[e] = f * ((ks_ < 2) ? s0[8 * (ks_ & 1) + e] : s1[8 * (ks_ & 1) + e]);
     if constexpr (T::kBytes == 2) {
+      // P' = head + tail: the head is P' truncated to bf16 (exact upper
+      // half), the tail the exact remainder rounded to bf16, so head + tail
+      // carries about 16 significant bits
       Frag<BF16> phi, plo;
-      phi.from_f32(pv);
-      float rem[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) rem[e] = pv[e] - static_cast<float>(phi.v[e]);
-      plo.from_f32(rem);
+      split_bf16(pv, phi, plo);
 #pragma unroll
       for (int dm = 0; dm < DM; ++dm) {
         Frag<BF16> a;
@@ -506,26 +560,27 @@ hipError_t launch_prefill_bucketing(const PrefillArgs& a, hipStream_t st);
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void prefill_remote_kernel(const typename T::storage* __restrict__ q,
                                                              const typename T::storage* __restrict__ kk,
-                                                             const typename T::storage* __restrict__ vv,
+                                                             const typename T::storage* __restrict__ vt_g,
                                                              const int* __restrict__ off,
                                                              const int32_t* __restrict__ pairs,
                                                              float* __restrict__ partial, int Hkv, int64_t T_len,
                                                              int64_t Nc, float scale) {
   using st = typename T::storage;
-  using Stage = KVStage<T, D, 256>;
+  using TL = Tile<T, D>;
   constexpr int KCH = D / 16;
   constexpr int DM = D / 32;
-  __shared__ __align__(16) char smem[Stage::BYTES];
+  __shared__ __align__(16) char smem[TL::BYTES];
   char* ks = smem;
-  char* vt = smem + kChunk * Stage::ROWB;
+  char* vt = smem + TL::KBYTES;
   const int64_t bucket = blockIdx.x;
   const int begin = off[bucket], end = off[bucket + 1];
   if (begin == end) return;
   const int64_t c = bucket % Nc;
   const int64_t bg = bucket / Nc;  // b * Hkv + g
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-  Stage stage;
-  stage.load(kk + bg * T_len * D, vv + bg * T_len * D, c, ks, vt, tid);
+  TL::template issue<4>(reinterpret_cast<const char*>(kk + (bg * T_len + c * kChunk) * D),
+                        reinterpret_cast<const char*>(vt_g) + bucket * (int64_t)TL::KBYTES, smem, wave, lane);
+  wait_loads();
   __syncthreads();
   const float cexp = scale * 1.4426950408889634f;
   for (int blk = wave; begin + 32 * blk < end; blk += 4) {
@@ -560,22 +615,23 @@ template <typename T, int D, int G, int KSEL>
 __global__ __launch_bounds__(kWave* G)
     __attribute__((amdgpu_waves_per_eu(HSA_ATTN_LOCAL_WAVES_PER_EU))) void prefill_local_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ kk,
-    const typename T::storage* __restrict__ vv, const int32_t* __restrict__ sel_idx,
+    const typename T::storage* __restrict__ vt_g, const int32_t* __restrict__ sel_idx,
     const float* __restrict__ sel_score, const int32_t* __restrict__ pair_pos, const float* __restrict__ partial,
-    float* __restrict__ out, int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int k, float scale) {
+    float* __restrict__ out, int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int k, float scale, int nbuf) {
   using st = typename T::storage;
-  constexpr int NTH = kWave * G;
-  using Stage = KVStage<T, D, NTH>;
+  using TL = Tile<T, D>;
   constexpr int KCH = D / 16;
   constexpr int DM = D / 32;
   constexpr int NW = kLocalWindow / 32;  // bitmap words of one window
+  // nbuf (1 or 2) chunk images, then the per-row tables: k entries per row,
+  // local (chunk, weight) ascending from the front, remote (pair position,
+  // weight) from the back
   extern __shared__ __align__(16) char smem[];
-  char* ks = smem;
-  char* vt = smem + kChunk * Stage::ROWB;
-  // per row k entries: local (chunk, weight) ascending from the front,
-  // remote (pair position, weight) from the back
-  int2* tab = reinterpret_cast<int2*>(smem + Stage::BYTES);
-  __shared__ uint32_t bm[NW];
+  int2* tab = reinterpret_cast<int2*>(smem + nbuf * TL::BYTES);
+  // bitmap of the union of the workgroup's local chunks; it lives in the
+  // last chunk buffer, which is first loaded after every wave holds the
+  // bitmap in registers (so two workgroups of 80 KiB fit a CU)
+  uint32_t* bm = reinterpret_cast<uint32_t*>(smem + (nbuf - 1) * TL::BYTES);
 
   const int bid = blockIdx.x;
   const int g = bid % Hkv;
@@ -645,34 +701,42 @@ __global__ __launch_bounds__(kWave* G)
   for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
 
   // walk the union of the block's local selections in ascending order
+  static_assert(NW == 2, "bitmap of one 64-chunk window");
+  uint32_t bw[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) bw[i] = __builtin_amdgcn_readfirstlane(bm[i]);
   int word = 0;
-  uint32_t bits = bm[0];
+  uint32_t bits = bw[0];
   auto next_chunk = [&]() -> int {
     while (bits == 0u) {
       if (++word >= NW) return -1;
-      bits = bm[word];
+      bits = bw[1];
     }
     const int c = ws + word * 32 + __builtin_ctz(bits);
     bits &= bits - 1u;
     return c;
   };
-  const st* kg = kk + ((int64_t)b * Hkv + g) * T_len * D;
-  const st* vg = vv + ((int64_t)b * Hkv + g) * T_len * D;
+  const char* kg = reinterpret_cast<const char*>(kk + ((int64_t)b * Hkv + g) * T_len * D);
+  const char* vtg = reinterpret_cast<const char*>(vt_g) + ((int64_t)b * Hkv + g) * Nc * TL::KBYTES;
+  auto issue = [&](int c, int buf) {
+    TL::template issue<G>(kg + (int64_t)c * TL::KBYTES, vtg + (int64_t)c * TL::KBYTES, smem + buf * TL::BYTES, hh,
+                          lane);
+  };
   const float cexp = scale * 1.4426950408889634f;
-  Stage stage;
   int ptr = 0;
   int c = next_chunk();
-  if (Stage::PASSES == 1 && c >= 0) stage.fetch(kg, vg, c, 0, tid);
-  while (c >= 0) {
-    __syncthreads();  // everyone is done with the previous tile
-    if constexpr (Stage::PASSES == 1) {
-      stage.stash(ks, vt, 0, tid);
-    } else {
-      stage.load(kg, vg, c, ks, vt, tid);
-    }
-    __syncthreads();
+  if (nbuf == 1) __syncthreads();  // the bitmap shares buffer 0: all waves have read it
+  if (c >= 0) issue(c, 0);
+  // Chunk i sits in buffer i % nbuf.  With two buffers the loads of chunk
+  // i+1 run during the computation of chunk i and one barrier per chunk
+  // suffices; with one buffer (large tiles) the loads wait for it.
+  for (int it = 0; c >= 0; ++it) {
+    wait_loads();
+    __syncthreads();  // chunk it is in LDS; every wave is done with chunk it-1
     const int cn = next_chunk();
-    if (Stage::PASSES == 1 && cn >= 0) stage.fetch(kg, vg, cn, 0, tid);
+    if (nbuf == 2 && cn >= 0) issue(cn, (it + 1) & 1);
+    const char* ks = smem + (it & (nbuf - 1)) * TL::BYTES;
+    const char* vt = ks + TL::KBYTES;
     float wgt = 0.0f;
     bool mine = false;
     if (ptr < m) {
@@ -684,6 +748,10 @@ __global__ __launch_bounds__(kWave* G)
       }
     }
     if (__ballot(mine)) attend_block<T, D>(qf, ks, vt, wgt, cexp, oacc, lane);
+    if (nbuf == 1 && cn >= 0) {
+      __syncthreads();  // every wave is done with the buffer
+      issue(cn, 0);
+    }
     c = cn;
   }
   // add the weighted outputs of the row's remote pairs
@@ -715,7 +783,9 @@ __global__ __launch_bounds__(kWave* G)
   }
 }
 
-size_t prefill_attn_lds_bytes(const Geometry& g);
+// LDS of the local kernel: nbuf chunk images and the per-row tables
+size_t prefill_local_lds_bytes(const Geometry& g, int nbuf);
+int prefill_local_buffers(const Geometry& g);
 
 template <typename T, int D, int G, int KSEL>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
@@ -732,18 +802,23 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(blocks * (G / HPW)), dim3(kWave * HPW), 0, st, q,
                      static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, g.B, g.Hkv, g.T, g.Nc, nqc, g.k, scale);
   mark_launch(st);
-  const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;  // remote-pair buckets
+  const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;  // chunks = remote-pair buckets
   if (nb > 0) {
+    mark_launch(st);
+    hipLaunchKernelGGL((prefill_vt_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, st, v, static_cast<stg*>(a.vt),
+                       g.T, g.Nc);
+    mark_launch(st);
     hipError_t e = launch_prefill_bucketing(a, st);
     if (e != hipSuccess) return e;
     mark_launch(st);
-    hipLaunchKernelGGL((prefill_remote_kernel<T, D, G>), dim3((unsigned)nb), dim3(256), 0, st, q, k, v, a.off,
-                       a.pairs, a.partial, g.Hkv, g.T, g.Nc, scale);
+    hipLaunchKernelGGL((prefill_remote_kernel<T, D, G>), dim3((unsigned)nb), dim3(256), 0, st, q, k,
+                       static_cast<const stg*>(a.vt), a.off, a.pairs, a.partial, g.Hkv, g.T, g.Nc, scale);
     mark_launch(st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = prefill_attn_lds_bytes(g);
+  const int nbuf = prefill_local_buffers(g);
+  const size_t lds = prefill_local_lds_bytes(g, nbuf);
   auto kern = prefill_local_kernel<T, D, G, KSEL>;
   if (lds > 65536) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -751,8 +826,9 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   mark_launch(st);
-  hipLaunchKernelGGL(kern, dim3(2 * blocks), dim3(kWave * G), lds, st, q, k, v, a.sel_idx, a.sel_score, a.pair_pos,
-                     a.partial, a.out, g.B, g.Hkv, g.T, g.Nc, nqc, g.k, scale);
+  hipLaunchKernelGGL(kern, dim3(2 * blocks), dim3(kWave * G), lds, st, q, k, static_cast<const stg*>(a.vt),
+                     a.sel_idx, a.sel_score, a.pair_pos, a.partial, a.out, g.B, g.Hkv, g.T, g.Nc, nqc, g.k, scale,
+                     nbuf);
   mark_launch(st);
   return hipGetLastError();
 }

@@ -99,10 +99,10 @@ hsa_attn_status_t hsa_build_landmarks(const hsa_attn_dims_t* d, const void* k, v
  * workspace: device scratch of at least hsa_attn_workspace_size(d, 0) bytes
  * (never NULL when T > 0).  It holds the selection when sel_idx is NULL,
  * the bucketing of selected chunks that lie before the query's aligned
- * window of 64 chunks, and one fp32 [D] attention output per such pair.
- * The size covers the worst case, every selected pair outside the window:
- * about B*Hq*T*k*(4*D + 16) bytes (69 GB at B=1, Hq=32, T=2^18, k=16,
- * D=128).
+ * window of 64 chunks, one fp32 [D] attention output per such pair, and a
+ * transposed copy of V.  The size covers the worst case, every selected
+ * pair outside the window: about B*Hq*T*k*(4*D + 16) bytes plus the size of
+ * V (69 GB at B=1, Hq=32, T=2^18, k=16, D=128, bf16).
  */
 hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, const void* k,
                                       const void* v, const void* landmarks, float* out,
@@ -130,7 +130,8 @@ hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, co
  * on its stream just before its i-th kernel launch and events[2*i+1] just
  * after it, for i < n_pairs; the index restarts at 0 with each call.
  * Launch order: landmarks: 1 kernel; prefill: select, then (when T >= S)
- * zero, count, scan, scatter, remote attention, then local attention; decode:
+ * V transpose, zero, count, scan, scatter, remote attention, then local
+ * attention; decode:
  * scan, merge, attention, fusion (scan and attention are skipped when the
  * cache has no complete chunk).  events == NULL or n_pairs == 0 turns
  * recording off.  The setting is thread-local; the events stay owned by the
