@@ -252,8 +252,8 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
             hsa.hsa_attn_set_timing_events(ev[2:])
         hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
 
-    names = ["landmarks", "prefill_select", "prefill_vt", "prefill_zero", "prefill_count", "prefill_scan",
-             "prefill_scatter", "prefill_remote", "prefill_local"]
+    names = ["landmarks", "prefill_zero", "prefill_select", "prefill_vt", "prefill_scan", "prefill_scatter",
+             "prefill_remote", "prefill_local"]
     secs, per = timed_steps(step, steps, warmup, len(names), events)
     ms_step = 1e3 * secs / steps
     # exact algorithmic work
@@ -270,11 +270,11 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
     remote_flops = 4.0 * w.S * w.D * n_remote
     local_flops = 4.0 * w.S * w.D * (n_pairs - n_remote)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    attn_ms = float(per[2:].sum())
-    sel_tf = score_flops / (per[1] / 1e3) / 1e12
+    attn_ms = float(per[3:].sum())
+    sel_tf = score_flops / (per[2] / 1e3) / 1e12
     att_tf = attn_flops / (attn_ms / 1e3) / 1e12
-    kern = {1: ("prefill_select_kernel", score_flops), 7: ("prefill_remote_kernel", remote_flops),
-            8: ("prefill_local_kernel", local_flops)}
+    kern = {2: ("prefill_select_kernel", score_flops), 6: ("prefill_remote_kernel", remote_flops),
+            7: ("prefill_local_kernel", local_flops)}
     dom = max(kern, key=lambda i: per[i])
     dom_name, dom_flops = kern[dom]
     dom_tf = dom_flops / (per[dom] / 1e3) / 1e12
@@ -284,8 +284,8 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
         "scoring_tflops": sel_tf, "scoring_mfma_frac": sel_tf / peak,
         "attention_ms": attn_ms, "attention_tflops": att_tf, "attention_mfma_frac": att_tf / peak,
         "remote_pair_frac": n_remote / max(n_pairs, 1),
-        "remote_tflops": remote_flops / (per[7] / 1e3) / 1e12,
-        "local_tflops": local_flops / (per[8] / 1e3) / 1e12,
+        "remote_tflops": remote_flops / (per[6] / 1e3) / 1e12,
+        "local_tflops": local_flops / (per[7] / 1e3) / 1e12,
         "landmark_GBps": (w.B * w.Hkv * Nc * w.S * w.D * esz) / (per[0] / 1e3) / 1e9,
         "config": {"workload": wname, "batch": w.B, "seq_len": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "chunk": w.S, "top_k": w.k, "lowrank": w.lowrank},

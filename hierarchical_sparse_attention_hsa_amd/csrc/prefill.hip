@@ -33,50 +33,6 @@ __global__ void prefill_zero_kernel(int* __restrict__ p, int64_t n) {
     p[i] = 0;
 }
 
-// pair_pos[i] = position of remote pair i inside its (b, g, chunk) bucket
-// (arbitrary order), -1 for local or empty slots; cnt[bucket] counts them.
-// Lanes of a wave that hit the same bucket share one atomic (neighbouring
-// rows select largely the same chunks, and popular chunks would otherwise
-// serialise on their counter).
-__global__ void prefill_count_kernel(const int32_t* __restrict__ sel_idx, int* __restrict__ cnt,
-                                     int32_t* __restrict__ pair_pos, int Hq, int G, int64_t T_len, int64_t Nc,
-                                     int k, int64_t total) {
-  // the host guarantees total < 2^31, so 32-bit index arithmetic suffices
-  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
-  const int lane = threadIdx.x & 63;
-  int bucket = -1;
-  if (i < total) {
-    const int row = i / k;
-    const int t = row % (int)T_len;
-    const int bh = row / (int)T_len;
-    const int h = bh % Hq;
-    const int b = bh / Hq;
-    const int c = sel_idx[i];
-    const int ws = (t / (kChunk * kLocalWindow)) * kLocalWindow;
-    if (c >= 0 && c < ws) bucket = (int)(((int64_t)b * (Hq / G) + h / G) * Nc + c);
-  }
-  // group the lanes by bucket (no memory traffic), then one atomic per group
-  // from its lowest lane, all groups at once
-  int leader = -1, rank = 0, group = 0;
-  uint64_t todo = __ballot(bucket >= 0);
-  while (todo) {
-    const int l = __builtin_ctzll(todo);
-    const int lb = __builtin_amdgcn_readlane(bucket, l);
-    const uint64_t same = __ballot(bucket == lb);
-    if (bucket == lb) {
-      leader = l;
-      rank = __popcll(same & ((1ull << lane) - 1ull));
-    }
-    if (lane == l) group = __popcll(same);
-    todo &= ~same;
-  }
-  int base = 0;
-  if (group > 0) base = atomicAdd(&cnt[bucket], group);
-  base = __shfl(base, leader < 0 ? lane : leader);
-  const int pos = leader < 0 ? -1 : base + rank;
-  if (i < total) pair_pos[i] = pos;
-}
-
 // exclusive prefix sum of n counts into off[0..n] (off[n] = total), one
 // workgroup of 1024 threads
 __global__ __launch_bounds__(1024) void prefill_scan_kernel(const int* __restrict__ cnt, int* __restrict__ off,
@@ -122,30 +78,28 @@ __global__ void prefill_scatter_kernel(const int32_t* __restrict__ sel_idx, cons
 }
 
 
+hipError_t launch_prefill_zero_counts(const PrefillArgs& a, hipStream_t st) {
+  const Geometry& g = a.g;
+  const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;
+  mark_launch(st);
+  hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)std::min<int64_t>((nb + 255) / 256, 4096)), dim3(256), 0,
+                     st, a.cnt, nb);
+  mark_launch(st);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_bucketing(const PrefillArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
   const int64_t total = (int64_t)g.B * g.Hq * g.T * g.k;
   const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;
   const unsigned pb = (unsigned)((total + 255) / 256);
   mark_launch(st);
-  hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)std::min<int64_t>((nb + 255) / 256, 4096)), dim3(256), 0,
-                     st, a.cnt, nb);
-  mark_launch(st);
-  if (pb > 0) {
-    mark_launch(st);
-    hipLaunchKernelGGL(prefill_count_kernel, dim3(pb), dim3(256), 0, st, a.sel_idx, a.cnt, a.pair_pos, g.Hq, g.G,
-                       g.T, g.Nc, g.k, total);
-    mark_launch(st);
-  }
-  mark_launch(st);
   hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, a.cnt, a.off, nb);
   mark_launch(st);
-  if (pb > 0) {
-    mark_launch(st);
-    hipLaunchKernelGGL(prefill_scatter_kernel, dim3(pb), dim3(256), 0, st, a.sel_idx, a.off, a.pair_pos, a.pairs,
-                       g.Hq, g.G, g.T, g.Nc, g.k, total);
-    mark_launch(st);
-  }
+  mark_launch(st);
+  hipLaunchKernelGGL(prefill_scatter_kernel, dim3(pb), dim3(256), 0, st, a.sel_idx, a.off, a.pair_pos, a.pairs, g.Hq,
+                     g.G, g.T, g.Nc, g.k, total);
+  mark_launch(st);
   return hipGetLastError();
 }
 

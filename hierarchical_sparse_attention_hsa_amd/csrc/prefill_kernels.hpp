@@ -34,6 +34,9 @@
 namespace hsa_attn {
 
 constexpr int kChunk = 64;
+// Query chunk j's aligned window: chunks [64 * floor(j / 64), j).  Selected
+// chunks inside it are "local" to the attention, the others "remote".
+constexpr int kLocalWindow = 64;
 
 template <typename T>
 __device__ __forceinline__ void load_frag_lds(Frag<T>& f, const char* row, int slot_xor, int kch, int half);
@@ -104,8 +107,8 @@ __device__ __forceinline__ void score_insert(float (&s)[K], float x) {
 template <typename T, int D, int G, int KSEL>
 __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ lm,
-    int32_t* __restrict__ sel_idx, float* __restrict__ sel_score, int B, int Hkv, int64_t T_len, int64_t Nc, int nqc,
-    int k, float scale) {
+    int32_t* __restrict__ sel_idx, float* __restrict__ sel_score, int* __restrict__ rcnt, int32_t* __restrict__ pair_pos,
+    int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int k, float scale) {
   using st = typename T::storage;
   constexpr int HPW = G < 4 ? G : 4;  // query heads (waves) per workgroup
   constexpr int HS = G / HPW;         // workgroups per (b, g, query chunk)
@@ -298,14 +301,62 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
       }
     }
   }
+  const int64_t base = (((int64_t)b * Hq + h) * T_len + t_row) * k;
   if (t_row < T_len) {
-    const int64_t base = (((int64_t)b * Hq + h) * T_len + t_row) * k;
 #pragma unroll
     for (int e = 0; e < KSEL; ++e) {
       if (e < k) {
         const bool ok = oi[e] != INT_MAX;
         sel_idx[base + e] = ok ? oi[e] : -1;
         sel_score[base + e] = ok ? os[e] * scale + 0.0f : -__builtin_inff();
+      }
+    }
+  }
+  if (rcnt == nullptr) return;  // no remote bucketing (fewer than one window)
+
+  // ---- bucket the remote selections (chunks before the query's aligned
+  // window): count them per (b, g, chunk) in rcnt and give each its position
+  // in its bucket.  The workgroup first groups its selections by chunk in an
+  // LDS hash table (cbuf's space: key, then count), so a chunk picked by many
+  // of its rows costs one global atomic.
+  constexpr int HASH = HPW * KSEL * kWave;  // >= the workgroup's selections
+  int* hkey = reinterpret_cast<int*>(&cbuf[0][0][0]);
+  int* hcnt = hkey + HASH;
+  __syncthreads();  // every wave is done with cbuf
+  for (int i = tid; i < HASH; i += kWave * HPW) {
+    hkey[i] = -1;
+    hcnt[i] = 0;
+  }
+  __syncthreads();
+  const int wsj = (j / kLocalWindow) * kLocalWindow;
+  uint32_t slot_rank[KSEL];  // slot << 16 | rank within the slot, or ~0
+#pragma unroll
+  for (int e = 0; e < KSEL; ++e) {
+    slot_rank[e] = ~0u;
+    if (e < k && t_row < T_len && oi[e] < wsj) {  // INT_MAX (empty) is never < wsj
+      const int c = oi[e];
+      int sl = (int)(((uint32_t)c * 2654435761u) >> 8) & (HASH - 1);
+      while (true) {
+        const int prev = atomicCAS(&hkey[sl], -1, c);
+        if (prev == -1 || prev == c) break;
+        sl = (sl + 1) & (HASH - 1);
+      }
+      slot_rank[e] = ((uint32_t)sl << 16) | (uint32_t)atomicAdd(&hcnt[sl], 1);
+    }
+  }
+  __syncthreads();
+  int* bucket0 = rcnt + ((int64_t)b * Hkv + g) * Nc;
+  for (int i = tid; i < HASH; i += kWave * HPW) {
+    const int n_i = hcnt[i];
+    if (n_i > 0) hcnt[i] = atomicAdd(&bucket0[hkey[i]], n_i);  // count -> first position
+  }
+  __syncthreads();
+  if (t_row < T_len) {
+#pragma unroll
+    for (int e = 0; e < KSEL; ++e) {
+      if (e < k) {
+        const uint32_t sr = slot_rank[e];
+        pair_pos[base + e] = sr == ~0u ? -1 : hcnt[sr >> 16] + (int)(sr & 0xffffu);
       }
     }
   }
@@ -324,7 +375,6 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
 // gathers its selecting rows 32 at a time into full MFMA tiles, and writes
 // each pair's normalised in-chunk output; the local kernel then adds the
 // weighted remote outputs of its rows.
-constexpr int kLocalWindow = 64;
 
 // V^T element position of token t inside the 64-token row of column d, in
 // the order the P' fragments present tokens: k-step t/16, lane half
@@ -551,9 +601,12 @@ __device__ __forceinline__ void attend_block(const Frag<T> (&qf)[D / 16], const 
 // register group q4, four consecutive columns starting at out_col(dm, q4).
 __device__ __forceinline__ int out_col(int dm, int q4, int half) { return 32 * dm + 8 * q4 + 4 * half; }
 
-// Buckets the remote pairs by (b, g, chunk): pair_pos[i] = position of
-// pair i in `pairs` (-1 when local or empty), off[] = bucket offsets,
-// pairs[] = query row of each pair.  Four launches (prefill.hip).
+// Remote-pair bucketing around the select kernel (prefill.hip): the bucket
+// counts are cleared before it (one launch); after it, their exclusive scan
+// gives the bucket offsets off[], and the scatter turns each pair's position
+// within its bucket into its position in pairs[] and records its query row
+// there (two launches).
+hipError_t launch_prefill_zero_counts(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_bucketing(const PrefillArgs& a, hipStream_t st);
 
 // ---- chunk-major attention of the remote pairs
@@ -798,11 +851,16 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   const stg* k = static_cast<const stg*>(a.k);
   const stg* v = static_cast<const stg*>(a.v);
   constexpr int HPW = G < 4 ? G : 4;
+  const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;  // chunks = remote-pair buckets
+  if (nb > 0) {
+    hipError_t e = launch_prefill_zero_counts(a, st);
+    if (e != hipSuccess) return e;
+  }
   mark_launch(st);
   hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(blocks * (G / HPW)), dim3(kWave * HPW), 0, st, q,
-                     static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, g.B, g.Hkv, g.T, g.Nc, nqc, g.k, scale);
+                     static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, nb > 0 ? a.cnt : nullptr, a.pair_pos,
+                     g.B, g.Hkv, g.T, g.Nc, nqc, g.k, scale);
   mark_launch(st);
-  const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;  // chunks = remote-pair buckets
   if (nb > 0) {
     mark_launch(st);
     hipLaunchKernelGGL((prefill_vt_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, st, v, static_cast<stg*>(a.vt),

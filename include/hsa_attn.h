@@ -129,9 +129,9 @@ hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, co
  * the calling thread records events[2*i] (hipEvent_t, created by the caller)
  * on its stream just before its i-th kernel launch and events[2*i+1] just
  * after it, for i < n_pairs; the index restarts at 0 with each call.
- * Launch order: landmarks: 1 kernel; prefill: select, then (when T >= S)
- * V transpose, zero, count, scan, scatter, remote attention, then local
- * attention; decode:
+ * Launch order: landmarks: 1 kernel; prefill (when T >= S): zero, select,
+ * V transpose, scan, scatter, remote attention, local attention (for T < S:
+ * select, local attention); decode:
  * scan, merge, attention, fusion (scan and attention are skipped when the
  * cache has no complete chunk).  events == NULL or n_pairs == 0 turns
  * recording off.  The setting is thread-local; the events stay owned by the
