@@ -97,18 +97,28 @@ def timed_steps(step, steps, warmup, n_launch, events):
     return t1 - t0, per / steps
 
 
+def source_digest():
+    """Digest of everything that shapes the kernels' code: the HIP sources and
+    the build flags."""
+    import hashlib
+    pkg = os.path.join(ROOT, "hierarchical_sparse_attention_hsa_amd")
+    files = sorted(os.path.join("csrc", f) for f in os.listdir(os.path.join(pkg, "csrc"))) + ["build.py"]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(pkg, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def profiled_traffic(workload, kernel_prefix):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter
     record (profiles/<workload>.traffic.json: FETCH_SIZE and WRITE_SIZE scaled
     by a 1 GiB copy), or None when the kernel sources changed since."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"{workload}.traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = b"".join(open(os.path.join(ROOT, "hierarchical_sparse_attention_hsa_amd", f), "rb").read()
-                   for f in rec["sources"])
-    if hashlib.sha256(src).hexdigest()[:16] != rec["source_sha256_16"]:
+    if rec.get("source_sha256_16") != source_digest():
         return None
     for name, b in rec["traffic_bytes_per_launch"].items():
         if kernel_prefix in name:
@@ -116,13 +126,63 @@ def profiled_traffic(workload, kernel_prefix):
     return None
 
 
-def blas_threads():
-    try:
-        from threadpoolctl import threadpool_info
-        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
-        return max(n) if n else 1
-    except Exception:
-        return 1
+def summarize_profile(workload, prof_dir, command, kernel):
+    """Turn the rocprofv3 CSVs of one workload (<workload>_kernel_stats.csv,
+    _FETCH_SIZE.csv, _WRITE_SIZE.csv in prof_dir) into profiles/<kernel>.<workload>.md,
+    named for the dominant kernel (kernel times and HBM bytes) and
+    profiles/<workload>.traffic.json (bytes
+    per launch, read by the benchmark).  Counter values are KiB per dispatch;
+    they are scaled so that the calibration copy (1 GiB read, 1 GiB written)
+    reads as exactly that."""
+    import csv
+    from collections import defaultdict
+
+    def short(name):
+        return name.replace("void ", "").split("(")[0]
+
+    stats = [r for r in csv.DictReader(open(os.path.join(prof_dir, f"{workload}_kernel_stats.csv")))
+             if "hsa_attn" in r["Name"]]
+    counters = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        per = defaultdict(list)
+        for r in csv.DictReader(open(os.path.join(prof_dir, f"{workload}_{c}.csv"))):
+            per[(int(r["Dispatch_Id"]), r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        counters[c] = {k: sum(v) for k, v in per.items()}
+    gib_kib = float(1 << 20)
+    # the copy: of the non-library dispatches that write 1 GiB (the fill of
+    # its source does too), the one that also reads
+    cands = [k for k, w in counters["WRITE_SIZE"].items()
+             if "hsa_attn" not in k[1] and abs(w - gib_kib) < 0.05 * gib_kib and k in counters["FETCH_SIZE"]]
+    copy_w = max(cands, key=lambda k: counters["FETCH_SIZE"][k])
+    read_scale = gib_kib / counters["FETCH_SIZE"][copy_w]
+    write_scale = gib_kib / counters["WRITE_SIZE"][copy_w]
+    rows = defaultdict(list)
+    for k, f in counters["FETCH_SIZE"].items():
+        if "hsa_attn" in k[1] and k in counters["WRITE_SIZE"]:
+            rows[short(k[1])].append((f, counters["WRITE_SIZE"][k]))
+    traffic = {n: 1024.0 * float(np.mean([f * read_scale + w * write_scale for f, w in v])) for n, v in rows.items()}
+    rec = {"workload": workload, "source_sha256_16": source_digest(), "read_scale": read_scale,
+           "write_scale": write_scale, "traffic_bytes_per_launch": traffic}
+    with open(os.path.join(ROOT, "profiles", f"{workload}.traffic.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    lines = [f"# {kernel} and the other library kernels: {workload}", "",
+             "Commands (repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`; REPO = the root):", ""]
+    lines += [f"    {c}" for c in command] + ["", "## Kernel trace (--stats), library kernels", "",
+                                               "| kernel | calls | average ns | total ns |", "|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{float(r['TotalDurationNs']):.0f} |")
+    lines += ["", "## HBM bytes per dispatch (--pmc, KiB per dispatch, averaged)", "",
+              f"Calibration: the 1 GiB device copy reads FETCH_SIZE = {counters['FETCH_SIZE'][copy_w]:.0f} KiB and "
+              f"WRITE_SIZE = {counters['WRITE_SIZE'][copy_w]:.0f} KiB, so reads are scaled by {read_scale:.3f} "
+              f"and writes by {write_scale:.3f}.", "",
+              "| kernel | dispatches | FETCH_SIZE | WRITE_SIZE | scaled HBM bytes |", "|---|---|---|---|---|"]
+    for n, v in sorted(rows.items(), key=lambda kv: -traffic[kv[0]]):
+        lines.append(f"| {n} | {len(v)} | {np.mean([f for f, _ in v]):.0f} | {np.mean([w for _, w in v]):.0f} | "
+                     f"{traffic[n] / 2**30:.3f} GiB |")
+    with open(os.path.join(ROOT, "profiles", f"{kernel}.{workload}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 # ---------------------------------------------------------------- decode
@@ -291,7 +351,8 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
                    "head_dim": w.D, "chunk": w.S, "top_k": w.k, "lowrank": w.lowrank},
         "dtype": w.dtype,
         "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": dom_tf, "peak": peak, "unit": "TFLOP/s",
-                     "frac": dom_tf / peak, "traffic": None, "alg_flops_per_launch": dom_flops},
+                     "frac": dom_tf / peak, "traffic": profiled_traffic(wname, dom_name),
+                     "alg_flops_per_launch": dom_flops},
     }
     log(f"[{wname}] {ms_step:.3f} ms/step, kernels {dict(zip(names, np.round(per, 4)))}, "
         f"scoring {sel_tf:.1f} TFLOP/s, attention {att_tf:.1f} TFLOP/s, remote pairs {n_remote / max(n_pairs, 1):.3f}")
@@ -336,7 +397,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one device copy of exactly 1 GiB (the reference kernel for HBM byte counters)")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="write profiles/<workload>.md and .traffic.json from the rocprofv3 CSVs in DIR and exit")
+    ap.add_argument("--profile-command", action="append", default=[],
+                    help="with --summarize-profile: a command line to record in the summary")
+    ap.add_argument("--profile-kernel", default="kernels",
+                    help="with --summarize-profile: the kernel the summary is named for")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.workload, args.summarize_profile, args.profile_command, args.profile_kernel)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this layer is measured on one GPU; the multi-GPU sharding is a design only "
               "(see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
