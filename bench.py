@@ -126,6 +126,15 @@ def profiled_traffic(workload, kernel_prefix):
     return None
 
 
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
 def summarize_profile(workload, prof_dir, command, kernel):
     """Turn the rocprofv3 CSVs of one workload (<workload>_kernel_stats.csv,
     _FETCH_SIZE.csv, _WRITE_SIZE.csv in prof_dir) into profiles/<kernel>.<workload>.md,
@@ -262,27 +271,37 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
     return res
 
 
-def decode_cpu_baseline(w, q, k, v, n_queries=2):
-    """The oracle on a bounded sample: the first n_queries queries, all heads.
-    Host copies and the oracle's own landmark build are untimed (landmarks are
+def decode_cpu_baseline(w, q, k, v, queries=(0, 37), min_seconds=10.0):
+    """The oracle on a bounded sample: the listed queries, all heads.  Host
+    copies and the oracle's own landmark build are untimed (landmarks are
     precomputed in this workload); scoring, top-k, chunk attention and fusion
-    are timed."""
+    are timed, repeated per KV group so that about min_seconds of work is
+    measured."""
     from oracle import hsa_oracle as O
     G = w.Hq // w.Hkv
+    queries = [b for b in queries if b < w.B]
+    reps = None
     total = 0.0
-    for b in range(n_queries):
+    for b in queries:
         qb = q[b].float().cpu().double().numpy()
         for g in range(w.Hkv):
             Kg = k[b, g].float().cpu().double().numpy()
             Vg = v[b, g].float().cpu().double().numpy()
             Lg = O.landmarks(Kg, w.S, w.dtype)
+            args = (qb[g * G:(g + 1) * G], np.full(G, w.T), Kg, Vg, Lg, w.S, w.k)
+            if reps is None:  # size the repetition count on the first group
+                t0 = time.perf_counter()
+                O.hsa_rows(*args)
+                one = time.perf_counter() - t0
+                reps = max(1, min(1000, int(min_seconds / (one * len(queries) * w.Hkv))))
             t0 = time.perf_counter()
-            O.hsa_rows(qb[g * G:(g + 1) * G], np.full(G, w.T), Kg, Vg, Lg, w.S, w.k)
+            for _ in range(reps):
+                O.hsa_rows(*args)
             total += time.perf_counter() - t0
             del Kg, Vg
-    return {"value": n_queries / total, "unit": "queries/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"{n_queries} of {w.B} queries (all {w.Hq} heads); oracle landmark build and host "
-                      f"copies untimed"}
+    return {"value": len(queries) * reps / total, "unit": "queries/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"queries {list(queries)} of {w.B} (all {w.Hq} heads), each KV group's oracle call repeated "
+                      f"{reps} times ({total:.1f} s timed); oracle landmark build and host copies untimed"}
 
 
 # ---------------------------------------------------------------- prefill
@@ -363,7 +382,7 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
     return res
 
 
-def prefill_cpu_baseline(w, q, k, v, chunks=(1000, 3000)):
+def prefill_cpu_baseline(w, q, k, v, chunks=tuple(range(250, 4001, 250))):
     """The oracle on a bounded sample: all heads of the query chunks listed
     (64 tokens each).  Host copies and landmark building are untimed."""
     from oracle import hsa_oracle as O
@@ -383,8 +402,8 @@ def prefill_cpu_baseline(w, q, k, v, chunks=(1000, 3000)):
             total += time.perf_counter() - t0
     tokens = len(chunks) * w.S
     return {"value": tokens / total, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"query chunks {list(chunks)} ({tokens} tokens, all {w.Hq} heads); host copies and "
-                      f"oracle landmark build untimed"}
+            "sample": f"query chunks {list(chunks)} ({tokens} tokens, all {w.Hq} heads; {total:.1f} s timed); "
+                      f"host copies and oracle landmark build untimed"}
 
 
 # ---------------------------------------------------------------- main
