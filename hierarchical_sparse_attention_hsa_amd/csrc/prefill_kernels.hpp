@@ -113,9 +113,21 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
   constexpr int HPW = G < 4 ? G : 4;  // query heads (waves) per workgroup
   constexpr int HS = G / HPW;         // workgroups per (b, g, query chunk)
   constexpr int KCH = D / 16;
-  constexpr int MAXT = 2048;          // tiles with a recorded pass-1 skip
+  constexpr int ROWB = D * T::kBytes;  // one landmark row
+  constexpr int NSL = ROWB / 16;       // its 16-byte slots
+  constexpr int TILE = 32 * ROWB;      // 32 landmarks
+  constexpr int NI = TILE / (kWave * 16);  // direct-to-LDS loads per tile
+  constexpr int PER = NI / HPW;            // of which each wave issues
+  constexpr int NST = 4;                   // tiles in flight (LDS ring)
+  constexpr int MAXT = 2048;               // Nc <= 65536
+  static_assert(NI % HPW == 0 && NSL >= 8, "tile loads split evenly; row swizzle needs 8 slots");
+  // ring of landmark tiles shared by the workgroup's waves: row r of a tile
+  // holds its 16-byte slots XOR-swizzled by (r & 7)
+  __shared__ __align__(16) char ring[NST][TILE];
   __shared__ float2 cbuf[HPW][KSEL][kWave];
-  __shared__ uint8_t tskip[HPW][MAXT];
+  __shared__ uint32_t tneed[HPW][MAXT / 32];  // pass 1: tile reached a row's threshold
+  __shared__ uint16_t tlist[MAXT];            // pass 2: tiles any wave needs, ascending
+  __shared__ int tcount;                      // and how many
 
   const int bid = blockIdx.x;
   const int g = bid % Hkv;  // consecutive workgroups on different XCDs share nothing
@@ -136,10 +148,8 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
   int cnt = 0;
   if (n > 0) {
     // Contraction index assignment (shared by both operands): in k-step s,
-    // lane half h supplies dims 16*s + 8*h .. +8, so the two lanes of a row
-    // read adjacent 16-byte pieces of one cache line.  Rows past the end of
-    // the sequence or of the candidate range read a valid row instead; their
-    // results are never used (query rows) or masked to -inf (landmarks).
+    // lane half h supplies dims 16*s + 8*h .. +8.  Query rows past the end of
+    // the sequence read a valid row; their results are never used.
     Frag<T> qf[2][KCH];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -148,25 +158,63 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
 #pragma unroll
       for (int s = 0; s < KCH; ++s) load_frag_global(qf[nb][s], qp + 16 * s, true);
     }
-    const st* lmg = lm + ((int64_t)b * Hkv + g) * Nc * D + 8 * half;
+    const char* lmg = reinterpret_cast<const char*>(lm + ((int64_t)b * Hkv + g) * Nc * D);
     const int ntiles = (int)((n + 31) / 32);
-    // landmark fragments (A operand) of one tile, double-buffered
-    Frag<T> fa[KCH], fb[KCH];
-    auto fetch = [&](Frag<T>(&f)[KCH], int ti) {
-      const int64_t c = min((int64_t)ti * 32 + (lane & 31), n - 1);
-      const st* p = lmg + c * D;
+    // this wave's share of the direct-to-LDS loads of tile ti into stage sg;
+    // landmark rows past the candidate range read row n-1 (masked later)
+    auto issue = [&](int ti, int sg) {
 #pragma unroll
-      for (int s = 0; s < KCH; ++s) load_frag_global(f[s], p + 16 * s, true);
+      for (int u = 0; u < PER; ++u) {
+        const int ii = hh * PER + u;
+        const int L = ii * kWave + lane;
+        const int r = L / NSL, sp = L % NSL;
+        const int64_t c = min((int64_t)ti * 32 + r, n - 1);
+        __builtin_amdgcn_global_load_lds(lmg + c * ROWB + ((sp ^ (r & 7)) * 16),
+                                         (__attribute__((address_space(3))) void*)(ring[sg] + ii * kWave * 16), 16,
+                                         0, 0);
+      }
+    };
+    // wait until at most `later` tiles of this wave's loads are in flight
+    auto wait_tiles = [&](int later) {
+      if constexpr (NST >= 4) {
+        if (later >= 2) {
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
+          return;
+        }
+      }
+      if (later >= 1) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
+        return;
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    // Run body(i, tile, stage) over the tile sequence tile_of(0 .. count-1)
+    // with NST-1 tiles in flight and one barrier per tile: after the barrier
+    // of step i every wave is done with step i-1, whose stage is refilled.
+    auto pipeline = [&](int count, auto tile_of, auto body) {
+#pragma unroll
+      for (int i = 0; i < NST - 1; ++i)
+        if (i < count) issue(tile_of(i), i);
+      for (int i = 0; i < count; ++i) {
+        wait_tiles(min(NST - 2, count - 1 - i));
+        __syncthreads();
+        if (i + NST - 1 < count) issue(tile_of(i + NST - 1), (i + NST - 1) % NST);
+        body(i, tile_of(i), ring[i % NST]);
+      }
+      __syncthreads();  // the ring is free again
     };
     // scores of a tile: lane l gets them for query rows (l%32) and
     // 32 + (l%32) at tile rows tile_row(r, l/32)
-    auto contract = [&](const Frag<T>(&f)[KCH], f32x16& acc0, f32x16& acc1) {
+    auto contract = [&](const char* tile, f32x16& acc0, f32x16& acc1) {
       acc0 = f32x16{};
       acc1 = f32x16{};
+      const char* row = tile + (lane & 31) * ROWB;
 #pragma unroll
       for (int s = 0; s < KCH; ++s) {
-        mfma(acc0, f[s], qf[0][s]);
-        mfma(acc1, f[s], qf[1][s]);
+        Frag<T> a;
+        load_frag_lds<T>(a, row, lane & 7, s, half);
+        mfma(acc0, a, qf[0][s]);
+        mfma(acc1, a, qf[1][s]);
       }
     };
     // per-row tile maximum: the per-lane maxima of acc0/acc1, swapped like
@@ -210,78 +258,84 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
     // ---- pass 1: the multiset of the k best scores.  List positions above
     // k hold +inf, so ls[KSEL-1] is the k-th best once k are seen; until
     // then the -FLT_MAX seeds keep masked (-inf) candidates out.  A tile in
-    // which no row reaches its running threshold is marked: the threshold
-    // only grows, so pass 2 can skip it too.
+    // which no row of the wave reaches its running threshold stays unmarked:
+    // the threshold only grows, so pass 2 can skip it for this wave.
+    for (int i = lane; i < MAXT / 32; i += kWave) tneed[hh][i] = 0u;
     float ls[KSEL];
 #pragma unroll
     for (int e = 0; e < KSEL; ++e) ls[e] = (e < KSEL - k) ? __builtin_inff() : -3.402823466e38f;
-    auto pass1 = [&](const Frag<T>(&f)[KCH], int ti) {
-      f32x16 acc0, acc1;
-      contract(f, acc0, acc1);
-      const bool top = (int64_t)ti * 32 + 32 > n;
-      if (!top && !__ballot(row_max(acc0, acc1) >= ls[KSEL - 1])) {
-        if (ti < MAXT && lane == 0) tskip[hh][ti] = 1;
-        return;
-      }
-      if (ti < MAXT && lane == 0) tskip[hh][ti] = 0;
-      float lo[16], hi[16];
-      to_rows(acc0, acc1, ti, lo, hi);
+    pipeline(
+        ntiles, [&](int i) { return ntiles - 1 - i; },
+        [&](int, int ti, const char* tile) {
+          f32x16 acc0, acc1;
+          contract(tile, acc0, acc1);
+          const bool top = (int64_t)ti * 32 + 32 > n;
+          if (!top && !__ballot(row_max(acc0, acc1) >= ls[KSEL - 1])) return;
+          if (lane == 0) tneed[hh][ti >> 5] |= 1u << (ti & 31);
+          float lo[16], hi[16];
+          to_rows(acc0, acc1, ti, lo, hi);
 #pragma unroll
-      for (int ii = 31; ii >= 0; --ii) {
-        const float x = cand(lo, hi, ii);
-        if (x >= ls[KSEL - 1]) score_insert<KSEL>(ls, x);
-      }
-    };
-    fetch(fa, ntiles - 1);
-    for (int ti = ntiles - 1; ti >= 0; ti -= 2) {
-      if (ti >= 1) fetch(fb, ti - 1);
-      pass1(fa, ti);
-      if (ti < 1) break;
-      if (ti >= 2) fetch(fa, ti - 2);
-      pass1(fb, ti - 1);
-    }
+          for (int ii = 31; ii >= 0; --ii) {
+            const float x = cand(lo, hi, ii);
+            if (x >= ls[KSEL - 1]) score_insert<KSEL>(ls, x);
+          }
+        });
 
-    // ---- pass 2: collect the k best in ascending chunk order
+    // ---- pass 2: collect the k best in ascending chunk order, over the
+    // tiles some wave still needs (the others skip their arithmetic)
+    if (hh == 0) {
+      int base = 0;
+      for (int w0 = 0; w0 < (ntiles + 31) / 32; w0 += kWave) {
+        const int wi = w0 + lane;
+        uint32_t bits = 0u;
+        if (wi < (ntiles + 31) / 32) {
+#pragma unroll
+          for (int w = 0; w < HPW; ++w) bits |= tneed[w][wi];
+        }
+        // exclusive prefix of the popcounts across the wave
+        int pc = __popc(bits), incl = pc;
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int o = __shfl_up(incl, off);
+          if (lane >= off) incl += o;
+        }
+        int pos = base + incl - pc;
+        while (bits) {
+          tlist[pos++] = (uint16_t)(wi * 32 + __builtin_ctz(bits));
+          bits &= bits - 1u;
+        }
+        base += __shfl(incl, kWave - 1);
+      }
+      if (lane == 0) tcount = base;
+    }
+    __syncthreads();
+    const int nneed = tcount;
     const float tau = ls[KSEL - 1];
     int quota = KSEL;  // entries equal to tau that still fit
 #pragma unroll
     for (int e = 0; e < KSEL; ++e) quota -= ls[e] > tau;
-    auto next_tile = [&](int ti) {
-      while (ti < ntiles && ti < MAXT && tskip[hh][ti]) ++ti;
-      return ti;
-    };
-    auto pass2 = [&](const Frag<T>(&f)[KCH], int ti) {
-      f32x16 acc0, acc1;
-      contract(f, acc0, acc1);
-      const bool top = (int64_t)ti * 32 + 32 > n;
-      if (!top && !__ballot(row_max(acc0, acc1) >= tau)) return;
-      float lo[16], hi[16];
-      to_rows(acc0, acc1, ti, lo, hi);
+    pipeline(
+        nneed, [&](int i) { return (int)tlist[i]; },
+        [&](int, int ti, const char* tile) {
+          if (!((tneed[hh][ti >> 5] >> (ti & 31)) & 1u)) return;
+          f32x16 acc0, acc1;
+          contract(tile, acc0, acc1);
+          const bool top = (int64_t)ti * 32 + 32 > n;
+          if (!top && !__ballot(row_max(acc0, acc1) >= tau)) return;
+          float lo[16], hi[16];
+          to_rows(acc0, acc1, ti, lo, hi);
 #pragma unroll
-      for (int ii = 0; ii < 32; ++ii) {
-        const float x = cand(lo, hi, ii);
-        if (x >= tau) {
-          const bool take = x > tau || quota > 0;
-          if (x == tau) --quota;
-          if (take && cnt < KSEL) {
-            cbuf[hh][cnt][lane] = make_float2(x, __int_as_float(ti * 32 + ii));
-            ++cnt;
+          for (int ii = 0; ii < 32; ++ii) {
+            const float x = cand(lo, hi, ii);
+            if (x >= tau) {
+              const bool take = x > tau || quota > 0;
+              if (x == tau) --quota;
+              if (take && cnt < KSEL) {
+                cbuf[hh][cnt][lane] = make_float2(x, __int_as_float(ti * 32 + ii));
+                ++cnt;
+              }
+            }
           }
-        }
-      }
-    };
-    int ti = next_tile(0);
-    if (ti < ntiles) fetch(fa, ti);
-    while (ti < ntiles) {
-      const int t1 = next_tile(ti + 1);
-      if (t1 < ntiles) fetch(fb, t1);
-      pass2(fa, ti);
-      if (t1 >= ntiles) break;
-      const int t2 = next_tile(t1 + 1);
-      if (t2 < ntiles) fetch(fa, t2);
-      pass2(fb, t1);
-      ti = t2;
-    }
+        });
   }
   const int64_t t_row = (int64_t)j * kChunk + lane;
   // order the kept set by (score desc, index asc)
