@@ -55,6 +55,165 @@ __device__ __forceinline__ float dot_slice(const u32x4& a, const u32x4& b, FP32)
   return acc;
 }
 
+// ---------------------------------------------------------------- split top-k
+// Exact top-m (m = min(k, n)) of n scores held in LDS, under the order
+// (score desc, index asc), by one wave, without per-candidate insertions:
+//   1. the score range [lo, hi] (wave min / max);
+//   2. a 256-bin histogram of t = (s - lo) * 256 / (hi - lo) (the bin is
+//      monotone in s) gives the bin B1 holding the m-th best; a second
+//      256-bin histogram of the fraction of t inside B1 narrows it to B2;
+//   3. every candidate in a higher (bin, sub-bin) plus every candidate of
+//      (B1, B2) is gathered (at most kGather; otherwise the caller falls
+//      back to list insertion) and
+//   4. a bitonic sort of the gathered (score, index) pairs across the wave
+//      leaves the e-th best in lane e.
+// Returns false when the gathered set does not fit.
+constexpr int kGather = 128;
+
+__device__ __forceinline__ float wave_min_f(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fminf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// sum over the lanes above this one (exclusive suffix sum)
+__device__ __forceinline__ int suffix_excl(int v, int lane) {
+  int incl = v;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_down(incl, off);
+    if (lane + off < kWave) incl += o;
+  }
+  return incl - v;
+}
+
+// Find the bin of the m-th largest element from a 256-bin histogram: returns
+// (bin, count strictly above it).  Lane l owns bins 4l .. 4l+3.
+__device__ __forceinline__ void hist_select(const int* hist, int m, int lane, int& bin, int& above) {
+  const int c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
+  const int sup = suffix_excl(c0 + c1 + c2 + c3, lane);  // elements in higher lanes' bins
+  int found = -1, abv = 0;
+  int cum = sup;
+  const int cs[4] = {c3, c2, c1, c0};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (found < 0 && cum + cs[q] >= m && cum < m) {
+      found = 4 * lane + 3 - q;
+      abv = cum;
+    }
+    cum += cs[q];
+  }
+  const uint64_t who = __ballot(found >= 0);
+  const int src = who ? __builtin_ctzll(who) : 0;
+  bin = __builtin_amdgcn_readlane(found, src);
+  above = __builtin_amdgcn_readlane(abv, src);
+}
+
+__device__ __forceinline__ bool split_topk(const float* sc, int n, int idx0, int k, int* hist, float2* buf,
+                                           float& out_s, int& out_i) {
+  const int lane = __lane_id();
+  const int m = min(k, n);
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  for (int r = lane; r < n; r += kWave) {
+    const float x = sc[r];
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+  }
+  lo = wave_min_f(lo);
+  hi = wave_max_f(hi);
+  float inv = hi > lo ? 256.0f / (hi - lo) : 0.0f;
+  if (!(inv < 1e30f)) inv = 0.0f;  // a range too narrow to bin: one bin (then gather or fall back)
+  auto tval = [&](float x) { return (x - lo) * inv; };
+  auto bin_of = [&](float t) { return min(255, (int)t); };
+  int B1 = 0, B2 = 0;
+  if (n > kGather) {
+    // pass 1
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
+    for (int r = lane; r < n; r += kWave) atomicAdd(&hist[bin_of(tval(sc[r]))], 1);
+    int above1;
+    hist_select(hist, m, lane, B1, above1);
+    // pass 2: inside B1
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
+    for (int r = lane; r < n; r += kWave) {
+      const float t = tval(sc[r]);
+      if (bin_of(t) == B1) atomicAdd(&hist[min(255, (int)((t - (float)B1) * 256.0f))], 1);
+    }
+    int above2;
+    hist_select(hist, m - above1, lane, B2, above2);
+  } else {
+    B1 = 0;
+    B2 = 0;  // gather everything
+  }
+  // gather (bin, sub-bin) >= (B1, B2), in index order
+  int cnt = 0;
+  for (int r0 = 0; r0 < n; r0 += kWave) {
+    const int r = r0 + lane;
+    bool take = false;
+    float x = 0.0f;
+    if (r < n) {
+      x = sc[r];
+      const float t = tval(x);
+      const int b1 = bin_of(t);
+      take = b1 > B1 || (b1 == B1 && min(255, (int)((t - (float)B1) * 256.0f)) >= B2);
+    }
+    const uint64_t mk = __ballot(take);
+    const int pos = cnt + __popcll(mk & ((1ull << lane) - 1ull));
+    if (take && pos < kGather) buf[pos] = make_float2(x, __int_as_float(idx0 + r));
+    cnt += __popcll(mk);
+  }
+  if (cnt > kGather) return false;
+  // bitonic sort of buf[0 .. kGather) (padding = worst), best first: element
+  // x = 64 t + lane sits in register t of lane `lane`
+  float s0, s1;
+  int i0, i1;
+  {
+    const float2 e0 = lane < cnt ? buf[lane] : make_float2(-__builtin_inff(), __int_as_float(INT_MAX));
+    const float2 e1 = lane + kWave < cnt ? buf[lane + kWave] : make_float2(-__builtin_inff(), __int_as_float(INT_MAX));
+    s0 = e0.x;
+    i0 = __float_as_int(e0.y);
+    s1 = e1.x;
+    i1 = __float_as_int(e1.y);
+  }
+  auto step = [&](float& sv, int& iv, int x, int k2, int jj) {
+    const float os = __shfl_xor(sv, jj);
+    const int oi = __shfl_xor(iv, jj);
+    const bool lower = (x & jj) == 0;
+    const bool asc = (x & k2) == 0;  // this run sorts best first
+    const bool keep_better = lower == asc;
+    const bool mine_better = better(sv, iv, os, oi);
+    if (keep_better != mine_better) {
+      sv = os;
+      iv = oi;
+    }
+  };
+  for (int k2 = 2; k2 <= 2 * kWave; k2 <<= 1) {
+    for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
+      if (jj == kWave) {  // partner is the other register of this lane
+        const bool asc = ((lane) & k2) == 0;  // x = lane for register 0 (k2 = 128 here: always)
+        const bool b01 = better(s0, i0, s1, i1);
+        if (asc != b01) {
+          const float ts = s0;
+          const int ti = i0;
+          s0 = s1;
+          i0 = i1;
+          s1 = ts;
+          i1 = ti;
+        }
+      } else {
+        step(s0, i0, lane, k2, jj);
+        step(s1, i1, lane + kWave, k2, jj);
+      }
+    }
+  }
+  out_s = s0;
+  out_i = i0;
+  return true;
+}
+
 // ---------------------------------------------------------------- 1. scan
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kScanThreads) void decode_scan_kernel(const typename T::storage* __restrict__ q,
@@ -113,19 +272,28 @@ __global__ __launch_bounds__(kScanThreads) void decode_scan_kernel(const typenam
   }
   __syncthreads();
 
+  int* hist = reinterpret_cast<int*>(sc + G * rows_per_split) + wave * 256;
+  float2* gbuf = reinterpret_cast<float2*>(sc + G * rows_per_split + WAVES * 256) + wave * kGather;
   for (int h = wave; h < G; h += WAVES) {
-    WaveTopK list;
-    list.init();
-    for (int i0 = 0; i0 < n; i0 += kWave) {
-      const int r = i0 + lane;
-      const bool valid = r < n;
-      const float s = valid ? sc[h * rows_per_split + r] : -__builtin_inff();
-      offer_wave(list, k, s, (int)(r_begin + r), valid);
+    float os;
+    int oi;
+    if (!split_topk(sc + h * rows_per_split, n, (int)r_begin, k, hist, gbuf, os, oi)) {
+      // many equal scores around the k-th: ordered insertion
+      WaveTopK list;
+      list.init();
+      for (int i0 = 0; i0 < n; i0 += kWave) {
+        const int r = i0 + lane;
+        const bool valid = r < n;
+        const float s = valid ? sc[h * rows_per_split + r] : -__builtin_inff();
+        offer_wave(list, k, s, (int)(r_begin + r), valid);
+      }
+      os = list.s;
+      oi = list.i;
     }
     if (lane < k) {
       float2 c;
-      c.x = list.s;
-      c.y = __int_as_float(list.i);
+      c.x = os;
+      c.y = __int_as_float(oi);
       cand[((((int64_t)b * Hkv + g) * splits + sp) * G + h) * k + lane] = c;
     }
   }
@@ -153,20 +321,26 @@ __global__ __launch_bounds__(kWave* G) void decode_merge_kernel(const float2* __
   list.init();
   const int total = splits * k;
   // rank-major order: every split's best first, so the list fills with
-  // strong candidates early and later ranks rarely get in
-  for (int i0 = 0; i0 < total; i0 += kWave) {
-    const int j = i0 + lane;
-    bool valid = j < total;
-    float s = -__builtin_inff();
-    int ci = INT_MAX;
-    if (valid) {
-      const int e = j / splits, sp = j % splits;
-      const float2 c = cand[((((int64_t)b * Hkv + g) * splits + sp) * G + hh) * k + e];
-      s = c.x;
-      ci = __float_as_int(c.y);
-      valid = ci != INT_MAX;
+  // strong candidates early and later ranks rarely get in; the loads of
+  // kMergeBatch rounds are issued together (the loop is latency-bound)
+  constexpr int kMergeBatch = 8;
+  const float2* cb = cand + (((int64_t)b * Hkv + g) * splits * G + hh) * k;
+  for (int i0 = 0; i0 < total; i0 += kWave * kMergeBatch) {
+    float2 c[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int j = i0 + u * kWave + lane;
+      c[u] = make_float2(-__builtin_inff(), __int_as_float(INT_MAX));
+      if (j < total) {
+        const int e = j / splits, sp = j % splits;
+        c[u] = cb[(int64_t)sp * G * k + e];
+      }
     }
-    offer_wave(list, k, s, ci, valid);
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int ci = __float_as_int(c[u].y);
+      offer_wave(list, k, c[u].x, ci, ci != INT_MAX);
+    }
   }
   const bool ok = list.i != INT_MAX;
   if (lane < k) {
@@ -419,7 +593,9 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipS
   const float scale = 1.0f / sqrtf((float)D);
   using stg = typename T::storage;
   if (p.splits > 0) {
-    const size_t lds = (size_t)G * p.rows_per_split * sizeof(float);
+    // scores, then per wave a 256-bin histogram and the gather buffer
+    const size_t lds = (size_t)G * p.rows_per_split * sizeof(float) +
+                       (size_t)(kScanThreads / kWave) * (256 * sizeof(int) + kGather * sizeof(float2));
     mark_launch(st);
     hipLaunchKernelGGL((decode_scan_kernel<T, D, G>), dim3(p.splits, g.Hkv, g.B), dim3(kScanThreads), lds, st,
                        static_cast<const stg*>(a.q), static_cast<const stg*>(a.lm), cand, g.Hkv, g.Nc,

@@ -92,3 +92,31 @@ def test_decode_is_deterministic():
     b = run_decode(q, k, v, 64, 32)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_decode_all_scores_equal_keep_lowest_indices():
+    """Every chunk identical (all retrieval scores equal): the kept set is the
+    k lowest chunk indices, in index order (ties toward the lower index)."""
+    B, Hq, Hkv, T, D, topk = 1, 4, 1, 64 * 300, 128, 32
+    q, k, v = small_inputs(B, Hq, Hkv, T, D, "bf16", seed=13, decode=True)
+    for c in range(1, T // 64):
+        k[0, 0, c * 64:(c + 1) * 64] = k[0, 0, 0:64]
+    out, sel, score = run_decode(q, k, v, 64, topk)
+    assert np.array_equal(sel[0], np.tile(np.arange(topk), (Hq, 1)))
+    compare(q, k, v, 64, topk, "bf16", out, sel, score)
+
+
+def test_decode_few_distinct_scores():
+    """Chunks drawn from a handful of distinct ones: many exact ties around
+    the k-th score, resolved toward the lower index."""
+    B, Hq, Hkv, T, D, topk = 2, 8, 2, 64 * 2000, 128, 64
+    q, k, v = small_inputs(B, Hq, Hkv, T, D, "bf16", seed=17, decode=True)
+    r = np.random.default_rng(3)
+    for b in range(B):
+        for g in range(Hkv):
+            src = r.integers(0, 5, size=T // 64)
+            for c in range(5, T // 64):
+                s0 = int(src[c])
+                k[b, g, c * 64:(c + 1) * 64] = k[b, g, s0 * 64:(s0 + 1) * 64]
+    out, sel, score = run_decode(q, k, v, 64, topk)
+    compare(q, k, v, 64, topk, "bf16", out, sel, score)
