@@ -111,6 +111,55 @@ __device__ __forceinline__ void hist_select(const int* hist, int m, int lane, in
   above = __builtin_amdgcn_readlane(abv, src);
 }
 
+// Bitonic sort of buf[0 .. cnt) (cnt <= kGather; the rest is padded with
+// the worst entry) by (score desc, index asc) across one wave: element
+// x = 64 t + lane sits in register t of lane `lane`; on return lane e holds
+// the e-th best.
+__device__ __forceinline__ void sort_gathered(const float2* buf, int cnt, float& out_s, int& out_i) {
+  const int lane = __lane_id();
+  float s0, s1;
+  int i0, i1;
+  {
+    const float2 e0 = lane < cnt ? buf[lane] : make_float2(-__builtin_inff(), __int_as_float(INT_MAX));
+    const float2 e1 = lane + kWave < cnt ? buf[lane + kWave] : make_float2(-__builtin_inff(), __int_as_float(INT_MAX));
+    s0 = e0.x;
+    i0 = __float_as_int(e0.y);
+    s1 = e1.x;
+    i1 = __float_as_int(e1.y);
+  }
+  auto step = [&](float& sv, int& iv, int x, int k2, int jj) {
+    const float os = __shfl_xor(sv, jj);
+    const int oi = __shfl_xor(iv, jj);
+    const bool lower = (x & jj) == 0;
+    const bool asc = (x & k2) == 0;  // this run sorts best first
+    const bool keep_better = lower == asc;
+    const bool mine_better = better(sv, iv, os, oi);
+    if (keep_better != mine_better) {
+      sv = os;
+      iv = oi;
+    }
+  };
+  for (int k2 = 2; k2 <= 2 * kWave; k2 <<= 1) {
+    for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
+      if (jj == kWave) {  // partner is the other register of this lane (k2 = 128: best first)
+        if (!better(s0, i0, s1, i1)) {
+          const float ts = s0;
+          const int ti = i0;
+          s0 = s1;
+          i0 = i1;
+          s1 = ts;
+          i1 = ti;
+        }
+      } else {
+        step(s0, i0, lane, k2, jj);
+        step(s1, i1, lane + kWave, k2, jj);
+      }
+    }
+  }
+  out_s = s0;
+  out_i = i0;
+}
+
 __device__ __forceinline__ bool split_topk(const float* sc, int n, int idx0, int k, int* hist, float2* buf,
                                            float& out_s, int& out_i) {
   const int lane = __lane_id();
@@ -166,51 +215,7 @@ __device__ __forceinline__ bool split_topk(const float* sc, int n, int idx0, int
     cnt += __popcll(mk);
   }
   if (cnt > kGather) return false;
-  // bitonic sort of buf[0 .. kGather) (padding = worst), best first: element
-  // x = 64 t + lane sits in register t of lane `lane`
-  float s0, s1;
-  int i0, i1;
-  {
-    const float2 e0 = lane < cnt ? buf[lane] : make_float2(-__builtin_inff(), __int_as_float(INT_MAX));
-    const float2 e1 = lane + kWave < cnt ? buf[lane + kWave] : make_float2(-__builtin_inff(), __int_as_float(INT_MAX));
-    s0 = e0.x;
-    i0 = __float_as_int(e0.y);
-    s1 = e1.x;
-    i1 = __float_as_int(e1.y);
-  }
-  auto step = [&](float& sv, int& iv, int x, int k2, int jj) {
-    const float os = __shfl_xor(sv, jj);
-    const int oi = __shfl_xor(iv, jj);
-    const bool lower = (x & jj) == 0;
-    const bool asc = (x & k2) == 0;  // this run sorts best first
-    const bool keep_better = lower == asc;
-    const bool mine_better = better(sv, iv, os, oi);
-    if (keep_better != mine_better) {
-      sv = os;
-      iv = oi;
-    }
-  };
-  for (int k2 = 2; k2 <= 2 * kWave; k2 <<= 1) {
-    for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
-      if (jj == kWave) {  // partner is the other register of this lane
-        const bool asc = ((lane) & k2) == 0;  // x = lane for register 0 (k2 = 128 here: always)
-        const bool b01 = better(s0, i0, s1, i1);
-        if (asc != b01) {
-          const float ts = s0;
-          const int ti = i0;
-          s0 = s1;
-          i0 = i1;
-          s1 = ts;
-          i1 = ti;
-        }
-      } else {
-        step(s0, i0, lane, k2, jj);
-        step(s1, i1, lane + kWave, k2, jj);
-      }
-    }
-  }
-  out_s = s0;
-  out_i = i0;
+  sort_gathered(buf, cnt, out_s, out_i);
   return true;
 }
 
@@ -312,19 +317,62 @@ __global__ __launch_bounds__(kWave* G) void decode_merge_kernel(const float2* __
                                                                 float* __restrict__ sel_score,
                                                                 int4* __restrict__ ulist, int* __restrict__ ucount,
                                                                 int Hkv, int splits, int k) {
+  constexpr int kMaxVals = 1024;  // threshold sample held in LDS per head
   __shared__ int ls[G * 64];
   __shared__ int wave_cnt[G];
+  __shared__ float tvals[G][kMaxVals];
+  __shared__ int hist[G][256];
+  __shared__ float2 gbuf[G][kGather];
+  __shared__ int gcnt[G];
   const int g = blockIdx.x, b = blockIdx.y;
   const int lane = __lane_id(), hh = threadIdx.x / kWave;
   const int64_t bh = (int64_t)b * Hkv * G + (int64_t)g * G + hh;
+  const float2* cb = cand + (((int64_t)b * Hkv + g) * splits * G + hh) * k;
   WaveTopK list;
   list.init();
-  const int total = splits * k;
+
+  // Fast path: the k-th best of the first r entries of every split's sorted
+  // list (at least 2k values) is a lower bound tau of the head's k-th best
+  // score; every entry at or above tau is gathered (each list is walked
+  // until it drops below tau) and sorted.  Too many gathered entries fall
+  // back to merging every candidate.
+  bool done = false;
+  {
+    const int r = min(k, max(1, (2 * k + splits - 1) / splits));
+    const int nv = splits * r;
+    if (nv > 0 && nv <= kMaxVals) {
+      for (int v = lane; v < nv; v += kWave) {
+        const float2 c = cb[(int64_t)(v / r) * G * k + v % r];
+        tvals[hh][v] = __float_as_int(c.y) != INT_MAX ? c.x : -__builtin_inff();
+      }
+      if (lane == 0) gcnt[hh] = 0;
+      float ts;
+      int ti;
+      if (split_topk(tvals[hh], nv, 0, k, hist[hh], gbuf[hh], ts, ti)) {
+        const float tau = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ts), min(k, nv) - 1));
+        if (tau > -__builtin_inff()) {
+          for (int sp = lane; sp < splits; sp += kWave) {
+            for (int e = 0; e < k; ++e) {
+              const float2 c = cb[(int64_t)sp * G * k + e];
+              if (__float_as_int(c.y) == INT_MAX || c.x < tau) break;
+              const int pos = atomicAdd(&gcnt[hh], 1);
+              if (pos < kGather) gbuf[hh][pos] = c;
+            }
+          }
+          const int cnt = gcnt[hh];
+          if (cnt <= kGather) {
+            sort_gathered(gbuf[hh], cnt, list.s, list.i);
+            done = true;
+          }
+        }
+      }
+    }
+  }
+  const int total = done ? 0 : splits * k;
   // rank-major order: every split's best first, so the list fills with
   // strong candidates early and later ranks rarely get in; the loads of
   // kMergeBatch rounds are issued together (the loop is latency-bound)
   constexpr int kMergeBatch = 8;
-  const float2* cb = cand + (((int64_t)b * Hkv + g) * splits * G + hh) * k;
   for (int i0 = 0; i0 < total; i0 += kWave * kMergeBatch) {
     float2 c[kMergeBatch];
 #pragma unroll
@@ -385,9 +433,10 @@ __global__ __launch_bounds__(kWave* G) void decode_merge_kernel(const float2* __
 // independent (no LDS, no barriers).  Logits of all G heads on MFMA:
 // S^T[token][head] = K_c . q_head (A = the chunk's keys, B = the group's
 // queries padded to 32 columns); each head's softmax stays in the two lanes
-// that hold its column.  P.V on the VALU: lane l owns key rows l/LPR + RPI*i
-// and a 16-byte column slice; the probabilities reach it by v_readlane from
-// the owning lanes; a cross-lane sum finishes each output column.
+// that hold its column.  P.V on the VALU: lane l owns value rows
+// l/LPR + RPI*i and a 16-byte column slice; the probabilities go through a
+// wave-private LDS table [token][head]; a cross-lane sum finishes each
+// output column.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void decode_attn_kernel(const typename T::storage* __restrict__ q,
                                                           const typename T::storage* __restrict__ kc,
@@ -405,6 +454,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const typename T::stor
   constexpr int VL = S / RPI;                  // V loads per lane (whole tile)
   constexpr int VPASS = VL > 16 ? 2 : 1;       // fp32 D=128 loads V in two passes
   constexpr int VLP = VL / VPASS;
+  __shared__ __align__(16) float pbuf[4][S][G];  // per wave: probability of (token, head)
   const int b = blockIdx.z, g = blockIdx.y;
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
   const int e = blockIdx.x * 4 + wave;
@@ -468,11 +518,20 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const typename T::stor
     }
   den += __shfl_xor(den, 32);
   const float inv = 1.0f / den;
+  if ((lane & 31) < G) {
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[tb][r] *= inv;
+      for (int r = 0; r < 16; ++r) pbuf[wave][32 * tb + tile_row(r, half)][lane & 31] = sacc[tb][r] * inv;
+  }
+  // the table is private to this wave: its LDS accesses complete in order
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+  bool sel_h[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) sel_h[hh] = ((slots[hh / 4] >> (8 * (hh % 4))) & 0xffu) != 0xffu;
   float o[G][EPS];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
@@ -486,31 +545,23 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const typename T::stor
         vr[i] = *reinterpret_cast<const u32x4*>(vtile + (int64_t)(RPI * (ps * VLP + i) + vrow0) * D + vcol);
     }
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const uint32_t sl = (slots[hh / 4] >> (8 * (hh % 4))) & 0xffu;
-      if (sl == 0xffu) continue;  // this head did not select the chunk (wave-uniform)
+    for (int i = 0; i < VLP; ++i) {
+      const int t = RPI * (ps * VLP + i) + vrow0;  // the value row this lane holds in load i
+      float pr[G];
 #pragma unroll
-      for (int i = 0; i < VLP; ++i) {
-        // probability of the token this lane holds in load i
-        float p = 0.0f;
+      for (int hh = 0; hh < G; ++hh) pr[hh] = pbuf[wave][t][hh];
 #pragma unroll
-        for (int jj = 0; jj < RPI; ++jj) {
-          const int t = RPI * (ps * VLP + i) + jj;
-          const int tb = t / 32, tt = t % 32;
-          const int src_lane = hh + 32 * ((tt / 4) % 2);
-          const int r = 4 * (tt / 8) + (tt % 4);
-          const float pt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sacc[tb][r]), src_lane));
-          p = (vrow0 == jj) ? pt : p;
-        }
+      for (int hh = 0; hh < G; ++hh) {
+        if (!sel_h[hh]) continue;  // this head did not select the chunk (wave-uniform)
         if constexpr (T::kBytes == 2) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            o[hh][2 * w] = fmaf(p, bf16_lo(vr[i][w]), o[hh][2 * w]);
-            o[hh][2 * w + 1] = fmaf(p, bf16_hi(vr[i][w]), o[hh][2 * w + 1]);
+            o[hh][2 * w] = fmaf(pr[hh], bf16_lo(vr[i][w]), o[hh][2 * w]);
+            o[hh][2 * w + 1] = fmaf(pr[hh], bf16_hi(vr[i][w]), o[hh][2 * w + 1]);
           }
         } else {
 #pragma unroll
-          for (int w = 0; w < 4; ++w) o[hh][w] = fmaf(p, __uint_as_float(vr[i][w]), o[hh][w]);
+          for (int w = 0; w < 4; ++w) o[hh][w] = fmaf(pr[hh], __uint_as_float(vr[i][w]), o[hh][w]);
         }
       }
     }
