@@ -274,10 +274,19 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
           if (lane == 0) tneed[hh][ti >> 5] |= 1u << (ti & 31);
           float lo[16], hi[16];
           to_rows(acc0, acc1, ti, lo, hi);
+          // groups of 8 candidates, skipped when no row's group maximum
+          // reaches its threshold
 #pragma unroll
-          for (int ii = 31; ii >= 0; --ii) {
-            const float x = cand(lo, hi, ii);
-            if (x >= ls[KSEL - 1]) score_insert<KSEL>(ls, x);
+          for (int gg = 3; gg >= 0; --gg) {
+            float gm = cand(lo, hi, 8 * gg);
+#pragma unroll
+            for (int q = 1; q < 8; ++q) gm = fmaxf(gm, cand(lo, hi, 8 * gg + q));
+            if (!__ballot(gm >= ls[KSEL - 1])) continue;
+#pragma unroll
+            for (int q = 7; q >= 0; --q) {
+              const float x = cand(lo, hi, 8 * gg + q);
+              if (x >= ls[KSEL - 1]) score_insert<KSEL>(ls, x);
+            }
           }
         });
 
@@ -324,14 +333,23 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
           float lo[16], hi[16];
           to_rows(acc0, acc1, ti, lo, hi);
 #pragma unroll
-          for (int ii = 0; ii < 32; ++ii) {
-            const float x = cand(lo, hi, ii);
-            if (x >= tau) {
-              const bool take = x > tau || quota > 0;
-              if (x == tau) --quota;
-              if (take && cnt < KSEL) {
-                cbuf[hh][cnt][lane] = make_float2(x, __int_as_float(ti * 32 + ii));
-                ++cnt;
+          for (int gg = 0; gg < 4; ++gg) {
+            // skip a group of 8 in which no row reaches tau
+            float gm = cand(lo, hi, 8 * gg);
+#pragma unroll
+            for (int q = 1; q < 8; ++q) gm = fmaxf(gm, cand(lo, hi, 8 * gg + q));
+            if (!__ballot(gm >= tau)) continue;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const int ii = 8 * gg + q;
+              const float x = cand(lo, hi, ii);
+              if (x >= tau) {
+                const bool take = x > tau || quota > 0;
+                if (x == tau) --quota;
+                if (take && cnt < KSEL) {
+                  cbuf[hh][cnt][lane] = make_float2(x, __int_as_float(ti * 32 + ii));
+                  ++cnt;
+                }
               }
             }
           }
