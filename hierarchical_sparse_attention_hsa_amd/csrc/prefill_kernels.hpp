@@ -99,11 +99,11 @@ __device__ __forceinline__ void score_insert(float (&s)[K], float x) {
 // the multiset of the k best scores (one v_med3 per list position per
 // admitted candidate), which yields the row's k-th best score tau and how
 // many of the k best are strictly above it.  Pass 2 recomputes the same
-// tiles (bit-identical: same operands, same instruction sequence) in
-// ascending chunk order and collects every candidate above tau plus the
-// lowest-index candidates equal to tau until k are kept: exactly the first
-// k in the order (score desc, index asc).  Tiles whose maximum cannot reach
-// a row's threshold are skipped in both passes.
+// tiles (bit-identical: same operands and MFMA sequence) in ascending chunk
+// order and collects every candidate above tau plus the lowest-index
+// candidates equal to tau until k are kept: exactly the first k in the order
+// (score desc, index asc).  Tiles whose maximum cannot reach a row's
+// threshold are skipped in both passes.
 template <typename T, int D, int G, int KSEL>
 __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ lm,
@@ -126,8 +126,6 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
   __shared__ __align__(16) char ring[NST][TILE];
   __shared__ float2 cbuf[HPW][KSEL][kWave];
   __shared__ uint32_t tneed[HPW][MAXT / 32];  // pass 1: tile reached a row's threshold
-  __shared__ uint16_t tlist[MAXT];            // pass 2: tiles any wave needs, ascending
-  __shared__ int tcount;                      // and how many
 
   const int bid = blockIdx.x;
   const int g = bid % Hkv;  // consecutive workgroups on different XCDs share nothing
@@ -290,70 +288,73 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
           }
         });
 
-    // ---- pass 2: collect the k best in ascending chunk order, over the
-    // tiles some wave still needs (the others skip their arithmetic)
-    if (hh == 0) {
-      int base = 0;
-      for (int w0 = 0; w0 < (ntiles + 31) / 32; w0 += kWave) {
-        const int wi = w0 + lane;
-        uint32_t bits = 0u;
-        if (wi < (ntiles + 31) / 32) {
-#pragma unroll
-          for (int w = 0; w < HPW; ++w) bits |= tneed[w][wi];
-        }
-        // exclusive prefix of the popcounts across the wave
-        int pc = __popc(bits), incl = pc;
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int o = __shfl_up(incl, off);
-          if (lane >= off) incl += o;
-        }
-        int pos = base + incl - pc;
-        while (bits) {
-          tlist[pos++] = (uint16_t)(wi * 32 + __builtin_ctz(bits));
-          bits &= bits - 1u;
-        }
-        base += __shfl(incl, kWave - 1);
-      }
-      if (lane == 0) tcount = base;
-    }
-    __syncthreads();
-    const int nneed = tcount;
+    // ---- pass 2: collect the k best in ascending chunk order.  Each wave
+    // recomputes only the tiles it marked, streaming their landmark
+    // fragments from L2 into registers (double-buffered; no barriers).
     const float tau = ls[KSEL - 1];
     int quota = KSEL;  // entries equal to tau that still fit
 #pragma unroll
     for (int e = 0; e < KSEL; ++e) quota -= ls[e] > tau;
-    pipeline(
-        nneed, [&](int i) { return (int)tlist[i]; },
-        [&](int, int ti, const char* tile) {
-          if (!((tneed[hh][ti >> 5] >> (ti & 31)) & 1u)) return;
-          f32x16 acc0, acc1;
-          contract(tile, acc0, acc1);
-          const bool top = (int64_t)ti * 32 + 32 > n;
-          if (!top && !__ballot(row_max(acc0, acc1) >= tau)) return;
-          float lo[16], hi[16];
-          to_rows(acc0, acc1, ti, lo, hi);
+    const st* lmr = lm + ((int64_t)b * Hkv + g) * Nc * D + 8 * half;
+    Frag<T> fa[KCH], fb[KCH];
+    auto fetch = [&](Frag<T>(&f)[KCH], int ti) {
+      const int64_t c = min((int64_t)ti * 32 + (lane & 31), n - 1);
+      const st* p = lmr + c * D;
 #pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            // skip a group of 8 in which no row reaches tau
-            float gm = cand(lo, hi, 8 * gg);
+      for (int s2 = 0; s2 < KCH; ++s2) load_frag_global(f[s2], p + 16 * s2, true);
+    };
+    auto marked = [&](int ti) {
+      return ((__builtin_amdgcn_readfirstlane(tneed[hh][ti >> 5]) >> (ti & 31)) & 1u) != 0u;
+    };
+    auto next_marked = [&](int ti) {
+      while (ti < ntiles && !marked(ti)) ++ti;
+      return ti;
+    };
+    auto pass2 = [&](const Frag<T>(&f)[KCH], int ti) {
+      f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
-            for (int q = 1; q < 8; ++q) gm = fmaxf(gm, cand(lo, hi, 8 * gg + q));
-            if (!__ballot(gm >= tau)) continue;
+      for (int s2 = 0; s2 < KCH; ++s2) {
+        mfma(acc0, f[s2], qf[0][s2]);
+        mfma(acc1, f[s2], qf[1][s2]);
+      }
+      const bool top = (int64_t)ti * 32 + 32 > n;
+      if (!top && !__ballot(row_max(acc0, acc1) >= tau)) return;
+      float lo[16], hi[16];
+      to_rows(acc0, acc1, ti, lo, hi);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const int ii = 8 * gg + q;
-              const float x = cand(lo, hi, ii);
-              if (x >= tau) {
-                const bool take = x > tau || quota > 0;
-                if (x == tau) --quota;
-                if (take && cnt < KSEL) {
-                  cbuf[hh][cnt][lane] = make_float2(x, __int_as_float(ti * 32 + ii));
-                  ++cnt;
-                }
-              }
+      for (int gg = 0; gg < 4; ++gg) {
+        // skip a group of 8 in which no row reaches tau
+        float gm = cand(lo, hi, 8 * gg);
+#pragma unroll
+        for (int q2 = 1; q2 < 8; ++q2) gm = fmaxf(gm, cand(lo, hi, 8 * gg + q2));
+        if (!__ballot(gm >= tau)) continue;
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2) {
+          const int ii = 8 * gg + q2;
+          const float x = cand(lo, hi, ii);
+          if (x >= tau) {
+            const bool take = x > tau || quota > 0;
+            if (x == tau) --quota;
+            if (take && cnt < KSEL) {
+              cbuf[hh][cnt][lane] = make_float2(x, __int_as_float(ti * 32 + ii));
+              ++cnt;
             }
           }
-        });
+        }
+      }
+    };
+    int ti = next_marked(0);
+    if (ti < ntiles) fetch(fa, ti);
+    while (ti < ntiles) {
+      const int t1 = next_marked(ti + 1);
+      if (t1 < ntiles) fetch(fb, t1);
+      pass2(fa, ti);
+      if (t1 >= ntiles) break;
+      const int t2 = next_marked(t1 + 1);
+      if (t2 < ntiles) fetch(fa, t2);
+      pass2(fb, t1);
+      ti = t2;
+    }
   }
   const int64_t t_row = (int64_t)j * kChunk + lane;
   // order the kept set by (score desc, index asc)
