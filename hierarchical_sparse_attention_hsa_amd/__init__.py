@@ -12,6 +12,8 @@ Functions carry the C names:
     hsa_build_landmarks(k, landmarks, chunk_size, chunk_begin=0, chunk_end=None)
     hsa_forward_prefill(q, k, v, landmarks, chunk_size, top_k, out=None, sel_idx=None, sel_score=None, workspace=None)
     hsa_forward_decode(q, k_cache, v_cache, landmarks, chunk_size, top_k, out=None, sel_idx=None, sel_score=None, workspace=None)
+    hsa_forward_decode_varlen(q, k_cache, v_cache, landmarks, cache_lens, chunk_size, top_k, ...)
+    hsa_append_kv(k_new, v_new, k_cache, v_cache, landmarks, cache_lens, chunk_size)
     hsa_attn_workspace_size(...)
 """
 from __future__ import annotations
@@ -21,15 +23,15 @@ import os
 
 __all__ = [
     "library_path", "load_library", "Dims", "HSAError", "EXPORTED_SYMBOLS",
-    "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_decode",
-    "hsa_attn_set_timing_events", "hsa_attn_workspace_size", "hsa_attn_status_string",
+    "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_decode", "hsa_forward_decode_varlen",
+    "hsa_append_kv", "hsa_attn_set_timing_events", "hsa_attn_workspace_size", "hsa_attn_status_string",
     "hsa_attn_last_error", "landmarks_shape",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 EXPORTED_SYMBOLS = (
-    "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_decode",
-    "hsa_attn_set_timing_events", "hsa_attn_workspace_size", "hsa_attn_status_string",
+    "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_decode", "hsa_forward_decode_varlen",
+    "hsa_append_kv", "hsa_attn_set_timing_events", "hsa_attn_workspace_size", "hsa_attn_status_string",
     "hsa_attn_last_error",
 )
 
@@ -80,14 +82,16 @@ def load_library():
     lib.hsa_build_landmarks.argtypes = [dims, P, P, I64, I64, P]
     lib.hsa_forward_prefill.argtypes = [dims, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_decode.argtypes = [dims, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_forward_decode_varlen.argtypes = [dims, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_append_kv.argtypes = [dims, P, P, P, P, P, P, P]
     lib.hsa_attn_workspace_size.argtypes = [dims, ctypes.c_int, ctypes.POINTER(SZ)]
     lib.hsa_attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.hsa_attn_status_string.argtypes = [ctypes.c_int]
     lib.hsa_attn_status_string.restype = ctypes.c_char_p
     lib.hsa_attn_last_error.argtypes = []
     lib.hsa_attn_last_error.restype = ctypes.c_char_p
-    for f in ("hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_decode", "hsa_attn_workspace_size",
-              "hsa_attn_set_timing_events"):
+    for f in ("hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_decode", "hsa_forward_decode_varlen",
+              "hsa_append_kv", "hsa_attn_workspace_size", "hsa_attn_set_timing_events"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -186,7 +190,7 @@ def hsa_build_landmarks(k, landmarks, chunk_size: int, chunk_begin: int = 0, chu
     return landmarks
 
 
-def _forward(is_decode, q, k, v, landmarks, chunk_size, top_k, out, sel_idx, sel_score, workspace):
+def _forward(is_decode, q, k, v, landmarks, chunk_size, top_k, out, sel_idx, sel_score, workspace, lens=None):
     torch = _torch()
     B, Hkv, T, D = k.shape
     Hq = q.shape[1]
@@ -205,7 +209,16 @@ def _forward(is_decode, q, k, v, landmarks, chunk_size, top_k, out, sel_idx, sel
     if workspace is None:
         need = hsa_attn_workspace_size(dims, is_decode)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    fn = load_library().hsa_forward_decode if is_decode else load_library().hsa_forward_prefill
+    lib = load_library()
+    if lens is not None:
+        if lens.dtype != torch.int64 or tuple(lens.shape) != (B,):
+            raise ValueError("cache_lens must be an int64 tensor of shape [B]")
+        st = lib.hsa_forward_decode_varlen(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(landmarks),
+                                           _ptr(lens), _ptr(out), _ptr(sel_idx), _ptr(sel_score), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(q.device))
+        _check(st, "hsa_forward_decode_varlen")
+        return out
+    fn = lib.hsa_forward_decode if is_decode else lib.hsa_forward_prefill
     st = fn(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(landmarks), _ptr(out), _ptr(sel_idx),
             _ptr(sel_score), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(st, "hsa_forward_decode" if is_decode else "hsa_forward_prefill")
@@ -222,3 +235,31 @@ def hsa_forward_decode(q, k_cache, v_cache, landmarks, chunk_size: int, top_k: i
                        sel_score=None, workspace=None):
     """HSA for single-token queries q [B,Hq,D] after caches k/v [B,Hkv,T,D] -> out [B,Hq,D] fp32."""
     return _forward(True, q, k_cache, v_cache, landmarks, chunk_size, top_k, out, sel_idx, sel_score, workspace)
+
+
+def hsa_forward_decode_varlen(q, k_cache, v_cache, landmarks, cache_lens, chunk_size: int, top_k: int, out=None,
+                              sel_idx=None, sel_score=None, workspace=None):
+    """HSA for single-token queries q [B,Hq,D] after caches k/v [B,Hkv,T_cap,D]
+    holding cache_lens[b] tokens each (int64 [B] on the device) -> out [B,Hq,D] fp32."""
+    return _forward(True, q, k_cache, v_cache, landmarks, chunk_size, top_k, out, sel_idx, sel_score, workspace,
+                    lens=cache_lens)
+
+
+def hsa_append_kv(k_new, v_new, k_cache, v_cache, landmarks, cache_lens, chunk_size: int):
+    """Append k_new/v_new [B,Hkv,D] at position cache_lens[b] of the caches
+    [B,Hkv,T_cap,D], build the landmark of a chunk the token completes, and
+    advance cache_lens (int64 [B], device), asynchronously."""
+    torch = _torch()
+    B, Hkv, T, D = k_cache.shape
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new and v_new must be [B, Hkv, D]")
+    if v_cache.shape != k_cache.shape or len({t.dtype for t in (k_new, v_new, k_cache, v_cache, landmarks)}) != 1:
+        raise ValueError("caches, new rows and landmarks must share dtype and cache shape")
+    if tuple(landmarks.shape) != landmarks_shape(k_cache.shape, chunk_size):
+        raise ValueError("landmarks must be [B, Hkv, T_cap // chunk_size, D]")
+    if cache_lens.dtype != torch.int64 or tuple(cache_lens.shape) != (B,):
+        raise ValueError("cache_lens must be an int64 tensor of shape [B]")
+    dims = make_dims(B, Hkv, Hkv, D, chunk_size, 1, T, _dtype_code(k_cache))
+    _check(load_library().hsa_append_kv(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(landmarks), _ptr(cache_lens), _stream(k_cache.device)),
+           "hsa_append_kv")

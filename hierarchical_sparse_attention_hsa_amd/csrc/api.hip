@@ -196,9 +196,10 @@ hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, c
   }
 }
 
-hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, const void* k_cache,
-                                     const void* v_cache, const void* landmarks, float* out, int32_t* sel_idx,
-                                     float* sel_score, void* workspace, size_t workspace_bytes, void* stream) {
+static hsa_attn_status_t forward_decode(const hsa_attn_dims_t* d, const void* q, const void* k_cache,
+                                        const void* v_cache, const void* landmarks, const int64_t* lens, float* out,
+                                        int32_t* sel_idx, float* sel_score, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
   try {
     hsa_attn::Geometry g;
     hsa_attn_status_t st = check_dims(d, Call::kDecode, &g);
@@ -210,6 +211,8 @@ hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, co
     for (const void* p : {q, k_cache, v_cache, landmarks, (const void*)out, (const void*)sel_idx,
                           (const void*)sel_score, (const void*)workspace})
       if (p && !aligned16(p)) return fail(HSA_ATTN_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    if (lens && (reinterpret_cast<uintptr_t>(lens) & 7u) != 0)
+      return fail(HSA_ATTN_INVALID_ARGUMENT, "cache_lens must be 8-byte aligned");
     const bool own = sel_idx == nullptr;
     const hsa_attn::DecodePlan plan = hsa_attn::plan_decode(g, own);
     if (workspace_bytes < plan.bytes)
@@ -220,8 +223,47 @@ hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, co
       sel_score = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.off_sel_score);
     }
     restart_timing();
-    hsa_attn::DecodeArgs a{g, q, k_cache, v_cache, landmarks, out, sel_idx, sel_score, workspace};
+    hsa_attn::DecodeArgs a{g, q, k_cache, v_cache, landmarks, out, sel_idx, sel_score, workspace, lens};
     return hip_status(hsa_attn::launch_decode(a, plan, static_cast<hipStream_t>(stream)), "decode launch");
+  } catch (const std::exception& e) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error");
+  }
+}
+
+hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, const void* k_cache,
+                                     const void* v_cache, const void* landmarks, float* out, int32_t* sel_idx,
+                                     float* sel_score, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_decode(d, q, k_cache, v_cache, landmarks, nullptr, out, sel_idx, sel_score, workspace,
+                        workspace_bytes, stream);
+}
+
+hsa_attn_status_t hsa_forward_decode_varlen(const hsa_attn_dims_t* d, const void* q, const void* k_cache,
+                                            const void* v_cache, const void* landmarks, const int64_t* cache_lens,
+                                            float* out, int32_t* sel_idx, float* sel_score, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  if (!cache_lens) return fail(HSA_ATTN_INVALID_ARGUMENT, "cache_lens is NULL");
+  return forward_decode(d, q, k_cache, v_cache, landmarks, cache_lens, out, sel_idx, sel_score, workspace,
+                        workspace_bytes, stream);
+}
+
+hsa_attn_status_t hsa_append_kv(const hsa_attn_dims_t* d, const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, void* landmarks, int64_t* cache_lens, void* stream) {
+  try {
+    hsa_attn::Geometry g;
+    hsa_attn_status_t st = check_dims(d, Call::kLandmarks, &g);
+    if (st != HSA_ATTN_OK) return st;
+    if (!k_new || !v_new || !k_cache || !v_cache || !cache_lens || (!landmarks && g.Nc > 0))
+      return fail(HSA_ATTN_INVALID_ARGUMENT, "k_new, v_new, k_cache, v_cache, landmarks and cache_lens must be non-NULL");
+    for (const void* p : {k_new, v_new, (const void*)k_cache, (const void*)v_cache, (const void*)landmarks})
+      if (p && !aligned16(p)) return fail(HSA_ATTN_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(cache_lens) & 7u) != 0)
+      return fail(HSA_ATTN_INVALID_ARGUMENT, "cache_lens must be 8-byte aligned");
+    restart_timing();
+    hsa_attn::AppendArgs a{k_new, v_new, k_cache, v_cache, landmarks, cache_lens, g.B, g.Hkv, g.T, g.Nc, g.S,
+                           g.D, g.bf16};
+    return hip_status(hsa_attn::launch_append(a, static_cast<hipStream_t>(stream)), "append launch");
   } catch (const std::exception& e) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
   } catch (...) {

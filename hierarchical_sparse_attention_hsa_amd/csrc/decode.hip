@@ -225,7 +225,8 @@ __global__ __launch_bounds__(kScanThreads) void decode_scan_kernel(const typenam
                                                                    const typename T::storage* __restrict__ lm,
                                                                    float2* __restrict__ cand, int Hkv, int64_t Nc,
                                                                    int rows_per_split, int splits, int k,
-                                                                   float scale) {
+                                                                   float scale, const int64_t* __restrict__ lens,
+                                                                   int64_t T_len) {
   constexpr int EPL = T::kVec;
   constexpr int LPR = D / EPL;       // lanes per landmark row
   constexpr int RPI = kWave / LPR;   // rows per load instruction
@@ -237,7 +238,16 @@ __global__ __launch_bounds__(kScanThreads) void decode_scan_kernel(const typenam
   const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x;
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
   const int64_t r_begin = (int64_t)sp * rows_per_split;
-  const int n = (int)min((int64_t)rows_per_split, Nc - r_begin);
+  // complete chunks of this sequence's cache (varlen batches: lens[b] tokens)
+  const int64_t ncb = lens ? min(max(lens[b], (int64_t)0), T_len) / 64 : Nc;
+  const int n = (int)min((int64_t)rows_per_split, ncb - r_begin);
+  if (n <= 0) {  // a split past the end of this cache: empty candidate lists
+    for (int h = wave; h < G; h += WAVES)
+      if (lane < k)
+        cand[((((int64_t)b * Hkv + g) * splits + sp) * G + h) * k + lane] =
+            make_float2(-__builtin_inff(), __int_as_float(INT_MAX));
+    return;
+  }
   const int col = (lane % LPR) * EPL;
 
   u32x4 qv[G];
@@ -650,7 +660,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipS
     mark_launch(st);
     hipLaunchKernelGGL((decode_scan_kernel<T, D, G>), dim3(p.splits, g.Hkv, g.B), dim3(kScanThreads), lds, st,
                        static_cast<const stg*>(a.q), static_cast<const stg*>(a.lm), cand, g.Hkv, g.Nc,
-                       p.rows_per_split, p.splits, g.k, scale);
+                       p.rows_per_split, p.splits, g.k, scale, a.lens, g.T);
     mark_launch(st);
   }
   mark_launch(st);

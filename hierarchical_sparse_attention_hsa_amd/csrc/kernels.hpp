@@ -23,6 +23,19 @@ struct LandmarkArgs {
 };
 hipError_t launch_landmarks(const LandmarkArgs& a, hipStream_t st);
 
+// one new token per sequence appended at position lens[b] of caches with
+// capacity T; a chunk it completes gets its landmark; lens[b] advances
+struct AppendArgs {
+  const void *k_new, *v_new;
+  void *k, *v, *lm;
+  int64_t* lens;
+  int B, Hkv;
+  int64_t T, Nc;
+  int S, D;
+  bool bf16;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+
 // Geometry shared by the forward passes.
 struct Geometry {
   int B, Hq, Hkv, G, D, S, k;
@@ -46,6 +59,7 @@ struct DecodeArgs {
   int32_t* sel_idx;
   float* sel_score;
   void* ws;
+  const int64_t* lens;  // per-sequence cache lengths (device), or null: all g.T
 };
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t st);
 

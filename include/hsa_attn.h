@@ -124,17 +124,46 @@ hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, co
                                      size_t workspace_bytes, void* stream);
 
 /*
+ * Decode over a batch of caches of different lengths (incremental decoding;
+ * card, "Core Technique": per-query cost O(n/S) for scoring, O(k*S) for
+ * attention, so a growing cache is served in place).  d->seq_len is the
+ * capacity T_cap of every cache: k_cache/v_cache [B,Hkv,T_cap,D],
+ * landmarks [B,Hkv,floor(T_cap/S),D].  cache_lens [B] (device int64,
+ * 8-byte aligned) holds each cache's current length; sequence b's query sits
+ * at position cache_lens[b] (values outside [0, T_cap] are clamped), so its
+ * candidates are its floor(cache_lens[b]/S) complete chunks, whose landmarks
+ * must be built.  Otherwise identical to hsa_forward_decode, including the
+ * workspace (sized for the capacity) and the outputs.
+ */
+hsa_attn_status_t hsa_forward_decode_varlen(const hsa_attn_dims_t* d, const void* q, const void* k_cache,
+                                            const void* v_cache, const void* landmarks, const int64_t* cache_lens,
+                                            float* out, int32_t* sel_idx, float* sel_score, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
+/*
+ * Append one token per sequence to the caches (card, "Implementation":
+ * chunks and their mean-pooled landmarks): k_new/v_new [B,Hkv,D] are written
+ * at position cache_lens[b] of k_cache/v_cache [B,Hkv,T_cap,D]
+ * (d->seq_len = T_cap); if the token completes chunk c (cache_lens[b] + 1 a
+ * multiple of S), landmarks[b,:,c,:] is built exactly as
+ * hsa_build_landmarks would; then cache_lens[b] (device int64) advances by
+ * one.  A sequence whose cache is full (cache_lens[b] >= T_cap) is left
+ * unchanged.  Any chunk size S >= 1; D in {64, 128}.
+ */
+hsa_attn_status_t hsa_append_kv(const hsa_attn_dims_t* d, const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, void* landmarks, int64_t* cache_lens, void* stream);
+
+/*
  * Diagnostics: per-launch timing.  After this call, every subsequent
- * hsa_build_landmarks / hsa_forward_prefill / hsa_forward_decode call made on
- * the calling thread records events[2*i] (hipEvent_t, created by the caller)
+ * forward, landmark or append call made on the calling thread records events[2*i] (hipEvent_t, created by the caller)
  * on its stream just before its i-th kernel launch and events[2*i+1] just
  * after it, for i < n_pairs; the index restarts at 0 with each call.
  * Launch order: landmarks: 1 kernel; prefill (when T >= S): zero, select,
  * V transpose, scan, scatter, remote attention, local attention (for T < S:
- * select, local attention); decode:
- * scan, merge, attention, fusion (scan and attention are skipped when the
- * cache has no complete chunk).  events == NULL or n_pairs == 0 turns
- * recording off.  The setting is thread-local; the events stay owned by the
+ * select, local attention); decode and varlen decode: scan, merge,
+ * attention, fusion (scan and attention are skipped when the cache capacity
+ * holds no complete chunk); append: 1 kernel.  events == NULL or
+ * n_pairs == 0 turns recording off.  The setting is thread-local; the events stay owned by the
  * caller and must outlive the calls that record them.
  */
 hsa_attn_status_t hsa_attn_set_timing_events(void** events, int n_pairs);

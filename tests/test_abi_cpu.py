@@ -113,3 +113,25 @@ def test_status_strings():
     assert hsa.hsa_attn_status_string(0) == "ok"
     assert hsa.hsa_attn_status_string(3) == "workspace too small"
     assert hsa.hsa_attn_status_string(99) == "unknown status"
+
+
+def test_varlen_and_append_validation():
+    lib = hsa.load_library()
+    p = ctypes.c_void_p(0x1000)
+    d = dims(seq_len=64 * 100)
+    # cache_lens is required and must be 8-byte aligned
+    assert lib.hsa_forward_decode_varlen(ctypes.byref(d), p, p, p, p, None, p, None, None, p, 1 << 30,
+                                         None) == hsa.HSA_ATTN_INVALID_ARGUMENT
+    assert "cache_lens" in hsa.hsa_attn_last_error()
+    assert lib.hsa_forward_decode_varlen(ctypes.byref(d), p, p, p, p, ctypes.c_void_p(0x1004), p, None, None, p,
+                                         1 << 30, None) == hsa.HSA_ATTN_INVALID_ARGUMENT
+    assert lib.hsa_forward_decode_varlen(ctypes.byref(d), p, p, p, p, p, p, None, None, p, 16,
+                                         None) == hsa.HSA_ATTN_WORKSPACE_TOO_SMALL
+    assert lib.hsa_forward_decode_varlen(ctypes.byref(dims(chunk_size=32)), p, p, p, p, p, p, None, None, p,
+                                         1 << 30, None) == hsa.HSA_ATTN_UNSUPPORTED
+    # append: every buffer is required; any chunk size; D in {64, 128}
+    assert lib.hsa_append_kv(ctypes.byref(d), p, p, p, p, p, None, None) == hsa.HSA_ATTN_INVALID_ARGUMENT
+    assert lib.hsa_append_kv(ctypes.byref(d), None, p, p, p, p, p, None) == hsa.HSA_ATTN_INVALID_ARGUMENT
+    assert lib.hsa_append_kv(ctypes.byref(d), p, p, p, p, p, ctypes.c_void_p(0x1004),
+                             None) == hsa.HSA_ATTN_INVALID_ARGUMENT
+    assert lib.hsa_append_kv(ctypes.byref(dims(head_dim=96)), p, p, p, p, p, p, None) == hsa.HSA_ATTN_UNSUPPORTED

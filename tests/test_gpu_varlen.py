@@ -1,0 +1,144 @@
+"""GPU parity of incremental decoding: hsa_forward_decode_varlen over caches
+of different lengths inside one capacity, and hsa_append_kv growing the
+caches token by token (landmarks of completed chunks built on the spot).
+Each sequence is checked against the oracle's decode on its own prefix; the
+varlen result must also equal, bit for bit, hsa_forward_decode run on each
+sequence's prefix alone (selection is exact and every per-chunk result is
+computed the same way)."""
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_hsa_amd as hsa
+from hierarchical_sparse_attention_hsa_amd.workloads import small_inputs
+from oracle import hsa_oracle as O
+from tests.gpu_util import TOL, check_rows, f64, new_stats
+
+pytestmark = pytest.mark.gpu
+S = 64
+
+
+def oracle_check(q, kc, vc, lens, topk, dtype, out, sel, score):
+    """q [B,Hq,D], caches [B,Hkv,Tcap,D] (CPU), lens: list of lengths."""
+    Q, K, V = f64(q), f64(kc), f64(vc)
+    B, Hq, D = Q.shape
+    Hkv = K.shape[1]
+    stats = new_stats()
+    for b in range(B):
+        T = int(lens[b])
+        L = O.landmarks(K[b, :, :T], S, dtype)
+        for h in range(Hq):
+            g = O.kv_head_of(h, Hq, Hkv)
+            check_rows(Q[b, h][None], np.array([T]), K[b, g, :T], V[b, g, :T], L[g], S, topk, out[b, h][None],
+                       sel[b, h][None], score[b, h][None], TOL[dtype], stats)
+    return stats
+
+
+def run_varlen(q, kc, vc, lens, topk):
+    B, Hkv, Tcap, D = kc.shape
+    qd, kd, vd = q.cuda(), kc.cuda(), vc.cuda()
+    L = torch.zeros((B, Hkv, Tcap // S, D), dtype=kc.dtype, device="cuda")
+    hsa.hsa_build_landmarks(kd, L, S)  # landmarks of every chunk; only complete prefixes are read
+    ln = torch.tensor(lens, dtype=torch.int64, device="cuda")
+    Hq = q.shape[1]
+    sel = torch.full((B, Hq, topk), -7, dtype=torch.int32, device="cuda")
+    score = torch.full((B, Hq, topk), 7.0, dtype=torch.float32, device="cuda")
+    out = hsa.hsa_forward_decode_varlen(qd, kd, vd, L, ln, S, topk, sel_idx=sel, sel_score=score)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy(), sel.cpu().numpy(), score.cpu().double().numpy()
+
+
+CASES = [
+    # B, Hq, Hkv, Tcap, D, k, dtype, lengths
+    (6, 16, 4, 64 * 80, 128, 16, "bf16", [0, 50, 64, 64 * 37 + 5, 4000, 64 * 80]),
+    (3, 8, 8, 64 * 40, 64, 8, "fp32", [64 * 40, 100, 64 * 9]),
+    (4, 8, 1, 64 * 3000, 128, 64, "bf16", [64 * 3000, 64 * 1500 + 7, 1, 64 * 700]),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_varlen_decode_matches_oracle_and_fixed_length_decode(case):
+    B, Hq, Hkv, Tcap, D, topk, dtype, lens = case
+    print(f"varlen case {case[:7]} lengths {lens}", flush=True)
+    q, kc, vc = small_inputs(B, Hq, Hkv, Tcap, D, dtype, seed=sum(lens) % 9973, decode=True)
+    out, sel, score = run_varlen(q, kc, vc, lens, topk)
+    print(oracle_check(q, kc, vc, lens, topk, dtype, out, sel, score))
+    for b in range(B):
+        T = lens[b]
+        kd = kc[b:b + 1, :, :T].contiguous().cuda()
+        vd = vc[b:b + 1, :, :T].contiguous().cuda()
+        L = torch.empty((1, Hkv, T // S, D), dtype=kc.dtype, device="cuda")
+        hsa.hsa_build_landmarks(kd, L, S)
+        o1 = hsa.hsa_forward_decode(q[b:b + 1].contiguous().cuda(), kd, vd, L, S, topk)
+        torch.cuda.synchronize()
+        assert np.array_equal(o1.cpu().double().numpy()[0], out[b]), f"sequence {b}"
+
+
+def test_append_grows_caches_and_landmarks():
+    """Start from different lengths, append 200 tokens one at a time with a
+    decode before every append; check decodes against the oracle along the
+    way, and the caches, landmarks and lengths at the end."""
+    B, Hq, Hkv, Tcap, D, topk = 3, 8, 2, 64 * 12, 128, 8
+    q0, kc, vc = small_inputs(B, Hq, Hkv, Tcap, D, "bf16", seed=77, decode=True)
+    start = [0, 100, 500]
+    steps = 200
+    r = np.random.default_rng(9)
+    qs = torch.from_numpy(r.standard_normal((steps, B, Hq, D), dtype=np.float32)).to(torch.bfloat16)
+    kn = torch.from_numpy(r.standard_normal((steps, B, Hkv, D), dtype=np.float32)).to(torch.bfloat16)
+    vn = torch.from_numpy(r.standard_normal((steps, B, Hkv, D), dtype=np.float32)).to(torch.bfloat16)
+    # expected final caches: the start prefixes, then the appended rows
+    ke, ve = kc.clone(), vc.clone()
+    for b in range(B):
+        ke[b, :, start[b]:start[b] + steps] = kn[:, b].permute(1, 0, 2)
+        ve[b, :, start[b]:start[b] + steps] = vn[:, b].permute(1, 0, 2)
+    kd, vd = kc.clone().cuda(), vc.clone().cuda()
+    # the rows past each start length are garbage the append must overwrite
+    for b in range(B):
+        kd[b, :, start[b]:] = 5.0
+        vd[b, :, start[b]:] = 5.0
+    L = torch.zeros((B, Hkv, Tcap // S, D), dtype=torch.bfloat16, device="cuda")
+    for b in range(B):
+        nb = start[b] // S
+        if nb:
+            Lb = torch.empty((1, Hkv, Tcap // S, D), dtype=torch.bfloat16, device="cuda")
+            hsa.hsa_build_landmarks(kd[b:b + 1], Lb, S, 0, nb)
+            L[b, :, :nb] = Lb[0, :, :nb]
+    lens = torch.tensor(start, dtype=torch.int64, device="cuda")
+    stats = new_stats()
+    for t in range(steps):
+        qd = qs[t].cuda()
+        sel = torch.empty((B, Hq, topk), dtype=torch.int32, device="cuda")
+        score = torch.empty((B, Hq, topk), dtype=torch.float32, device="cuda")
+        out = hsa.hsa_forward_decode_varlen(qd, kd, vd, L, lens, S, topk, sel_idx=sel, sel_score=score)
+        hsa.hsa_append_kv(kn[t].cuda(), vn[t].cuda(), kd, vd, L, lens, S)
+        if t % 40 == 7 or t == steps - 1:
+            torch.cuda.synchronize()
+            cur = [start[b] + t for b in range(B)]
+            st = oracle_check(qs[t], ke, ve, cur, topk, "bf16", out.cpu().double().numpy(), sel.cpu().numpy(),
+                              score.cpu().double().numpy())
+            for key in ("rows", "near_tie_rows"):
+                stats[key] += st[key]
+    torch.cuda.synchronize()
+    print(stats)
+    assert lens.cpu().tolist() == [s + steps for s in start]
+    for b in range(B):
+        n = start[b] + steps
+        assert torch.equal(kd[b, :, :n].cpu(), ke[b, :, :n]) and torch.equal(vd[b, :, :n].cpu(), ve[b, :, :n])
+        ref = O.landmarks(f64(ke[b, :, :n]), S, "bf16")
+        assert np.array_equal(f64(L[b, :, :n // S]), ref), f"landmarks of sequence {b}"
+
+
+def test_append_full_cache_is_left_unchanged():
+    B, Hkv, Tcap, D = 2, 2, 128, 64
+    kd = torch.zeros((B, Hkv, Tcap, D), dtype=torch.float32, device="cuda")
+    vd = torch.zeros_like(kd)
+    L = torch.zeros((B, Hkv, Tcap // S, D), dtype=torch.float32, device="cuda")
+    lens = torch.tensor([Tcap, Tcap - 1], dtype=torch.int64, device="cuda")
+    kn = torch.ones((B, Hkv, D), dtype=torch.float32, device="cuda")
+    hsa.hsa_append_kv(kn, kn, kd, vd, L, lens, S)
+    torch.cuda.synchronize()
+    assert lens.cpu().tolist() == [Tcap, Tcap]
+    assert float(kd[0].abs().sum()) == 0.0
+    assert float(kd[1, :, Tcap - 1].sum()) == Hkv * D
+    # sequence 1 completed its last chunk: mean of 63 zeros and one row of ones
+    assert torch.allclose(L[1, :, 1], torch.full((Hkv, D), 1.0 / 64, device="cuda"))
