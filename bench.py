@@ -271,6 +271,72 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
     return res
 
 
+def bench_decode_varlen(wname, steps, warmup):
+    """Incremental decoding: each step decodes one query per sequence over
+    its current cache length (hsa_forward_decode_varlen) and appends one
+    token (hsa_append_kv), so lengths advance by one per step."""
+    import torch
+    import hierarchical_sparse_attention_hsa_amd as hsa
+    from hierarchical_sparse_attention_hsa_amd.workloads import WORKLOADS, cache_lengths, decode_inputs
+
+    w = WORKLOADS[wname]
+    G = w.Hq // w.Hkv
+    esz = 2 if w.dtype == "bf16" else 4
+    Nc = w.T // w.S
+    t0 = time.perf_counter()
+    q, k, v = decode_inputs(w, "cuda")
+    L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
+    hsa.hsa_build_landmarks(k, L, w.S)
+    lens0 = cache_lengths(w)
+    lens = torch.tensor(lens0, dtype=torch.int64, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 6)
+    k_new = torch.randn((w.B, w.Hkv, w.D), generator=gen, device="cuda").to(k.dtype)
+    v_new = torch.randn((w.B, w.Hkv, w.D), generator=gen, device="cuda").to(k.dtype)
+    torch.cuda.synchronize()
+    log(f"[{wname}] generated inputs in {time.perf_counter() - t0:.1f} s; cache lengths "
+        f"{int(lens0.min())} .. {int(lens0.max())}")
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, w.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, w.k), dtype=torch.float32, device="cuda")
+    dims = hsa.make_dims(w.B, w.Hq, w.Hkv, w.D, w.S, w.k, w.T, hsa.HSA_ATTN_BF16 if esz == 2 else hsa.HSA_ATTN_FP32)
+    ws = torch.empty(hsa.hsa_attn_workspace_size(dims, True), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if ev is not None:
+            hsa.hsa_attn_set_timing_events(ev[:8])
+        hsa.hsa_forward_decode_varlen(q, k, v, L, lens, w.S, w.k, out=out, sel_idx=sel, sel_score=sc, workspace=ws)
+        if ev is not None:
+            hsa.hsa_attn_set_timing_events(ev[8:])
+        hsa.hsa_append_kv(k_new, v_new, k, v, L, lens, w.S)
+
+    secs, per = timed_steps(step, steps, warmup, 5, HipEvents())
+    ms_step = 1e3 * secs / steps
+    # landmark bytes the scan reads in the timed steps (lengths grow by one per step)
+    ln = lens.cpu().numpy()
+    mid = ln - steps // 2
+    lm_bytes = float(np.sum(mid // w.S)) * w.Hkv * w.D * esz
+    names = ["decode_scan", "decode_merge", "decode_attn", "decode_fuse", "append_kv"]
+    res = {
+        "workload": wname, "value": w.B / (ms_step / 1e3), "unit": "queries/s", "ms_per_step": ms_step,
+        "kernel_ms": {n: float(x) for n, x in zip(names, per)},
+        "config": {"workload": wname, "batch_queries": w.B, "cache_capacity": w.T,
+                   "cache_tokens": [int(lens0.min()), int(lens0.max())], "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "chunk": w.S, "top_k": w.k, "needles": w.needles},
+        "dtype": w.dtype,
+        "roofline": {"kernel": "decode_scan_kernel", "bound": "hbm",
+                     "achieved": lm_bytes / (per[0] / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": lm_bytes / (per[0] / 1e3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": profiled_traffic(wname, "decode_scan_kernel"), "alg_bytes_per_launch": lm_bytes},
+    }
+    log(f"[{wname}] {ms_step:.3f} ms/step, kernels {dict(zip(names, np.round(per, 4)))}, "
+        f"scan {res['roofline']['achieved']:.0f} GB/s")
+    del q, k, v, L, out, sel, sc, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_cpu_baseline(w, q, k, v, queries=(0, 37), min_seconds=10.0):
     """The oracle on a bounded sample: the listed queries, all heads.  Host
     copies and the oracle's own landmark build are untimed (landmarks are
@@ -449,6 +515,8 @@ def main():
     if args.workload == "all":
         results["prefill"] = bench_prefill("prefill_256k_bf16", args.steps, args.warmup, cpu)
         main_res = bench_decode("decode_1m_bf16", args.steps, args.warmup, cpu)
+    elif "varlen" in args.workload:
+        main_res = bench_decode_varlen(args.workload, args.steps, args.warmup)
     elif args.workload.startswith("decode"):
         main_res = bench_decode(args.workload, args.steps, args.warmup, cpu)
     else:

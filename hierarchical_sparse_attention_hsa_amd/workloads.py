@@ -14,6 +14,8 @@ Workloads (all with chunk size 64):
   prefill_256k_bf16  B=1, T=262144, Hq=32, Hkv=8, D=128, k=16, bf16, N(0,1)
                      plus a rank-8 component shared per 4096-token segment
   decode_16m_bf16    B=4 queries, 2^24-token caches, k=64, 16 needles per cache
+  decode_1m_varlen_bf16  as decode_1m_bf16 in caches of capacity 2^20 that
+                     hold seeded lengths in [2^19, 2^20) (cache_lengths)
 
 Needles: per cache, distinct chunk indices drawn uniformly; every key of a
 needle chunk gets 3 * u added (before rounding), u = the normalised sum of
@@ -29,7 +31,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "small_inputs", "prefill_inputs", "decode_inputs", "needle_chunks"]
+__all__ = ["Workload", "WORKLOADS", "small_inputs", "prefill_inputs", "decode_inputs", "needle_chunks",
+           "cache_lengths"]
 
 
 @dataclass(frozen=True)
@@ -60,6 +63,11 @@ WORKLOADS = {
         Workload("decode_1m_bf16", "decode", 64, 32, 8, 1 << 20, 128, 64, 32, "bf16", 3000, needles=8),
         Workload("prefill_256k_bf16", "prefill", 1, 32, 8, 262144, 128, 64, 16, "bf16", 4000, lowrank=8),
         Workload("decode_16m_bf16", "decode", 4, 32, 8, 1 << 24, 128, 64, 64, "bf16", 5000, needles=16),
+        # incremental decoding: caches of capacity 2^20 holding 2^19 .. 2^20
+        # tokens each; every step decodes one query per sequence and appends
+        # one token
+        Workload("decode_1m_varlen_bf16", "decode", 64, 32, 8, 1 << 20, 128, 64, 32, "bf16", 6000, needles=8,
+                 extra={"min_len": 1 << 19}),
     ]
 }
 
@@ -163,3 +171,9 @@ def decode_inputs(w: Workload, device="cuda", slab_tokens=1 << 21, progress=None
         if progress:
             progress(b)
     return q, k, v
+
+
+def cache_lengths(w: Workload):
+    """Seeded per-sequence cache lengths of a varlen decode workload."""
+    r = np.random.default_rng([w.seed + 5])
+    return r.integers(w.extra.get("min_len", w.T), w.T, size=w.B, endpoint=False).astype(np.int64)
