@@ -12,6 +12,7 @@ Functions carry the C names:
     hsa_build_landmarks(k, landmarks, chunk_size, chunk_begin=0, chunk_end=None)
     hsa_forward_prefill(q, k, v, landmarks, chunk_size, top_k, out=None, sel_idx=None, sel_score=None, workspace=None)
     hsa_forward_decode(q, k_cache, v_cache, landmarks, chunk_size, top_k, out=None, sel_idx=None, sel_score=None, workspace=None)
+    hsa_forward_prefill_cached(q_new, k, v, landmarks, q_offset, chunk_size, top_k, ...)
     hsa_forward_decode_varlen(q, k_cache, v_cache, landmarks, cache_lens, chunk_size, top_k, ...)
     hsa_append_kv(k_new, v_new, k_cache, v_cache, landmarks, cache_lens, chunk_size)
     hsa_attn_workspace_size(...)
@@ -23,14 +24,15 @@ import os
 
 __all__ = [
     "library_path", "load_library", "Dims", "HSAError", "EXPORTED_SYMBOLS",
-    "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_decode", "hsa_forward_decode_varlen",
-    "hsa_append_kv", "hsa_attn_set_timing_events", "hsa_attn_workspace_size", "hsa_attn_status_string",
-    "hsa_attn_last_error", "landmarks_shape",
+    "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
+    "hsa_forward_decode_varlen", "hsa_append_kv", "hsa_attn_set_timing_events", "hsa_attn_workspace_size",
+    "hsa_attn_status_string", "hsa_attn_last_error", "landmarks_shape",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 EXPORTED_SYMBOLS = (
-    "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_decode", "hsa_forward_decode_varlen",
+    "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
+    "hsa_forward_decode_varlen",
     "hsa_append_kv", "hsa_attn_set_timing_events", "hsa_attn_workspace_size", "hsa_attn_status_string",
     "hsa_attn_last_error",
 )
@@ -83,6 +85,7 @@ def load_library():
     lib.hsa_forward_prefill.argtypes = [dims, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_decode.argtypes = [dims, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_decode_varlen.argtypes = [dims, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_forward_prefill_cached.argtypes = [dims, I64, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_append_kv.argtypes = [dims, P, P, P, P, P, P, P]
     lib.hsa_attn_workspace_size.argtypes = [dims, ctypes.c_int, ctypes.POINTER(SZ)]
     lib.hsa_attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
@@ -90,7 +93,8 @@ def load_library():
     lib.hsa_attn_status_string.restype = ctypes.c_char_p
     lib.hsa_attn_last_error.argtypes = []
     lib.hsa_attn_last_error.restype = ctypes.c_char_p
-    for f in ("hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_decode", "hsa_forward_decode_varlen",
+    for f in ("hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
+              "hsa_forward_decode_varlen",
               "hsa_append_kv", "hsa_attn_workspace_size", "hsa_attn_set_timing_events"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
@@ -263,3 +267,34 @@ def hsa_append_kv(k_new, v_new, k_cache, v_cache, landmarks, cache_lens, chunk_s
     _check(load_library().hsa_append_kv(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                         _ptr(landmarks), _ptr(cache_lens), _stream(k_cache.device)),
            "hsa_append_kv")
+
+
+def hsa_forward_prefill_cached(q, k, v, landmarks, q_offset: int, chunk_size: int, top_k: int, out=None,
+                               sel_idx=None, sel_score=None, workspace=None):
+    """Causal HSA for the last Tq = T - q_offset positions of a sequence whose
+    keys k/v [B,Hkv,T,D] (prefix and new tokens) and landmarks are given:
+    q [B,Hq,Tq,D] -> out [B,Hq,Tq,D] fp32."""
+    torch = _torch()
+    B, Hkv, T, D = k.shape
+    Hq = q.shape[1]
+    Tq = T - q_offset
+    if v.shape != k.shape or v.dtype != k.dtype or q.dtype != k.dtype:
+        raise ValueError("q, k and v must share dtype; v must match k's shape")
+    if tuple(q.shape) != (B, Hq, Tq, D):
+        raise ValueError(f"q must be {(B, Hq, Tq, D)}, got {tuple(q.shape)}")
+    if tuple(landmarks.shape) != landmarks_shape(k.shape, chunk_size) or landmarks.dtype != k.dtype:
+        raise ValueError("landmarks must be [B, Hkv, T // chunk_size, D] with the dtype of k")
+    dims = make_dims(B, Hq, Hkv, D, chunk_size, top_k, T, _dtype_code(k))
+    if out is None:
+        out = torch.empty((B, Hq, Tq, D), dtype=torch.float32, device=q.device)
+    if (sel_idx is None) != (sel_score is None):
+        raise ValueError("give both sel_idx and sel_score or neither")
+    if workspace is None:
+        need = hsa_attn_workspace_size(dims, False)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = load_library().hsa_forward_prefill_cached(ctypes.byref(dims), int(q_offset), _ptr(q), _ptr(k), _ptr(v),
+                                                   _ptr(landmarks), _ptr(out), _ptr(sel_idx), _ptr(sel_score),
+                                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                   _stream(q.device))
+    _check(st, "hsa_forward_prefill_cached")
+    return out

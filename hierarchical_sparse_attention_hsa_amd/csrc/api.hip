@@ -78,6 +78,8 @@ hsa_attn_status_t check_dims(const hsa_attn_dims_t* d, Call call, hsa_attn::Geom
   g->T = d->seq_len;
   g->Nc = Nc;
   g->bf16 = d->dtype == HSA_ATTN_BF16;
+  g->Tq = d->seq_len;  // every position is a query row unless a caller narrows it
+  g->J0 = 0;
   return HSA_ATTN_OK;
 }
 
@@ -158,13 +160,18 @@ hsa_attn_status_t hsa_build_landmarks(const hsa_attn_dims_t* d, const void* k, v
   }
 }
 
-hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, const void* k, const void* v,
-                                      const void* landmarks, float* out, int32_t* sel_idx, float* sel_score,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+static hsa_attn_status_t forward_prefill(const hsa_attn_dims_t* d, int64_t q_offset, const void* q, const void* k,
+                                         const void* v, const void* landmarks, float* out, int32_t* sel_idx,
+                                         float* sel_score, void* workspace, size_t workspace_bytes, void* stream) {
   try {
     hsa_attn::Geometry g;
     hsa_attn_status_t st = check_dims(d, Call::kPrefill, &g);
     if (st != HSA_ATTN_OK) return st;
+    if (q_offset < 0 || q_offset > g.T || q_offset % g.S != 0)
+      return fail(HSA_ATTN_INVALID_ARGUMENT, "q_offset %lld must be a multiple of chunk_size in [0, seq_len]",
+                  (long long)q_offset);
+    g.Tq = g.T - q_offset;
+    g.J0 = q_offset / g.S;
     if (!q || !k || !v || !out || (!landmarks && g.Nc > 0))
       return fail(HSA_ATTN_INVALID_ARGUMENT, "q, k, v, landmarks and out must be non-NULL");
     if ((sel_idx == nullptr) != (sel_score == nullptr))
@@ -176,7 +183,7 @@ hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, c
     const hsa_attn::PrefillPlan plan = hsa_attn::plan_prefill(g, own);
     if (workspace_bytes < plan.bytes)
       return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes, workspace_bytes);
-    if (g.T == 0) return ok();
+    if (g.Tq == 0) return ok();
     if (!workspace) return fail(HSA_ATTN_INVALID_ARGUMENT, "workspace is NULL");
     char* ws = static_cast<char*>(workspace);
     if (own) {
@@ -194,6 +201,20 @@ hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, c
   } catch (...) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error");
   }
+}
+
+hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, const void* k, const void* v,
+                                      const void* landmarks, float* out, int32_t* sel_idx, float* sel_score,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_prefill(d, 0, q, k, v, landmarks, out, sel_idx, sel_score, workspace, workspace_bytes, stream);
+}
+
+hsa_attn_status_t hsa_forward_prefill_cached(const hsa_attn_dims_t* d, int64_t q_offset, const void* q,
+                                             const void* k, const void* v, const void* landmarks, float* out,
+                                             int32_t* sel_idx, float* sel_score, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  return forward_prefill(d, q_offset, q, k, v, landmarks, out, sel_idx, sel_score, workspace, workspace_bytes,
+                         stream);
 }
 
 static hsa_attn_status_t forward_decode(const hsa_attn_dims_t* d, const void* q, const void* k_cache,

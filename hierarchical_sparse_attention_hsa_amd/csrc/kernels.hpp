@@ -39,9 +39,11 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 // Geometry shared by the forward passes.
 struct Geometry {
   int B, Hq, Hkv, G, D, S, k;
-  int64_t T;    // prefill: sequence length; decode: cache length
+  int64_t T;    // prefill: key length; decode: cache length (capacity)
   int64_t Nc;   // floor(T / S)
   bool bf16;
+  int64_t Tq = 0;  // prefill: query rows, the last Tq of the T positions
+  int64_t J0 = 0;  // prefill: (T - Tq) / S, the chunk of the first query row
 };
 
 // ---------------------------------------------------------------- decode

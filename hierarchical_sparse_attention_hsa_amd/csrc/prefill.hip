@@ -90,7 +90,7 @@ hipError_t launch_prefill_zero_counts(const PrefillArgs& a, hipStream_t st) {
 
 hipError_t launch_prefill_bucketing(const PrefillArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
-  const int64_t total = (int64_t)g.B * g.Hq * g.T * g.k;
+  const int64_t total = (int64_t)g.B * g.Hq * g.Tq * g.k;
   const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;
   const unsigned pb = (unsigned)((total + 255) / 256);
   mark_launch(st);
@@ -98,7 +98,7 @@ hipError_t launch_prefill_bucketing(const PrefillArgs& a, hipStream_t st) {
   mark_launch(st);
   mark_launch(st);
   hipLaunchKernelGGL(prefill_scatter_kernel, dim3(pb), dim3(256), 0, st, a.sel_idx, a.off, a.pair_pos, a.pairs, g.Hq,
-                     g.G, g.T, g.Nc, g.k, total);
+                     g.G, g.Tq, g.Nc, g.k, total);
   mark_launch(st);
   return hipGetLastError();
 }
@@ -106,7 +106,7 @@ hipError_t launch_prefill_bucketing(const PrefillArgs& a, hipStream_t st) {
 PrefillPlan plan_prefill(const Geometry& g, bool own_sel) {
   PrefillPlan p{};
   size_t off = 0;
-  const size_t pairs = (size_t)g.B * g.Hq * (size_t)g.T * g.k;
+  const size_t pairs = (size_t)g.B * g.Hq * (size_t)g.Tq * g.k;
   const size_t nb = (size_t)g.B * g.Hkv * (size_t)g.Nc;
   if (own_sel) {
     p.off_sel_idx = off;

@@ -108,7 +108,8 @@ template <typename T, int D, int G, int KSEL>
 __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ lm,
     int32_t* __restrict__ sel_idx, float* __restrict__ sel_score, int* __restrict__ rcnt, int32_t* __restrict__ pair_pos,
-    int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int k, float scale) {
+    int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int j0, int k, float scale) {
+  // T_len: query rows per (b, h); query row r sits at position 64*j0 + r
   using st = typename T::storage;
   constexpr int HPW = G < 4 ? G : 4;  // query heads (waves) per workgroup
   constexpr int HS = G / HPW;         // workgroups per (b, g, query chunk)
@@ -136,7 +137,8 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
   const int j = nqc - 1 - rest / B;  // heaviest query chunks first
   const int tid = threadIdx.x, lane = tid & 63, hh = tid >> 6, half = lane >> 5;
   const int Hq = Hkv * G, h = g * G + hs * HPW + hh;
-  const int64_t n = min((int64_t)j, Nc);
+  const int ja = j0 + j;  // absolute query chunk
+  const int64_t n = min((int64_t)ja, Nc);
 
   auto wave_max_i = [&](int v) {
     for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
     hcnt[i] = 0;
   }
   __syncthreads();
-  const int wsj = (j / kLocalWindow) * kLocalWindow;
+  const int wsj = (ja / kLocalWindow) * kLocalWindow;
   uint32_t slot_rank[KSEL];  // slot << 16 | rank within the slot, or ~0
 #pragma unroll
   for (int e = 0; e < KSEL; ++e) {
@@ -743,7 +745,8 @@ __global__ __launch_bounds__(kWave* G)
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ kk,
     const typename T::storage* __restrict__ vt_g, const int32_t* __restrict__ sel_idx,
     const float* __restrict__ sel_score, const int32_t* __restrict__ pair_pos, const float* __restrict__ partial,
-    float* __restrict__ out, int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int k, float scale, int nbuf) {
+    float* __restrict__ out, int B, int Hkv, int64_t T_len, int64_t T_q, int64_t Nc, int nqc, int j0, int k,
+    float scale, int nbuf) {
   using st = typename T::storage;
   using TL = Tile<T, D>;
   constexpr int KCH = D / 16;
@@ -765,14 +768,15 @@ __global__ __launch_bounds__(kWave* G)
   const int b = rest % B;
   rest /= B;
   const int hc = rest & 1;
-  const int j = nqc - 1 - (rest >> 1);
+  const int j = nqc - 1 - (rest >> 1);  // query chunk among the T_q query rows
+  const int ja = j0 + j;                 // its absolute chunk (keys: T_len rows)
   const int tid = threadIdx.x, lane = tid & 63, hh = tid >> 6, half = lane >> 5;
   const int Hq = Hkv * G, h = g * G + hh;
-  const int64_t n = min((int64_t)j, Nc);
-  const int ws = (j / kLocalWindow) * kLocalWindow;  // first chunk of the query's window
+  const int64_t n = min((int64_t)ja, Nc);
+  const int ws = (ja / kLocalWindow) * kLocalWindow;  // first chunk of the query's window
   const int row = hh * 32 + (lane & 31);
   const int64_t tok = (int64_t)j * kChunk + 32 * hc + (lane & 31);
-  const bool tok_ok = tok < T_len;
+  const bool tok_ok = tok < T_q;
 
   if (tid < NW) bm[tid] = 0u;
   __syncthreads();
@@ -781,7 +785,7 @@ __global__ __launch_bounds__(kWave* G)
   // ascending chunk order, remote ones with their pair positions
   int m = 0, rc = 0;
   if (lane < 32 && tok_ok && n > 0) {
-    const int64_t base = (((int64_t)b * Hq + h) * T_len + tok) * k;
+    const int64_t base = (((int64_t)b * Hq + h) * T_q + tok) * k;
     int ci[KSEL];
     float sc[KSEL];
 #pragma unroll
@@ -818,7 +822,7 @@ __global__ __launch_bounds__(kWave* G)
 
   Frag<T> qf[KCH];
   {
-    const st* qp = q + (((int64_t)b * Hq + h) * T_len + (tok_ok ? tok : 0)) * D + 8 * half;
+    const st* qp = q + (((int64_t)b * Hq + h) * T_q + (tok_ok ? tok : 0)) * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < KCH; ++s) load_frag_global(qf[s], qp + 16 * s, tok_ok);
   }
@@ -899,7 +903,7 @@ __global__ __launch_bounds__(kWave* G)
     }
   }
   if (tok_ok) {
-    float* op = out + (((int64_t)b * Hq + h) * T_len + tok) * D;
+    float* op = out + (((int64_t)b * Hq + h) * T_q + tok) * D;
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm)
 #pragma unroll
@@ -917,7 +921,8 @@ template <typename T, int D, int G, int KSEL>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
   using stg = typename T::storage;
-  const int nqc = (int)((g.T + kChunk - 1) / kChunk);
+  const int nqc = (int)((g.Tq + kChunk - 1) / kChunk);  // query chunks
+  const int j0 = (int)g.J0;
   const float scale = 1.0f / sqrtf((float)D);
   const unsigned blocks = (unsigned)((int64_t)nqc * g.B * g.Hkv);
   const stg* q = static_cast<const stg*>(a.q);
@@ -932,7 +937,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   mark_launch(st);
   hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(blocks * (G / HPW)), dim3(kWave * HPW), 0, st, q,
                      static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, nb > 0 ? a.cnt : nullptr, a.pair_pos,
-                     g.B, g.Hkv, g.T, g.Nc, nqc, g.k, scale);
+                     g.B, g.Hkv, g.Tq, g.Nc, nqc, j0, g.k, scale);
   mark_launch(st);
   if (nb > 0) {
     mark_launch(st);
@@ -958,8 +963,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   }
   mark_launch(st);
   hipLaunchKernelGGL(kern, dim3(2 * blocks), dim3(kWave * G), lds, st, q, k, static_cast<const stg*>(a.vt),
-                     a.sel_idx, a.sel_score, a.pair_pos, a.partial, a.out, g.B, g.Hkv, g.T, g.Nc, nqc, g.k, scale,
-                     nbuf);
+                     a.sel_idx, a.sel_score, a.pair_pos, a.partial, a.out, g.B, g.Hkv, g.T, g.Tq, g.Nc, nqc, j0,
+                     g.k, scale, nbuf);
   mark_launch(st);
   return hipGetLastError();
 }

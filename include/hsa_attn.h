@@ -110,6 +110,23 @@ hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, c
                                       size_t workspace_bytes, void* stream);
 
 /*
+ * Chunked prefill over a cached prefix (serving: new tokens appended to a
+ * cache; card, "Core Technique"): the keys are the whole sequence,
+ * k/v [B,Hkv,T,D] with d->seq_len = T, and landmarks [B,Hkv,floor(T/S),D]
+ * (the prefix's and the new tokens' complete chunks); the queries are the
+ * last T - q_offset positions only, q [B,Hq,T-q_offset,D], and out, sel_idx
+ * and sel_score cover those rows ([B,Hq,T-q_offset,...]).  Query row r sits
+ * at position q_offset + r and uses the complete chunks before its own, as
+ * in hsa_forward_prefill; its results equal that call's row q_offset + r.
+ * q_offset must be a multiple of S (the prefix is whole chunks).  The
+ * workspace of hsa_forward_prefill for the same dims is sufficient.
+ */
+hsa_attn_status_t hsa_forward_prefill_cached(const hsa_attn_dims_t* d, int64_t q_offset, const void* q,
+                                             const void* k, const void* v, const void* landmarks, float* out,
+                                             int32_t* sel_idx, float* sel_score, void* workspace,
+                                             size_t workspace_bytes, void* stream);
+
+/*
  * HSA forward for B independent single-token queries, each after its own
  * cache of T tokens (card, "Core Technique": scoring is O(n/S) per query and
  * attention O(k*S)).  The query sits at position T, so its candidates are

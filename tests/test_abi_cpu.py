@@ -135,3 +135,16 @@ def test_varlen_and_append_validation():
     assert lib.hsa_append_kv(ctypes.byref(d), p, p, p, p, p, ctypes.c_void_p(0x1004),
                              None) == hsa.HSA_ATTN_INVALID_ARGUMENT
     assert lib.hsa_append_kv(ctypes.byref(dims(head_dim=96)), p, p, p, p, p, p, None) == hsa.HSA_ATTN_UNSUPPORTED
+
+
+def test_prefill_cached_offset_validation():
+    lib = hsa.load_library()
+    p = ctypes.c_void_p(0x1000)
+    d = dims(seq_len=64 * 100)
+    for off in (-64, 65, 64 * 101):
+        assert lib.hsa_forward_prefill_cached(ctypes.byref(d), off, p, p, p, p, p, None, None, p, 1 << 40,
+                                              None) == hsa.HSA_ATTN_INVALID_ARGUMENT
+    assert "q_offset" in hsa.hsa_attn_last_error()
+    # the whole sequence as prefix: nothing to compute
+    assert lib.hsa_forward_prefill_cached(ctypes.byref(d), 64 * 100, p, p, p, p, p, None, None, p, 1 << 40,
+                                          None) == hsa.HSA_ATTN_OK
