@@ -379,37 +379,46 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
     w = WORKLOADS[wname]
     esz = 2 if w.dtype == "bf16" else 4
     Nc = w.T // w.S
+    off = int(w.extra.get("q_offset", 0))  # cached prefix (chunked prefill)
+    Tq = w.T - off
     t0 = time.perf_counter()
     q, k, v = prefill_inputs(w, "cuda")
+    if off:
+        q = q[:, :, off:].contiguous()
     torch.cuda.synchronize()
     log(f"[{wname}] generated inputs in {time.perf_counter() - t0:.1f} s")
     L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
-    out = torch.empty((w.B, w.Hq, w.T, w.D), dtype=torch.float32, device="cuda")
-    sel = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.int32, device="cuda")
-    sc = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.float32, device="cuda")
+    if off:  # the prefix's landmarks exist already
+        hsa.hsa_build_landmarks(k, L, w.S, 0, off // w.S)
+    out = torch.empty((w.B, w.Hq, Tq, w.D), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, Tq, w.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, Tq, w.k), dtype=torch.float32, device="cuda")
     events = HipEvents()
 
     def step(ev):
         if ev is not None:
             hsa.hsa_attn_set_timing_events(ev[:2])
-        hsa.hsa_build_landmarks(k, L, w.S)
+        hsa.hsa_build_landmarks(k, L, w.S, off // w.S, Nc)  # the new tokens' chunks
         if ev is not None:
             hsa.hsa_attn_set_timing_events(ev[2:])
-        hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
+        if off:
+            hsa.hsa_forward_prefill_cached(q, k, v, L, off, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
+        else:
+            hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
 
     names = ["landmarks", "prefill_zero", "prefill_select", "prefill_vt", "prefill_scan", "prefill_scatter",
              "prefill_remote", "prefill_local"]
     secs, per = timed_steps(step, steps, warmup, len(names), events)
     ms_step = 1e3 * secs / steps
     # exact algorithmic work
-    p = np.arange(w.T)
+    p = np.arange(off, w.T)
     n_p = np.minimum(p // w.S, Nc)
     m_p = np.minimum(n_p, w.k)
     score_flops = 2.0 * w.B * w.Hq * w.D * n_p.sum()
     attn_flops = 4.0 * w.S * w.D * w.B * w.Hq * m_p.sum()
     # split of the selected pairs into remote (chunk before the query's
     # 64-chunk window) and local ones, counted from this run's selection
-    win0 = torch.div(torch.arange(w.T, device="cuda") // w.S, 64, rounding_mode="floor") * 64
+    win0 = torch.div(torch.arange(off, w.T, device="cuda") // w.S, 64, rounding_mode="floor") * 64
     n_remote = int(((sel >= 0) & (sel < win0[None, None, :, None])).sum().item())
     n_pairs = int(m_p.sum()) * w.B * w.Hq
     remote_flops = 4.0 * w.S * w.D * n_remote
@@ -424,16 +433,16 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
     dom_name, dom_flops = kern[dom]
     dom_tf = dom_flops / (per[dom] / 1e3) / 1e12
     res = {
-        "workload": wname, "value": w.B * w.T / (ms_step / 1e3), "unit": "tokens/s", "ms_per_step": ms_step,
+        "workload": wname, "value": w.B * Tq / (ms_step / 1e3), "unit": "tokens/s", "ms_per_step": ms_step,
         "kernel_ms": {n: float(x) for n, x in zip(names, per)},
         "scoring_tflops": sel_tf, "scoring_mfma_frac": sel_tf / peak,
         "attention_ms": attn_ms, "attention_tflops": att_tf, "attention_mfma_frac": att_tf / peak,
         "remote_pair_frac": n_remote / max(n_pairs, 1),
         "remote_tflops": remote_flops / (per[6] / 1e3) / 1e12,
         "local_tflops": local_flops / (per[7] / 1e3) / 1e12,
-        "landmark_GBps": (w.B * w.Hkv * Nc * w.S * w.D * esz) / (per[0] / 1e3) / 1e9,
-        "config": {"workload": wname, "batch": w.B, "seq_len": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv,
-                   "head_dim": w.D, "chunk": w.S, "top_k": w.k, "lowrank": w.lowrank},
+        "landmark_GBps": (w.B * w.Hkv * (Nc - off // w.S) * w.S * w.D * esz) / (per[0] / 1e3) / 1e9,
+        "config": {"workload": wname, "batch": w.B, "seq_len": w.T, "query_tokens": Tq, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.D, "chunk": w.S, "top_k": w.k, "lowrank": w.lowrank},
         "dtype": w.dtype,
         "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": dom_tf, "peak": peak, "unit": "TFLOP/s",
                      "frac": dom_tf / peak, "traffic": profiled_traffic(wname, dom_name),
@@ -453,7 +462,10 @@ def prefill_cpu_baseline(w, q, k, v, chunks=tuple(range(250, 4001, 250))):
     (64 tokens each).  Host copies and landmark building are untimed."""
     from oracle import hsa_oracle as O
     G = w.Hq // w.Hkv
-    chunks = [c for c in chunks if c * w.S < w.T] or [w.T // w.S - 1]
+    off = int(w.extra.get("q_offset", 0))  # q holds the rows from off on
+    if off:  # 16 chunks spread over the new tokens
+        chunks = sorted({int(c) for c in np.linspace(off // w.S, w.T // w.S - 1, 16)})
+    chunks = [c for c in chunks if off <= c * w.S < w.T] or [w.T // w.S - 1]
     total = 0.0
     for g in range(w.Hkv):
         Kg = k[0, g].float().cpu().double().numpy()
@@ -461,7 +473,7 @@ def prefill_cpu_baseline(w, q, k, v, chunks=tuple(range(250, 4001, 250))):
         Lg = O.landmarks(Kg, w.S, w.dtype)
         for c in chunks:
             pos = np.arange(c * w.S, min(w.T, (c + 1) * w.S))
-            qq = q[0, g * G:(g + 1) * G, c * w.S:(c + 1) * w.S].float().cpu().double().numpy()
+            qq = q[0, g * G:(g + 1) * G, c * w.S - off:(c + 1) * w.S - off].float().cpu().double().numpy()
             t0 = time.perf_counter()
             for hh in range(G):
                 O.hsa_rows(qq[hh], pos, Kg, Vg, Lg, w.S, w.k)

@@ -16,6 +16,8 @@ Workloads (all with chunk size 64):
   decode_16m_bf16    B=4 queries, 2^24-token caches, k=64, 16 needles per cache
   decode_1m_varlen_bf16  as decode_1m_bf16 in caches of capacity 2^20 that
                      hold seeded lengths in [2^19, 2^20) (cache_lengths)
+  prefill_256k_chunk_bf16  the last 65536 tokens of prefill_256k_bf16 over
+                     its cached first 196608 tokens
 
 Needles: per cache, distinct chunk indices drawn uniformly; every key of a
 needle chunk gets 3 * u added (before rounding), u = the normalised sum of
@@ -68,6 +70,10 @@ WORKLOADS = {
         # one token
         Workload("decode_1m_varlen_bf16", "decode", 64, 32, 8, 1 << 20, 128, 64, 32, "bf16", 6000, needles=8,
                  extra={"min_len": 1 << 19}),
+        # chunked prefill: the last 64K tokens of the 256K sequence after a
+        # cached prefix of 192K tokens (same inputs as prefill_256k_bf16)
+        Workload("prefill_256k_chunk_bf16", "prefill", 1, 32, 8, 262144, 128, 64, 16, "bf16", 4000, lowrank=8,
+                 extra={"q_offset": 196608}),
     ]
 }
 

@@ -59,19 +59,29 @@ def check_landmarks(L_gpu, L_ref, dtype):
 
 def run_prefill_workload(name, chunks, heads=None):
     w = WORKLOADS[name]
+    off = int(w.extra.get("q_offset", 0))  # chunked prefill after a cached prefix
     print(f"workload {name}: sampled query chunks {chunks}", flush=True)
     q, k, v = prefill_inputs(w, "cuda")
     Nc = w.T // w.S
+    Tq = w.T - off
     L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
-    out = torch.empty((w.B, w.Hq, w.T, w.D), dtype=torch.float32, device="cuda")
-    sel = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.int32, device="cuda")
-    sc = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.float32, device="cuda")
-    hsa.hsa_build_landmarks(k, L, w.S)
-    hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
+    out = torch.empty((w.B, w.Hq, Tq, w.D), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, Tq, w.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, Tq, w.k), dtype=torch.float32, device="cuda")
+    if off:  # prefix landmarks first, then the new tokens' chunks, as the benchmark does
+        hsa.hsa_build_landmarks(k, L, w.S, 0, off // w.S)
+        hsa.hsa_build_landmarks(k, L, w.S, off // w.S, Nc)
+        hsa.hsa_forward_prefill_cached(q[:, :, off:].contiguous(), k, v, L, off, w.S, w.k, out=out, sel_idx=sel,
+                                       sel_score=sc)
+    else:
+        hsa.hsa_build_landmarks(k, L, w.S)
+        hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
     torch.cuda.synchronize()
     pos = np.concatenate([np.arange(c * w.S, min(w.T, (c + 1) * w.S)) for c in chunks]) if chunks is not None \
-        else np.arange(w.T)
+        else np.arange(off, w.T)
+    assert pos.min() >= off
     pos_t = torch.as_tensor(pos, device="cuda")
+    row_t = pos_t - off  # rows of the outputs
     G = w.Hq // w.Hkv
     stats = new_stats()
     for b in range(w.B):
@@ -82,8 +92,8 @@ def run_prefill_workload(name, chunks, heads=None):
             for h in range(g * G, (g + 1) * G):
                 if heads is not None and h not in heads:
                     continue
-                check_rows(host64(q[b, h, pos_t]), pos, Kg, Vg, Lg, w.S, w.k, host64(out[b, h, pos_t]),
-                           sel[b, h, pos_t].cpu().numpy(), host64(sc[b, h, pos_t]), TOL[w.dtype], stats)
+                check_rows(host64(q[b, h, pos_t]), pos, Kg, Vg, Lg, w.S, w.k, host64(out[b, h, row_t]),
+                           sel[b, h, row_t].cpu().numpy(), host64(sc[b, h, row_t]), TOL[w.dtype], stats)
     print(name, stats, flush=True)
     del q, k, v, L, out, sel, sc
     torch.cuda.empty_cache()
@@ -104,6 +114,36 @@ def test_prefill_256k_bf16_sampled():
     # the special chunks, chunks around window and segment edges, and chunks
     # spread over the sequence
     run_prefill_workload("prefill_256k_bf16", [0, 1, 16, 17, 63, 64, 65, 1000, 2047, 3333, 4095])
+
+
+def test_prefill_256k_chunk_bf16_sampled():
+    # the first new chunk, chunks at window edges, and the last
+    run_prefill_workload("prefill_256k_chunk_bf16", [3072, 3073, 3135, 3136, 3500, 4095])
+
+
+def test_prefill_256k_chunk_bf16_equals_full_prefill_rows():
+    """Every output row of the chunked prefill equals the full-sequence
+    prefill's row at the same position, bit for bit (same selection, same
+    per-chunk arithmetic and fusion order)."""
+    w = WORKLOADS["prefill_256k_chunk_bf16"]
+    off = w.extra["q_offset"]
+    Tq = w.T - off
+    q, k, v = prefill_inputs(w, "cuda")
+    Nc = w.T // w.S
+    L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
+    hsa.hsa_build_landmarks(k, L, w.S)
+    sel_f = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.int32, device="cuda")
+    sc_f = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.float32, device="cuda")
+    full = hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, sel_idx=sel_f, sel_score=sc_f)[:, :, off:].clone()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    sel = torch.empty((w.B, w.Hq, Tq, w.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, Tq, w.k), dtype=torch.float32, device="cuda")
+    part = hsa.hsa_forward_prefill_cached(q[:, :, off:].contiguous(), k, v, L, off, w.S, w.k, sel_idx=sel,
+                                          sel_score=sc)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel_f[:, :, off:]) and torch.equal(sc, sc_f[:, :, off:])
+    assert torch.equal(part, full)
 
 
 def run_decode_workload(name, queries):
