@@ -69,10 +69,43 @@ def hsa_query(q, p: int, K, V, S: int, k: int, dtype: str):
     n = min(p // S, Nc)
     if n == 0:
         return [0.0] * D, [], []
-    lms = [landmark(K[c * S:(c + 1) * S], dtype) for c in range(n)]
-    exact = [sum((Fraction(q[d]) * Fraction(lm[d]) for d in range(D)), Fraction(0)) for lm in lms]
+    exact = _exact_scores(q, K, S, n, dtype)
     order = sorted(range(n), key=lambda c: (-exact[c], c))
     sel = order[:min(k, n)]
+    return _attend_and_fuse(q, sel, exact, K, V, S)
+
+
+def hsa_query_adaptive(q, p: int, K, V, S: int, k: int, tau: float, dtype: str):
+    """As hsa_query, with the near-tie adaptive budget of the value-of-
+    information router abstract (automata-index page): when the query has
+    more than k candidates and its k-th best score exceeds its (k+1)-th by
+    less than tau (scores scaled by 1/sqrt(D)), it keeps its best 2k chunks
+    (or all, if fewer) instead of k.  The gap is taken from the exact dot
+    products.  Returns (out, sel, scores, doubled)."""
+    D = len(q)
+    n = min(p // S, len(K) // S)
+    if n == 0:
+        return [0.0] * D, [], [], False
+    exact = _exact_scores(q, K, S, n, dtype)
+    order = sorted(range(n), key=lambda c: (-exact[c], c))
+    m = min(k, n)
+    if n > k and float(exact[order[k - 1]] - exact[order[k]]) / math.sqrt(D) < tau:
+        m = min(2 * k, n)
+    out, sel, scores = _attend_and_fuse(q, order[:m], exact, K, V, S)
+    return out, sel, scores, m > k
+
+
+def _exact_scores(q, K, S: int, n: int, dtype: str):
+    """Exact (unscaled) q . landmark for the first n chunks."""
+    D = len(q)
+    lms = [landmark(K[c * S:(c + 1) * S], dtype) for c in range(n)]
+    return [sum((Fraction(q[d]) * Fraction(lm[d]) for d in range(D)), Fraction(0)) for lm in lms]
+
+
+def _attend_and_fuse(q, sel, exact, K, V, S: int):
+    """Softmax attention inside every chunk of sel, fused by a softmax over
+    the kept scaled scores."""
+    D = len(q)
     scale = 1.0 / math.sqrt(D)
     scores = [float(exact[c]) * scale for c in sel]
     outs = []

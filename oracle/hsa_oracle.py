@@ -30,6 +30,9 @@ Readings of points the pages leave open (each is listed in the design doc):
 * the in-chunk softmax and the fusion softmax both use the 1/sqrt(D) scale;
   each chunk output is normalised on its own.
 * the output is float (fp64 here; fp32 on the GPU) even for bf16 inputs.
+* near-tie adaptive budget (value-of-information router abstract): a row
+  whose k-th best score beats its (k+1)-th by less than a threshold tau keeps
+  its best 2k chunks instead of k (adaptive_keep_count).
 
 Every input array handed to this module holds the exact values of the stored
 tensors as float64 (bf16 and fp32 upcast exactly).  Parity unpinned: nothing.
@@ -47,7 +50,8 @@ __all__ = [
     "bf16_bits_to_f64", "f32_to_bf16_bits", "round_to_bf16", "round_to_f32",
     "round_to_dtype", "landmarks", "num_candidates", "scores_for_rows",
     "select_topk", "chunk_attention", "fuse", "hsa_rows", "prefill", "decode",
-    "near_tie_info", "check_selection", "HSARowsResult",
+    "near_tie_info", "check_selection", "HSARowsResult", "adaptive_keep_count",
+    "hsa_rows_adaptive",
 ]
 
 
@@ -295,6 +299,73 @@ def decode(q, Kc, Vc, L, S: int, k: int):
             r = hsa_rows(q[b, h][None], np.array([T]), Kc[b, g], Vc[b, g], L[b, g], S, k)
             out[b, h], sel_idx[b, h], sel_score[b, h] = r.out[0], r.sel_idx[0], r.sel_score[0]
     return out, sel_idx, sel_score
+
+
+# ---------------------------------------------------------------------------
+# near-tie adaptive budget
+# ---------------------------------------------------------------------------
+
+def adaptive_keep_count(s_sorted: np.ndarray, k: int, tau: float):
+    """Kept count of one row under the near-tie adaptive budget, and its gap.
+
+    Value-of-information router abstract (automata-index page): the selector
+    measures how decisively its top-k cut was made -- the gap between the
+    k-th and (k+1)-th best block scores -- and doubles the kept set of the
+    queries whose gap is smallest.  Read here as a per-row threshold tau on
+    that gap (in score units, the 1/sqrt(D) scale included): s_sorted holds a
+    row's candidate scores in selection order (score descending, index
+    ascending), n = len(s_sorted).  With n > k the row keeps min(2k, n)
+    chunks when s_sorted[k-1] - s_sorted[k] < tau and k otherwise; with
+    n <= k no cut is made and all n are kept.  Strict comparison: tau = 0
+    never doubles (a gap is never negative), tau = +inf always does.
+    Returns (m, gap); gap is nan when n <= k.
+    """
+    n = len(s_sorted)
+    if n <= k:
+        return n, float("nan")
+    gap = float(s_sorted[k - 1] - s_sorted[k])
+    return (min(2 * k, n) if gap < tau else k), gap
+
+
+def hsa_rows_adaptive(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.ndarray,
+                      Lg: np.ndarray, S: int, k: int, tau: float):
+    """HSA with the near-tie adaptive budget (adaptive_keep_count) for query
+    rows q[r] at positions pos[r] against one KV head.
+
+    Each row ranks its candidates as in select_topk, keeps its first m chunks
+    (m from the gap rule) and then attends and fuses exactly as hsa_rows
+    does over those m chunks.  Returns (result, doubled, gap): result is an
+    HSARowsResult whose selection arrays have 2k columns (-1 / -inf
+    padding), doubled[r] says whether row r kept more than k chunks, gap[r]
+    is its k-th minus (k+1)-th score (nan when it has at most k candidates).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    R = q.shape[0]
+    Nc = Kg.shape[0] // S
+    n_all = num_candidates(pos, S, Nc)
+    keep = []
+    doubled = np.zeros(R, dtype=bool)
+    gap = np.full(R, np.nan)
+    for r in range(R):
+        n = int(n_all[r])
+        if n == 0:
+            keep.append(np.zeros(0, dtype=np.int64))
+            continue
+        s = scores_for_rows(q[r:r + 1], Lg, n)
+        order = select_topk(s, 2 * k)[0]
+        m, gap[r] = adaptive_keep_count(s[0, order], k, tau)
+        doubled[r] = m > k
+        keep.append(order[:m])
+    out = np.zeros_like(q)
+    sel_idx = np.full((R, 2 * k), -1, dtype=np.int64)
+    sel_score = np.full((R, 2 * k), -np.inf)
+    # rows keeping the same number of chunks go through hsa_rows together
+    for m in sorted({len(c) for c in keep}):
+        rows = np.array([r for r in range(R) if len(keep[r]) == m])
+        res = hsa_rows(q[rows], pos[rows], Kg, Vg, Lg, S, 2 * k, sel_override=[keep[r] for r in rows])
+        out[rows], sel_idx[rows], sel_score[rows] = res.out, res.sel_idx, res.sel_score
+    return HSARowsResult(out, sel_idx, sel_score, n_all), doubled, gap
 
 
 # ---------------------------------------------------------------------------
