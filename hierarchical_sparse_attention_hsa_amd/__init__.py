@@ -25,14 +25,15 @@ import os
 __all__ = [
     "library_path", "load_library", "Dims", "HSAError", "EXPORTED_SYMBOLS",
     "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
-    "hsa_forward_decode_varlen", "hsa_append_kv", "hsa_attn_set_timing_events", "hsa_attn_workspace_size",
+    "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_append_kv", "hsa_attn_set_timing_events",
+    "hsa_attn_workspace_size",
     "hsa_attn_status_string", "hsa_attn_last_error", "landmarks_shape",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 EXPORTED_SYMBOLS = (
     "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
-    "hsa_forward_decode_varlen",
+    "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive",
     "hsa_append_kv", "hsa_attn_set_timing_events", "hsa_attn_workspace_size", "hsa_attn_status_string",
     "hsa_attn_last_error",
 )
@@ -86,6 +87,7 @@ def load_library():
     lib.hsa_forward_decode.argtypes = [dims, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_decode_varlen.argtypes = [dims, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_prefill_cached.argtypes = [dims, I64, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_forward_decode_adaptive.argtypes = [dims, ctypes.c_float, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_append_kv.argtypes = [dims, P, P, P, P, P, P, P]
     lib.hsa_attn_workspace_size.argtypes = [dims, ctypes.c_int, ctypes.POINTER(SZ)]
     lib.hsa_attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
@@ -94,7 +96,7 @@ def load_library():
     lib.hsa_attn_last_error.argtypes = []
     lib.hsa_attn_last_error.restype = ctypes.c_char_p
     for f in ("hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
-              "hsa_forward_decode_varlen",
+              "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive",
               "hsa_append_kv", "hsa_attn_workspace_size", "hsa_attn_set_timing_events"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
@@ -173,9 +175,10 @@ def hsa_attn_set_timing_events(events) -> None:
 _EVENT_ARRAY = None
 
 
-def hsa_attn_workspace_size(dims: Dims, is_decode: bool) -> int:
+def hsa_attn_workspace_size(dims: Dims, is_decode) -> int:
+    """Workspace bytes; is_decode: False/0 prefill, True/1 decode, 2 adaptive-budget decode."""
     n = ctypes.c_size_t(0)
-    _check(load_library().hsa_attn_workspace_size(ctypes.byref(dims), int(bool(is_decode)), ctypes.byref(n)),
+    _check(load_library().hsa_attn_workspace_size(ctypes.byref(dims), int(is_decode), ctypes.byref(n)),
            "hsa_attn_workspace_size")
     return n.value
 
@@ -247,6 +250,40 @@ def hsa_forward_decode_varlen(q, k_cache, v_cache, landmarks, cache_lens, chunk_
     holding cache_lens[b] tokens each (int64 [B] on the device) -> out [B,Hq,D] fp32."""
     return _forward(True, q, k_cache, v_cache, landmarks, chunk_size, top_k, out, sel_idx, sel_score, workspace,
                     lens=cache_lens)
+
+
+def hsa_forward_decode_adaptive(q, k_cache, v_cache, landmarks, chunk_size: int, top_k: int, gap_threshold: float,
+                                cache_lens=None, out=None, sel_idx=None, sel_score=None, workspace=None):
+    """Decode with the near-tie adaptive budget: a query head keeps its best
+    2*top_k chunks when its top_k-th and (top_k+1)-th scores differ by less
+    than gap_threshold, else top_k.  q [B,Hq,D], caches [B,Hkv,T,D] (cache_lens
+    optional, int64 [B] device) -> out [B,Hq,D] fp32; sel_idx/sel_score
+    [B,Hq,2*top_k]."""
+    torch = _torch()
+    B, Hkv, T, D = k_cache.shape
+    Hq = q.shape[1]
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype or q.dtype != k_cache.dtype:
+        raise ValueError("q, k and v must share dtype; v must match k's shape")
+    if tuple(q.shape) != (B, Hq, D):
+        raise ValueError(f"q must be {(B, Hq, D)}, got {tuple(q.shape)}")
+    if tuple(landmarks.shape) != landmarks_shape(k_cache.shape, chunk_size) or landmarks.dtype != k_cache.dtype:
+        raise ValueError("landmarks must be [B, Hkv, T // chunk_size, D] with the dtype of k")
+    if cache_lens is not None and (cache_lens.dtype != torch.int64 or tuple(cache_lens.shape) != (B,)):
+        raise ValueError("cache_lens must be an int64 tensor of shape [B]")
+    dims = make_dims(B, Hq, Hkv, D, chunk_size, top_k, T, _dtype_code(k_cache))
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if (sel_idx is None) != (sel_score is None):
+        raise ValueError("give both sel_idx and sel_score or neither")
+    if workspace is None:
+        need = hsa_attn_workspace_size(dims, 2)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = load_library().hsa_forward_decode_adaptive(
+        ctypes.byref(dims), float(gap_threshold), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(landmarks),
+        _ptr(cache_lens), _ptr(out), _ptr(sel_idx), _ptr(sel_score), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(st, "hsa_forward_decode_adaptive")
+    return out
 
 
 def hsa_append_kv(k_new, v_new, k_cache, v_cache, landmarks, cache_lens, chunk_size: int):

@@ -32,10 +32,11 @@ hsa_attn_status_t ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-enum class Call { kLandmarks, kPrefill, kDecode };
+enum class Call { kLandmarks, kPrefill, kDecode, kDecodeAdaptive };
 
 // Validates the dimension block and fills a Geometry.
 hsa_attn_status_t check_dims(const hsa_attn_dims_t* d, Call call, hsa_attn::Geometry* g) {
+  const bool adaptive = call == Call::kDecodeAdaptive;
   if (!d) return fail(HSA_ATTN_INVALID_ARGUMENT, "dims is NULL");
   if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1)
     return fail(HSA_ATTN_INVALID_ARGUMENT, "batch and head counts must be >= 1");
@@ -55,9 +56,12 @@ hsa_attn_status_t check_dims(const hsa_attn_dims_t* d, Call call, hsa_attn::Geom
     if (G != 1 && G != 2 && G != 4 && G != 8)
       return fail(HSA_ATTN_UNSUPPORTED, "query heads per KV head %d unsupported (1, 2, 4, 8)", G);
     if (d->chunk_size != 64) return fail(HSA_ATTN_UNSUPPORTED, "chunk_size %d unsupported (64)", d->chunk_size);
+    // decode keeps one list entry per lane of a wave; the adaptive budget
+    // may double k
     const int kmax = call == Call::kDecode ? 64 : 32;
     if (d->top_k > kmax) return fail(HSA_ATTN_UNSUPPORTED, "top_k %d unsupported (<= %d)", d->top_k, kmax);
   }
+  if (call == Call::kDecodeAdaptive) call = Call::kDecode;
   const int64_t Nc = d->seq_len / d->chunk_size;
   if (call == Call::kPrefill) {
     if (Nc > 65536) return fail(HSA_ATTN_UNSUPPORTED, "prefill supports at most 65536 chunks");
@@ -76,6 +80,7 @@ hsa_attn_status_t check_dims(const hsa_attn_dims_t* d, Call call, hsa_attn::Geom
   g->S = d->chunk_size;
   g->k = d->top_k;
   g->T = d->seq_len;
+  if (adaptive) g->k = 2 * d->top_k;  // the list holds the doubled budget
   g->Nc = Nc;
   g->bf16 = d->dtype == HSA_ATTN_BF16;
   g->Tq = d->seq_len;  // every position is a query row unless a caller narrows it
@@ -125,8 +130,10 @@ const char* hsa_attn_last_error(void) { return g_last_error; }
 hsa_attn_status_t hsa_attn_workspace_size(const hsa_attn_dims_t* d, int is_decode, size_t* bytes) {
   try {
     if (!bytes) return fail(HSA_ATTN_INVALID_ARGUMENT, "bytes is NULL");
+    if (is_decode < 0 || is_decode > 2) return fail(HSA_ATTN_INVALID_ARGUMENT, "kind must be 0, 1 or 2");
     hsa_attn::Geometry g;
-    const hsa_attn_status_t st = check_dims(d, is_decode ? Call::kDecode : Call::kPrefill, &g);
+    const Call call = is_decode == 2 ? Call::kDecodeAdaptive : is_decode ? Call::kDecode : Call::kPrefill;
+    const hsa_attn_status_t st = check_dims(d, call, &g);
     if (st != HSA_ATTN_OK) return st;
     // the size assumes the library keeps the selection itself (sel outputs NULL)
     *bytes = is_decode ? hsa_attn::plan_decode(g, true).bytes : hsa_attn::plan_prefill(g, true).bytes;
@@ -217,13 +224,15 @@ hsa_attn_status_t hsa_forward_prefill_cached(const hsa_attn_dims_t* d, int64_t q
                          stream);
 }
 
+// gap_tau < 0: plain top-k; otherwise the adaptive budget with threshold gap_tau
 static hsa_attn_status_t forward_decode(const hsa_attn_dims_t* d, const void* q, const void* k_cache,
                                         const void* v_cache, const void* landmarks, const int64_t* lens, float* out,
                                         int32_t* sel_idx, float* sel_score, void* workspace, size_t workspace_bytes,
-                                        void* stream) {
+                                        void* stream, float gap_tau = -1.0f) {
   try {
     hsa_attn::Geometry g;
-    hsa_attn_status_t st = check_dims(d, Call::kDecode, &g);
+    const bool adaptive = gap_tau >= 0.0f;
+    hsa_attn_status_t st = check_dims(d, adaptive ? Call::kDecodeAdaptive : Call::kDecode, &g);
     if (st != HSA_ATTN_OK) return st;
     if (!q || !out || (g.Nc > 0 && (!k_cache || !v_cache || !landmarks)))
       return fail(HSA_ATTN_INVALID_ARGUMENT, "q, k_cache, v_cache, landmarks and out must be non-NULL");
@@ -245,6 +254,10 @@ static hsa_attn_status_t forward_decode(const hsa_attn_dims_t* d, const void* q,
     }
     restart_timing();
     hsa_attn::DecodeArgs a{g, q, k_cache, v_cache, landmarks, out, sel_idx, sel_score, workspace, lens};
+    if (adaptive) {
+      a.k_base = d->top_k;
+      a.gap_tau = gap_tau;
+    }
     return hip_status(hsa_attn::launch_decode(a, plan, static_cast<hipStream_t>(stream)), "decode launch");
   } catch (const std::exception& e) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
@@ -267,6 +280,17 @@ hsa_attn_status_t hsa_forward_decode_varlen(const hsa_attn_dims_t* d, const void
   if (!cache_lens) return fail(HSA_ATTN_INVALID_ARGUMENT, "cache_lens is NULL");
   return forward_decode(d, q, k_cache, v_cache, landmarks, cache_lens, out, sel_idx, sel_score, workspace,
                         workspace_bytes, stream);
+}
+
+hsa_attn_status_t hsa_forward_decode_adaptive(const hsa_attn_dims_t* d, float gap_threshold, const void* q,
+                                              const void* k_cache, const void* v_cache, const void* landmarks,
+                                              const int64_t* cache_lens, float* out, int32_t* sel_idx,
+                                              float* sel_score, void* workspace, size_t workspace_bytes,
+                                              void* stream) {
+  if (!(gap_threshold >= 0.0f))
+    return fail(HSA_ATTN_INVALID_ARGUMENT, "gap_threshold must be >= 0 (or +inf), got %g", (double)gap_threshold);
+  return forward_decode(d, q, k_cache, v_cache, landmarks, cache_lens, out, sel_idx, sel_score, workspace,
+                        workspace_bytes, stream, gap_threshold);
 }
 
 hsa_attn_status_t hsa_append_kv(const hsa_attn_dims_t* d, const void* k_new, const void* v_new, void* k_cache,

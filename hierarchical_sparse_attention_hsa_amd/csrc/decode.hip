@@ -321,12 +321,18 @@ __global__ __launch_bounds__(kScanThreads) void decode_scan_kernel(const typenam
 // each with the slot it holds in every head's selection (0xff = not
 // selected).  The list order is deterministic (first occurrence in head-major
 // slot order).
+// Adaptive budget (k_base > 0, k = 2 * k_base; value-of-information router
+// abstract, k-th versus (k+1)-th gap): a head whose k_base-th best score
+// beats its (k_base+1)-th by less than gap_tau keeps all k entries, any
+// other head only its first k_base (the rest become padding before the
+// group's chunk list is built).
 template <int G>
 __global__ __launch_bounds__(kWave* G) void decode_merge_kernel(const float2* __restrict__ cand,
                                                                 int32_t* __restrict__ sel_idx,
                                                                 float* __restrict__ sel_score,
                                                                 int4* __restrict__ ulist, int* __restrict__ ucount,
-                                                                int Hkv, int splits, int k) {
+                                                                int Hkv, int splits, int k, int k_base,
+                                                                float gap_tau) {
   constexpr int kMaxVals = 1024;  // threshold sample held in LDS per head
   __shared__ int ls[G * 64];
   __shared__ int wave_cnt[G];
@@ -398,6 +404,17 @@ __global__ __launch_bounds__(kWave* G) void decode_merge_kernel(const float2* __
     for (int u = 0; u < kMergeBatch; ++u) {
       const int ci = __float_as_int(c[u].y);
       offer_wave(list, k, c[u].x, ci, ci != INT_MAX);
+    }
+  }
+  if (k_base > 0) {
+    const float s_k = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(list.s), k_base - 1));
+    const float s_k1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(list.s), k_base));
+    const int i_k1 = __builtin_amdgcn_readlane(list.i, k_base);
+    // an invalid (k_base+1)-th entry means at most k_base candidates: no cut
+    const bool doubled = i_k1 != INT_MAX && s_k - s_k1 < gap_tau;
+    if (!doubled && lane >= k_base) {
+      list.s = -__builtin_inff();
+      list.i = INT_MAX;
     }
   }
   const bool ok = list.i != INT_MAX;
@@ -665,7 +682,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipS
   }
   mark_launch(st);
   hipLaunchKernelGGL((decode_merge_kernel<G>), dim3(g.Hkv, g.B), dim3(kWave * G), 0, st, cand, a.sel_idx,
-                     a.sel_score, ulist, ucount, g.Hkv, p.splits, g.k);
+                     a.sel_score, ulist, ucount, g.Hkv, p.splits, g.k, a.k_base, a.gap_tau);
   mark_launch(st);
   if (p.splits > 0) {
     mark_launch(st);

@@ -62,6 +62,11 @@ struct DecodeArgs {
   float* sel_score;
   void* ws;
   const int64_t* lens;  // per-sequence cache lengths (device), or null: all g.T
+  // adaptive budget: 0 = plain top-g.k; otherwise g.k == 2 * k_base and a
+  // head keeps g.k entries only when its k_base-th vs (k_base+1)-th score
+  // gap is below gap_tau
+  int k_base = 0;
+  float gap_tau = 0.0f;
 };
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t st);
 

@@ -158,6 +158,32 @@ hsa_attn_status_t hsa_forward_decode_varlen(const hsa_attn_dims_t* d, const void
                                             size_t workspace_bytes, void* stream);
 
 /*
+ * Decode with the near-tie adaptive budget (value-of-information router
+ * abstract on the automata-index page: the gap between a query's k-th and
+ * (k+1)-th best block scores measures how decisively its top-k cut was made,
+ * and the queries with the smallest gaps get twice the budget).  Each query
+ * head ranks its candidates as hsa_forward_decode does (k = d->top_k) and
+ * computes gap = s_k - s_(k+1) from its fp32 scores (1/sqrt(D) included);
+ * when it has more than k candidates and gap < gap_threshold it keeps its
+ * best min(2k, n) chunks, otherwise its best k (all n if n <= k).
+ * Attention and fusion then run over the kept chunks exactly as in
+ * hsa_forward_decode, so gap_threshold = 0 reproduces hsa_forward_decode
+ * with top_k = k and gap_threshold = +inf reproduces it with top_k = 2k,
+ * bit for bit.  gap_threshold must be >= 0 (+inf allowed; NaN or negative:
+ * HSA_ATTN_INVALID_ARGUMENT).  Requires k <= 32.
+ * cache_lens: NULL (every cache holds d->seq_len tokens) or as in
+ * hsa_forward_decode_varlen.  sel_idx/sel_score [B,Hq,2k] (optional): the
+ * kept chunks in selection order, -1 / -inf padding (a head that did not
+ * double has padding from slot k on).
+ * workspace: at least hsa_attn_workspace_size(d, 2) bytes.
+ */
+hsa_attn_status_t hsa_forward_decode_adaptive(const hsa_attn_dims_t* d, float gap_threshold, const void* q,
+                                              const void* k_cache, const void* v_cache, const void* landmarks,
+                                              const int64_t* cache_lens, float* out, int32_t* sel_idx,
+                                              float* sel_score, void* workspace, size_t workspace_bytes,
+                                              void* stream);
+
+/*
  * Append one token per sequence to the caches (card, "Implementation":
  * chunks and their mean-pooled landmarks): k_new/v_new [B,Hkv,D] are written
  * at position cache_lens[b] of k_cache/v_cache [B,Hkv,T_cap,D]
@@ -178,14 +204,15 @@ hsa_attn_status_t hsa_append_kv(const hsa_attn_dims_t* d, const void* k_new, con
  * Launch order: landmarks: 1 kernel; prefill (when T >= S): zero, select,
  * V transpose, scan, scatter, remote attention, local attention (for T < S:
  * select, local attention); decode and varlen decode: scan, merge,
- * attention, fusion (scan and attention are skipped when the cache capacity
+ * attention, fusion, for adaptive decode too (scan and attention are skipped when the cache capacity
  * holds no complete chunk); append: 1 kernel.  events == NULL or
  * n_pairs == 0 turns recording off.  The setting is thread-local; the events stay owned by the
  * caller and must outlive the calls that record them.
  */
 hsa_attn_status_t hsa_attn_set_timing_events(void** events, int n_pairs);
 
-/* Bytes of device workspace a forward call needs (is_decode: 0 prefill, 1 decode). */
+/* Bytes of device workspace a forward call needs (is_decode: 0 prefill and
+ * cached prefill, 1 decode and varlen decode, 2 adaptive-budget decode). */
 hsa_attn_status_t hsa_attn_workspace_size(const hsa_attn_dims_t* d, int is_decode, size_t* bytes);
 
 /* Static description of a status code. */

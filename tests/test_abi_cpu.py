@@ -148,3 +148,23 @@ def test_prefill_cached_offset_validation():
     # the whole sequence as prefix: nothing to compute
     assert lib.hsa_forward_prefill_cached(ctypes.byref(d), 64 * 100, p, p, p, p, p, None, None, p, 1 << 40,
                                           None) == hsa.HSA_ATTN_OK
+
+
+def test_adaptive_decode_validation():
+    lib = hsa.load_library()
+    p = ctypes.c_void_p(0x1000)
+
+    def call(d, tau, lens=None, ws=1 << 30):
+        return lib.hsa_forward_decode_adaptive(ctypes.byref(d), tau, p, p, p, p, lens, p, None, None, p, ws, None)
+
+    for bad in (float("nan"), -1e-6, float("-inf")):
+        assert call(dims(), bad) == hsa.HSA_ATTN_INVALID_ARGUMENT
+    assert call(dims(top_k=33), 0.1) == hsa.HSA_ATTN_UNSUPPORTED  # 2k must fit 64 list slots
+    assert call(dims(), 0.1, lens=ctypes.c_void_p(0x1004)) == hsa.HSA_ATTN_INVALID_ARGUMENT  # misaligned
+    assert call(dims(), 0.1, ws=16) == hsa.HSA_ATTN_WORKSPACE_TOO_SMALL
+    # the adaptive workspace is the plain decode workspace of the doubled budget
+    d = dims(top_k=16, seq_len=1 << 20)
+    assert hsa.hsa_attn_workspace_size(d, 2) == hsa.hsa_attn_workspace_size(dims(top_k=32, seq_len=1 << 20), 1)
+    assert hsa.hsa_attn_workspace_size(dims(top_k=32), 2) > hsa.hsa_attn_workspace_size(dims(top_k=32), 1)
+    n = ctypes.c_size_t(0)
+    assert lib.hsa_attn_workspace_size(ctypes.byref(d), 3, ctypes.byref(n)) == hsa.HSA_ATTN_INVALID_ARGUMENT

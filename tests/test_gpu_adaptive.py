@@ -1,0 +1,132 @@
+"""GPU parity of decoding with the near-tie adaptive budget
+(hsa_forward_decode_adaptive; value-of-information router abstract: the
+k-th versus (k+1)-th score gap decides whether a query head keeps 2k chunks).
+
+Each (query, head) row is checked against the oracle's adaptive rule: its
+kept count must be the oracle's unless the oracle's fp64 gap lies within the
+fp32 score error of the threshold (then either count is valid), its kept set
+must be a valid top-m set for that count, and its output must match the
+oracle's for that set.  The limits are checked bit for bit against the plain
+decode: threshold 0 gives hsa_forward_decode with k, +inf gives it with 2k,
+and any threshold gives every row exactly one of the two."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_hsa_amd as hsa
+from hierarchical_sparse_attention_hsa_amd.workloads import small_inputs
+from oracle import hsa_oracle as O
+from tests.gpu_util import TOL, Mismatch, check_rows, f64, new_stats
+
+pytestmark = pytest.mark.gpu
+S = 64
+
+CASES = [
+    # B, Hq, Hkv, T, D, k, dtype, lengths (None: fixed length T)
+    (4, 16, 4, 64 * 3000, 128, 16, "bf16", None),
+    (3, 8, 2, 64 * 500 + 17, 64, 8, "fp32", None),
+    (2, 8, 1, 64 * 5000, 128, 32, "bf16", None),
+    (4, 8, 2, 64 * 900, 128, 16, "bf16", [64 * 900, 20, 64 * 16 + 3, 64 * 451]),
+]
+
+
+def oracle_gaps(q, Kc, Lc, lens, k):
+    """fp64 k-th minus (k+1)-th score of every (b, h) row (nan: <= k candidates)."""
+    B, Hq, D = q.shape
+    Hkv = Kc.shape[1]
+    gaps = np.full((B, Hq), np.nan)
+    for b in range(B):
+        n = int(lens[b]) // S
+        for h in range(Hq):
+            g = O.kv_head_of(h, Hq, Hkv)
+            if n > k:
+                s = O.scores_for_rows(q[b, h][None], Lc[b, g], n)[0]
+                order = O.select_topk(s[None], k + 1)[0]
+                gaps[b, h] = s[order[k - 1]] - s[order[k]]
+    return gaps
+
+
+def pick_threshold(gaps):
+    """A threshold halfway between two neighbouring observed gaps near the
+    median, so that about half of the rows with a cut double."""
+    g = np.sort(gaps[~np.isnan(gaps)])
+    i = max(1, len(g) // 2)
+    while i < len(g) - 1 and g[i] - g[i - 1] < 1e-4 * abs(g[i]):
+        i += 1
+    return float(0.5 * (g[i - 1] + g[i]))
+
+
+def run(fn_args, lens_t, k, tau, B, Hq, kk):
+    q, kd, vd, L = fn_args
+    sel = torch.full((B, Hq, kk), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((B, Hq, kk), 7.0, dtype=torch.float32, device="cuda")
+    out = hsa.hsa_forward_decode_adaptive(q, kd, vd, L, S, k, tau, cache_lens=lens_t, sel_idx=sel, sel_score=sc)
+    return out, sel, sc
+
+
+def plain(fn_args, lens_t, kk):
+    q, kd, vd, L = fn_args
+    if lens_t is None:
+        return hsa.hsa_forward_decode(q, kd, vd, L, S, kk)
+    return hsa.hsa_forward_decode_varlen(q, kd, vd, L, lens_t, S, kk)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_adaptive_decode(case):
+    B, Hq, Hkv, T, D, k, dtype, lens = case
+    print(f"adaptive case {case}", flush=True)
+    lens = [T] * B if lens is None else lens
+    q, kc, vc = small_inputs(B, Hq, Hkv, T, D, dtype, seed=1000 + T % 977 + k, decode=True)
+    Q, K, V = f64(q), f64(kc), f64(vc)
+    Lc = O.landmarks(K, S, dtype)
+    gaps = oracle_gaps(Q, K, Lc, lens, k)
+    tau = pick_threshold(gaps)
+    args = (q.cuda(), kc.cuda(), vc.cuda(), None)
+    L = torch.empty((B, Hkv, T // S, D), dtype=kc.dtype, device="cuda")
+    hsa.hsa_build_landmarks(args[1], L, S)
+    args = args[:3] + (L,)
+    lens_t = torch.tensor(lens, dtype=torch.int64, device="cuda") if case[7] is not None else None
+
+    ref_k = plain(args, lens_t, k)
+    ref_2k = plain(args, lens_t, 2 * k)
+    out0, sel0, _ = run(args, lens_t, k, 0.0, B, Hq, 2 * k)
+    outi, seli, _ = run(args, lens_t, k, math.inf, B, Hq, 2 * k)
+    out, sel, sc = run(args, lens_t, k, tau, B, Hq, 2 * k)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, ref_k) and torch.all(sel0[..., k:] == -1)
+    assert torch.equal(outi, ref_2k)
+    m_gpu = (sel >= 0).sum(-1).cpu().numpy()
+    same_k = (out == ref_k).all(-1).cpu().numpy()
+    same_2k = (out == ref_2k).all(-1).cpu().numpy()
+    assert np.all(np.where(m_gpu > k, same_2k, same_k)), "rows must equal the plain decode at their budget"
+
+    sel_h, sc_h, out_h = sel.cpu().numpy(), f64(sc), f64(out)
+    stats = new_stats()
+    stats["doubled"] = int((m_gpu > k).sum())
+    stats["ambiguous"] = 0
+    for b in range(B):
+        n = lens[b] // S
+        for h in range(Hq):
+            g = O.kv_head_of(h, Hq, Hkv)
+            m = int(m_gpu[b, h])
+            if n <= k:
+                allowed = {n}
+            else:
+                want = min(2 * k, n) if gaps[b, h] < tau else k
+                allowed = {want}
+                _, band, _ = O.near_tie_info(Q[b, h], Lc[b, g], n, k)
+                if abs(gaps[b, h] - tau) <= 2 * band:
+                    allowed = {k, min(2 * k, n)}
+                    stats["ambiguous"] += 1
+            if m not in allowed:
+                raise Mismatch(f"(b {b}, h {h}): kept {m}, expected {sorted(allowed)} (gap {gaps[b, h]}, tau {tau})")
+            if np.any(sel_h[b, h, m:] != -1):
+                raise Mismatch(f"(b {b}, h {h}): padding after slot {m}: {sel_h[b, h]}")
+            check_rows(Q[b, h][None], np.array([lens[b]]), K[b, g, :lens[b]], V[b, g, :lens[b]], Lc[b, g], S,
+                       max(m, 1), out_h[b, h][None], sel_h[b, h, :max(m, 1)][None], sc_h[b, h, :max(m, 1)][None],
+                       TOL[dtype], stats)
+    print(stats, f"tau {tau:.3e}", flush=True)
+    rows_with_cut = int((~np.isnan(gaps)).sum())
+    assert 0 < stats["doubled"] < rows_with_cut
