@@ -218,22 +218,29 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
     log(f"[{wname}] generated inputs in {time.perf_counter() - t0:.1f} s")
     L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
     hsa.hsa_build_landmarks(k, L, w.S)
+    adaptive = "gap_threshold" in w.extra  # near-tie adaptive budget
+    kk = 2 * w.k if adaptive else w.k  # selection slots per head
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device="cuda")
-    sel = torch.empty((w.B, w.Hq, w.k), dtype=torch.int32, device="cuda")
-    sc = torch.empty((w.B, w.Hq, w.k), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, kk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, kk), dtype=torch.float32, device="cuda")
     dims = hsa.make_dims(w.B, w.Hq, w.Hkv, w.D, w.S, w.k, w.T, hsa.HSA_ATTN_BF16 if esz == 2 else hsa.HSA_ATTN_FP32)
-    ws = torch.empty(hsa.hsa_attn_workspace_size(dims, True), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(hsa.hsa_attn_workspace_size(dims, 2 if adaptive else 1), dtype=torch.uint8, device="cuda")
+    tau = float(w.extra["gap_threshold"]) if adaptive else None
     torch.cuda.synchronize()
 
     def step(ev):
         if ev is not None:
             hsa.hsa_attn_set_timing_events(ev)
-        hsa.hsa_forward_decode(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc, workspace=ws)
+        if adaptive:
+            hsa.hsa_forward_decode_adaptive(q, k, v, L, w.S, w.k, tau, out=out, sel_idx=sel, sel_score=sc,
+                                            workspace=ws)
+        else:
+            hsa.hsa_forward_decode(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc, workspace=ws)
 
     secs, per = timed_steps(step, steps, warmup, 4, HipEvents())
     ms_step = 1e3 * secs / steps
     # distinct selected (b, g, chunk) tiles
-    s = sel.view(w.B, w.Hkv, G * w.k).cpu().numpy()
+    s = sel.view(w.B, w.Hkv, G * kk).cpu().numpy()
     distinct = sum(len(set(s[b, g][s[b, g] >= 0].tolist())) for b in range(w.B) for g in range(w.Hkv))
     tile_bytes = 2 * w.S * w.D * esz
     alg_bytes = lm_bytes + distinct * tile_bytes
@@ -251,6 +258,10 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
                      "traffic": profiled_traffic(wname, "decode_scan_kernel"),
                      "alg_bytes_per_launch": lm_bytes},
     }
+    if adaptive:
+        res["gap_threshold"] = tau
+        res["doubled_head_frac"] = float(((sel >= 0).sum(-1) > w.k).float().mean())
+        res["config"]["gap_threshold"] = tau
     # needle recall (semantic sanity of the synthetic retrieval task)
     from hierarchical_sparse_attention_hsa_amd.workloads import needle_chunks
     sh = sel.cpu().numpy()
@@ -265,7 +276,7 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
     log(f"[{wname}] {ms_step:.3f} ms/step, kernels {dict(zip(names, np.round(per, 4)))}, "
         f"scan {res['roofline']['achieved']:.0f} GB/s, needle recall {res['needle_recall']:.4f}")
     if cpu_baseline:
-        res["cpu_baseline"] = decode_cpu_baseline(w, q, k, v)
+        res["cpu_baseline"] = decode_cpu_baseline(w, q, k, v, tau=tau)
     del q, k, v, L, out, sel, sc, ws
     torch.cuda.empty_cache()
     return res
@@ -337,7 +348,7 @@ def bench_decode_varlen(wname, steps, warmup):
     return res
 
 
-def decode_cpu_baseline(w, q, k, v, queries=(0, 37), min_seconds=10.0):
+def decode_cpu_baseline(w, q, k, v, queries=(0, 37), min_seconds=10.0, tau=None):
     """The oracle on a bounded sample: the listed queries, all heads.  Host
     copies and the oracle's own landmark build are untimed (landmarks are
     precomputed in this workload); scoring, top-k, chunk attention and fusion
@@ -355,14 +366,17 @@ def decode_cpu_baseline(w, q, k, v, queries=(0, 37), min_seconds=10.0):
             Vg = v[b, g].float().cpu().double().numpy()
             Lg = O.landmarks(Kg, w.S, w.dtype)
             args = (qb[g * G:(g + 1) * G], np.full(G, w.T), Kg, Vg, Lg, w.S, w.k)
+            fn = O.hsa_rows
+            if tau is not None:  # near-tie adaptive budget
+                args, fn = args + (tau,), O.hsa_rows_adaptive
             if reps is None:  # size the repetition count on the first group
                 t0 = time.perf_counter()
-                O.hsa_rows(*args)
+                fn(*args)
                 one = time.perf_counter() - t0
                 reps = max(1, min(1000, int(min_seconds / (one * len(queries) * w.Hkv))))
             t0 = time.perf_counter()
             for _ in range(reps):
-                O.hsa_rows(*args)
+                fn(*args)
             total += time.perf_counter() - t0
             del Kg, Vg
     return {"value": len(queries) * reps / total, "unit": "queries/s", "cores": blas_threads(), "kind": "oracle",
@@ -541,7 +555,7 @@ def main():
     }
     if "cpu_baseline" in main_res:
         line["cpu_baseline"] = main_res["cpu_baseline"]
-    for key in ("kernel_ms", "step_alg_GBps", "needle_recall"):
+    for key in ("kernel_ms", "step_alg_GBps", "needle_recall", "gap_threshold", "doubled_head_frac"):
         if key in main_res:
             line[key] = main_res[key]
     if "prefill" in results:

@@ -16,6 +16,9 @@ Workloads (all with chunk size 64):
   decode_16m_bf16    B=4 queries, 2^24-token caches, k=64, 16 needles per cache
   decode_1m_varlen_bf16  as decode_1m_bf16 in caches of capacity 2^20 that
                      hold seeded lengths in [2^19, 2^20) (cache_lengths)
+  decode_1m_adaptive_bf16  decode_1m_bf16's inputs with the near-tie adaptive
+                     budget, base k=16 (2k=32), gap threshold 1.25e-3 (the
+                     0.25 quantile of these heads' k-th vs (k+1)-th gaps)
   prefill_256k_chunk_bf16  the last 65536 tokens of prefill_256k_bf16 over
                      its cached first 196608 tokens
 
@@ -70,6 +73,10 @@ WORKLOADS = {
         # one token
         Workload("decode_1m_varlen_bf16", "decode", 64, 32, 8, 1 << 20, 128, 64, 32, "bf16", 6000, needles=8,
                  extra={"min_len": 1 << 19}),
+        # decode_1m with the near-tie adaptive budget: base k = 16 (2k = 32);
+        # the gap threshold doubles about a quarter of the heads here
+        Workload("decode_1m_adaptive_bf16", "decode", 64, 32, 8, 1 << 20, 128, 64, 16, "bf16", 3000, needles=8,
+                 extra={"gap_threshold": 1.25e-3}),
         # chunked prefill: the last 64K tokens of the 256K sequence after a
         # cached prefix of 192K tokens (same inputs as prefill_256k_bf16)
         Workload("prefill_256k_chunk_bf16", "prefill", 1, 32, 8, 262144, 128, 64, 16, "bf16", 4000, lowrank=8,

@@ -62,3 +62,32 @@ def check_rows(q_rows, pos, Kg, Vg, Lg, S, k, gpu_out, gpu_sel, gpu_score, tol, 
 
 def new_stats():
     return {"rows": 0, "near_tie_rows": 0, "max_err": 0.0}
+
+
+def check_rows_adaptive(q_row, pos, Kg, Vg, Lg, S, k, tau, gpu_out, gpu_sel, gpu_score, tol, stats):
+    """One query row under the near-tie adaptive budget (base k, threshold
+    tau).  The kept count (valid entries of gpu_sel, 2k slots) must be the
+    oracle's unless the oracle's fp64 k-th vs (k+1)-th gap lies within the
+    fp32 score error band of tau, where either count is valid; the kept set
+    and output are then checked as a plain top-m row."""
+    n = int(O.num_candidates(np.array([pos]), S, Kg.shape[0] // S)[0])
+    m = int((gpu_sel >= 0).sum())
+    if n <= k:
+        allowed = {n}
+    else:
+        s = O.scores_for_rows(q_row[None], Lg, n)[0]
+        order = O.select_topk(s[None], 2 * k)[0]
+        want, gap = O.adaptive_keep_count(s[order], k, tau)
+        allowed = {want}
+        _, band, _ = O.near_tie_info(q_row, Lg, n, k)
+        if abs(gap - tau) <= 2 * band:
+            allowed = {k, min(2 * k, n)}
+            stats["ambiguous"] = stats.get("ambiguous", 0) + 1
+    if m not in allowed:
+        raise Mismatch(f"kept {m} chunks, expected {sorted(allowed)} (tau {tau})")
+    if np.any(gpu_sel[m:] != -1):
+        raise Mismatch(f"padding expected after slot {m}: {gpu_sel}")
+    stats["doubled"] = stats.get("doubled", 0) + int(m > k)
+    mm = max(m, 1)
+    check_rows(q_row[None], np.array([pos]), Kg, Vg, Lg, S, mm, gpu_out[None], gpu_sel[:mm][None],
+               gpu_score[:mm][None], tol, stats)

@@ -14,7 +14,7 @@ import torch
 import hierarchical_sparse_attention_hsa_amd as hsa
 from hierarchical_sparse_attention_hsa_amd.workloads import WORKLOADS, decode_inputs, prefill_inputs
 from oracle import hsa_oracle as O
-from tests.gpu_util import TOL, check_rows, new_stats
+from tests.gpu_util import TOL, check_rows, check_rows_adaptive, new_stats
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -155,13 +155,18 @@ def run_decode_workload(name, queries):
     if need + (2 << 30) > free:
         pytest.skip(f"{name} needs {need / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} GiB free")
     print(f"workload {name}: sampled queries {queries}", flush=True)
+    tau = w.extra.get("gap_threshold")  # near-tie adaptive budget
+    kk = w.k if tau is None else 2 * w.k
     q, k, v = decode_inputs(w, "cuda")
     L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
     hsa.hsa_build_landmarks(k, L, w.S)
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device="cuda")
-    sel = torch.empty((w.B, w.Hq, w.k), dtype=torch.int32, device="cuda")
-    sc = torch.empty((w.B, w.Hq, w.k), dtype=torch.float32, device="cuda")
-    hsa.hsa_forward_decode(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
+    sel = torch.empty((w.B, w.Hq, kk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, kk), dtype=torch.float32, device="cuda")
+    if tau is None:
+        hsa.hsa_forward_decode(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
+    else:
+        hsa.hsa_forward_decode_adaptive(q, k, v, L, w.S, w.k, tau, out=out, sel_idx=sel, sel_score=sc)
     torch.cuda.synchronize()
     G = w.Hq // w.Hkv
     stats = new_stats()
@@ -170,8 +175,14 @@ def run_decode_workload(name, queries):
             Lg = oracle_landmarks(k[b, g], w.S, w.dtype)
             check_landmarks(L[b, g], Lg, w.dtype)
             hs = slice(g * G, (g + 1) * G)
-            check_rows(host64(q[b, hs]), np.full(G, w.T), DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lg, w.S, w.k,
-                       host64(out[b, hs]), sel[b, hs].cpu().numpy(), host64(sc[b, hs]), TOL[w.dtype], stats)
+            if tau is None:
+                check_rows(host64(q[b, hs]), np.full(G, w.T), DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lg, w.S,
+                           w.k, host64(out[b, hs]), sel[b, hs].cpu().numpy(), host64(sc[b, hs]), TOL[w.dtype], stats)
+                continue
+            qh, oh, sh, ch = host64(q[b, hs]), host64(out[b, hs]), sel[b, hs].cpu().numpy(), host64(sc[b, hs])
+            for i in range(G):
+                check_rows_adaptive(qh[i], w.T, DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lg, w.S, w.k, tau, oh[i],
+                                    sh[i], ch[i], TOL[w.dtype], stats)
         print(name, "query", b, stats, flush=True)
     del q, k, v, L, out, sel, sc
     torch.cuda.empty_cache()
@@ -180,6 +191,11 @@ def run_decode_workload(name, queries):
 
 def test_decode_1m_bf16_sampled():
     run_decode_workload("decode_1m_bf16", [0, 41])
+
+
+def test_decode_1m_adaptive_bf16_sampled():
+    stats = run_decode_workload("decode_1m_adaptive_bf16", [0, 41])
+    assert stats.get("doubled", 0) > 0
 
 
 def test_decode_16m_bf16_sampled():
