@@ -25,15 +25,15 @@ import os
 __all__ = [
     "library_path", "load_library", "Dims", "HSAError", "EXPORTED_SYMBOLS",
     "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
-    "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_append_kv", "hsa_attn_set_timing_events",
-    "hsa_attn_workspace_size",
+    "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive", "hsa_append_kv",
+    "hsa_attn_set_timing_events", "hsa_attn_workspace_size",
     "hsa_attn_status_string", "hsa_attn_last_error", "landmarks_shape",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 EXPORTED_SYMBOLS = (
     "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
-    "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive",
+    "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive",
     "hsa_append_kv", "hsa_attn_set_timing_events", "hsa_attn_workspace_size", "hsa_attn_status_string",
     "hsa_attn_last_error",
 )
@@ -88,6 +88,7 @@ def load_library():
     lib.hsa_forward_decode_varlen.argtypes = [dims, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_prefill_cached.argtypes = [dims, I64, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_decode_adaptive.argtypes = [dims, ctypes.c_float, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_forward_prefill_adaptive.argtypes = [dims, ctypes.c_float, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_append_kv.argtypes = [dims, P, P, P, P, P, P, P]
     lib.hsa_attn_workspace_size.argtypes = [dims, ctypes.c_int, ctypes.POINTER(SZ)]
     lib.hsa_attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
@@ -96,7 +97,7 @@ def load_library():
     lib.hsa_attn_last_error.argtypes = []
     lib.hsa_attn_last_error.restype = ctypes.c_char_p
     for f in ("hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
-              "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive",
+              "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive",
               "hsa_append_kv", "hsa_attn_workspace_size", "hsa_attn_set_timing_events"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
@@ -176,7 +177,8 @@ _EVENT_ARRAY = None
 
 
 def hsa_attn_workspace_size(dims: Dims, is_decode) -> int:
-    """Workspace bytes; is_decode: False/0 prefill, True/1 decode, 2 adaptive-budget decode."""
+    """Workspace bytes; is_decode: False/0 prefill, True/1 decode, 2 adaptive-budget decode,
+    3 adaptive-budget prefill."""
     n = ctypes.c_size_t(0)
     _check(load_library().hsa_attn_workspace_size(ctypes.byref(dims), int(is_decode), ctypes.byref(n)),
            "hsa_attn_workspace_size")
@@ -283,6 +285,37 @@ def hsa_forward_decode_adaptive(q, k_cache, v_cache, landmarks, chunk_size: int,
         _ptr(cache_lens), _ptr(out), _ptr(sel_idx), _ptr(sel_score), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(st, "hsa_forward_decode_adaptive")
+    return out
+
+
+def hsa_forward_prefill_adaptive(q, k, v, landmarks, chunk_size: int, top_k: int, gap_threshold: float, out=None,
+                                 sel_idx=None, sel_score=None, workspace=None):
+    """Causal prefill with the near-tie adaptive budget: a query row keeps its
+    best 2*top_k chunks when its top_k-th and (top_k+1)-th scores differ by
+    less than gap_threshold, else top_k.  q [B,Hq,T,D], k/v [B,Hkv,T,D] ->
+    out [B,Hq,T,D] fp32; sel_idx/sel_score [B,Hq,T,2*top_k]."""
+    torch = _torch()
+    B, Hkv, T, D = k.shape
+    Hq = q.shape[1]
+    if v.shape != k.shape or v.dtype != k.dtype or q.dtype != k.dtype:
+        raise ValueError("q, k and v must share dtype; v must match k's shape")
+    if tuple(q.shape) != (B, Hq, T, D):
+        raise ValueError(f"q must be {(B, Hq, T, D)}, got {tuple(q.shape)}")
+    if tuple(landmarks.shape) != landmarks_shape(k.shape, chunk_size) or landmarks.dtype != k.dtype:
+        raise ValueError("landmarks must be [B, Hkv, T // chunk_size, D] with the dtype of k")
+    dims = make_dims(B, Hq, Hkv, D, chunk_size, top_k, T, _dtype_code(k))
+    if out is None:
+        out = torch.empty((B, Hq, T, D), dtype=torch.float32, device=q.device)
+    if (sel_idx is None) != (sel_score is None):
+        raise ValueError("give both sel_idx and sel_score or neither")
+    if workspace is None:
+        need = hsa_attn_workspace_size(dims, 3)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = load_library().hsa_forward_prefill_adaptive(
+        ctypes.byref(dims), float(gap_threshold), _ptr(q), _ptr(k), _ptr(v), _ptr(landmarks), _ptr(out),
+        _ptr(sel_idx), _ptr(sel_score), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q.device))
+    _check(st, "hsa_forward_prefill_adaptive")
     return out
 
 

@@ -32,11 +32,11 @@ hsa_attn_status_t ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-enum class Call { kLandmarks, kPrefill, kDecode, kDecodeAdaptive };
+enum class Call { kLandmarks, kPrefill, kDecode, kDecodeAdaptive, kPrefillAdaptive };
 
 // Validates the dimension block and fills a Geometry.
 hsa_attn_status_t check_dims(const hsa_attn_dims_t* d, Call call, hsa_attn::Geometry* g) {
-  const bool adaptive = call == Call::kDecodeAdaptive;
+  const bool adaptive = call == Call::kDecodeAdaptive || call == Call::kPrefillAdaptive;
   if (!d) return fail(HSA_ATTN_INVALID_ARGUMENT, "dims is NULL");
   if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1)
     return fail(HSA_ATTN_INVALID_ARGUMENT, "batch and head counts must be >= 1");
@@ -56,19 +56,21 @@ hsa_attn_status_t check_dims(const hsa_attn_dims_t* d, Call call, hsa_attn::Geom
     if (G != 1 && G != 2 && G != 4 && G != 8)
       return fail(HSA_ATTN_UNSUPPORTED, "query heads per KV head %d unsupported (1, 2, 4, 8)", G);
     if (d->chunk_size != 64) return fail(HSA_ATTN_UNSUPPORTED, "chunk_size %d unsupported (64)", d->chunk_size);
-    // decode keeps one list entry per lane of a wave; the adaptive budget
-    // may double k
-    const int kmax = call == Call::kDecode ? 64 : 32;
+    // decode keeps one list entry per lane of a wave, prefill up to 32 per
+    // row in registers; the adaptive budget doubles k
+    const int kmax = (call == Call::kDecode || call == Call::kDecodeAdaptive ? 64 : 32) / (adaptive ? 2 : 1);
     if (d->top_k > kmax) return fail(HSA_ATTN_UNSUPPORTED, "top_k %d unsupported (<= %d)", d->top_k, kmax);
   }
   if (call == Call::kDecodeAdaptive) call = Call::kDecode;
+  if (call == Call::kPrefillAdaptive) call = Call::kPrefill;
+  const int64_t k_slots = (int64_t)d->top_k * (adaptive ? 2 : 1);
   const int64_t Nc = d->seq_len / d->chunk_size;
   if (call == Call::kPrefill) {
     if (Nc > 65536) return fail(HSA_ATTN_UNSUPPORTED, "prefill supports at most 65536 chunks");
     if ((d->seq_len + 63) / 64 * (int64_t)d->batch * d->num_kv_heads * 2 > 0x7fffffffLL)
       return fail(HSA_ATTN_UNSUPPORTED, "prefill grid too large");
     // remote-pair positions and row indices are int32
-    if ((int64_t)d->batch * d->num_q_heads * d->seq_len * d->top_k > 0x7fffffffLL)
+    if ((int64_t)d->batch * d->num_q_heads * d->seq_len * k_slots > 0x7fffffffLL)
       return fail(HSA_ATTN_UNSUPPORTED, "prefill: batch * q_heads * seq_len * top_k must stay below 2^31");
   }
   if (call == Call::kDecode && Nc > 0x7fffffffLL) return fail(HSA_ATTN_UNSUPPORTED, "cache too long");
@@ -130,13 +132,15 @@ const char* hsa_attn_last_error(void) { return g_last_error; }
 hsa_attn_status_t hsa_attn_workspace_size(const hsa_attn_dims_t* d, int is_decode, size_t* bytes) {
   try {
     if (!bytes) return fail(HSA_ATTN_INVALID_ARGUMENT, "bytes is NULL");
-    if (is_decode < 0 || is_decode > 2) return fail(HSA_ATTN_INVALID_ARGUMENT, "kind must be 0, 1 or 2");
+    if (is_decode < 0 || is_decode > 3) return fail(HSA_ATTN_INVALID_ARGUMENT, "kind must be 0, 1, 2 or 3");
     hsa_attn::Geometry g;
-    const Call call = is_decode == 2 ? Call::kDecodeAdaptive : is_decode ? Call::kDecode : Call::kPrefill;
+    static const Call kinds[4] = {Call::kPrefill, Call::kDecode, Call::kDecodeAdaptive, Call::kPrefillAdaptive};
+    const Call call = kinds[is_decode];
     const hsa_attn_status_t st = check_dims(d, call, &g);
     if (st != HSA_ATTN_OK) return st;
     // the size assumes the library keeps the selection itself (sel outputs NULL)
-    *bytes = is_decode ? hsa_attn::plan_decode(g, true).bytes : hsa_attn::plan_prefill(g, true).bytes;
+    const bool dec = is_decode == 1 || is_decode == 2;
+    *bytes = dec ? hsa_attn::plan_decode(g, true).bytes : hsa_attn::plan_prefill(g, true).bytes;
     return ok();
   } catch (const std::exception& e) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
@@ -167,12 +171,15 @@ hsa_attn_status_t hsa_build_landmarks(const hsa_attn_dims_t* d, const void* k, v
   }
 }
 
+// gap_tau < 0: plain top-k; otherwise the adaptive budget with threshold gap_tau
 static hsa_attn_status_t forward_prefill(const hsa_attn_dims_t* d, int64_t q_offset, const void* q, const void* k,
                                          const void* v, const void* landmarks, float* out, int32_t* sel_idx,
-                                         float* sel_score, void* workspace, size_t workspace_bytes, void* stream) {
+                                         float* sel_score, void* workspace, size_t workspace_bytes, void* stream,
+                                         float gap_tau = -1.0f) {
   try {
     hsa_attn::Geometry g;
-    hsa_attn_status_t st = check_dims(d, Call::kPrefill, &g);
+    const bool adaptive = gap_tau >= 0.0f;
+    hsa_attn_status_t st = check_dims(d, adaptive ? Call::kPrefillAdaptive : Call::kPrefill, &g);
     if (st != HSA_ATTN_OK) return st;
     if (q_offset < 0 || q_offset > g.T || q_offset % g.S != 0)
       return fail(HSA_ATTN_INVALID_ARGUMENT, "q_offset %lld must be a multiple of chunk_size in [0, seq_len]",
@@ -202,6 +209,10 @@ static hsa_attn_status_t forward_prefill(const hsa_attn_dims_t* d, int64_t q_off
                             reinterpret_cast<int32_t*>(ws + plan.off_pair_pos), reinterpret_cast<int*>(ws + plan.off_cnt),
                             reinterpret_cast<int*>(ws + plan.off_off), reinterpret_cast<int32_t*>(ws + plan.off_pairs),
                             reinterpret_cast<float*>(ws + plan.off_partial), ws + plan.off_vt};
+    if (adaptive) {
+      a.k_base = d->top_k;
+      a.gap_tau = gap_tau;
+    }
     return hip_status(hsa_attn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
   } catch (const std::exception& e) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
@@ -225,6 +236,16 @@ hsa_attn_status_t hsa_forward_prefill_cached(const hsa_attn_dims_t* d, int64_t q
 }
 
 // gap_tau < 0: plain top-k; otherwise the adaptive budget with threshold gap_tau
+hsa_attn_status_t hsa_forward_prefill_adaptive(const hsa_attn_dims_t* d, float gap_threshold, const void* q,
+                                               const void* k, const void* v, const void* landmarks, float* out,
+                                               int32_t* sel_idx, float* sel_score, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
+  if (!(gap_threshold >= 0.0f))
+    return fail(HSA_ATTN_INVALID_ARGUMENT, "gap_threshold must be >= 0 (or +inf), got %g", (double)gap_threshold);
+  return forward_prefill(d, 0, q, k, v, landmarks, out, sel_idx, sel_score, workspace, workspace_bytes, stream,
+                         gap_threshold);
+}
+
 static hsa_attn_status_t forward_decode(const hsa_attn_dims_t* d, const void* q, const void* k_cache,
                                         const void* v_cache, const void* landmarks, const int64_t* lens, float* out,
                                         int32_t* sel_idx, float* sel_score, void* workspace, size_t workspace_bytes,

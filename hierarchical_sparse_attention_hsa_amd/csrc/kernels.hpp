@@ -89,6 +89,9 @@ struct PrefillArgs {
   int32_t* pairs;     // [B * Hq * T * k] (worst case)
   float* partial;     // [B * Hq * T * k, D] (worst case)
   void* vt;           // [B, Hkv, Nc, D, 64] transposed V tiles (storage dtype)
+  // adaptive budget, as in DecodeArgs: g.k == 2 * k_base when k_base > 0
+  int k_base = 0;
+  float gap_tau = 0.0f;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 

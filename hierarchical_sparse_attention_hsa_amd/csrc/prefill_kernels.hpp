@@ -108,8 +108,9 @@ template <typename T, int D, int G, int KSEL>
 __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ lm,
     int32_t* __restrict__ sel_idx, float* __restrict__ sel_score, int* __restrict__ rcnt, int32_t* __restrict__ pair_pos,
-    int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int j0, int k, float scale) {
-  // T_len: query rows per (b, h); query row r sits at position 64*j0 + r
+    int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int j0, int k, float scale, int k_base, float gap_tau) {
+  // T_len: query rows per (b, h); query row r sits at position 64*j0 + r.
+  // k_base > 0: adaptive budget, k == 2 * k_base (see the epilogue)
   using st = typename T::storage;
   constexpr int HPW = G < 4 ? G : 4;  // query heads (waves) per workgroup
   constexpr int HS = G / HPW;         // workgroups per (b, g, query chunk)
@@ -368,11 +369,39 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
     oi[e] = INT_MAX;
   }
   {
+    // cbuf holds the kept set in ascending chunk order; list_insert lets the
+    // newest element win score ties, so offer it from the highest index down
     const int mx = wave_max_i(cnt);
-    for (int e = 0; e < mx; ++e) {
+    for (int e = mx - 1; e >= 0; --e) {
       if (e < cnt) {
         const float2 c = cbuf[hh][e][lane];
         list_insert<KSEL>(os, oi, c.x, __float_as_int(c.y));
+      }
+    }
+  }
+  // near-tie adaptive budget (value-of-information router abstract, k-th
+  // versus (k+1)-th gap): the row keeps all k = 2 * k_base entries only when
+  // its k_base-th best scaled score beats the next one by less than gap_tau
+  // (the same fp32 values it stores in sel_score); otherwise entries from
+  // k_base on become padding before they are written or bucketed
+  if (k_base > 0) {
+    float s_k = -__builtin_inff(), s_k1 = -__builtin_inff();
+    bool has_k1 = false;
+#pragma unroll
+    for (int e = 0; e < KSEL; ++e) {
+      if (e == k_base - 1) s_k = os[e] * scale + 0.0f;
+      if (e == k_base) {
+        s_k1 = os[e] * scale + 0.0f;
+        has_k1 = oi[e] != INT_MAX;
+      }
+    }
+    if (!(has_k1 && s_k - s_k1 < gap_tau)) {
+#pragma unroll
+      for (int e = 0; e < KSEL; ++e) {
+        if (e >= k_base) {
+          os[e] = -__builtin_inff();
+          oi[e] = INT_MAX;
+        }
       }
     }
   }
@@ -937,7 +966,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   mark_launch(st);
   hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(blocks * (G / HPW)), dim3(kWave * HPW), 0, st, q,
                      static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, nb > 0 ? a.cnt : nullptr, a.pair_pos,
-                     g.B, g.Hkv, g.Tq, g.Nc, nqc, j0, g.k, scale);
+                     g.B, g.Hkv, g.Tq, g.Nc, nqc, j0, g.k, scale, a.k_base, a.gap_tau);
   mark_launch(st);
   if (nb > 0) {
     mark_launch(st);

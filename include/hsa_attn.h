@@ -127,6 +127,23 @@ hsa_attn_status_t hsa_forward_prefill_cached(const hsa_attn_dims_t* d, int64_t q
                                              size_t workspace_bytes, void* stream);
 
 /*
+ * Causal prefill with the near-tie adaptive budget (value-of-information
+ * router abstract; the rule of hsa_forward_decode_adaptive applied to every
+ * query row): row p of head h ranks its candidates as hsa_forward_prefill
+ * does (k = d->top_k), and keeps its best min(2k, n_p) chunks when it has
+ * more than k candidates and s_k - s_(k+1) < gap_threshold (fp32 scores with
+ * the 1/sqrt(D) scale, the values written to sel_score), its best k
+ * otherwise.  gap_threshold = 0 reproduces hsa_forward_prefill with top_k = k
+ * and +inf with top_k = 2k, bit for bit.  gap_threshold must be >= 0 (+inf
+ * allowed).  Requires k <= 16.  sel_idx/sel_score [B,Hq,T,2k] optional, -1 /
+ * -inf padding.  workspace: at least hsa_attn_workspace_size(d, 3) bytes.
+ */
+hsa_attn_status_t hsa_forward_prefill_adaptive(const hsa_attn_dims_t* d, float gap_threshold, const void* q,
+                                               const void* k, const void* v, const void* landmarks, float* out,
+                                               int32_t* sel_idx, float* sel_score, void* workspace,
+                                               size_t workspace_bytes, void* stream);
+
+/*
  * HSA forward for B independent single-token queries, each after its own
  * cache of T tokens (card, "Core Technique": scoring is O(n/S) per query and
  * attention O(k*S)).  The query sits at position T, so its candidates are
@@ -201,7 +218,7 @@ hsa_attn_status_t hsa_append_kv(const hsa_attn_dims_t* d, const void* k_new, con
  * forward, landmark or append call made on the calling thread records events[2*i] (hipEvent_t, created by the caller)
  * on its stream just before its i-th kernel launch and events[2*i+1] just
  * after it, for i < n_pairs; the index restarts at 0 with each call.
- * Launch order: landmarks: 1 kernel; prefill (when T >= S): zero, select,
+ * Launch order: landmarks: 1 kernel; prefill, cached and adaptive prefill (when T >= S): zero, select,
  * V transpose, scan, scatter, remote attention, local attention (for T < S:
  * select, local attention); decode and varlen decode: scan, merge,
  * attention, fusion, for adaptive decode too (scan and attention are skipped when the cache capacity
@@ -212,7 +229,8 @@ hsa_attn_status_t hsa_append_kv(const hsa_attn_dims_t* d, const void* k_new, con
 hsa_attn_status_t hsa_attn_set_timing_events(void** events, int n_pairs);
 
 /* Bytes of device workspace a forward call needs (is_decode: 0 prefill and
- * cached prefill, 1 decode and varlen decode, 2 adaptive-budget decode). */
+ * cached prefill, 1 decode and varlen decode, 2 adaptive-budget decode,
+ * 3 adaptive-budget prefill). */
 hsa_attn_status_t hsa_attn_workspace_size(const hsa_attn_dims_t* d, int is_decode, size_t* bytes);
 
 /* Static description of a status code. */

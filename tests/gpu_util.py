@@ -46,6 +46,9 @@ def check_rows(q_rows, pos, Kg, Vg, Lg, S, k, gpu_out, gpu_sel, gpu_score, tol, 
             sc = gpu_score[r, :m]
             if m > 1 and np.any(np.diff(sc) > 0):
                 raise Mismatch(f"row {r}: slot scores not sorted: {sc}")
+            ids = gpu_sel[r, :m]
+            if m > 1 and np.any((np.diff(sc) == 0) & (np.diff(ids) < 0)):
+                raise Mismatch(f"row {r}: equal scores not in ascending chunk order: {list(ids)} {list(sc)}")
             np.testing.assert_allclose(np.sort(sc), np.sort(ref.sel_score[r, :m]), rtol=1e-4, atol=1e-5,
                                        err_msg=f"row {r} retrieval scores")
     expect = ref.out.copy()
@@ -64,30 +67,47 @@ def new_stats():
     return {"rows": 0, "near_tie_rows": 0, "max_err": 0.0}
 
 
-def check_rows_adaptive(q_row, pos, Kg, Vg, Lg, S, k, tau, gpu_out, gpu_sel, gpu_score, tol, stats):
-    """One query row under the near-tie adaptive budget (base k, threshold
-    tau).  The kept count (valid entries of gpu_sel, 2k slots) must be the
-    oracle's unless the oracle's fp64 k-th vs (k+1)-th gap lies within the
-    fp32 score error band of tau, where either count is valid; the kept set
-    and output are then checked as a plain top-m row."""
-    n = int(O.num_candidates(np.array([pos]), S, Kg.shape[0] // S)[0])
-    m = int((gpu_sel >= 0).sum())
-    if n <= k:
-        allowed = {n}
-    else:
-        s = O.scores_for_rows(q_row[None], Lg, n)[0]
-        order = O.select_topk(s[None], 2 * k)[0]
-        want, gap = O.adaptive_keep_count(s[order], k, tau)
-        allowed = {want}
-        _, band, _ = O.near_tie_info(q_row, Lg, n, k)
-        if abs(gap - tau) <= 2 * band:
-            allowed = {k, min(2 * k, n)}
-            stats["ambiguous"] = stats.get("ambiguous", 0) + 1
-    if m not in allowed:
-        raise Mismatch(f"kept {m} chunks, expected {sorted(allowed)} (tau {tau})")
-    if np.any(gpu_sel[m:] != -1):
-        raise Mismatch(f"padding expected after slot {m}: {gpu_sel}")
-    stats["doubled"] = stats.get("doubled", 0) + int(m > k)
-    mm = max(m, 1)
-    check_rows(q_row[None], np.array([pos]), Kg, Vg, Lg, S, mm, gpu_out[None], gpu_sel[:mm][None],
-               gpu_score[:mm][None], tol, stats)
+def check_rows_adaptive(q_rows, pos, Kg, Vg, Lg, S, k, tau, gpu_out, gpu_sel, gpu_score, tol, stats):
+    """Query rows of one (b, h) under the near-tie adaptive budget (base k,
+    threshold tau); gpu_sel/gpu_score have 2k slots per row.  A row's kept
+    count (its valid slots) must be the oracle's unless the oracle's fp64
+    k-th vs (k+1)-th gap lies within the fp32 score error band of tau, where
+    either count is valid; the kept sets and outputs are then checked as
+    plain top-m rows (check_rows), grouped by m."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    D = q_rows.shape[1]
+    n_all = O.num_candidates(pos, S, Kg.shape[0] // S)
+    m_gpu = (gpu_sel >= 0).sum(axis=1)
+    for r in range(len(pos)):
+        if np.any(gpu_sel[r, m_gpu[r]:] != -1):
+            raise Mismatch(f"row {r} (pos {pos[r]}): padding expected after slot {m_gpu[r]}: {gpu_sel[r]}")
+    for n in np.unique(n_all):
+        rows = np.nonzero(n_all == n)[0]
+        n = int(n)
+        if n <= k:
+            bad = rows[m_gpu[rows] != n]
+            if bad.size:
+                raise Mismatch(f"row {bad[0]} (pos {pos[bad[0]]}): kept {m_gpu[bad[0]]}, expected all {n}")
+            continue
+        s = O.scores_for_rows(q_rows[rows], Lg, n)
+        order = O.select_topk(s, 2 * k)
+        ss = np.take_along_axis(s, order, axis=1)
+        A = (np.abs(q_rows[rows]) @ np.abs(Lg[:n]).T) / np.sqrt(D)  # fp32 error scale of each score
+        for i, r in enumerate(rows):
+            want, gap = O.adaptive_keep_count(ss[i], k, tau)
+            a, b = order[i, k - 1], order[i, k]
+            band = 1e-5 * max(abs(s[i, a]), abs(s[i, b]), A[i, a], A[i, b])
+            allowed = {want}
+            if abs(gap - tau) <= 2 * band:
+                allowed = {k, min(2 * k, n)}
+                stats["ambiguous"] = stats.get("ambiguous", 0) + 1
+            if int(m_gpu[r]) not in allowed:
+                raise Mismatch(f"row {r} (pos {pos[r]}): kept {m_gpu[r]}, expected {sorted(allowed)} "
+                               f"(gap {gap}, tau {tau})")
+    stats["doubled"] = stats.get("doubled", 0) + int((m_gpu > k).sum())
+    for m in np.unique(m_gpu):
+        rows = np.nonzero(m_gpu == m)[0]
+        mm = max(int(m), 1)
+        check_rows(q_rows[rows], pos[rows], Kg, Vg, Lg, S, mm, gpu_out[rows], gpu_sel[rows, :mm],
+                   gpu_score[rows, :mm], tol, stats)

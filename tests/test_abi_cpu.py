@@ -167,4 +167,19 @@ def test_adaptive_decode_validation():
     assert hsa.hsa_attn_workspace_size(d, 2) == hsa.hsa_attn_workspace_size(dims(top_k=32, seq_len=1 << 20), 1)
     assert hsa.hsa_attn_workspace_size(dims(top_k=32), 2) > hsa.hsa_attn_workspace_size(dims(top_k=32), 1)
     n = ctypes.c_size_t(0)
-    assert lib.hsa_attn_workspace_size(ctypes.byref(d), 3, ctypes.byref(n)) == hsa.HSA_ATTN_INVALID_ARGUMENT
+    assert lib.hsa_attn_workspace_size(ctypes.byref(d), 4, ctypes.byref(n)) == hsa.HSA_ATTN_INVALID_ARGUMENT
+
+
+def test_adaptive_prefill_validation():
+    lib = hsa.load_library()
+    p = ctypes.c_void_p(0x1000)
+
+    def call(d, tau, ws=1 << 40):
+        return lib.hsa_forward_prefill_adaptive(ctypes.byref(d), tau, p, p, p, p, p, None, None, p, ws, None)
+
+    for bad in (float("nan"), -0.5):
+        assert call(dims(), bad) == hsa.HSA_ATTN_INVALID_ARGUMENT
+    assert call(dims(top_k=17), 0.1) == hsa.HSA_ATTN_UNSUPPORTED  # 2k must stay <= 32
+    assert call(dims(), 0.1, ws=16) == hsa.HSA_ATTN_WORKSPACE_TOO_SMALL
+    d = dims(top_k=16, seq_len=1 << 15)
+    assert hsa.hsa_attn_workspace_size(d, 3) == hsa.hsa_attn_workspace_size(dims(top_k=32, seq_len=1 << 15), 0)

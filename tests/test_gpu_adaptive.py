@@ -108,10 +108,71 @@ def test_adaptive_decode(case):
         for h in range(Hq):
             g = O.kv_head_of(h, Hq, Hkv)
             try:
-                check_rows_adaptive(Q[b, h], lens[b], K[b, g, :lens[b]], V[b, g, :lens[b]], Lc[b, g], S, k, tau,
-                                    out_h[b, h], sel_h[b, h], sc_h[b, h], TOL[dtype], stats)
+                check_rows_adaptive(Q[b, h][None], [lens[b]], K[b, g, :lens[b]], V[b, g, :lens[b]], Lc[b, g], S,
+                                    k, tau, out_h[b, h][None], sel_h[b, h][None], sc_h[b, h][None], TOL[dtype],
+                                    stats)
             except Mismatch as e:
                 raise Mismatch(f"(b {b}, h {h}): {e}") from None
     print(stats, f"tau {tau:.3e}", flush=True)
     rows_with_cut = int((~np.isnan(gaps)).sum())
     assert 0 < stats.get("doubled", 0) < rows_with_cut
+
+
+PREFILL_CASES = [
+    # B, Hq, Hkv, T, D, k, dtype
+    (1, 8, 2, 64 * 70 + 13, 128, 8, "bf16"),  # 2k = 16
+    (1, 4, 4, 64 * 80, 64, 16, "fp32"),       # 2k = 32, past one 64-chunk window
+    (2, 4, 1, 64 * 140, 128, 16, "bf16"),     # two windows: remote pairs
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES)
+def test_adaptive_prefill(case):
+    B, Hq, Hkv, T, D, k, dtype = case
+    print(f"adaptive prefill case {case}", flush=True)
+    q, kc, vc = small_inputs(B, Hq, Hkv, T, D, dtype, seed=2000 + T % 991 + k)
+    Q, K, V = f64(q), f64(kc), f64(vc)
+    Lc = O.landmarks(K, S, dtype)
+    # threshold from the oracle's gaps of every row with a cut
+    pos = np.arange(T)
+    gaps = []
+    for b in range(B):
+        for h in range(Hq):
+            g = O.kv_head_of(h, Hq, Hkv)
+            _, _, gp = O.hsa_rows_adaptive(Q[b, h], pos, K[b, g], V[b, g], Lc[b, g], S, k, 0.0)
+            gaps.append(gp)
+    tau = pick_threshold(np.concatenate(gaps))
+    qd, kd, vd = q.cuda(), kc.cuda(), vc.cuda()
+    L = torch.empty((B, Hkv, T // S, D), dtype=kc.dtype, device="cuda")
+    hsa.hsa_build_landmarks(kd, L, S)
+
+    def adaptive(t):
+        sel = torch.full((B, Hq, T, 2 * k), -7, dtype=torch.int32, device="cuda")
+        sc = torch.full((B, Hq, T, 2 * k), 7.0, dtype=torch.float32, device="cuda")
+        out = hsa.hsa_forward_prefill_adaptive(qd, kd, vd, L, S, k, t, sel_idx=sel, sel_score=sc)
+        return out, sel, sc
+
+    ref_k = hsa.hsa_forward_prefill(qd, kd, vd, L, S, k)
+    ref_2k = hsa.hsa_forward_prefill(qd, kd, vd, L, S, 2 * k)
+    out0, sel0, _ = adaptive(0.0)
+    outi, _, _ = adaptive(math.inf)
+    out, sel, sc = adaptive(tau)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, ref_k) and torch.all(sel0[..., k:] == -1)
+    assert torch.equal(outi, ref_2k)
+    m_gpu = (sel >= 0).sum(-1)
+    rows_ok = torch.where(m_gpu > k, (out == ref_2k).all(-1), (out == ref_k).all(-1))
+    assert bool(rows_ok.all()), "rows must equal the plain prefill at their budget"
+
+    sel_h, sc_h, out_h = sel.cpu().numpy(), f64(sc), f64(out)
+    stats = new_stats()
+    for b in range(B):
+        for h in range(Hq):
+            g = O.kv_head_of(h, Hq, Hkv)
+            try:
+                check_rows_adaptive(Q[b, h], pos, K[b, g], V[b, g], Lc[b, g], S, k, tau, out_h[b, h], sel_h[b, h],
+                                    sc_h[b, h], TOL[dtype], stats)
+            except Mismatch as e:
+                raise Mismatch(f"(b {b}, h {h}): {e}") from None
+    print(stats, f"tau {tau:.3e}", flush=True)
+    assert 0 < stats.get("doubled", 0) < int(sum((~np.isnan(x)).sum() for x in gaps))

@@ -179,10 +179,9 @@ def run_decode_workload(name, queries):
                 check_rows(host64(q[b, hs]), np.full(G, w.T), DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lg, w.S,
                            w.k, host64(out[b, hs]), sel[b, hs].cpu().numpy(), host64(sc[b, hs]), TOL[w.dtype], stats)
                 continue
-            qh, oh, sh, ch = host64(q[b, hs]), host64(out[b, hs]), sel[b, hs].cpu().numpy(), host64(sc[b, hs])
-            for i in range(G):
-                check_rows_adaptive(qh[i], w.T, DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lg, w.S, w.k, tau, oh[i],
-                                    sh[i], ch[i], TOL[w.dtype], stats)
+            check_rows_adaptive(host64(q[b, hs]), np.full(G, w.T), DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lg,
+                                w.S, w.k, tau, host64(out[b, hs]), sel[b, hs].cpu().numpy(), host64(sc[b, hs]),
+                                TOL[w.dtype], stats)
         print(name, "query", b, stats, flush=True)
     del q, k, v, L, out, sel, sc
     torch.cuda.empty_cache()

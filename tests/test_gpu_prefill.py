@@ -97,3 +97,39 @@ def test_prefill_is_deterministic():
     b = run_prefill(q, k, v, 64, 16)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("topk", [4, 16, 32])
+def test_prefill_duplicate_chunks_keep_index_order(topk):
+    """Chunks with bit-equal keys score bit-equal: when both are kept the
+    lower index takes the earlier slot, and a cut between them keeps the
+    lower one (ties toward the lower chunk index)."""
+    B, Hq, Hkv, T, D = 1, 4, 1, 64 * 140, 128
+    q, k, v = small_inputs(B, Hq, Hkv, T, D, "bf16", seed=31)
+    pairs = ((44, 71), (2, 30), (9, 100), (60, 61))
+    for lo, hi in pairs:
+        k[0, 0, hi * 64:(hi + 1) * 64] = k[0, 0, lo * 64:(lo + 1) * 64]
+    out, sel, score = run_prefill(q, k, v, 64, topk)
+    compare(q, k, v, 64, topk, "bf16", out, sel, score)
+    for lo, hi in pairs:
+        for h in range(Hq):
+            for p in range((hi + 1) * 64, T):
+                s = list(sel[0, h, p])
+                if hi in s:
+                    assert lo in s and s.index(lo) < s.index(hi), (lo, hi, h, p, s)
+
+
+@pytest.mark.parametrize("topk", [8, 32])
+def test_prefill_all_scores_equal_keep_lowest_indices(topk):
+    """Every chunk identical: each row keeps its topk lowest chunk indices in
+    index order."""
+    B, Hq, Hkv, T, D = 1, 2, 1, 64 * 130, 64
+    q, k, v = small_inputs(B, Hq, Hkv, T, D, "bf16", seed=32)
+    for c in range(1, T // 64):
+        k[0, 0, c * 64:(c + 1) * 64] = k[0, 0, :64]
+    out, sel, score = run_prefill(q, k, v, 64, topk)
+    for p in range(T):
+        n = min(p // 64, topk)
+        assert np.array_equal(sel[0, :, p, :n], np.tile(np.arange(n), (Hq, 1))), p
+        assert np.all(sel[0, :, p, n:] == -1)
+    compare(q, k, v, 64, topk, "bf16", out, sel, score, rows=np.arange(0, T, 37))
