@@ -404,9 +404,11 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
     L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
     if off:  # the prefix's landmarks exist already
         hsa.hsa_build_landmarks(k, L, w.S, 0, off // w.S)
+    tau = w.extra.get("gap_threshold")  # near-tie adaptive budget
+    kk = w.k if tau is None else 2 * w.k  # selection slots per row
     out = torch.empty((w.B, w.Hq, Tq, w.D), dtype=torch.float32, device="cuda")
-    sel = torch.empty((w.B, w.Hq, Tq, w.k), dtype=torch.int32, device="cuda")
-    sc = torch.empty((w.B, w.Hq, Tq, w.k), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, Tq, kk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, Tq, kk), dtype=torch.float32, device="cuda")
     events = HipEvents()
 
     def step(ev):
@@ -417,6 +419,8 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
             hsa.hsa_attn_set_timing_events(ev[2:])
         if off:
             hsa.hsa_forward_prefill_cached(q, k, v, L, off, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
+        elif tau is not None:
+            hsa.hsa_forward_prefill_adaptive(q, k, v, L, w.S, w.k, tau, out=out, sel_idx=sel, sel_score=sc)
         else:
             hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
 
@@ -427,14 +431,13 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
     # exact algorithmic work
     p = np.arange(off, w.T)
     n_p = np.minimum(p // w.S, Nc)
-    m_p = np.minimum(n_p, w.k)
     score_flops = 2.0 * w.B * w.Hq * w.D * n_p.sum()
-    attn_flops = 4.0 * w.S * w.D * w.B * w.Hq * m_p.sum()
+    n_pairs = int((sel >= 0).sum().item())  # kept (row, chunk) pairs: sum of min(n_p, k) without adaptivity
+    attn_flops = 4.0 * w.S * w.D * n_pairs
     # split of the selected pairs into remote (chunk before the query's
     # 64-chunk window) and local ones, counted from this run's selection
     win0 = torch.div(torch.arange(off, w.T, device="cuda") // w.S, 64, rounding_mode="floor") * 64
     n_remote = int(((sel >= 0) & (sel < win0[None, None, :, None])).sum().item())
-    n_pairs = int(m_p.sum()) * w.B * w.Hq
     remote_flops = 4.0 * w.S * w.D * n_remote
     local_flops = 4.0 * w.S * w.D * (n_pairs - n_remote)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -464,14 +467,18 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
     }
     log(f"[{wname}] {ms_step:.3f} ms/step, kernels {dict(zip(names, np.round(per, 4)))}, "
         f"scoring {sel_tf:.1f} TFLOP/s, attention {att_tf:.1f} TFLOP/s, remote pairs {n_remote / max(n_pairs, 1):.3f}")
+    if tau is not None:
+        res["gap_threshold"] = tau
+        res["doubled_row_frac"] = float(((sel >= 0).sum(-1) > w.k).float().mean())
+        res["config"]["gap_threshold"] = tau
     if cpu_baseline:
-        res["cpu_baseline"] = prefill_cpu_baseline(w, q, k, v)
+        res["cpu_baseline"] = prefill_cpu_baseline(w, q, k, v, tau=tau)
     del q, k, v, L, out, sel, sc
     torch.cuda.empty_cache()
     return res
 
 
-def prefill_cpu_baseline(w, q, k, v, chunks=tuple(range(250, 4001, 250))):
+def prefill_cpu_baseline(w, q, k, v, chunks=tuple(range(250, 4001, 250)), tau=None):
     """The oracle on a bounded sample: all heads of the query chunks listed
     (64 tokens each).  Host copies and landmark building are untimed."""
     from oracle import hsa_oracle as O
@@ -490,7 +497,10 @@ def prefill_cpu_baseline(w, q, k, v, chunks=tuple(range(250, 4001, 250))):
             qq = q[0, g * G:(g + 1) * G, c * w.S - off:(c + 1) * w.S - off].float().cpu().double().numpy()
             t0 = time.perf_counter()
             for hh in range(G):
-                O.hsa_rows(qq[hh], pos, Kg, Vg, Lg, w.S, w.k)
+                if tau is None:
+                    O.hsa_rows(qq[hh], pos, Kg, Vg, Lg, w.S, w.k)
+                else:  # near-tie adaptive budget
+                    O.hsa_rows_adaptive(qq[hh], pos, Kg, Vg, Lg, w.S, w.k, tau)
             total += time.perf_counter() - t0
     tokens = len(chunks) * w.S
     return {"value": tokens / total, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
@@ -555,7 +565,8 @@ def main():
     }
     if "cpu_baseline" in main_res:
         line["cpu_baseline"] = main_res["cpu_baseline"]
-    for key in ("kernel_ms", "step_alg_GBps", "needle_recall", "gap_threshold", "doubled_head_frac"):
+    for key in ("kernel_ms", "step_alg_GBps", "needle_recall", "gap_threshold", "doubled_head_frac",
+                "doubled_row_frac"):
         if key in main_res:
             line[key] = main_res[key]
     if "prefill" in results:

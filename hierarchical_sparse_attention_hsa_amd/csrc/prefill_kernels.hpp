@@ -405,6 +405,30 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
       }
     }
   }
+  // The kept set is ranked by the unscaled dot products; the stored scores
+  // carry the 1/sqrt(D) factor, which can round two neighbouring dot
+  // products to one value.  Slots follow the stored scores, ties by index:
+  // such neighbours are swapped into index order (odd-even passes until no
+  // pair is out of order; a run of equal scores is rare and short).
+  float ss[KSEL];
+#pragma unroll
+  for (int e = 0; e < KSEL; ++e) ss[e] = oi[e] != INT_MAX ? os[e] * scale + 0.0f : -__builtin_inff();
+  for (bool again = true; again;) {
+    bool swapped = false;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+#pragma unroll
+      for (int e = par; e + 1 < KSEL; e += 2) {
+        if (ss[e] == ss[e + 1] && oi[e] > oi[e + 1]) {
+          const int t = oi[e];
+          oi[e] = oi[e + 1];
+          oi[e + 1] = t;
+          swapped = true;
+        }
+      }
+    }
+    again = __ballot(swapped) != 0;
+  }
   const int64_t base = (((int64_t)b * Hq + h) * T_len + t_row) * k;
   if (t_row < T_len) {
 #pragma unroll
@@ -412,7 +436,7 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
       if (e < k) {
         const bool ok = oi[e] != INT_MAX;
         sel_idx[base + e] = ok ? oi[e] : -1;
-        sel_score[base + e] = ok ? os[e] * scale + 0.0f : -__builtin_inff();
+        sel_score[base + e] = ok ? ss[e] : -__builtin_inff();
       }
     }
   }

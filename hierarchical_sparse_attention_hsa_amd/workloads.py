@@ -19,6 +19,9 @@ Workloads (all with chunk size 64):
   decode_1m_adaptive_bf16  decode_1m_bf16's inputs with the near-tie adaptive
                      budget, base k=16 (2k=32), gap threshold 1.25e-3 (the
                      0.25 quantile of these heads' k-th vs (k+1)-th gaps)
+  prefill_256k_adaptive_bf16  prefill_256k_bf16's inputs with the near-tie
+                     adaptive budget, base k=16 (2k=32), gap threshold 1e-2
+                     (about the 0.25 quantile of the rows' 16th vs 17th gaps)
   prefill_256k_chunk_bf16  the last 65536 tokens of prefill_256k_bf16 over
                      its cached first 196608 tokens
 
@@ -77,6 +80,10 @@ WORKLOADS = {
         # the gap threshold doubles about a quarter of the heads here
         Workload("decode_1m_adaptive_bf16", "decode", 64, 32, 8, 1 << 20, 128, 64, 16, "bf16", 3000, needles=8,
                  extra={"gap_threshold": 1.25e-3}),
+        # prefill_256k with the near-tie adaptive budget: base k = 16 (2k =
+        # 32); the gap threshold doubles about a quarter of the rows here
+        Workload("prefill_256k_adaptive_bf16", "prefill", 1, 32, 8, 262144, 128, 64, 16, "bf16", 4000, lowrank=8,
+                 extra={"gap_threshold": 1e-2}),
         # chunked prefill: the last 64K tokens of the 256K sequence after a
         # cached prefix of 192K tokens (same inputs as prefill_256k_bf16)
         Workload("prefill_256k_chunk_bf16", "prefill", 1, 32, 8, 262144, 128, 64, 16, "bf16", 4000, lowrank=8,

@@ -95,7 +95,10 @@ hsa_attn_status_t hsa_build_landmarks(const hsa_attn_dims_t* d, const void* k, v
  * q [B,Hq,T,D], k/v [B,Hkv,T,D], landmarks [B,Hkv,floor(T/S),D] (from
  * hsa_build_landmarks), out [B,Hq,T,D] fp32.  sel_idx / sel_score
  * [B,Hq,T,k] are optional outputs (NULL: kept in the workspace); slots are
- * ordered by score descending, then index ascending.
+ * ordered by score descending, then index ascending.  The selection ranks
+ * the fp32 dot products q.L before the 1/sqrt(D) factor is applied; where
+ * that factor rounds two different dot products to one stored score, the
+ * larger dot product is the one kept at the cut.
  * workspace: device scratch of at least hsa_attn_workspace_size(d, 0) bytes
  * (never NULL when T > 0).  It holds the selection when sel_idx is NULL,
  * the bucketing of selected chunks that lie before the query's aligned

@@ -7,6 +7,8 @@ acceptance rule.  Landmarks of the sampled KV heads are checked bit for bit
 Inputs come from the seeded generators in workloads.py; the oracle reads
 them from the device (the same values the kernels read), never any output of
 the HIP path."""
+import gc
+
 import numpy as np
 import pytest
 import torch
@@ -17,6 +19,17 @@ from oracle import hsa_oracle as O
 from tests.gpu_util import TOL, check_rows, check_rows_adaptive, new_stats
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+
+@pytest.fixture(autouse=True)
+def release_device_memory():
+    """Each workload needs most of the device: return what earlier tests
+    left in torch's cache before the next one sizes itself."""
+    gc.collect()
+    torch.cuda.empty_cache()
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
 
 
 def host64(t):
@@ -64,15 +77,20 @@ def run_prefill_workload(name, chunks, heads=None):
     q, k, v = prefill_inputs(w, "cuda")
     Nc = w.T // w.S
     Tq = w.T - off
+    tau = w.extra.get("gap_threshold")  # near-tie adaptive budget
+    kk = w.k if tau is None else 2 * w.k
     L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
     out = torch.empty((w.B, w.Hq, Tq, w.D), dtype=torch.float32, device="cuda")
-    sel = torch.empty((w.B, w.Hq, Tq, w.k), dtype=torch.int32, device="cuda")
-    sc = torch.empty((w.B, w.Hq, Tq, w.k), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, Tq, kk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, Tq, kk), dtype=torch.float32, device="cuda")
     if off:  # prefix landmarks first, then the new tokens' chunks, as the benchmark does
         hsa.hsa_build_landmarks(k, L, w.S, 0, off // w.S)
         hsa.hsa_build_landmarks(k, L, w.S, off // w.S, Nc)
         hsa.hsa_forward_prefill_cached(q[:, :, off:].contiguous(), k, v, L, off, w.S, w.k, out=out, sel_idx=sel,
                                        sel_score=sc)
+    elif tau is not None:
+        hsa.hsa_build_landmarks(k, L, w.S)
+        hsa.hsa_forward_prefill_adaptive(q, k, v, L, w.S, w.k, tau, out=out, sel_idx=sel, sel_score=sc)
     else:
         hsa.hsa_build_landmarks(k, L, w.S)
         hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
@@ -92,8 +110,12 @@ def run_prefill_workload(name, chunks, heads=None):
             for h in range(g * G, (g + 1) * G):
                 if heads is not None and h not in heads:
                     continue
-                check_rows(host64(q[b, h, pos_t]), pos, Kg, Vg, Lg, w.S, w.k, host64(out[b, h, row_t]),
-                           sel[b, h, row_t].cpu().numpy(), host64(sc[b, h, row_t]), TOL[w.dtype], stats)
+                args = (host64(q[b, h, pos_t]), pos, Kg, Vg, Lg, w.S, w.k)
+                res = (host64(out[b, h, row_t]), sel[b, h, row_t].cpu().numpy(), host64(sc[b, h, row_t]))
+                if tau is None:
+                    check_rows(*args, *res, TOL[w.dtype], stats)
+                else:
+                    check_rows_adaptive(*args, tau, *res, TOL[w.dtype], stats)
     print(name, stats, flush=True)
     del q, k, v, L, out, sel, sc
     torch.cuda.empty_cache()
@@ -114,6 +136,11 @@ def test_prefill_256k_bf16_sampled():
     # the special chunks, chunks around window and segment edges, and chunks
     # spread over the sequence
     run_prefill_workload("prefill_256k_bf16", [0, 1, 16, 17, 63, 64, 65, 1000, 2047, 3333, 4095])
+
+
+def test_prefill_256k_adaptive_bf16_sampled():
+    stats = run_prefill_workload("prefill_256k_adaptive_bf16", [0, 1, 16, 17, 63, 64, 65, 2047, 4095])
+    assert stats.get("doubled", 0) > 0
 
 
 def test_prefill_256k_chunk_bf16_sampled():
