@@ -33,6 +33,8 @@ Readings of points the pages leave open (each is listed in the design doc):
 * near-tie adaptive budget (value-of-information router abstract): a row
   whose k-th best score beats its (k+1)-th by less than a threshold tau keeps
   its best 2k chunks instead of k (adaptive_keep_count).
+* backward: the selection is held fixed (piecewise constant) and the
+  landmark's rounding is taken as the identity (hsa_rows_backward).
 
 Every input array handed to this module holds the exact values of the stored
 tensors as float64 (bf16 and fp32 upcast exactly).  Parity unpinned: nothing.
@@ -51,7 +53,7 @@ __all__ = [
     "round_to_dtype", "landmarks", "num_candidates", "scores_for_rows",
     "select_topk", "chunk_attention", "fuse", "hsa_rows", "prefill", "decode",
     "near_tie_info", "check_selection", "HSARowsResult", "adaptive_keep_count",
-    "hsa_rows_adaptive",
+    "hsa_rows_adaptive", "hsa_rows_backward", "prefill_backward", "BackwardResult",
 ]
 
 
@@ -104,10 +106,14 @@ def round_to_f32(x) -> np.ndarray:
 
 
 def round_to_dtype(x, dtype: str) -> np.ndarray:
+    """Round to the storage dtype; "fp64" keeps float64 (no rounding), which
+    the gradient pins use so that the forward is smooth in its inputs."""
     if dtype == "bf16":
         return round_to_bf16(x)
     if dtype == "fp32":
         return round_to_f32(x)
+    if dtype == "fp64":
+        return np.asarray(x, dtype=np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -366,6 +372,116 @@ def hsa_rows_adaptive(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.nda
         res = hsa_rows(q[rows], pos[rows], Kg, Vg, Lg, S, 2 * k, sel_override=[keep[r] for r in rows])
         out[rows], sel_idx[rows], sel_score[rows] = res.out, res.sel_idx, res.sel_score
     return HSARowsResult(out, sel_idx, sel_score, n_all), doubled, gap
+
+
+# ---------------------------------------------------------------------------
+# backward pass
+# ---------------------------------------------------------------------------
+
+@dataclass
+class BackwardResult:
+    dq: np.ndarray    # [R, D]
+    dK: np.ndarray    # [T, D]
+    dV: np.ndarray    # [T, D]
+    # element-wise error scales of a lower-precision evaluation: sums of the
+    # magnitudes of the terms each gradient entry adds up
+    abs_dK: np.ndarray
+    abs_dV: np.ndarray
+
+
+def hsa_rows_backward(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.ndarray, Lg: np.ndarray,
+                      S: int, sel, dout: np.ndarray) -> BackwardResult:
+    """Gradients of the layer's output rows with respect to q, K and V.
+
+    The forward (hsa_rows) for a row is: s_c = q.L_c/sqrt(D) over its kept
+    chunks c (a fixed list sel[r]: the selection is piecewise constant, so
+    no gradient flows through it), w = softmax(s), a_c = softmax over the
+    chunk's tokens of q.k_t/sqrt(D), o_c = sum_t a_ct v_t, out = sum_c w_c o_c,
+    with L_c the mean of the chunk's keys (its rounding to the storage dtype
+    is taken as the identity, so every key of the chunk receives 1/S of the
+    landmark's gradient).  The derivation is the chain rule on those steps
+    (card, "Core Technique" / "Implementation"; training the landmarks and
+    attention end to end is what the abstract describes):
+
+      do_c = w_c g                         (g = dL/dout of the row)
+      ds_c = w_c (g.o_c - g.out)           (softmax of the fusion weights)
+      dv_t += a_ct do_c
+      dlogit_ct = a_ct (do_c.v_t - do_c.o_c)
+      dq = (sum_c sum_t dlogit_ct k_t + sum_c ds_c L_c) / sqrt(D)
+      dk_t += (dlogit_ct q + ds_c q / S) / sqrt(D)    for t in chunk c
+
+    q: [R, D] rows at positions pos; Kg, Vg: [T, D]; Lg: landmarks; sel: one
+    index list per row (its kept chunks); dout: [R, D].  Returns dq [R, D] and
+    the rows' contributions dK, dV [T, D], plus the magnitude sums
+    abs_dV = sum |a_ct| |do_c| and abs_dK = sum (|dlogit_ct| + |ds_c| / S) |q| / sqrt(D).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    R, D = q.shape
+    T = Kg.shape[0]
+    sig = 1.0 / math.sqrt(D)
+    dq = np.zeros((R, D))
+    dK = np.zeros((T, D))
+    dV = np.zeros((T, D))
+    abs_dK = np.zeros((T, D))
+    abs_dV = np.zeros((T, D))
+    for r in range(R):
+        chunks = np.asarray(sel[r], dtype=np.int64)
+        chunks = chunks[chunks >= 0]
+        if chunks.size == 0:
+            continue
+        g = dout[r]
+        tok = chunks[:, None] * S + np.arange(S)[None, :]     # [m, S]
+        Kc, Vc = Kg[tok], Vg[tok]                             # [m, S, D]
+        s = (Lg[chunks] @ q[r]) * sig                         # [m]
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        logits = (Kc @ q[r]) * sig                            # [m, S]
+        a = np.exp(logits - logits.max(axis=1, keepdims=True))
+        a /= a.sum(axis=1, keepdims=True)
+        o = np.einsum("mt,mtd->md", a, Vc)                    # [m, D]
+        out = w @ o
+        do = w[:, None] * g[None, :]                          # [m, D]
+        ds = w * (o @ g - out @ g)                            # [m]
+        da = np.einsum("mtd,md->mt", Vc, do)                  # do_c . v_t
+        dlogit = a * (da - np.sum(a * da, axis=1, keepdims=True))
+        dq[r] = (np.einsum("mt,mtd->d", dlogit, Kc) + ds @ Lg[chunks]) * sig
+        gk = (dlogit + ds[:, None] / S)                       # [m, S]
+        np.add.at(dK, tok.reshape(-1), (gk.reshape(-1, 1) * q[r][None, :]) * sig)
+        np.add.at(dV, tok.reshape(-1), (a[:, :, None] * do[:, None, :]).reshape(-1, D))
+        np.add.at(abs_dK, tok.reshape(-1),
+                  ((np.abs(dlogit) + np.abs(ds)[:, None] / S).reshape(-1, 1) * np.abs(q[r])[None, :]) * sig)
+        np.add.at(abs_dV, tok.reshape(-1), (np.abs(a)[:, :, None] * np.abs(do)[:, None, :]).reshape(-1, D))
+    return BackwardResult(dq, dK, dV, abs_dK, abs_dV)
+
+
+def prefill_backward(Q, K, V, S: int, k: int, dtype: str, dOut, sel_idx=None):
+    """Gradients of the causal prefill with respect to Q [B,Hq,T,D] and K, V
+    [B,Hkv,T,D] for the upstream gradient dOut [B,Hq,T,D].  The selection is
+    the forward's (prefill) unless sel_idx [B,Hq,T,k'] is given.  Returns
+    (dQ, dK, dV, abs_dK, abs_dV)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    B, Hq, T, D = Q.shape
+    Hkv = K.shape[1]
+    L = landmarks(K, S, dtype)
+    if sel_idx is None:
+        _, sel_idx, _, _ = prefill(Q, K, V, S, k, dtype, L=L)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros(K.shape)
+    dV = np.zeros(V.shape)
+    aK = np.zeros(K.shape)
+    aV = np.zeros(V.shape)
+    pos = np.arange(T)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            r = hsa_rows_backward(Q[b, h], pos, K[b, g], V[b, g], L[b, g], S, sel_idx[b, h], dOut[b, h])
+            dQ[b, h] = r.dq
+            dK[b, g] += r.dK
+            dV[b, g] += r.dV
+            aK[b, g] += r.abs_dK
+            aV[b, g] += r.abs_dV
+    return dQ, dK, dV, aK, aV
 
 
 # ---------------------------------------------------------------------------
