@@ -508,6 +508,91 @@ def prefill_cpu_baseline(w, q, k, v, chunks=tuple(range(250, 4001, 250)), tau=No
                       f"host copies and oracle landmark build untimed"}
 
 
+# ---------------------------------------------------------------- backward
+def bench_backward(wname, steps, warmup, cpu_baseline):
+    import torch
+    import hierarchical_sparse_attention_hsa_amd as hsa
+    from hierarchical_sparse_attention_hsa_amd.workloads import WORKLOADS, prefill_inputs
+
+    w = WORKLOADS[wname]
+    Nc = w.T // w.S
+    t0 = time.perf_counter()
+    q, k, v = prefill_inputs(w, "cuda")
+    dout = torch.randn((w.B, w.Hq, w.T, w.D), dtype=torch.float32, device="cuda",
+                       generator=torch.Generator("cuda").manual_seed(w.seed + 100))
+    L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
+    hsa.hsa_build_landmarks(k, L, w.S)
+    sel = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.float32, device="cuda")
+    out = hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, sel_idx=sel, sel_score=sc)  # the forward, untimed
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"[{wname}] inputs and forward in {time.perf_counter() - t0:.1f} s")
+    dq = torch.empty_like(out)
+    dk = torch.empty((w.B, w.Hkv, w.T, w.D), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    dims = hsa.make_dims(w.B, w.Hq, w.Hkv, w.D, w.S, w.k, w.T, hsa.HSA_ATTN_BF16)
+    ws = torch.empty(hsa.hsa_attn_workspace_size(dims, 4), dtype=torch.uint8, device="cuda")
+
+    def step(ev):
+        if ev is not None:
+            hsa.hsa_attn_set_timing_events(ev)
+        hsa.hsa_backward_prefill(q, k, v, L, out, dout, sel, sc, w.S, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    names = ["bwd_zero", "bwd_prep", "bwd_scan", "bwd_scatter", "bwd_kt", "bwd_chunk", "bwd_dq"]
+    if w.T % w.S:
+        names.append("bwd_tail")
+    secs, per = timed_steps(step, steps, warmup, len(names), HipEvents())
+    ms_step = 1e3 * secs / steps
+    n_pairs = int((sel >= 0).sum().item())
+    # per kept pair: S = K q, dA = V do, dq = K^T dlogit, dV += a do, dK += dlogit q
+    flops = 10.0 * w.S * w.D * n_pairs
+    ci = names.index("bwd_chunk")
+    tf = flops / (per[ci] / 1e3) / 1e12
+    res = {
+        "workload": wname, "value": w.B * w.T / (ms_step / 1e3), "unit": "tokens/s", "ms_per_step": ms_step,
+        "kernel_ms": {n: float(x) for n, x in zip(names, per)},
+        "config": {"workload": wname, "batch": w.B, "seq_len": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "chunk": w.S, "top_k": w.k, "lowrank": w.lowrank},
+        "dtype": w.dtype,
+        "roofline": {"kernel": "bwd_chunk_kernel", "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                     "traffic": profiled_traffic(wname, "bwd_chunk_kernel"), "alg_flops_per_launch": flops},
+    }
+    log(f"[{wname}] {ms_step:.3f} ms/step, kernels {dict(zip(names, np.round(per, 4)))}, chunk kernel {tf:.1f} TFLOP/s")
+    if cpu_baseline:
+        res["cpu_baseline"] = backward_cpu_baseline(w, q, k, v, dout, sel)
+    del q, k, v, L, out, sel, sc, dq, dk, dv, ws, dout
+    torch.cuda.empty_cache()
+    return res
+
+
+def backward_cpu_baseline(w, q, k, v, dout, sel, chunks=(500, 1500, 2500, 3500)):
+    """The oracle's backward on a bounded sample: all heads of the query chunks
+    listed (64 tokens each), with the forward's selection; host copies and
+    the oracle's landmark build untimed."""
+    from oracle import hsa_oracle as O
+    G = w.Hq // w.Hkv
+    total = 0.0
+    for g in range(w.Hkv):
+        Kg = k[0, g].float().cpu().double().numpy()
+        Vg = v[0, g].float().cpu().double().numpy()
+        Lg = O.landmarks(Kg, w.S, w.dtype)
+        for c in chunks:
+            pos = np.arange(c * w.S, (c + 1) * w.S)
+            for hh in range(g * G, (g + 1) * G):
+                qq = q[0, hh, c * w.S:(c + 1) * w.S].float().cpu().double().numpy()
+                gg = dout[0, hh, c * w.S:(c + 1) * w.S].double().cpu().numpy()
+                ss = sel[0, hh, c * w.S:(c + 1) * w.S].cpu().numpy()
+                t0 = time.perf_counter()
+                O.hsa_rows_backward(qq, pos, Kg, Vg, Lg, w.S, ss, gg)
+                total += time.perf_counter() - t0
+    tokens = len(chunks) * w.S
+    return {"value": tokens / total, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"query chunks {list(chunks)} ({tokens} tokens, all {w.Hq} heads; {total:.1f} s timed); "
+                      f"forward selection from the layer, host copies and oracle landmark build untimed"}
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -553,6 +638,8 @@ def main():
         main_res = bench_decode("decode_1m_bf16", args.steps, args.warmup, cpu)
     elif "varlen" in args.workload:
         main_res = bench_decode_varlen(args.workload, args.steps, args.warmup)
+    elif args.workload.startswith("backward"):
+        main_res = bench_backward(args.workload, args.steps, args.warmup, cpu)
     elif args.workload.startswith("decode"):
         main_res = bench_decode(args.workload, args.steps, args.warmup, cpu)
     else:

@@ -26,7 +26,7 @@ __all__ = [
     "library_path", "load_library", "Dims", "HSAError", "EXPORTED_SYMBOLS",
     "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
     "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive", "hsa_append_kv",
-    "hsa_attn_set_timing_events", "hsa_attn_workspace_size",
+    "hsa_backward_prefill", "hsa_attn_set_timing_events", "hsa_attn_workspace_size",
     "hsa_attn_status_string", "hsa_attn_last_error", "landmarks_shape",
 ]
 
@@ -34,7 +34,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 EXPORTED_SYMBOLS = (
     "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
     "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive",
-    "hsa_append_kv", "hsa_attn_set_timing_events", "hsa_attn_workspace_size", "hsa_attn_status_string",
+    "hsa_append_kv", "hsa_backward_prefill", "hsa_attn_set_timing_events", "hsa_attn_workspace_size",
+    "hsa_attn_status_string",
     "hsa_attn_last_error",
 )
 
@@ -89,6 +90,7 @@ def load_library():
     lib.hsa_forward_prefill_cached.argtypes = [dims, I64, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_decode_adaptive.argtypes = [dims, ctypes.c_float, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_prefill_adaptive.argtypes = [dims, ctypes.c_float, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_backward_prefill.argtypes = [dims, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_append_kv.argtypes = [dims, P, P, P, P, P, P, P]
     lib.hsa_attn_workspace_size.argtypes = [dims, ctypes.c_int, ctypes.POINTER(SZ)]
     lib.hsa_attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
@@ -98,7 +100,7 @@ def load_library():
     lib.hsa_attn_last_error.restype = ctypes.c_char_p
     for f in ("hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
               "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive",
-              "hsa_append_kv", "hsa_attn_workspace_size", "hsa_attn_set_timing_events"):
+              "hsa_append_kv", "hsa_backward_prefill", "hsa_attn_workspace_size", "hsa_attn_set_timing_events"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -178,7 +180,7 @@ _EVENT_ARRAY = None
 
 def hsa_attn_workspace_size(dims: Dims, is_decode) -> int:
     """Workspace bytes; is_decode: False/0 prefill, True/1 decode, 2 adaptive-budget decode,
-    3 adaptive-budget prefill."""
+    3 adaptive-budget prefill, 4 prefill backward."""
     n = ctypes.c_size_t(0)
     _check(load_library().hsa_attn_workspace_size(ctypes.byref(dims), int(is_decode), ctypes.byref(n)),
            "hsa_attn_workspace_size")
@@ -317,6 +319,46 @@ def hsa_forward_prefill_adaptive(q, k, v, landmarks, chunk_size: int, top_k: int
         _stream(q.device))
     _check(st, "hsa_forward_prefill_adaptive")
     return out
+
+
+def hsa_backward_prefill(q, k, v, landmarks, out, dout, sel_idx, sel_score, chunk_size: int, dq=None, dk=None,
+                         dv=None, workspace=None):
+    """Gradients of the causal prefill: q [B,Hq,T,D], k/v [B,Hkv,T,D] (bf16),
+    the forward's out [B,Hq,T,D] fp32 and selection sel_idx/sel_score
+    [B,Hq,T,k], and the upstream gradient dout [B,Hq,T,D] fp32 ->
+    (dq [B,Hq,T,D], dk, dv [B,Hkv,T,D]) fp32."""
+    torch = _torch()
+    B, Hkv, T, D = k.shape
+    Hq = q.shape[1]
+    if v.shape != k.shape or v.dtype != k.dtype or q.dtype != k.dtype:
+        raise ValueError("q, k and v must share dtype; v must match k's shape")
+    if tuple(q.shape) != (B, Hq, T, D) or tuple(out.shape) != (B, Hq, T, D) or tuple(dout.shape) != (B, Hq, T, D):
+        raise ValueError("q, out and dout must be [B, Hq, T, D]")
+    if out.dtype != torch.float32 or dout.dtype != torch.float32:
+        raise ValueError("out and dout must be float32")
+    if tuple(landmarks.shape) != landmarks_shape(k.shape, chunk_size) or landmarks.dtype != k.dtype:
+        raise ValueError("landmarks must be [B, Hkv, T // chunk_size, D] with the dtype of k")
+    top_k = sel_idx.shape[-1]
+    if tuple(sel_idx.shape) != (B, Hq, T, top_k) or sel_score.shape != sel_idx.shape:
+        raise ValueError("sel_idx and sel_score must be [B, Hq, T, k]")
+    if sel_idx.dtype != torch.int32 or sel_score.dtype != torch.float32:
+        raise ValueError("sel_idx must be int32 and sel_score float32")
+    dims = make_dims(B, Hq, Hkv, D, chunk_size, top_k, T, _dtype_code(k))
+    if dq is None:
+        dq = torch.empty((B, Hq, T, D), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, Hkv, T, D), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, Hkv, T, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = hsa_attn_workspace_size(dims, 4)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = load_library().hsa_backward_prefill(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(landmarks), _ptr(out), _ptr(dout), _ptr(sel_idx),
+        _ptr(sel_score), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q.device))
+    _check(st, "hsa_backward_prefill")
+    return dq, dk, dv
 
 
 def hsa_append_kv(k_new, v_new, k_cache, v_cache, landmarks, cache_lens, chunk_size: int):

@@ -32,7 +32,7 @@ hsa_attn_status_t ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-enum class Call { kLandmarks, kPrefill, kDecode, kDecodeAdaptive, kPrefillAdaptive };
+enum class Call { kLandmarks, kPrefill, kDecode, kDecodeAdaptive, kPrefillAdaptive, kBackward };
 
 // Validates the dimension block and fills a Geometry.
 hsa_attn_status_t check_dims(const hsa_attn_dims_t* d, Call call, hsa_attn::Geometry* g) {
@@ -63,6 +63,10 @@ hsa_attn_status_t check_dims(const hsa_attn_dims_t* d, Call call, hsa_attn::Geom
   }
   if (call == Call::kDecodeAdaptive) call = Call::kDecode;
   if (call == Call::kPrefillAdaptive) call = Call::kPrefill;
+  if (call == Call::kBackward) {
+    if (d->dtype != HSA_ATTN_BF16) return fail(HSA_ATTN_UNSUPPORTED, "the backward pass supports bf16 storage only");
+    call = Call::kPrefill;
+  }
   const int64_t k_slots = (int64_t)d->top_k * (adaptive ? 2 : 1);
   const int64_t Nc = d->seq_len / d->chunk_size;
   if (call == Call::kPrefill) {
@@ -132,12 +136,17 @@ const char* hsa_attn_last_error(void) { return g_last_error; }
 hsa_attn_status_t hsa_attn_workspace_size(const hsa_attn_dims_t* d, int is_decode, size_t* bytes) {
   try {
     if (!bytes) return fail(HSA_ATTN_INVALID_ARGUMENT, "bytes is NULL");
-    if (is_decode < 0 || is_decode > 3) return fail(HSA_ATTN_INVALID_ARGUMENT, "kind must be 0, 1, 2 or 3");
+    if (is_decode < 0 || is_decode > 4) return fail(HSA_ATTN_INVALID_ARGUMENT, "kind must be 0 .. 4");
     hsa_attn::Geometry g;
-    static const Call kinds[4] = {Call::kPrefill, Call::kDecode, Call::kDecodeAdaptive, Call::kPrefillAdaptive};
+    static const Call kinds[5] = {Call::kPrefill, Call::kDecode, Call::kDecodeAdaptive, Call::kPrefillAdaptive,
+                                  Call::kBackward};
     const Call call = kinds[is_decode];
     const hsa_attn_status_t st = check_dims(d, call, &g);
     if (st != HSA_ATTN_OK) return st;
+    if (is_decode == 4) {
+      *bytes = hsa_attn::plan_backward(g).bytes;
+      return ok();
+    }
     // the size assumes the library keeps the selection itself (sel outputs NULL)
     const bool dec = is_decode == 1 || is_decode == 2;
     *bytes = dec ? hsa_attn::plan_decode(g, true).bytes : hsa_attn::plan_prefill(g, true).bytes;
@@ -244,6 +253,37 @@ hsa_attn_status_t hsa_forward_prefill_adaptive(const hsa_attn_dims_t* d, float g
     return fail(HSA_ATTN_INVALID_ARGUMENT, "gap_threshold must be >= 0 (or +inf), got %g", (double)gap_threshold);
   return forward_prefill(d, 0, q, k, v, landmarks, out, sel_idx, sel_score, workspace, workspace_bytes, stream,
                          gap_threshold);
+}
+
+hsa_attn_status_t hsa_backward_prefill(const hsa_attn_dims_t* d, const void* q, const void* k, const void* v,
+                                       const void* landmarks, const float* out, const float* dout,
+                                       const int32_t* sel_idx, const float* sel_score, float* dq, float* dk, float* dv,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    hsa_attn::Geometry g;
+    hsa_attn_status_t st = check_dims(d, Call::kBackward, &g);
+    if (st != HSA_ATTN_OK) return st;
+    if (!q || !k || !v || !out || !dout || !sel_idx || !sel_score || !dq || !dk || !dv || (!landmarks && g.Nc > 0))
+      return fail(HSA_ATTN_INVALID_ARGUMENT,
+                  "q, k, v, landmarks, out, dout, sel_idx, sel_score, dq, dk and dv must be non-NULL");
+    for (const void* p : {q, k, v, landmarks, (const void*)out, (const void*)dout, (const void*)sel_idx,
+                          (const void*)sel_score, (const void*)dq, (const void*)dk, (const void*)dv,
+                          (const void*)workspace})
+      if (p && !aligned16(p)) return fail(HSA_ATTN_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    const hsa_attn::BackwardPlan plan = hsa_attn::plan_backward(g);
+    if (workspace_bytes < plan.bytes)
+      return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes, workspace_bytes);
+    if (g.T == 0) return ok();
+    if (!workspace) return fail(HSA_ATTN_INVALID_ARGUMENT, "workspace is NULL");
+    restart_timing();
+    hsa_attn::BackwardArgs a{g,  q,  k,  v,  landmarks, out, dout, sel_idx, sel_score,
+                             dq, dk, dv, workspace};
+    return hip_status(hsa_attn::launch_backward(a, plan, static_cast<hipStream_t>(stream)), "backward launch");
+  } catch (const std::exception& e) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error");
+  }
 }
 
 static hsa_attn_status_t forward_decode(const hsa_attn_dims_t* d, const void* q, const void* k_cache,

@@ -95,4 +95,26 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 
+// shared by the forward and backward bucketing: p[0..n) = 0; off[0..n] =
+// exclusive prefix sum of cnt[0..n) (off[n] = total)
+hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t st);
+hipError_t launch_exclusive_scan(const int* cnt, int* off, int64_t n, hipStream_t st);
+
+// ---------------------------------------------------------------- backward
+struct BackwardPlan {
+  size_t off_kt, off_cnt, off_off, off_pair_pos, off_pairs, off_w, off_delta, off_dqp, bytes;
+};
+BackwardPlan plan_backward(const Geometry& g);
+
+struct BackwardArgs {
+  Geometry g;  // g.k = selection slots per row
+  const void *q, *k, *v, *lm;
+  const float *out, *dout;
+  const int32_t* sel_idx;
+  const float* sel_score;
+  float *dq, *dk, *dv;
+  void* ws;
+};
+hipError_t launch_backward(const BackwardArgs& a, const BackwardPlan& p, hipStream_t st);
+
 }  // namespace hsa_attn

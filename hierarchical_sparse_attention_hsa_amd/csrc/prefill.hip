@@ -78,6 +78,17 @@ __global__ void prefill_scatter_kernel(const int32_t* __restrict__ sel_idx, cons
 }
 
 
+hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
+                     st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_exclusive_scan(const int* cnt, int* off, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, cnt, off, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_zero_counts(const PrefillArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
   const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;

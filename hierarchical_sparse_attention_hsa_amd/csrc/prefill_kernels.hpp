@@ -625,7 +625,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 // x = head + tail with head = x truncated to bf16 and tail = the exact
-// remainder rounded to bf16 (relative error of head + tail below 2^-16)
+// remainder rounded to bf16 (relative error of head + tail below 2^-15)
 __device__ __forceinline__ void split_bf16(const float (&x)[8], Frag<BF16>& head, Frag<BF16>& tail) {
   u32x4 hw, tw;
 #pragma unroll

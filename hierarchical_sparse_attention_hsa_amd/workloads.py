@@ -22,6 +22,8 @@ Workloads (all with chunk size 64):
   prefill_256k_adaptive_bf16  prefill_256k_bf16's inputs with the near-tie
                      adaptive budget, base k=16 (2k=32), gap threshold 1e-2
                      (about the 0.25 quantile of the rows' 16th vs 17th gaps)
+  backward_256k_bf16  the backward pass of prefill_256k_bf16 (its inputs,
+                     selection and output; dOut ~ N(0, 1) fp32, seed 4100)
   prefill_256k_chunk_bf16  the last 65536 tokens of prefill_256k_bf16 over
                      its cached first 196608 tokens
 
@@ -84,6 +86,8 @@ WORKLOADS = {
         # 32); the gap threshold doubles about a quarter of the rows here
         Workload("prefill_256k_adaptive_bf16", "prefill", 1, 32, 8, 262144, 128, 64, 16, "bf16", 4000, lowrank=8,
                  extra={"gap_threshold": 1e-2}),
+        # backward pass of prefill_256k (same inputs; dOut seeded N(0, 1))
+        Workload("backward_256k_bf16", "backward", 1, 32, 8, 262144, 128, 64, 16, "bf16", 4000, lowrank=8),
         # chunked prefill: the last 64K tokens of the 256K sequence after a
         # cached prefix of 192K tokens (same inputs as prefill_256k_bf16)
         Workload("prefill_256k_chunk_bf16", "prefill", 1, 32, 8, 262144, 128, 64, 16, "bf16", 4000, lowrank=8,

@@ -147,6 +147,33 @@ hsa_attn_status_t hsa_forward_prefill_adaptive(const hsa_attn_dims_t* d, float g
                                                size_t workspace_bytes, void* stream);
 
 /*
+ * Backward pass of the causal prefill (training; the chain rule through the
+ * steps of the card's "Core Technique" and "Implementation"): given the
+ * forward's inputs, its output `out` [B,Hq,T,D] fp32, its selection sel_idx /
+ * sel_score [B,Hq,T,k] (k = d->top_k slots, -1 / -inf padding, as written by
+ * hsa_forward_prefill or hsa_forward_prefill_adaptive with k = its slot
+ * count) and the upstream gradient dout [B,Hq,T,D] fp32, writes
+ * dq [B,Hq,T,D] and dk, dv [B,Hkv,T,D] (fp32, every element).  The selection
+ * is held fixed (it is piecewise constant in the inputs) and the landmark's
+ * rounding to the storage dtype is taken as the identity, so each key of a
+ * kept chunk receives 1/S of the chunk's landmark gradient.  Slots whose
+ * index is not a candidate of the row (outside [0, floor(p/S))) are ignored.
+ * Storage dtype bf16 only (HSA_ATTN_UNSUPPORTED otherwise); products run on
+ * bf16 MFMA with fp32 accumulation: the gradients that feed dq are split
+ * into a bf16 head and tail (relative error below 2^-15), the
+ * probabilities and gradients that feed dk and dv are rounded to bf16
+ * (2^-8).  dk and dv accumulate over pairs in an order that depends
+ * on scheduling, so they are not bit-reproducible.
+ * workspace: at least hsa_attn_workspace_size(d, 4) bytes (about
+ * B*Hq*T*k*(4*D + 12) bytes plus a transposed copy of K: 69 GB at B=1,
+ * Hq=32, T=2^18, k=16, D=128).
+ */
+hsa_attn_status_t hsa_backward_prefill(const hsa_attn_dims_t* d, const void* q, const void* k, const void* v,
+                                       const void* landmarks, const float* out, const float* dout,
+                                       const int32_t* sel_idx, const float* sel_score, float* dq, float* dk, float* dv,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * HSA forward for B independent single-token queries, each after its own
  * cache of T tokens (card, "Core Technique": scoring is O(n/S) per query and
  * attention O(k*S)).  The query sits at position T, so its candidates are
@@ -225,15 +252,18 @@ hsa_attn_status_t hsa_append_kv(const hsa_attn_dims_t* d, const void* k_new, con
  * V transpose, scan, scatter, remote attention, local attention (for T < S:
  * select, local attention); decode and varlen decode: scan, merge,
  * attention, fusion, for adaptive decode too (scan and attention are skipped when the cache capacity
- * holds no complete chunk); append: 1 kernel.  events == NULL or
+ * holds no complete chunk); append: 1 kernel; backward: zero counts, row
+ * preparation, scan, scatter, K transpose, chunk gradients, dq (scan,
+ * scatter, K transpose and chunk gradients only when T >= S), then zeros
+ * for the tokens after the last complete chunk when T is not a multiple of S.  events == NULL or
  * n_pairs == 0 turns recording off.  The setting is thread-local; the events stay owned by the
  * caller and must outlive the calls that record them.
  */
 hsa_attn_status_t hsa_attn_set_timing_events(void** events, int n_pairs);
 
-/* Bytes of device workspace a forward call needs (is_decode: 0 prefill and
- * cached prefill, 1 decode and varlen decode, 2 adaptive-budget decode,
- * 3 adaptive-budget prefill). */
+/* Bytes of device workspace a call needs (is_decode: 0 prefill and cached
+ * prefill, 1 decode and varlen decode, 2 adaptive-budget decode,
+ * 3 adaptive-budget prefill, 4 prefill backward). */
 hsa_attn_status_t hsa_attn_workspace_size(const hsa_attn_dims_t* d, int is_decode, size_t* bytes);
 
 /* Static description of a status code. */

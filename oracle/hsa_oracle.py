@@ -384,9 +384,12 @@ class BackwardResult:
     dK: np.ndarray    # [T, D]
     dV: np.ndarray    # [T, D]
     # element-wise error scales of a lower-precision evaluation: sums of the
-    # magnitudes of the terms each gradient entry adds up
+    # magnitudes of the terms each gradient entry adds up, every dot product
+    # inside (da, u, delta) taken over absolute values, so that the scales
+    # also bound the cancellation errors of dlogit and ds
     abs_dK: np.ndarray
     abs_dV: np.ndarray
+    abs_dq: np.ndarray
 
 
 def hsa_rows_backward(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.ndarray, Lg: np.ndarray,
@@ -413,7 +416,10 @@ def hsa_rows_backward(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.nda
     q: [R, D] rows at positions pos; Kg, Vg: [T, D]; Lg: landmarks; sel: one
     index list per row (its kept chunks); dout: [R, D].  Returns dq [R, D] and
     the rows' contributions dK, dV [T, D], plus the magnitude sums
-    abs_dV = sum |a_ct| |do_c| and abs_dK = sum (|dlogit_ct| + |ds_c| / S) |q| / sqrt(D).
+    abs_dV = sum a_ct |do_c|,
+    abs_dK = sum (a_ct (A_ct + U_c) + (U_c + w_c E) / S) |q| / sqrt(D),
+    abs_dq = (sum a_ct (A_ct + U_c) |k_t| + sum (U_c + w_c E) |L_c|) / sqrt(D)
+    with A_ct = |do_c| . |v_t|, U_c = sum_t a_ct A_ct and E = |g| . |out|.
     """
     q = np.asarray(q, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
@@ -425,6 +431,7 @@ def hsa_rows_backward(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.nda
     dV = np.zeros((T, D))
     abs_dK = np.zeros((T, D))
     abs_dV = np.zeros((T, D))
+    abs_dq = np.zeros((R, D))
     for r in range(R):
         chunks = np.asarray(sel[r], dtype=np.int64)
         chunks = chunks[chunks >= 0]
@@ -447,19 +454,24 @@ def hsa_rows_backward(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.nda
         dlogit = a * (da - np.sum(a * da, axis=1, keepdims=True))
         dq[r] = (np.einsum("mt,mtd->d", dlogit, Kc) + ds @ Lg[chunks]) * sig
         gk = (dlogit + ds[:, None] / S)                       # [m, S]
-        np.add.at(dK, tok.reshape(-1), (gk.reshape(-1, 1) * q[r][None, :]) * sig)
-        np.add.at(dV, tok.reshape(-1), (a[:, :, None] * do[:, None, :]).reshape(-1, D))
-        np.add.at(abs_dK, tok.reshape(-1),
-                  ((np.abs(dlogit) + np.abs(ds)[:, None] / S).reshape(-1, 1) * np.abs(q[r])[None, :]) * sig)
-        np.add.at(abs_dV, tok.reshape(-1), (np.abs(a)[:, :, None] * np.abs(do)[:, None, :]).reshape(-1, D))
-    return BackwardResult(dq, dK, dV, abs_dK, abs_dV)
+        ti = tok.reshape(-1)  # distinct tokens (the kept chunks are distinct)
+        dK[ti] += (gk.reshape(-1, 1) * q[r][None, :]) * sig
+        dV[ti] += (a[:, :, None] * do[:, None, :]).reshape(-1, D)
+        A = np.einsum("mtd,md->mt", np.abs(Vc), np.abs(do))  # >= |da|
+        U = np.sum(a * A, axis=1)                             # >= |u|
+        mag_l = a * (A + U[:, None])                          # >= |dlogit|
+        mag_s = U + w * (np.abs(out) @ np.abs(g))             # >= |ds|
+        abs_dK[ti] += ((mag_l + mag_s[:, None] / S).reshape(-1, 1) * np.abs(q[r])[None, :]) * sig
+        abs_dV[ti] += (a[:, :, None] * np.abs(do)[:, None, :]).reshape(-1, D)
+        abs_dq[r] = (np.einsum("mt,mtd->d", mag_l, np.abs(Kc)) + mag_s @ np.abs(Lg[chunks])) * sig
+    return BackwardResult(dq, dK, dV, abs_dK, abs_dV, abs_dq)
 
 
 def prefill_backward(Q, K, V, S: int, k: int, dtype: str, dOut, sel_idx=None):
     """Gradients of the causal prefill with respect to Q [B,Hq,T,D] and K, V
     [B,Hkv,T,D] for the upstream gradient dOut [B,Hq,T,D].  The selection is
     the forward's (prefill) unless sel_idx [B,Hq,T,k'] is given.  Returns
-    (dQ, dK, dV, abs_dK, abs_dV)."""
+    (dQ, dK, dV, abs_dK, abs_dV, abs_dQ)."""
     Q = np.asarray(Q, dtype=np.float64)
     B, Hq, T, D = Q.shape
     Hkv = K.shape[1]
@@ -471,6 +483,7 @@ def prefill_backward(Q, K, V, S: int, k: int, dtype: str, dOut, sel_idx=None):
     dV = np.zeros(V.shape)
     aK = np.zeros(K.shape)
     aV = np.zeros(V.shape)
+    aQ = np.zeros_like(Q)
     pos = np.arange(T)
     for b in range(B):
         for h in range(Hq):
@@ -481,7 +494,8 @@ def prefill_backward(Q, K, V, S: int, k: int, dtype: str, dOut, sel_idx=None):
             dV[b, g] += r.dV
             aK[b, g] += r.abs_dK
             aV[b, g] += r.abs_dV
-    return dQ, dK, dV, aK, aV
+            aQ[b, h] = r.abs_dq
+    return dQ, dK, dV, aK, aV, aQ
 
 
 # ---------------------------------------------------------------------------

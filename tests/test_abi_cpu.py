@@ -167,7 +167,7 @@ def test_adaptive_decode_validation():
     assert hsa.hsa_attn_workspace_size(d, 2) == hsa.hsa_attn_workspace_size(dims(top_k=32, seq_len=1 << 20), 1)
     assert hsa.hsa_attn_workspace_size(dims(top_k=32), 2) > hsa.hsa_attn_workspace_size(dims(top_k=32), 1)
     n = ctypes.c_size_t(0)
-    assert lib.hsa_attn_workspace_size(ctypes.byref(d), 4, ctypes.byref(n)) == hsa.HSA_ATTN_INVALID_ARGUMENT
+    assert lib.hsa_attn_workspace_size(ctypes.byref(d), 5, ctypes.byref(n)) == hsa.HSA_ATTN_INVALID_ARGUMENT
 
 
 def test_adaptive_prefill_validation():
@@ -183,3 +183,27 @@ def test_adaptive_prefill_validation():
     assert call(dims(), 0.1, ws=16) == hsa.HSA_ATTN_WORKSPACE_TOO_SMALL
     d = dims(top_k=16, seq_len=1 << 15)
     assert hsa.hsa_attn_workspace_size(d, 3) == hsa.hsa_attn_workspace_size(dims(top_k=32, seq_len=1 << 15), 0)
+
+
+def test_backward_validation():
+    lib = hsa.load_library()
+    p = ctypes.c_void_p(0x1000)
+
+    def call(d, ws=1 << 40, **null):
+        args = [p] * 11
+        for i in null.get("null", []):
+            args[i] = None
+        return lib.hsa_backward_prefill(ctypes.byref(d), *args, p, ws, None)
+
+    assert call(dims(dtype=hsa.HSA_ATTN_FP32)) == hsa.HSA_ATTN_UNSUPPORTED  # bf16 only
+    assert call(dims(top_k=33)) == hsa.HSA_ATTN_UNSUPPORTED
+    for i in range(11):  # q k v landmarks out dout sel_idx sel_score dq dk dv
+        assert call(dims(), null=[i]) == hsa.HSA_ATTN_INVALID_ARGUMENT, i
+    assert call(dims(), ws=16) == hsa.HSA_ATTN_WORKSPACE_TOO_SMALL
+    assert lib.hsa_backward_prefill(ctypes.byref(dims()), *([ctypes.c_void_p(0x1008)] + [p] * 10), p, 1 << 40,
+                                    None) == hsa.HSA_ATTN_INVALID_ARGUMENT  # misaligned
+    # workspace: pairs * (4 D + 12) + rows * 4 + transposed K + bucket tables
+    d = dims(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, top_k=16, seq_len=1 << 18)
+    pairs = 32 * (1 << 18) * 16
+    need = hsa.hsa_attn_workspace_size(d, 4)
+    assert pairs * (4 * 128 + 12) < need < pairs * (4 * 128 + 12) + (1 << 30) + 8 * 4096 * 64 * 128 * 2

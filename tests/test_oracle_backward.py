@@ -41,7 +41,7 @@ def forward_fixed(Q, K, V, S, sel, dtype="fp64"):
 
 def finite_difference_check(Q, K, V, S, k, G, eps=1e-6, rtol=2e-6):
     _, sel, _, _ = O.prefill(Q, K, V, S, k, "fp64")
-    dQ, dK, dV, _, _ = O.prefill_backward(Q, K, V, S, k, "fp64", G, sel_idx=sel)
+    dQ, dK, dV, _, _, _ = O.prefill_backward(Q, K, V, S, k, "fp64", G, sel_idx=sel)
 
     def loss(Q_, K_, V_):
         return float(np.sum(G * forward_fixed(Q_, K_, V_, S, sel)))
@@ -85,7 +85,7 @@ def test_chunk1_dense_causal_gradients():
     T, D = 24, 6
     Q, K, V = rand_qkv(70, 1, 1, 1, T, D, "fp32")
     G = np.random.default_rng(71).standard_normal(Q.shape)
-    dQ, dK, dV, _, _ = O.prefill_backward(Q, K, V, 1, T + 3, "fp64", G)
+    dQ, dK, dV, _, _, _ = O.prefill_backward(Q, K, V, 1, T + 3, "fp64", G)
     mask = np.tril(np.ones((T, T), dtype=bool), k=-1)[1:]
     rq, rk, rv = torch_attention_grads(Q[0, 0, 1:], K[0, 0], V[0, 0], mask, G[0, 0, 1:])
     np.testing.assert_allclose(dQ[0, 0, 1:], rq, rtol=0, atol=1e-12)
@@ -99,7 +99,7 @@ def test_chunk1_sparse_gradients_are_masked_attention():
     Q, K, V = rand_qkv(72, 1, 1, 1, T, D, "fp32")
     G = np.random.default_rng(73).standard_normal(Q.shape)
     _, sel, _, _ = O.prefill(Q, K, V, 1, k, "fp64")
-    dQ, dK, dV, _, _ = O.prefill_backward(Q, K, V, 1, k, "fp64", G, sel_idx=sel)
+    dQ, dK, dV, _, _, _ = O.prefill_backward(Q, K, V, 1, k, "fp64", G, sel_idx=sel)
     mask = np.zeros((T, T), dtype=bool)
     for t in range(T):
         mask[t, [c for c in sel[0, 0, t] if c >= 0]] = True
@@ -115,7 +115,7 @@ def test_two_chunk_gradients_are_plain_attention_over_chunk0(S):
     D = 5
     Q, K, V = rand_qkv(74 + S, 1, 1, 1, 2 * S, D, "bf16")
     G = np.random.default_rng(75).standard_normal(Q.shape)
-    dQ, dK, dV, _, _ = O.prefill_backward(Q, K, V, S, 3, "bf16", G)
+    dQ, dK, dV, _, _, _ = O.prefill_backward(Q, K, V, S, 3, "bf16", G)
     rq, rk, rv = torch_attention_grads(Q[0, 0, S:], K[0, 0, :S], V[0, 0, :S], np.ones((S, S), dtype=bool),
                                        G[0, 0, S:])
     np.testing.assert_allclose(dQ[0, 0, S:], rq, rtol=0, atol=1e-12)
