@@ -27,10 +27,12 @@
 namespace hsa_attn {
 
 // ---------------------------------------------------------------- 1. rows
-// 16 lanes per row, 16 consecutive rows of the [B, Hq, T] order per
-// workgroup.  The workgroup groups its kept pairs by bucket in an LDS hash
-// table first, so each distinct bucket costs one global atomic; pair_pos
-// gets each pair's position inside its bucket (-1: no pair).
+// 16 lanes per row; a workgroup takes 64 consecutive rows of the [B, Hq, T]
+// order, 16 at a time (all loads issued first).  The workgroup groups its
+// kept pairs by bucket in an LDS hash table, so each distinct bucket costs
+// one global atomic; pair_pos gets each pair's position inside its bucket
+// (-1: no pair).
+constexpr int kPrepRows = 64;
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ out, const float* __restrict__ dout,
                                                        const int32_t* __restrict__ sel_idx,
@@ -38,70 +40,88 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
                                                        float* __restrict__ delta, int* __restrict__ cnt,
                                                        int32_t* __restrict__ pair_pos, int64_t rows, int Hq, int G,
                                                        int64_t T_len, int64_t Nc, int k) {
-  constexpr int HASH = 1024;  // >= 16 rows x 32 slots
+  constexpr int SUB = kPrepRows / 16;    // rows per thread group of 16 lanes
+  constexpr int HASH = 4096;             // >= 64 rows x 32 slots
+  constexpr int DV = D / 64;             // float4 loads per lane and row
   __shared__ int hkey[HASH];
   __shared__ int hcnt[HASH];
   const int tid = threadIdx.x, j = tid & 15;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
-  const bool rok = row < rows;
   for (int i = tid; i < HASH; i += 256) {
     hkey[i] = -1;
     hcnt[i] = 0;
   }
-  // delta = dout . out
-  float acc = 0.0f;
-  if (rok) {
-    for (int d = 4 * j; d < D; d += 64) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(out + row * D + d);
-      const f32x4 y = *reinterpret_cast<const f32x4*>(dout + row * D + d);
-      acc = fmaf(x[0], y[0], fmaf(x[1], y[1], fmaf(x[2], y[2], fmaf(x[3], y[3], acc))));
+  int64_t row[SUB];
+  bool rok[SUB];
+  f32x4 xo[SUB][DV], xg[SUB][DV];
+  int cc[SUB][2];
+  float s[SUB][2];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+    row[u] = (int64_t)blockIdx.x * kPrepRows + 16 * u + (tid >> 4);
+    rok[u] = row[u] < rows;
+#pragma unroll
+    for (int x = 0; x < DV; ++x) {
+      const int d = 4 * j + 64 * x;
+      const f32x4 z{0.f, 0.f, 0.f, 0.f};
+      xo[u][x] = rok[u] ? *reinterpret_cast<const f32x4*>(out + row[u] * D + d) : z;
+      xg[u][x] = rok[u] ? *reinterpret_cast<const f32x4*>(dout + row[u] * D + d) : z;
+    }
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int e = j + 16 * v;
+      const bool inl = rok[u] && e < k;
+      cc[u][v] = inl ? sel_idx[row[u] * k + e] : -1;
+      s[u][v] = inl ? sel_score[row[u] * k + e] : -__builtin_inff();
     }
   }
-  acc = group_sum<16>(acc);
-  if (rok && j == 0) delta[row] = acc;
-
-  // fusion weights: softmax over the row's kept scores (slots j and j + 16)
-  const int64_t t = rok ? row % T_len : 0;
-  const int64_t bh = rok ? row / T_len : 0;
-  const int h = (int)(bh % Hq);
-  const int64_t b = bh / Hq;
-  const int64_t n = min(t / kChunk, Nc);
-  float s[2];
-  int cc[2];
-  bool v[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = j + 16 * u;
-    const bool inl = rok && e < k;
-    cc[u] = inl ? sel_idx[row * k + e] : -1;
-    v[u] = inl && cc[u] >= 0 && cc[u] < n;
-    s[u] = v[u] ? sel_score[row * k + e] : -__builtin_inff();
-  }
-  const float mx = group_max<16>(fmaxf(s[0], s[1]));
-  float ex[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) ex[u] = v[u] ? expf(s[u] - mx) : 0.0f;
-  const float den = group_sum<16>(ex[0] + ex[1]);
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = j + 16 * u;
-    if (rok && e < k) wts[row * k + e] = v[u] ? ex[u] / den : 0.0f;
-  }
-
-  // bucketing
   __syncthreads();  // the hash table is cleared
-  uint32_t slot_rank[2] = {~0u, ~0u};
+  uint32_t slot_rank[SUB][2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    if (!v[u]) continue;
-    const int key = (int)(((b * (Hq / G) + h / G) * Nc) + cc[u]);
-    int sl = (int)(((uint32_t)key * 2654435761u) >> 8) & (HASH - 1);
-    while (true) {
-      const int prev = atomicCAS(&hkey[sl], -1, key);
-      if (prev == -1 || prev == key) break;
-      sl = (sl + 1) & (HASH - 1);
+  for (int u = 0; u < SUB; ++u) {
+    // delta = dout . out
+    float acc = 0.0f;
+#pragma unroll
+    for (int x = 0; x < DV; ++x)
+      acc = fmaf(xo[u][x][0], xg[u][x][0],
+                 fmaf(xo[u][x][1], xg[u][x][1], fmaf(xo[u][x][2], xg[u][x][2], fmaf(xo[u][x][3], xg[u][x][3], acc))));
+    acc = group_sum<16>(acc);
+    if (rok[u] && j == 0) delta[row[u]] = acc;
+    // fusion weights: softmax over the row's kept (and valid) scores
+    const int64_t t = rok[u] ? row[u] % T_len : 0;
+    const int64_t bh = rok[u] ? row[u] / T_len : 0;
+    const int h = (int)(bh % Hq);
+    const int64_t b = bh / Hq;
+    const int64_t n = min(t / kChunk, Nc);
+    bool v[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      v[x] = cc[u][x] >= 0 && cc[u][x] < n;
+      if (!v[x]) s[u][x] = -__builtin_inff();
     }
-    slot_rank[u] = ((uint32_t)sl << 16) | (uint32_t)atomicAdd(&hcnt[sl], 1);
+    const float mx = group_max<16>(fmaxf(s[u][0], s[u][1]));
+    float ex[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) ex[x] = v[x] ? expf(s[u][x] - mx) : 0.0f;
+    const float den = group_sum<16>(ex[0] + ex[1]);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int e = j + 16 * x;
+      if (rok[u] && e < k) wts[row[u] * k + e] = v[x] ? ex[x] / den : 0.0f;
+    }
+    // group the pairs by bucket
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      slot_rank[u][x] = ~0u;
+      if (!v[x]) continue;
+      const int key = (int)(((b * (Hq / G) + h / G) * Nc) + cc[u][x]);
+      int sl = (int)(((uint32_t)key * 2654435761u) >> 8) & (HASH - 1);
+      while (true) {
+        const int prev = atomicCAS(&hkey[sl], -1, key);
+        if (prev == -1 || prev == key) break;
+        sl = (sl + 1) & (HASH - 1);
+      }
+      slot_rank[u][x] = ((uint32_t)sl << 16) | (uint32_t)atomicAdd(&hcnt[sl], 1);
+    }
   }
   __syncthreads();
   for (int i = tid; i < HASH; i += 256) {
@@ -110,13 +130,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
   }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = j + 16 * u;
-    if (rok && e < k) {
-      const uint32_t sr = slot_rank[u];
-      pair_pos[row * k + e] = sr == ~0u ? -1 : hcnt[sr >> 16] + (int)(sr & 0xffffu);
+  for (int u = 0; u < SUB; ++u)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int e = j + 16 * x;
+      if (rok[u] && e < k) {
+        const uint32_t sr = slot_rank[u][x];
+        pair_pos[row[u] * k + e] = sr == ~0u ? -1 : hcnt[sr >> 16] + (int)(sr & 0xffffu);
+      }
     }
-  }
 }
 
 // pairs[off[bucket] + pair_pos[i]] = i (the pair id: row * k + slot)
@@ -499,7 +521,8 @@ static hipError_t launch_backward_d(const BackwardArgs& a, const BackwardPlan& p
   if (nb > 0 && (e = launch_zero_ints(cnt, nb, st)) != hipSuccess) return e;
   mark_launch(st);
   mark_launch(st);
-  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, a.out, a.dout,
+  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + kPrepRows - 1) / kPrepRows)), dim3(256), 0, st,
+                     a.out, a.dout,
                      a.sel_idx, a.sel_score, wts, delta, cnt, pair_pos, rows, g.Hq, g.G, g.T, g.Nc, g.k);
   mark_launch(st);
   if (nb > 0) {
