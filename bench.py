@@ -240,11 +240,10 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
     secs, per = timed_steps(step, steps, warmup, 4, HipEvents())
     ms_step = 1e3 * secs / steps
     # distinct selected (b, g, chunk) tiles
-    s = sel.view(w.B, w.Hkv, G * kk).cpu().numpy()
-    distinct = sum(len(set(s[b, g][s[b, g] >= 0].tolist())) for b in range(w.B) for g in range(w.Hkv))
-    tile_bytes = 2 * w.S * w.D * esz
-    alg_bytes = lm_bytes + distinct * tile_bytes
+    attn_bytes = distinct_tile_bytes(sel, w)
+    alg_bytes = lm_bytes + attn_bytes
     names = ["decode_scan", "decode_merge", "decode_attn", "decode_fuse"]
+    dom, other = decode_roofline(wname, per[0], lm_bytes, per[2], attn_bytes)
     res = {
         "workload": wname, "value": w.B / (ms_step / 1e3), "unit": "queries/s", "ms_per_step": ms_step,
         "kernel_ms": {n: float(x) for n, x in zip(names, per)},
@@ -252,11 +251,8 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
         "config": {"workload": wname, "batch_queries": w.B, "cache_tokens": w.T, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.D, "chunk": w.S, "top_k": w.k, "needles": w.needles},
         "dtype": w.dtype,
-        "roofline": {"kernel": "decode_scan_kernel", "bound": "hbm",
-                     "achieved": lm_bytes / (per[0] / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": lm_bytes / (per[0] / 1e3) / 1e9 / PEAK_HBM_GBS,
-                     "traffic": profiled_traffic(wname, "decode_scan_kernel"),
-                     "alg_bytes_per_launch": lm_bytes},
+        "roofline": dom,
+        "roofline_other": other,
     }
     if adaptive:
         res["gap_threshold"] = tau
@@ -274,7 +270,8 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
             tot += len(nd)
     res["needle_recall"] = hit / max(tot, 1)
     log(f"[{wname}] {ms_step:.3f} ms/step, kernels {dict(zip(names, np.round(per, 4)))}, "
-        f"scan {res['roofline']['achieved']:.0f} GB/s, needle recall {res['needle_recall']:.4f}")
+        f"{dom['kernel']} {dom['achieved']:.0f} GB/s, {other['kernel']} {other['achieved']:.0f} GB/s, "
+        f"needle recall {res['needle_recall']:.4f}")
     if cpu_baseline:
         res["cpu_baseline"] = decode_cpu_baseline(w, q, k, v, tau=tau)
     del q, k, v, L, out, sel, sc, ws
@@ -329,6 +326,7 @@ def bench_decode_varlen(wname, steps, warmup):
     mid = ln - steps // 2
     lm_bytes = float(np.sum(mid // w.S)) * w.Hkv * w.D * esz
     names = ["decode_scan", "decode_merge", "decode_attn", "decode_fuse", "append_kv"]
+    dom, other = decode_roofline(wname, per[0], lm_bytes, per[2], distinct_tile_bytes(sel, w))
     res = {
         "workload": wname, "value": w.B / (ms_step / 1e3), "unit": "queries/s", "ms_per_step": ms_step,
         "kernel_ms": {n: float(x) for n, x in zip(names, per)},
@@ -336,16 +334,40 @@ def bench_decode_varlen(wname, steps, warmup):
                    "cache_tokens": [int(lens0.min()), int(lens0.max())], "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "chunk": w.S, "top_k": w.k, "needles": w.needles},
         "dtype": w.dtype,
-        "roofline": {"kernel": "decode_scan_kernel", "bound": "hbm",
-                     "achieved": lm_bytes / (per[0] / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": lm_bytes / (per[0] / 1e3) / 1e9 / PEAK_HBM_GBS,
-                     "traffic": profiled_traffic(wname, "decode_scan_kernel"), "alg_bytes_per_launch": lm_bytes},
+        "roofline": dom,
+        "roofline_other": other,
     }
     log(f"[{wname}] {ms_step:.3f} ms/step, kernels {dict(zip(names, np.round(per, 4)))}, "
-        f"scan {res['roofline']['achieved']:.0f} GB/s")
+        f"{dom['kernel']} {dom['achieved']:.0f} GB/s, {other['kernel']} {other['achieved']:.0f} GB/s")
     del q, k, v, L, out, sel, sc, ws
     torch.cuda.empty_cache()
     return res
+
+
+def decode_roofline(wname, per_scan_ms, lm_bytes, per_attn_ms, attn_bytes):
+    """Roofline of the dominant decode kernel (the longer of the landmark scan
+    and the chunk attention, both HBM-bound) with the other one beside it.
+    Algorithmic bytes: the landmarks the scan reads; the distinct selected
+    K/V tiles the attention reads."""
+    kern = {"decode_scan_kernel": (per_scan_ms, lm_bytes), "decode_attn_kernel": (per_attn_ms, attn_bytes)}
+    out = {}
+    for name, (ms, nbytes) in kern.items():
+        gbs = nbytes / (ms / 1e3) / 1e9
+        out[name] = {"kernel": name, "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": profiled_traffic(wname, name),
+                     "alg_bytes_per_launch": nbytes, "ms": ms}
+    dom = max(kern, key=lambda n: kern[n][0])
+    other = [n for n in kern if n != dom][0]
+    return out[dom], out[other]
+
+
+def distinct_tile_bytes(sel, w):
+    """K and V bytes of the distinct (b, g, chunk) tiles the heads selected."""
+    G = w.Hq // w.Hkv
+    kk = sel.shape[-1]
+    s = sel.view(w.B, w.Hkv, G * kk).cpu().numpy()
+    distinct = sum(len(set(s[b, g][s[b, g] >= 0].tolist())) for b in range(w.B) for g in range(w.Hkv))
+    return distinct * 2 * w.S * w.D * (2 if w.dtype == "bf16" else 4)
 
 
 def decode_cpu_baseline(w, q, k, v, queries=(0, 37), min_seconds=10.0, tau=None):
@@ -652,8 +674,8 @@ def main():
     }
     if "cpu_baseline" in main_res:
         line["cpu_baseline"] = main_res["cpu_baseline"]
-    for key in ("kernel_ms", "step_alg_GBps", "needle_recall", "gap_threshold", "doubled_head_frac",
-                "doubled_row_frac"):
+    for key in ("roofline_other", "kernel_ms", "step_alg_GBps", "needle_recall", "gap_threshold",
+                "doubled_head_frac", "doubled_row_frac"):
         if key in main_res:
             line[key] = main_res[key]
     if "prefill" in results:

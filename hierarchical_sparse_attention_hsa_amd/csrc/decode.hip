@@ -479,7 +479,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const typename T::stor
   constexpr int LPR = D / EPS;                 // lanes per V row
   constexpr int RPI = kWave / LPR;             // V rows per load instruction
   constexpr int VL = S / RPI;                  // V loads per lane (whole tile)
-  constexpr int VPASS = VL > 16 ? 2 : 1;       // fp32 D=128 loads V in two passes
+  // more than 8 V loads per lane go in two passes (fewer live registers: 3
+  // waves per SIMD instead of 2 for bf16 at D = 128)
+  constexpr int VPASS = VL > 8 ? 2 : 1;
   constexpr int VLP = VL / VPASS;
   __shared__ __align__(16) float pbuf[4][S][G];  // per wave: probability of (token, head)
   const int b = blockIdx.z, g = blockIdx.y;
