@@ -636,8 +636,8 @@ def main():
         summarize_profile(args.workload, args.summarize_profile, args.profile_command, args.profile_kernel)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this layer is measured on one GPU; the multi-GPU sharding is a design only "
-              "(see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py: this layer is measured on one GPU; its multi-GPU sharding is a design only, not "
+              "built. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

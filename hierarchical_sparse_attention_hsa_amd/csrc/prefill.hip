@@ -146,8 +146,10 @@ size_t prefill_local_lds_bytes(const Geometry& g, int nbuf) {
   return (size_t)nbuf * 2 * kChunk * g.D * esz + (size_t)32 * g.G * g.k * 8;
 }
 
-// two chunk images when they fit next to the tables in the 160 KiB of LDS
-int prefill_local_buffers(const Geometry& g) { return prefill_local_lds_bytes(g, 2) <= 160 * 1024 ? 2 : 1; }
+// two chunk images when two such workgroups still fit in the 160 KiB of LDS
+// of a CU; otherwise one image, which keeps two workgroups per CU (the
+// 32-slot tables)
+int prefill_local_buffers(const Geometry& g) { return 2 * prefill_local_lds_bytes(g, 2) <= 160 * 1024 ? 2 : 1; }
 
 // the register top-k list holds 16 or 32 entries; k <= 16 uses the short list
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {

@@ -120,13 +120,17 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
   constexpr int TILE = 32 * ROWB;      // 32 landmarks
   constexpr int NI = TILE / (kWave * 16);  // direct-to-LDS loads per tile
   constexpr int PER = NI / HPW;            // of which each wave issues
-  constexpr int NST = 4;                   // tiles in flight (LDS ring)
+  // tiles in flight (LDS ring); three for the 32-entry lists keep two
+  // workgroups per CU
+  constexpr int NST = KSEL > 16 ? 3 : 4;
   constexpr int MAXT = 2048;               // Nc <= 65536
   static_assert(NI % HPW == 0 && NSL >= 8, "tile loads split evenly; row swizzle needs 8 slots");
   // ring of landmark tiles shared by the workgroup's waves: row r of a tile
   // holds its 16-byte slots XOR-swizzled by (r & 7)
   __shared__ __align__(16) char ring[NST][TILE];
-  __shared__ float2 cbuf[HPW][KSEL][kWave];
+  // pass 2's kept candidates: score and chunk index (Nc <= 65536)
+  __shared__ float cs[HPW][KSEL][kWave];
+  __shared__ uint16_t ci[HPW][KSEL][kWave];
   __shared__ uint32_t tneed[HPW][MAXT / 32];  // pass 1: tile reached a row's threshold
 
   const int bid = blockIdx.x;
@@ -339,7 +343,8 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
             const bool take = x > tau || quota > 0;
             if (x == tau) --quota;
             if (take && cnt < KSEL) {
-              cbuf[hh][cnt][lane] = make_float2(x, __int_as_float(ti * 32 + ii));
+              cs[hh][cnt][lane] = x;
+              ci[hh][cnt][lane] = (uint16_t)(ti * 32 + ii);
               ++cnt;
             }
           }
@@ -369,13 +374,12 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
     oi[e] = INT_MAX;
   }
   {
-    // cbuf holds the kept set in ascending chunk order; list_insert lets the
+    // cs/ci hold the kept set in ascending chunk order; list_insert lets the
     // newest element win score ties, so offer it from the highest index down
     const int mx = wave_max_i(cnt);
     for (int e = mx - 1; e >= 0; --e) {
       if (e < cnt) {
-        const float2 c = cbuf[hh][e][lane];
-        list_insert<KSEL>(os, oi, c.x, __float_as_int(c.y));
+        list_insert<KSEL>(os, oi, cs[hh][e][lane], (int)ci[hh][e][lane]);
       }
     }
   }
@@ -445,16 +449,14 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
   // ---- bucket the remote selections (chunks before the query's aligned
   // window): count them per (b, g, chunk) in rcnt and give each its position
   // in its bucket.  The workgroup first groups its selections by chunk in an
-  // LDS hash table (cbuf's space: key, then count), so a chunk picked by many
-  // of its rows costs one global atomic.
+  // LDS hash table in cs's space, one word per slot: chunk << 16 | count
+  // (empty: all ones; counts stay below 2^16), so a chunk picked by many of
+  // its rows costs one global atomic.
   constexpr int HASH = HPW * KSEL * kWave;  // >= the workgroup's selections
-  int* hkey = reinterpret_cast<int*>(&cbuf[0][0][0]);
-  int* hcnt = hkey + HASH;
-  __syncthreads();  // every wave is done with cbuf
-  for (int i = tid; i < HASH; i += kWave * HPW) {
-    hkey[i] = -1;
-    hcnt[i] = 0;
-  }
+  constexpr uint32_t kEmpty = 0xffffffffu;
+  uint32_t* hw = reinterpret_cast<uint32_t*>(&cs[0][0][0]);
+  __syncthreads();  // every wave is done with cs and ci
+  for (int i = tid; i < HASH; i += kWave * HPW) hw[i] = kEmpty;
   __syncthreads();
   const int wsj = (ja / kLocalWindow) * kLocalWindow;
   uint32_t slot_rank[KSEL];  // slot << 16 | rank within the slot, or ~0
@@ -465,18 +467,18 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
       const int c = oi[e];
       int sl = (int)(((uint32_t)c * 2654435761u) >> 8) & (HASH - 1);
       while (true) {
-        const int prev = atomicCAS(&hkey[sl], -1, c);
-        if (prev == -1 || prev == c) break;
+        const uint32_t prev = atomicCAS(&hw[sl], kEmpty, (uint32_t)c << 16);
+        if (prev == kEmpty || (prev >> 16) == (uint32_t)c) break;
         sl = (sl + 1) & (HASH - 1);
       }
-      slot_rank[e] = ((uint32_t)sl << 16) | (uint32_t)atomicAdd(&hcnt[sl], 1);
+      slot_rank[e] = ((uint32_t)sl << 16) | (atomicAdd(&hw[sl], 1u) & 0xffffu);
     }
   }
   __syncthreads();
   int* bucket0 = rcnt + ((int64_t)b * Hkv + g) * Nc;
   for (int i = tid; i < HASH; i += kWave * HPW) {
-    const int n_i = hcnt[i];
-    if (n_i > 0) hcnt[i] = atomicAdd(&bucket0[hkey[i]], n_i);  // count -> first position
+    const uint32_t w = hw[i];
+    if (w != kEmpty) hw[i] = (uint32_t)atomicAdd(&bucket0[w >> 16], (int)(w & 0xffffu));  // -> first position
   }
   __syncthreads();
   if (t_row < T_len) {
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
     for (int e = 0; e < KSEL; ++e) {
       if (e < k) {
         const uint32_t sr = slot_rank[e];
-        pair_pos[base + e] = sr == ~0u ? -1 : hcnt[sr >> 16] + (int)(sr & 0xffffu);
+        pair_pos[base + e] = sr == ~0u ? -1 : (int)hw[sr >> 16] + (int)(sr & 0xffffu);
       }
     }
   }
