@@ -226,3 +226,108 @@ def test_decode_1m_adaptive_bf16_sampled():
 
 def test_decode_16m_bf16_sampled():
     run_decode_workload("decode_16m_bf16", [2])
+
+
+def test_decode_1m_varlen_bf16_sampled():
+    """Caches of seeded lengths inside the 2^20 capacity: each sampled query
+    against the oracle on its own prefix."""
+    from hierarchical_sparse_attention_hsa_amd.workloads import cache_lengths
+    w = WORKLOADS["decode_1m_varlen_bf16"]
+    Nc = w.T // w.S
+    lens = cache_lengths(w)
+    q, k, v = decode_inputs(w, "cuda")
+    L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
+    hsa.hsa_build_landmarks(k, L, w.S)
+    lens_t = torch.as_tensor(lens, device="cuda")
+    sel = torch.empty((w.B, w.Hq, w.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, w.k), dtype=torch.float32, device="cuda")
+    out = hsa.hsa_forward_decode_varlen(q, k, v, L, lens_t, w.S, w.k, sel_idx=sel, sel_score=sc)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    stats = new_stats()
+    for b in (int(np.argmin(lens)), int(np.argmax(lens)), 5):
+        n = int(lens[b])
+        print(f"query {b}: cache length {n}", flush=True)
+        for g in range(w.Hkv):
+            Lg = oracle_landmarks(k[b, g, :n], w.S, w.dtype)
+            check_landmarks(L[b, g, :n // w.S], Lg, w.dtype)
+            hs = slice(g * G, (g + 1) * G)
+            check_rows(host64(q[b, hs]), np.full(G, n), DeviceRows(k[b, g, :n]), DeviceRows(v[b, g, :n]), Lg, w.S,
+                       w.k, host64(out[b, hs]), sel[b, hs].cpu().numpy(), host64(sc[b, hs]), TOL[w.dtype], stats)
+    print(stats, flush=True)
+
+
+def test_backward_256k_bf16_sampled():
+    """The backward at full size in the benchmark's configuration.  The
+    selection it is given is the forward's; every row used below has its
+    selection validated against the oracle's rule first (exact, or a valid
+    set within the near-tie band), and the oracle then differentiates with
+    that same selection.  The GPU backward uses the GPU forward's output for
+    delta = dOut . out, so the forward's own rounding enters ds: the bound is
+    the bf16 one, 9e-3 of the magnitude sums (plus 1e-6), for dq of sampled
+    rows and for dK, dV of two chunks summed over every row that kept them."""
+    w = WORKLOADS["backward_256k_bf16"]
+    S, D = w.S, w.D
+    G = w.Hq // w.Hkv
+    Nc = w.T // S
+    q, k, v = prefill_inputs(w, "cuda")
+    dout = torch.randn((w.B, w.Hq, w.T, D), dtype=torch.float32, device="cuda",
+                       generator=torch.Generator("cuda").manual_seed(w.seed + 100))
+    L = torch.empty((w.B, w.Hkv, Nc, D), dtype=k.dtype, device="cuda")
+    hsa.hsa_build_landmarks(k, L, S)
+    sel = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.float32, device="cuda")
+    out = hsa.hsa_forward_prefill(q, k, v, L, S, w.k, sel_idx=sel, sel_score=sc)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    dq, dk, dv = hsa.hsa_backward_prefill(q, k, v, L, out, dout, sel, sc, S)
+    torch.cuda.synchronize()
+
+    def rows_of(b, h, pos):
+        pos_t = torch.as_tensor(pos, device="cuda")
+        return host64(q[b, h, pos_t]), sel[b, h, pos_t].cpu().numpy(), host64(dout[b, h, pos_t])
+
+    def validated(qr, pos, Lg, sl):
+        for r in range(len(pos)):
+            n = int(O.num_candidates(np.array([pos[r]]), S, Nc)[0])
+            ok, _, msg = O.check_selection(sl[r], qr[r], Lg, n, w.k)
+            assert ok, f"position {pos[r]}: {msg}"
+
+    b = 0
+    Lh = {}
+    for g in range(w.Hkv):
+        Lh[g] = O.landmarks(host64(k[b, g]), S, w.dtype)
+    # dq of sampled rows
+    pos = np.concatenate([np.arange(c * S, (c + 1) * S) for c in (1, 17, 64, 1000, 4095)])
+    for h in (0, 13, 31):
+        g = O.kv_head_of(h, w.Hq, w.Hkv)
+        qr, sl, gr = rows_of(b, h, pos)
+        validated(qr, pos, Lh[g], sl)
+        ref = O.hsa_rows_backward(qr, pos, DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lh[g], S, sl, gr)
+        got = host64(dq[b, h, torch.as_tensor(pos, device="cuda")])
+        err = np.abs(got - ref.dq)
+        assert np.all(err <= 9e-3 * ref.abs_dq + 1e-6), f"dq head {h}: worst {err.max():.3e}"
+    # dK, dV of two chunks of KV head 2: every (head, row) that kept them
+    g = 2
+    for c in (100, 3000):
+        acc_k = np.zeros((S, D))
+        acc_v = np.zeros((S, D))
+        abs_k = np.zeros((S, D))
+        abs_v = np.zeros((S, D))
+        for h in range(g * G, (g + 1) * G):
+            rows = torch.nonzero((sel[b, h] == c).any(dim=-1)).flatten().cpu().numpy()
+            if rows.size == 0:
+                continue
+            qr, sl, gr = rows_of(b, h, rows)
+            validated(qr, rows, Lh[g], sl)
+            ref = O.hsa_rows_backward(qr, rows, DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lh[g], S, sl, gr)
+            acc_k += ref.dK[c * S:(c + 1) * S]
+            acc_v += ref.dV[c * S:(c + 1) * S]
+            abs_k += ref.abs_dK[c * S:(c + 1) * S]
+            abs_v += ref.abs_dV[c * S:(c + 1) * S]
+        got_k = host64(dk[b, g, c * S:(c + 1) * S])
+        got_v = host64(dv[b, g, c * S:(c + 1) * S])
+        print(f"chunk {c}: max |dK| {np.abs(acc_k).max():.3e}, |dV| {np.abs(acc_v).max():.3e}", flush=True)
+        assert np.all(np.abs(got_k - acc_k) <= 9e-3 * abs_k + 1e-6), f"dK chunk {c}"
+        assert np.all(np.abs(got_v - acc_v) <= 9e-3 * abs_v + 1e-6), f"dV chunk {c}"
+    del q, k, v, L, sel, sc, out, dq, dk, dv, dout
