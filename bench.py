@@ -97,17 +97,12 @@ def timed_steps(step, steps, warmup, n_launch, events):
     return t1 - t0, per / steps
 
 
-def source_digest():
-    """Digest of everything that shapes the kernels' code: the HIP sources and
-    the build flags."""
+def library_digest():
+    """Digest of the built library (the code the profile measured; the build
+    is deterministic, and comments do not change it)."""
     import hashlib
-    pkg = os.path.join(ROOT, "hierarchical_sparse_attention_hsa_amd")
-    files = sorted(os.path.join("csrc", f) for f in os.listdir(os.path.join(pkg, "csrc"))) + ["build.py"]
-    h = hashlib.sha256()
-    for f in files:
-        h.update(f.encode())
-        h.update(open(os.path.join(pkg, f), "rb").read())
-    return h.hexdigest()[:16]
+    path = os.path.join(ROOT, "hierarchical_sparse_attention_hsa_amd", "libhsa_attn.so")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
 def profiled_traffic(workload, kernel_prefix):
@@ -118,7 +113,7 @@ def profiled_traffic(workload, kernel_prefix):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256_16") != source_digest():
+    if rec.get("library_sha256_16") != library_digest():
         return None
     for name, b in rec["traffic_bytes_per_launch"].items():
         if kernel_prefix in name:
@@ -170,7 +165,7 @@ def summarize_profile(workload, prof_dir, command, kernel):
         if "hsa_attn" in k[1] and k in counters["WRITE_SIZE"]:
             rows[short(k[1])].append((f, counters["WRITE_SIZE"][k]))
     traffic = {n: 1024.0 * float(np.mean([f * read_scale + w * write_scale for f, w in v])) for n, v in rows.items()}
-    rec = {"workload": workload, "source_sha256_16": source_digest(), "read_scale": read_scale,
+    rec = {"workload": workload, "library_sha256_16": library_digest(), "read_scale": read_scale,
            "write_scale": write_scale, "traffic_bytes_per_launch": traffic}
     with open(os.path.join(ROOT, "profiles", f"{workload}.traffic.json"), "w") as fh:
         json.dump(rec, fh, indent=1)

@@ -6,7 +6,8 @@
 // rows per instruction (LPR lanes per row, RPI = 64/LPR rows per load), so
 // every load instruction covers 1 KiB of consecutive bytes.  Sums are kept in
 // fp64, which is exact for bf16 keys; the mean is rounded once to the storage
-// dtype.
+// dtype.  append_kv_kernel (incremental decoding) writes one new token per
+// sequence and builds the landmark of a chunk it completes the same way.
 #include "common.hpp"
 #include "kernels.hpp"
 

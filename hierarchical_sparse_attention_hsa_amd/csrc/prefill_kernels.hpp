@@ -1,28 +1,29 @@
-// HSA prefill: causal HSA over a whole sequence (skill card "Every Token
-// Counts 16m Context", sections "Core Technique" and "Implementation").
+// HSA prefill: causal HSA over a whole sequence, or over its last rows after
+// a cached prefix (skill card "Every Token Counts 16m Context", sections
+// "Core Technique" and "Implementation").  Kernels on one stream:
 //
-// Two kernels on one stream:
-//
-// prefill_select  one workgroup per (b, g, query chunk j), one wave per query
-//   head of the group, 64 query rows per wave.  Landmark tiles of 32 rows are
-//   staged in LDS (shared by the G waves) and contracted with the wave's
-//   queries on MFMA (bf16 in, fp32 accumulate): the causal-block GEMM
-//   Q . L^T restricted to the j earlier chunks.  Tiles run from the newest
-//   chunk to the oldest.  After every tile the two lane halves swap
-//   accumulator halves (v_permlane32_swap) so that each lane holds the 32
-//   scores of one query row; the lane keeps that row's top-k in registers
-//   (descending order, so a new candidate always has the lowest index so far
-//   and wins ties, which realises "ties toward the lower chunk index").  The
-//   score matrix never reaches memory.
-//
-// prefill_attn  one workgroup per (b, g, query chunk j, 32-token half), one
-//   wave per query head.  The union of the rows' selected chunks is walked in
-//   ascending order; each chunk's K and V tiles are staged in LDS once for all
-//   the workgroup's rows.  S^T = K_c Q^T on MFMA, an fp32 softmax per row,
-//   and O^T += V_c^T P'^T on MFMA, where P' is the in-chunk probability
-//   already multiplied by the row's fusion weight (softmax of its kept
-//   retrieval scores); rows that did not select the chunk have weight 0.
-//   P' is fed to the bf16 MFMA as a hi + lo pair so it keeps ~16 bits.
+// prefill_select  one workgroup per (b, g, query chunk j) and group of up to
+//   four query heads, one wave per head, 64 query rows per wave.  Landmark
+//   tiles of 32 rows are staged in LDS (shared by the waves) and contracted
+//   with the wave's queries on MFMA (bf16 in, fp32 accumulate): the
+//   causal-block GEMM Q . L^T restricted to the chunks before j.  Pass 1 runs
+//   the tiles from the newest chunk down and finds each row's k-th best
+//   score; pass 2 recomputes the tiles that can hold a kept chunk and
+//   collects the exact top-k (ties to the lower chunk index).  The scores
+//   never reach memory.  The epilogue writes the selection and buckets the
+//   selected chunks that lie before the query's aligned 64-chunk window.
+// prefill_vt      V^T tiles (tokens in the order the P.V fragments use them).
+// prefill_zero / scan / scatter (prefill.hip)  counts, offsets and lists of
+//   those remote pairs per (b, g, chunk).
+// prefill_remote  one workgroup per remote bucket: the chunk's K and V^T are
+//   staged once and its selecting rows gathered 32 at a time; writes each
+//   pair's in-chunk attention output.
+// prefill_local   one workgroup per (b, g, query chunk, 32-token half), one
+//   wave per query head: walks the union of the rows' selected chunks inside
+//   the window (K and V^T staged in LDS), S^T = K_c Q^T and O^T += V_c^T P'^T
+//   on MFMA with P' = fusion weight x in-chunk probability (0 for rows that
+//   did not select the chunk, fed as a bf16 head + tail pair), then adds the
+//   weighted remote outputs and writes the rows.
 #pragma once
 
 #include <climits>
