@@ -105,8 +105,12 @@ __device__ __forceinline__ void score_insert(float (&s)[K], float x) {
 // candidates equal to tau until k are kept: exactly the first k in the order
 // (score desc, index asc).  Tiles whose maximum cannot reach a row's
 // threshold are skipped in both passes.
+// Three waves per SIMD for the 16-entry lists (the register budget drops to
+// 168 at the cost of a few spilled values; measured faster than two waves),
+// two for 32 entries (whose LDS allows only two workgroups per CU).
 template <typename T, int D, int G, int KSEL>
-__global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
+__global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) __attribute__((amdgpu_waves_per_eu(KSEL > 16 ? 2 : 3)))
+void prefill_select_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ lm,
     int32_t* __restrict__ sel_idx, float* __restrict__ sel_score, int* __restrict__ rcnt, int32_t* __restrict__ pair_pos,
     int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int j0, int k, float scale, int k_base, float gap_tau) {
@@ -121,9 +125,9 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) void prefill_select_kernel(
   constexpr int TILE = 32 * ROWB;      // 32 landmarks
   constexpr int NI = TILE / (kWave * 16);  // direct-to-LDS loads per tile
   constexpr int PER = NI / HPW;            // of which each wave issues
-  // tiles in flight (LDS ring); three for the 32-entry lists keep two
-  // workgroups per CU
-  constexpr int NST = KSEL > 16 ? 3 : 4;
+  // tiles in flight (LDS ring): three keep three 16-entry-list workgroups
+  // (two with 32 entries) per CU
+  constexpr int NST = 3;
   constexpr int MAXT = 2048;               // Nc <= 65536
   static_assert(NI % HPW == 0 && NSL >= 8, "tile loads split evenly; row swizzle needs 8 slots");
   // ring of landmark tiles shared by the workgroup's waves: row r of a tile
