@@ -614,17 +614,31 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const typename T::stor
 }
 
 // ---------------------------------------------------------------- 4. fusion
+// The kept slots come first (padding after them), so the loop runs over all
+// k slots without an early exit: the loads are independent and overlap; a
+// padding slot's partial (never written) is loaded and discarded.
 __global__ void decode_fuse_kernel(const float* __restrict__ partial, const int32_t* __restrict__ sel_idx,
                                    const float* __restrict__ sel_score, float* __restrict__ out, int k, int D) {
   const int64_t bh = blockIdx.x;
   const int d = threadIdx.x;
   const float mx = sel_score[bh * k];
   float den = 0.0f, num = 0.0f;
-  for (int s = 0; s < k; ++s) {
-    if (sel_idx[bh * k + s] < 0) break;
-    const float w = __expf(sel_score[bh * k + s] - mx);
-    den += w;
-    num = fmaf(w, partial[(bh * k + s) * D + d], num);
+  constexpr int U = 8;  // slots whose loads are issued together
+  for (int s0 = 0; s0 < k; s0 += U) {
+    bool kept[U];
+    float w[U], x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u;
+      kept[u] = s < k && sel_idx[bh * k + s] >= 0;
+      w[u] = kept[u] ? __expf(sel_score[bh * k + s] - mx) : 0.0f;
+      x[u] = s < k ? partial[(bh * k + s) * D + d] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      den += w[u];
+      num = kept[u] ? fmaf(w[u], x[u], num) : num;
+    }
   }
   out[bh * D + d] = den > 0.0f ? num / den : 0.0f;
 }
