@@ -456,6 +456,10 @@ __global__ __launch_bounds__(kWave* G) void decode_merge_kernel(const float2* __
 }
 
 // ---------------------------------------------------------------- 3. chunk attention
+// The waves are independent, so a workgroup holds one: 65K small
+// workgroups over the group entries finish more evenly than 16K of four
+// (measured 5% faster at 1M).
+constexpr int kAttnWaves = 1;
 // One wave per distinct selected chunk of a (b, g) group; waves are
 // independent (no LDS, no barriers).  Logits of all G heads on MFMA:
 // S^T[token][head] = K_c . q_head (A = the chunk's keys, B = the group's
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(kWave* G) void decode_merge_kernel(const float2* __
 // wave-private LDS table [token][head]; a cross-lane sum finishes each
 // output column.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void decode_attn_kernel(const typename T::storage* __restrict__ q,
+__global__ __launch_bounds__(kAttnWaves * kWave) void decode_attn_kernel(const typename T::storage* __restrict__ q,
                                                           const typename T::storage* __restrict__ kc,
                                                           const typename T::storage* __restrict__ vc,
                                                           const int4* __restrict__ ulist,
@@ -483,10 +487,10 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const typename T::stor
   // waves per SIMD instead of 2 for bf16 at D = 128)
   constexpr int VPASS = VL > 8 ? 2 : 1;
   constexpr int VLP = VL / VPASS;
-  __shared__ __align__(16) float pbuf[4][S][G];  // per wave: probability of (token, head)
+  __shared__ __align__(16) float pbuf[kAttnWaves][S][G];  // per wave: probability of (token, head)
   const int b = blockIdx.z, g = blockIdx.y;
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
-  const int e = blockIdx.x * 4 + wave;
+  const int e = blockIdx.x * kAttnWaves + wave;
   const int64_t grp = (int64_t)b * Hkv + g;
   if (e >= ucount[grp]) return;
   const int4 ent = ulist[grp * (G * k) + e];
@@ -702,7 +706,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipS
   mark_launch(st);
   if (p.splits > 0) {
     mark_launch(st);
-    hipLaunchKernelGGL((decode_attn_kernel<T, D, G>), dim3((G * g.k + 3) / 4, g.Hkv, g.B), dim3(256), 0, st,
+    hipLaunchKernelGGL((decode_attn_kernel<T, D, G>), dim3((G * g.k + kAttnWaves - 1) / kAttnWaves, g.Hkv, g.B),
+                       dim3(kAttnWaves * kWave), 0, st,
                        static_cast<const stg*>(a.q), static_cast<const stg*>(a.k), static_cast<const stg*>(a.v),
                        ulist, ucount, partial, g.Hkv, g.T, g.k, scale);
     mark_launch(st);
