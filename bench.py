@@ -35,6 +35,9 @@ import numpy as np  # noqa: E402
 
 METRIC = "HSA layer queries/s + achieved HBM GB/s (1M decode); tokens/s + MFMA% (256K prefill)"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+# the prefill kernels' split of window chunks between the local and the
+# chunk-major attention (HSA_LOCAL_MIN_ROWS in csrc/prefill_kernels.hpp)
+LOCAL_MIN_ROWS = 8
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 
@@ -451,10 +454,20 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
     score_flops = 2.0 * w.B * w.Hq * w.D * n_p.sum()
     n_pairs = int((sel >= 0).sum().item())  # kept (row, chunk) pairs: sum of min(n_p, k) without adaptivity
     attn_flops = 4.0 * w.S * w.D * n_pairs
-    # split of the selected pairs into remote (chunk before the query's
-    # 64-chunk window) and local ones, counted from this run's selection
+    # split of the selected pairs into remote and local ones, counted from
+    # this run's selection by the library's rule: remote = a chunk before
+    # the query's 64-chunk window, or a window chunk selected by fewer than
+    # LOCAL_MIN_ROWS rows of the query's 32-row block (same head)
     win0 = torch.div(torch.arange(off, w.T, device="cuda") // w.S, 64, rounding_mode="floor") * 64
-    n_remote = int(((sel >= 0) & (sel < win0[None, None, :, None])).sum().item())
+    kept = sel >= 0
+    in_win = kept & (sel >= win0[None, None, :, None])
+    blk = (torch.arange(Tq, device="cuda") // 32)[None, None, :, None]
+    bh = torch.arange(w.B * w.Hq, device="cuda").view(w.B, w.Hq, 1, 1)
+    key = ((bh * ((Tq + 31) // 32) + blk) * 64 + (sel - win0[None, None, :, None]).clamp(0, 63)).expand_as(sel)
+    cnt = torch.bincount(key[in_win].flatten(), minlength=w.B * w.Hq * ((Tq + 31) // 32) * 64)
+    n_local = int((cnt[cnt >= LOCAL_MIN_ROWS]).sum().item())
+    n_remote = int(kept.sum().item()) - n_local
+    del in_win, key, cnt
     remote_flops = 4.0 * w.S * w.D * n_remote
     local_flops = 4.0 * w.S * w.D * (n_pairs - n_remote)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS

@@ -11,7 +11,9 @@
 //   score; pass 2 recomputes the tiles that can hold a kept chunk and
 //   collects the exact top-k (ties to the lower chunk index).  The scores
 //   never reach memory.  The epilogue writes the selection and buckets the
-//   selected chunks that lie before the query's aligned 64-chunk window.
+//   "remote" pairs: selected chunks before the query's aligned 64-chunk
+//   window, and window chunks that fewer than kLocalMinRows rows of the
+//   query's 32-row block (same head) selected.
 // prefill_vt      V^T tiles (tokens in the order the P.V fragments use them).
 // prefill_zero / scan / scatter (prefill.hip)  counts, offsets and lists of
 //   those remote pairs per (b, g, chunk).
@@ -19,8 +21,8 @@
 //   staged once and its selecting rows gathered 32 at a time; writes each
 //   pair's in-chunk attention output.
 // prefill_local   one workgroup per (b, g, query chunk, 32-token half), one
-//   wave per query head: walks the union of the rows' selected chunks inside
-//   the window (K and V^T staged in LDS), S^T = K_c Q^T and O^T += V_c^T P'^T
+//   wave per query head: walks the union of the rows' other ("local")
+//   selected chunks (K and V^T staged in LDS), S^T = K_c Q^T and O^T += V_c^T P'^T
 //   on MFMA with P' = fusion weight x in-chunk probability (0 for rows that
 //   did not select the chunk, fed as a bf16 head + tail pair), then adds the
 //   weighted remote outputs and writes the rows.
@@ -38,6 +40,14 @@ constexpr int kChunk = 64;
 // Query chunk j's aligned window: chunks [64 * floor(j / 64), j).  Selected
 // chunks inside it are "local" to the attention, the others "remote".
 constexpr int kLocalWindow = 64;
+// A window chunk selected by fewer than this many rows of a 32-row query
+// block (one head) is attended like the chunks before the window (one
+// chunk-major pass over all its selecting rows) rather than by running the
+// whole block through it.
+#ifndef HSA_LOCAL_MIN_ROWS
+#define HSA_LOCAL_MIN_ROWS 8
+#endif
+constexpr int kLocalMinRows = HSA_LOCAL_MIN_ROWS;
 
 template <typename T>
 __device__ __forceinline__ void load_frag_lds(Frag<T>& f, const char* row, int slot_xor, int kch, int half);
@@ -125,17 +135,32 @@ void prefill_select_kernel(
   constexpr int TILE = 32 * ROWB;      // 32 landmarks
   constexpr int NI = TILE / (kWave * 16);  // direct-to-LDS loads per tile
   constexpr int PER = NI / HPW;            // of which each wave issues
-  // tiles in flight (LDS ring): three keep three 16-entry-list workgroups
-  // (two with 32 entries) per CU
-  constexpr int NST = 3;
+  // LDS ring of NG groups of TPB tiles: one barrier per group, NG-1 groups
+  // in flight.  Pass 1 uses only the ring and pass 2 only the candidate
+  // store, so the two share their space.
+#ifndef HSA_SEL_TPB
+#define HSA_SEL_TPB 2
+#endif
+#ifndef HSA_SEL_NG
+#define HSA_SEL_NG 3
+#endif
+  // (groups of one tile when the ring would hold more than 8 KiB per wave)
+  constexpr int TPB = TILE * HSA_SEL_TPB <= 2 * 8192 && HPW >= 4 ? HSA_SEL_TPB : 1;
+  constexpr int NG = HSA_SEL_NG;
+  constexpr int NST = NG * TPB;
   constexpr int MAXT = 2048;               // Nc <= 65536
   static_assert(NI % HPW == 0 && NSL >= 8, "tile loads split evenly; row swizzle needs 8 slots");
+  static_assert(NG >= 2 && (NG - 2) * TPB <= 4, "wait_tiles covers up to four later tiles");
   // ring of landmark tiles shared by the workgroup's waves: row r of a tile
-  // holds its 16-byte slots XOR-swizzled by (r & 7)
-  __shared__ __align__(16) char ring[NST][TILE];
-  // pass 2's kept candidates: score and chunk index (Nc <= 65536)
-  __shared__ float cs[HPW][KSEL][kWave];
-  __shared__ uint16_t ci[HPW][KSEL][kWave];
+  // holds its 16-byte slots XOR-swizzled by (r & 7); pass 2's kept
+  // candidates: score and chunk index (Nc <= 65536)
+  constexpr int RING = NST * TILE;
+  constexpr int CS_BYTES = HPW * KSEL * kWave * 4;
+  constexpr int STORE = CS_BYTES + HPW * KSEL * kWave * 2;
+  __shared__ __align__(16) char shm[RING > STORE ? RING : STORE];
+  auto ring = [&](int sg) { return shm + sg * TILE; };
+  auto cs = reinterpret_cast<float(*)[KSEL][kWave]>(shm);
+  auto ci = reinterpret_cast<uint16_t(*)[KSEL][kWave]>(shm + CS_BYTES);
   __shared__ uint32_t tneed[HPW][MAXT / 32];  // pass 1: tile reached a row's threshold
 
   const int bid = blockIdx.x;
@@ -180,36 +205,50 @@ void prefill_select_kernel(
         const int r = L / NSL, sp = L % NSL;
         const int64_t c = min((int64_t)ti * 32 + r, n - 1);
         __builtin_amdgcn_global_load_lds(lmg + c * ROWB + ((sp ^ (r & 7)) * 16),
-                                         (__attribute__((address_space(3))) void*)(ring[sg] + ii * kWave * 16), 16,
+                                         (__attribute__((address_space(3))) void*)(ring(sg) + ii * kWave * 16), 16,
                                          0, 0);
       }
     };
     // wait until at most `later` tiles of this wave's loads are in flight
     auto wait_tiles = [&](int later) {
-      if constexpr (NST >= 4) {
-        if (later >= 2) {
+      if constexpr ((NG - 2) * TPB >= 4) {
+        if (later >= 4) {
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PER) : "memory");
+          return;
+        }
+        if (later == 3) {
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
+          return;
+        }
+      }
+      if constexpr ((NG - 2) * TPB >= 2) {
+        if (later == 2) {
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
           return;
         }
       }
-      if (later >= 1) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
-        return;
+      if constexpr ((NG - 2) * TPB >= 1) {
+        if (later == 1) {
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
+          return;
+        }
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
     // Run body(i, tile, stage) over the tile sequence tile_of(0 .. count-1)
-    // with NST-1 tiles in flight and one barrier per tile: after the barrier
-    // of step i every wave is done with step i-1, whose stage is refilled.
+    // in groups of TPB tiles with NG-1 groups in flight and one barrier per
+    // group: after the barrier of group gi every wave is done with group
+    // gi-1, whose stages are refilled.
     auto pipeline = [&](int count, auto tile_of, auto body) {
-#pragma unroll
-      for (int i = 0; i < NST - 1; ++i)
-        if (i < count) issue(tile_of(i), i);
-      for (int i = 0; i < count; ++i) {
-        wait_tiles(min(NST - 2, count - 1 - i));
+      const int ngr = (count + TPB - 1) / TPB;
+      for (int i = 0; i < (NG - 1) * TPB && i < count; ++i) issue(tile_of(i), i % NST);
+      for (int gi = 0; gi < ngr; ++gi) {
+        const int done = min(count, (gi + 1) * TPB);  // tiles needed now
+        const int issued = min(count, (gi + NG - 1) * TPB);
+        wait_tiles(issued - done);
         __syncthreads();
-        if (i + NST - 1 < count) issue(tile_of(i + NST - 1), (i + NST - 1) % NST);
-        body(i, tile_of(i), ring[i % NST]);
+        for (int i = (gi + NG - 1) * TPB; i < (gi + NG) * TPB && i < count; ++i) issue(tile_of(i), i % NST);
+        for (int i = gi * TPB; i < done; ++i) body(i, tile_of(i), ring(i % NST));
       }
       __syncthreads();  // the ring is free again
     };
@@ -452,7 +491,9 @@ void prefill_select_kernel(
   if (rcnt == nullptr) return;  // no remote bucketing (fewer than one window)
 
   // ---- bucket the remote selections (chunks before the query's aligned
-  // window): count them per (b, g, chunk) in rcnt and give each its position
+  // window, and window chunks selected by fewer than kLocalMinRows rows of
+  // the 32-row half of the wave): count them per (b, g, chunk) in rcnt and
+  // give each its position
   // in its bucket.  The workgroup first groups its selections by chunk in an
   // LDS hash table in cs's space, one word per slot: chunk << 16 | count
   // (empty: all ones; counts stay below 2^16), so a chunk picked by many of
@@ -460,15 +501,23 @@ void prefill_select_kernel(
   constexpr int HASH = HPW * KSEL * kWave;  // >= the workgroup's selections
   constexpr uint32_t kEmpty = 0xffffffffu;
   uint32_t* hw = reinterpret_cast<uint32_t*>(&cs[0][0][0]);
+  // rows of each 32-row half of the wave that selected each window chunk
+  __shared__ int wcnt[HPW][2][kLocalWindow];
+  for (int i = lane; i < 2 * kLocalWindow; i += kWave) (&wcnt[hh][0][0])[i] = 0;
   __syncthreads();  // every wave is done with cs and ci
   for (int i = tid; i < HASH; i += kWave * HPW) hw[i] = kEmpty;
-  __syncthreads();
   const int wsj = (ja / kLocalWindow) * kLocalWindow;
+  const int hf = lane >> 5;
+#pragma unroll
+  for (int e = 0; e < KSEL; ++e)
+    if (e < k && t_row < T_len && oi[e] >= wsj && oi[e] != INT_MAX) atomicAdd(&wcnt[hh][hf][oi[e] - wsj], 1);
+  __syncthreads();
   uint32_t slot_rank[KSEL];  // slot << 16 | rank within the slot, or ~0
 #pragma unroll
   for (int e = 0; e < KSEL; ++e) {
     slot_rank[e] = ~0u;
-    if (e < k && t_row < T_len && oi[e] < wsj) {  // INT_MAX (empty) is never < wsj
+    const bool remote = oi[e] != INT_MAX && (oi[e] < wsj || wcnt[hh][hf][oi[e] - wsj] < kLocalMinRows);
+    if (e < k && t_row < T_len && remote) {
       const int c = oi[e];
       int sl = (int)(((uint32_t)c * 2654435761u) >> 8) & (HASH - 1);
       while (true) {
@@ -500,12 +549,15 @@ void prefill_select_kernel(
 // ---------------------------------------------------------------- attention
 //
 // A selected (row, chunk) pair is "local" when the chunk lies in the query's
-// aligned window of kLocalWindow chunks and "remote" otherwise.  Local pairs
-// are shared by many rows of a query block (measured: most selections fall
-// in the query's own window), so prefill_local_kernel walks the union of a
-// block's local selections and runs every row of the block through each
-// chunk on MFMA (rows that did not select it get weight 0).  Remote pairs
-// are scattered, so they are processed chunk-major: they are bucketed by
+// aligned window of kLocalWindow chunks and at least kLocalMinRows rows of
+// the row's 32-row block (same head) selected it, and "remote" otherwise.
+// Local pairs are shared by many rows of a query block (measured: most
+// selections fall in the query's own window), so prefill_local_kernel walks
+// the union of a block's local selections and runs every row of the block
+// through each chunk on MFMA (rows that did not select it get weight 0): a
+// chunk's cost does not depend on how many rows selected it, hence the
+// minimum.  Remote pairs are scattered, so they are processed chunk-major:
+// they are bucketed by
 // (b, g, chunk), prefill_remote_kernel loads each chunk's K/V tile once and
 // gathers its selecting rows 32 at a time into full MFMA tiles, and writes
 // each pair's normalised in-chunk output; the local kernel then adds the
@@ -567,6 +619,14 @@ struct Tile {
 
 // wait for this wave's direct-to-LDS loads
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Order one wave's LDS accesses across its lanes: the hardware executes a
+// wave's LDS instructions in order, so only the compiler must not move
+// accesses across this point.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Transposed copy of V for the attention kernels: for every complete chunk,
 // D rows of its 64 values of dimension d, tokens in vt_pos order, so that a
@@ -757,7 +817,16 @@ __global__ __launch_bounds__(256) void prefill_remote_kernel(const typename T::s
   using TL = Tile<T, D>;
   constexpr int KCH = D / 16;
   constexpr int DM = D / 32;
+#ifndef HSA_REMOTE_STAGE_TILES
+#define HSA_REMOTE_STAGE_TILES 2
+#endif
+  constexpr int SDM = HSA_REMOTE_STAGE_TILES;  // 32-column tiles per stage round
+  static_assert(DM % SDM == 0, "rounds cover the output columns");
+  // per wave: 32 rows of 32 * SDM fp32 columns, rows padded by 16 bytes so
+  // that 16 rows' pieces at one column fall on distinct banks
+  constexpr int kStageRow = 32 * SDM + 4;
   __shared__ __align__(16) char smem[TL::BYTES];
+  __shared__ __align__(16) float stage[4][32 * kStageRow];
   char* ks = smem;
   char* vt = smem + TL::KBYTES;
   const int64_t bucket = blockIdx.x;
@@ -766,6 +835,7 @@ __global__ __launch_bounds__(256) void prefill_remote_kernel(const typename T::s
   const int64_t c = bucket % Nc;
   const int64_t bg = bucket / Nc;  // b * Hkv + g
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  float* stg = stage[wave];
   TL::template issue<4>(reinterpret_cast<const char*>(kk + (bg * T_len + c * kChunk) * D),
                         reinterpret_cast<const char*>(vt_g) + bucket * (int64_t)TL::KBYTES, smem, wave, lane);
   wait_loads();
@@ -783,14 +853,30 @@ __global__ __launch_bounds__(256) void prefill_remote_kernel(const typename T::s
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
     attend_block<T, D>(qf, ks, vt, 1.0f, cexp, oacc, lane);
-    if (ok) {
-      float* op = partial + (int64_t)p * D;
+    // The block's 32 output rows leave through the wave's LDS stage, SDM
+    // tiles of 32 columns at a time: a lane holds 16-byte pieces of one row,
+    // which would make every store touch 32 rows; read back, each store
+    // writes whole 128-byte lines.
+    const int pb = begin + 32 * blk, nrow = min(end - pb, 32);
 #pragma unroll
-      for (int dm = 0; dm < DM; ++dm)
+    for (int r0 = 0; r0 < DM; r0 += SDM) {
+#pragma unroll
+      for (int dd = 0; dd < SDM; ++dd)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4*>(op + out_col(dm, q4, half)) =
-              f32x4{oacc[dm][4 * q4], oacc[dm][4 * q4 + 1], oacc[dm][4 * q4 + 2], oacc[dm][4 * q4 + 3]};
+          *reinterpret_cast<f32x4*>(stg + (lane & 31) * kStageRow + out_col(dd, q4, half)) =
+              f32x4{oacc[r0 + dd][4 * q4], oacc[r0 + dd][4 * q4 + 1], oacc[r0 + dd][4 * q4 + 2],
+                    oacc[r0 + dd][4 * q4 + 3]};
+      wave_lds_fence();  // the wave's LDS operations run in order; keep the compiler's too
+      constexpr int LPR = 8 * SDM;   // lanes per row of the stage
+      constexpr int RPI = kWave / LPR;  // rows per read
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = RPI * i + lane / LPR;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(stg + r * kStageRow + 4 * (lane % LPR));
+        if (r < nrow) *reinterpret_cast<f32x4*>(partial + (int64_t)(pb + r) * D + 32 * r0 + 4 * (lane % LPR)) = x;
+      }
+      wave_lds_fence();
     }
   }
 }
@@ -861,18 +947,22 @@ __global__ __launch_bounds__(kWave* G)
       den += w[e];
     }
     const float inv = 1.0f / den;
+    // a pair with a bucket position (pair_pos >= 0) was attended chunk-major
+    int pp[KSEL];
+#pragma unroll
+    for (int e = 0; e < KSEL; ++e) pp[e] = ci[e] >= 0 ? pair_pos[base + e] : 0;
 #pragma unroll
     for (int e = 0; e < KSEL; ++e) {
-      if (ci[e] >= ws) {
+      if (ci[e] >= 0 && pp[e] < 0) {
         int rank = 0;
 #pragma unroll
-        for (int f = 0; f < KSEL; ++f) rank += (ci[f] >= ws && ci[f] < ci[e]);
+        for (int f = 0; f < KSEL; ++f) rank += (ci[f] >= 0 && pp[f] < 0 && ci[f] < ci[e]);
         tab[row * k + rank] = make_int2(ci[e], __float_as_int(w[e] * inv));
         atomicOr(&bm[(ci[e] - ws) >> 5], 1u << ((ci[e] - ws) & 31));
         ++m;
       } else if (ci[e] >= 0) {
         ++rc;
-        tab[row * k + k - rc] = make_int2(pair_pos[base + e], __float_as_int(w[e] * inv));
+        tab[row * k + k - rc] = make_int2(pp[e], __float_as_int(w[e] * inv));
       }
     }
   }
