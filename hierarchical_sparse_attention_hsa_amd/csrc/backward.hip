@@ -240,25 +240,50 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     accK[i] = f32x16{};
   }
 
+  // The gathered rows of a round's tile (pair id, weight, delta, q, dOut)
+  // are fetched one round ahead, while the previous round's chunk side
+  // runs; the pair ids two steps ahead, while the row side runs.
+  int pid_n = 0;       // pair id of this lane's next tile
+  int pid = 0;         // ... of the tile being fetched or processed
+  bool ok = false;
+  float w = 0.0f, dlt = 0.0f;
+  u32x4 qraw[KCH];
+  f32x4 graw[2 * KCH];
+  auto fetch_id = [&](int t) {
+    const int p = begin + 32 * t + pr;
+    pid_n = (t < ntiles && p < end) ? pairs[p] : -1;
+  };
+  auto fetch_rows = [&]() {
+    pid = pid_n;
+    ok = pid >= 0;
+    const int64_t row = ok ? pid / k : 0;
+    w = ok ? wts[pid] : 0.0f;
+    dlt = ok ? delta[row] : 0.0f;
+    const uint16_t* qp = q + row * D + 8 * half;
+    const float* gp = dout + row * D + 8 * half;
+    const f32x4 z{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KCH; ++s) {
+      qraw[s] = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+      graw[2 * s] = ok ? reinterpret_cast<const f32x4*>(gp + 16 * s)[0] : z;
+      graw[2 * s + 1] = ok ? reinterpret_cast<const f32x4*>(gp + 16 * s)[1] : z;
+    }
+  };
+  fetch_id(wave);
+  fetch_rows();
   for (int r = 0; r < rounds; ++r) {
     const int ti = 4 * r + wave;
+    fetch_id(ti + 4);
     if (ti < ntiles) {
       char* At = my;
       char* Lt = my + SA;
       char* Ot = my + 2 * SA;
       char* Qt = my + 2 * SA + SO;
-      const int p = begin + 32 * ti + pr;
-      const bool ok = p < end;
-      const int pid = ok ? pairs[p] : 0;
-      const int64_t row = pid / k;
-      const float w = ok ? wts[pid] : 0.0f;
-      const float dlt = ok ? delta[row] : 0.0f;
       // q (B operand: pair column, dims 16 s + 8 half + 0..7) and its staging
       Frag<BF16> qf[KCH];
-      const uint16_t* qp = q + row * D + 8 * half;
 #pragma unroll
       for (int s = 0; s < KCH; ++s) {
-        const u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 raw = qraw[s];
         qf[s].v = as_bf16x8(raw);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -268,12 +293,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
       }
       // do = w * dout: head + tail fragments, and its bf16 staging
       Frag<BF16> dh[KCH], dtl[KCH];
-      const float* gp = dout + row * D + 8 * half;
 #pragma unroll
       for (int s = 0; s < KCH; ++s) {
-        const f32x4 z{0.f, 0.f, 0.f, 0.f};
-        const f32x4 g0 = ok ? reinterpret_cast<const f32x4*>(gp + 16 * s)[0] : z;
-        const f32x4 g1 = ok ? reinterpret_cast<const f32x4*>(gp + 16 * s)[1] : z;
+        const f32x4 g0 = graw[2 * s], g1 = graw[2 * s + 1];
         float x[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -393,6 +415,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
       }
     }
     __syncthreads();  // every wave's slot is written
+    fetch_rows();     // the next round's tile
     // chunk side: dV += A^T dO, dK += dlogit'^T Q over the round's tiles
     for (int sl = 0; sl < 4 && 4 * r + sl < ntiles; ++sl) {
       const char* base = stage + sl * SLOT;
