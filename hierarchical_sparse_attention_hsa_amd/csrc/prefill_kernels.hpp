@@ -115,11 +115,10 @@ __device__ __forceinline__ void score_insert(float (&s)[K], float x) {
 // candidates equal to tau until k are kept: exactly the first k in the order
 // (score desc, index asc).  Tiles whose maximum cannot reach a row's
 // threshold are skipped in both passes.
-// Three waves per SIMD for the 16-entry lists (the register budget drops to
-// 168 at the cost of a few spilled values; measured faster than two waves),
-// two for 32 entries (whose LDS allows only two workgroups per CU).
+// Three waves per SIMD (the register budget drops to 168 at the cost of a
+// few spilled values; measured faster than two waves for both list sizes).
 template <typename T, int D, int G, int KSEL>
-__global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) __attribute__((amdgpu_waves_per_eu(KSEL > 16 ? 2 : 3)))
+__global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) __attribute__((amdgpu_waves_per_eu(3)))
 void prefill_select_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ lm,
     int32_t* __restrict__ sel_idx, float* __restrict__ sel_score, int* __restrict__ rcnt, int32_t* __restrict__ pair_pos,
