@@ -469,13 +469,25 @@ __global__ void bwd_dq_kernel(const float* __restrict__ dqp, const int32_t* __re
   if (row >= rows) return;
   const int d = 4 * (int)(i % (D / 4));
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
-  for (int e = 0; e < k; ++e) {
-    if (pair_pos[row * k + e] < 0) continue;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(dqp + (row * k + e) * D + d);
-    acc[0] += x[0];
-    acc[1] += x[1];
-    acc[2] += x[2];
-    acc[3] += x[3];
+  // eight slots' loads in flight at a time; the sum keeps the slot order
+  constexpr int U = 8;
+  for (int e0 = 0; e0 < k; e0 += U) {
+    bool ok[U];
+    f32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ok[u] = e0 + u < k && pair_pos[row * k + e0 + u] >= 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      x[u] = ok[u] ? *reinterpret_cast<const f32x4*>(dqp + (row * k + e0 + u) * D + d) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ok[u]) {
+        acc[0] += x[u][0];
+        acc[1] += x[u][1];
+        acc[2] += x[u][2];
+        acc[3] += x[u][3];
+      }
+    }
   }
   *reinterpret_cast<f32x4*>(dq + row * D + d) = acc;
 }
