@@ -101,10 +101,11 @@ hsa_attn_status_t hsa_build_landmarks(const hsa_attn_dims_t* d, const void* k, v
  * larger dot product is the one kept at the cut.
  * workspace: device scratch of at least hsa_attn_workspace_size(d, 0) bytes
  * (never NULL when T > 0).  It holds the selection when sel_idx is NULL,
- * the bucketing of selected chunks that lie before the query's aligned
- * window of 64 chunks, one fp32 [D] attention output per such pair, and a
- * transposed copy of V.  The size covers the worst case, every selected
- * pair outside the window: about B*Hq*T*k*(4*D + 16) bytes plus the size of
+ * the bucketing of the pairs attended chunk-major (selected chunks before
+ * the query's aligned window of 64 chunks, and window chunks that few rows
+ * of the query's 32-row block selected), one fp32 [D] attention output per
+ * such pair, and a transposed copy of V.  The size covers the worst case,
+ * every selected pair chunk-major: about B*Hq*T*k*(4*D + 16) bytes plus the size of
  * V (69 GB at B=1, Hq=32, T=2^18, k=16, D=128, bf16).
  */
 hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, const void* k,
