@@ -342,6 +342,50 @@ def bench_decode_varlen(wname, steps, warmup):
     return res
 
 
+# attainable HBM read bandwidth measured in this run (attainable_read_gbps),
+# reported beside the nominal peak in the HBM-bound rooflines
+ATTAINABLE = {}
+
+
+def attainable_read_gbps(gib=8, reps=5):
+    """Best read bandwidth of the stream probe (measure/stream_read.hip, a
+    library of its own) over a few launch shapes on a `gib` GiB buffer,
+    timed with events on torch's current stream, where the probe launches."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "hierarchical_sparse_attention_hsa_amd", "libhsa_attn_stream.so"))
+    lib.hsa_attn_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.hsa_attn_stream_read.restype = ctypes.c_int
+    nbytes = gib << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    best = (0.0, None)
+    for blocks in (1024, 2048, 4096, 8192):
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+        for unroll in (4, 8):
+            def run():
+                rc = lib.hsa_attn_stream_read(buf.data_ptr(), nbytes, blocks, unroll, sink.data_ptr(), stream)
+                if rc != 0:
+                    raise RuntimeError(f"stream probe launch failed: HIP error {rc}")
+            run()
+            run()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = reps * nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9
+            if gbs > best[0]:
+                best = (gbs, f"{blocks} workgroups x 256 threads, {unroll} 16-byte loads in flight per thread")
+        del sink
+    del buf
+    torch.cuda.empty_cache()
+    log(f"attainable HBM read bandwidth (stream probe, {gib} GiB): {best[0]:.0f} GB/s ({best[1]})")
+    return best
+
+
 def decode_roofline(wname, per_scan_ms, lm_bytes, per_attn_ms, attn_bytes):
     """Roofline of the dominant decode kernel (the longer of the landmark scan
     and the chunk attention, both HBM-bound) with the other one beside it.
@@ -354,6 +398,9 @@ def decode_roofline(wname, per_scan_ms, lm_bytes, per_attn_ms, attn_bytes):
         out[name] = {"kernel": name, "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": profiled_traffic(wname, name),
                      "alg_bytes_per_launch": nbytes, "ms": ms}
+        if ATTAINABLE:
+            out[name]["attainable"] = ATTAINABLE["GBps"]
+            out[name]["frac_of_attainable"] = gbs / ATTAINABLE["GBps"]
     dom = max(kern, key=lambda n: kern[n][0])
     other = [n for n in kern if n != dom][0]
     return out[dom], out[other]
@@ -663,6 +710,9 @@ def main():
         log("calibration copy: 1 GiB read + 1 GiB written")
         del src, dst
     results = {}
+    if args.workload == "all" or args.workload.startswith("decode"):
+        gbs, how = attainable_read_gbps()
+        ATTAINABLE.update({"GBps": gbs, "probe": how})
     if args.workload == "all":
         results["prefill"] = bench_prefill("prefill_256k_bf16", args.steps, args.warmup, cpu)
         main_res = bench_decode("decode_1m_bf16", args.steps, args.warmup, cpu)
@@ -688,6 +738,9 @@ def main():
             line[key] = main_res[key]
     if "prefill" in results:
         line["prefill"] = results["prefill"]
+    if ATTAINABLE:
+        line["hbm_read_attainable"] = {"GBps": ATTAINABLE["GBps"], "frac_of_peak": ATTAINABLE["GBps"] / PEAK_HBM_GBS,
+                                       "probe": ATTAINABLE["probe"]}
     print(json.dumps(line), flush=True)
 
 

@@ -3,7 +3,8 @@
     python -m hierarchical_sparse_attention_hsa_amd.build
 
 Compiles every csrc/*.hip with hipcc for gfx950 and links one shared
-library.  No fast-math and no denormal flushing; packed fp32 VALU ops are
+library; the benchmark's read-bandwidth probe (measure/stream_read.hip) is
+built into a library of its own, libhsa_attn_stream.so.  No fast-math and no denormal flushing; packed fp32 VALU ops are
 disabled for device code.
 """
 from __future__ import annotations
@@ -18,6 +19,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhsa_attn.so")
+# the benchmark's read-bandwidth probe, a library of its own (measure/)
+STREAM_SRC = os.path.join(HERE, "measure", "stream_read.hip")
+STREAM_LIB = os.path.join(HERE, "libhsa_attn_stream.so")
 ARCH = "gfx950"
 
 CXXFLAGS = [
@@ -90,8 +94,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = STREAM_LIB + ".tmp"
+    cmd = [hipcc(), *CXXFLAGS, "-shared", "-o", tmp, STREAM_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, STREAM_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {STREAM_LIB}")
     return LIB
 
 

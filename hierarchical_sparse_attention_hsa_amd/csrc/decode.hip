@@ -26,7 +26,7 @@ namespace hsa_attn {
 // best on MI355X): loads in flight per lane, register double-buffering,
 // largest landmark range per workgroup, non-temporal loads.
 #ifndef HSA_ATTN_SCAN_UNROLL
-#define HSA_ATTN_SCAN_UNROLL 8
+#define HSA_ATTN_SCAN_UNROLL 16
 #endif
 #ifndef HSA_ATTN_SCAN_PREFETCH
 #define HSA_ATTN_SCAN_PREFETCH 0
