@@ -881,10 +881,10 @@ __global__ __launch_bounds__(256) void prefill_remote_kernel(const typename T::s
 }
 
 // ---- local pairs and fusion
-template <typename T, int D, int G, int KSEL>
 #ifndef HSA_ATTN_LOCAL_WAVES_PER_EU
 #define HSA_ATTN_LOCAL_WAVES_PER_EU 2
 #endif
+template <typename T, int D, int G, int KSEL>
 __global__ __launch_bounds__(kWave* G)
     __attribute__((amdgpu_waves_per_eu(HSA_ATTN_LOCAL_WAVES_PER_EU))) void prefill_local_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ kk,
