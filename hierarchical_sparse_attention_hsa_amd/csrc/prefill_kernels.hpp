@@ -933,10 +933,28 @@ __global__ __launch_bounds__(kWave* G)
     const int64_t base = (((int64_t)b * Hq + h) * T_q + tok) * k;
     int ci[KSEL];
     float sc[KSEL];
+    if (k % 4 == 0) {
+      // the row's slots as 16-byte loads (its row starts 16-byte aligned);
+      // padding slots hold -1 / -inf
 #pragma unroll
-    for (int e = 0; e < KSEL; ++e) {
-      ci[e] = (e < k) ? sel_idx[base + e] : -1;
-      sc[e] = (e < k && ci[e] >= 0) ? sel_score[base + e] : -__builtin_inff();
+      for (int e4 = 0; e4 < KSEL / 4; ++e4) {
+        const bool in = 4 * e4 < k;
+        const u32x4 c4 = in ? *reinterpret_cast<const u32x4*>(sel_idx + base + 4 * e4)
+                            : u32x4{~0u, ~0u, ~0u, ~0u};
+        const f32x4 s4 = in ? *reinterpret_cast<const f32x4*>(sel_score + base + 4 * e4)
+                            : f32x4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ci[4 * e4 + u] = (int)c4[u];
+          sc[4 * e4 + u] = (int)c4[u] >= 0 ? s4[u] : -__builtin_inff();
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < KSEL; ++e) {
+        ci[e] = (e < k) ? sel_idx[base + e] : -1;
+        sc[e] = (e < k && ci[e] >= 0) ? sel_score[base + e] : -__builtin_inff();
+      }
     }
     const float smax = sc[0];
     float w[KSEL], den = 0.0f;
@@ -948,8 +966,18 @@ __global__ __launch_bounds__(kWave* G)
     const float inv = 1.0f / den;
     // a pair with a bucket position (pair_pos >= 0) was attended chunk-major
     int pp[KSEL];
+    if (k % 4 == 0) {
 #pragma unroll
-    for (int e = 0; e < KSEL; ++e) pp[e] = ci[e] >= 0 ? pair_pos[base + e] : 0;
+      for (int e4 = 0; e4 < KSEL / 4; ++e4) {
+        const u32x4 p4 = 4 * e4 < k ? *reinterpret_cast<const u32x4*>(pair_pos + base + 4 * e4)
+                                    : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pp[4 * e4 + u] = ci[4 * e4 + u] >= 0 ? (int)p4[u] : 0;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < KSEL; ++e) pp[e] = ci[e] >= 0 ? pair_pos[base + e] : 0;
+    }
 #pragma unroll
     for (int e = 0; e < KSEL; ++e) {
       if (ci[e] >= 0 && pp[e] < 0) {
