@@ -478,12 +478,30 @@ void prefill_select_kernel(
   }
   const int64_t base = (((int64_t)b * Hq + h) * T_len + t_row) * k;
   if (t_row < T_len) {
+    if (k % 4 == 0) {  // the row's slots as 16-byte stores (its row starts 16-byte aligned)
 #pragma unroll
-    for (int e = 0; e < KSEL; ++e) {
-      if (e < k) {
-        const bool ok = oi[e] != INT_MAX;
-        sel_idx[base + e] = ok ? oi[e] : -1;
-        sel_score[base + e] = ok ? ss[e] : -__builtin_inff();
+      for (int e4 = 0; e4 < KSEL / 4; ++e4) {
+        if (4 * e4 < k) {
+          u32x4 i4;
+          f32x4 s4;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const bool ok = oi[4 * e4 + u] != INT_MAX;
+            i4[u] = ok ? (uint32_t)oi[4 * e4 + u] : ~0u;
+            s4[u] = ok ? ss[4 * e4 + u] : -__builtin_inff();
+          }
+          *reinterpret_cast<u32x4*>(sel_idx + base + 4 * e4) = i4;
+          *reinterpret_cast<f32x4*>(sel_score + base + 4 * e4) = s4;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < KSEL; ++e) {
+        if (e < k) {
+          const bool ok = oi[e] != INT_MAX;
+          sel_idx[base + e] = ok ? oi[e] : -1;
+          sel_score[base + e] = ok ? ss[e] : -__builtin_inff();
+        }
       }
     }
   }
@@ -535,12 +553,24 @@ void prefill_select_kernel(
   }
   __syncthreads();
   if (t_row < T_len) {
+    auto pos_of = [&](int e) {
+      const uint32_t sr = slot_rank[e];
+      return sr == ~0u ? -1 : (int)hw[sr >> 16] + (int)(sr & 0xffffu);
+    };
+    if (k % 4 == 0) {
 #pragma unroll
-    for (int e = 0; e < KSEL; ++e) {
-      if (e < k) {
-        const uint32_t sr = slot_rank[e];
-        pair_pos[base + e] = sr == ~0u ? -1 : (int)hw[sr >> 16] + (int)(sr & 0xffffu);
+      for (int e4 = 0; e4 < KSEL / 4; ++e4) {
+        if (4 * e4 < k) {
+          u32x4 p4;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) p4[u] = (uint32_t)pos_of(4 * e4 + u);
+          *reinterpret_cast<u32x4*>(pair_pos + base + 4 * e4) = p4;
+        }
       }
+    } else {
+#pragma unroll
+      for (int e = 0; e < KSEL; ++e)
+        if (e < k) pair_pos[base + e] = pos_of(e);
     }
   }
 }
