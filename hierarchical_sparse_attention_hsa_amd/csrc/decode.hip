@@ -461,9 +461,10 @@ __global__ __launch_bounds__(kWave* G) void decode_merge_kernel(const float2* __
 // (measured 5% faster at 1M).
 constexpr int kAttnWaves = 1;
 // One wave per distinct selected chunk of a (b, g) group; waves are
-// independent (no LDS, no barriers).  Logits of all G heads on MFMA:
-// S^T[token][head] = K_c . q_head (A = the chunk's keys, B = the group's
-// queries padded to 32 columns); each head's softmax stays in the two lanes
+// independent (wave-private LDS, no barriers).  Logits of all G heads on
+// MFMA: S^T[token][head] = K_c . q_head (A = the chunk's keys, staged in
+// LDS by whole-line direct loads, B = the group's queries padded to 32
+// columns); each head's softmax stays in the two lanes
 // that hold its column.  P.V on the VALU: lane l owns value rows
 // l/LPR + RPI*i and a 16-byte column slice; the probabilities go through a
 // wave-private LDS table [token][head]; a cross-lane sum finishes each
@@ -509,15 +510,22 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void decode_attn_kernel(const t
 #pragma unroll
     for (int s = 0; s < KCH; ++s) load_frag_global(qf[s], qp + 16 * s, okq);
   }
-  // every load of the tile is issued before any use: keys as A operands of
-  // both 32-token blocks, and the first pass of V slices (lane owns rows
+  // every load of the tile is issued before any use: the key tile into LDS
+  // by direct global->LDS loads (whole 1 KiB pieces; row r's 16-byte slots
+  // XOR-swizzled by r & 7 on the global side; read back as the A operands
+  // of both 32-token blocks), and the first pass of V slices (lane owns rows
   // RPI*i + lane/LPR, elements (lane%LPR)*EPS..)
-  Frag<T> ka[2][KCH];
+  constexpr int ROWB = D * T::kBytes, NSL = ROWB / 16, KTB = S * ROWB, NKI = KTB / (kWave * 16);
+  __shared__ __align__(16) char ktl[kAttnWaves][KTB];
+  {
+    const char* kb = reinterpret_cast<const char*>(ktile);
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const st* kp = ktile + (int64_t)(32 * tb + (lane & 31)) * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < KCH; ++s) load_frag_global(ka[tb][s], kp + 16 * s, true);
+    for (int ii = 0; ii < NKI; ++ii) {
+      const int L = ii * kWave + lane, t = L / NSL, sp = L % NSL;
+      __builtin_amdgcn_global_load_lds(kb + t * ROWB + ((sp ^ (t & 7)) * 16),
+                                       (__attribute__((address_space(3))) void*)(ktl[wave] + ii * kWave * 16), 16,
+                                       0, 0);
+    }
   }
   u32x4 vr[VLP];
   const int vcol = (lane % LPR) * EPS;
@@ -527,10 +535,28 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void decode_attn_kernel(const t
     vr[i] = *reinterpret_cast<const u32x4*>(vtile + (int64_t)(RPI * i + vrow0) * D + vcol);
   __builtin_amdgcn_sched_barrier(0);
   f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  // the queries and the key tile are in (the value loads may still fly)
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VLP) : "memory");
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
+  for (int tb = 0; tb < 2; ++tb) {
+    const char* row = ktl[wave] + (32 * tb + (lane & 31)) * ROWB;
 #pragma unroll
-    for (int s = 0; s < KCH; ++s) mfma(sacc[tb], ka[tb][s], qf[s]);
+    for (int s = 0; s < KCH; ++s) {
+      Frag<T> a;
+      if constexpr (T::kBytes == 2) {
+        a.load16(row + (((2 * s + half) ^ (lane & 7)) * 16));
+      } else {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(row + (((4 * s + 2 * half) ^ (lane & 7)) * 16));
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(row + (((4 * s + 2 * half + 1) ^ (lane & 7)) * 16));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a.v[e] = x0[e];
+          a.v[4 + e] = x1[e];
+        }
+      }
+      mfma(sacc[tb], a, qf[s]);
+    }
+  }
 
   // softmax per head column: lane l (l%32 = head) holds tokens
   // 32*tb + tile_row(r, half); its partner l^32 holds the rest
