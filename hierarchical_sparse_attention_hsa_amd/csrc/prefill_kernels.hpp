@@ -870,14 +870,37 @@ __global__ __launch_bounds__(256) void prefill_remote_kernel(const typename T::s
   wait_loads();
   __syncthreads();
   const float cexp = scale * 1.4426950408889634f;
+  // the block's query rows come into the wave's stage by direct
+  // global->LDS loads, whole rows per load (row r's 16-byte slots
+  // XOR-swizzled by r & 7), when 32 rows fit the stage; else as per-lane
+  // MFMA fragments (which touch 32 rows per load)
+  constexpr int QROWB = D * T::kBytes, QNSL = QROWB / 16, QRPI = kWave / QNSL;
+  constexpr bool kQStage = 32 * QROWB <= 32 * kStageRow * 4 && QNSL >= 8 && kWave % QNSL == 0;
   for (int blk = wave; begin + 32 * blk < end; blk += 4) {
     const int p = begin + 32 * blk + (lane & 31);
     const bool ok = p < end;
     const int64_t row = ok ? pairs[p] : 0;
     Frag<T> qf[KCH];
-    const st* qp = q + row * D + 8 * half;
+    if constexpr (kQStage) {
+      char* qs = reinterpret_cast<char*>(stg);
+      const char* qb = reinterpret_cast<const char*>(q);
 #pragma unroll
-    for (int s = 0; s < KCH; ++s) load_frag_global(qf[s], qp + 16 * s, ok);
+      for (int ii = 0; ii < 32 / QRPI; ++ii) {
+        const int r = ii * QRPI + lane / QNSL, sp = lane % QNSL;
+        const int64_t rr = __shfl(row, r);  // row r's query (a valid row for past-the-end pairs)
+        __builtin_amdgcn_global_load_lds(qb + rr * QROWB + ((sp ^ (r & 7)) * 16),
+                                         (__attribute__((address_space(3))) void*)(qs + ii * kWave * 16), 16, 0, 0);
+      }
+      wait_loads();
+      const char* qrow = qs + (lane & 31) * QROWB;
+#pragma unroll
+      for (int s = 0; s < KCH; ++s) load_frag_lds<T>(qf[s], qrow, lane & 7, s, half);
+      wave_lds_fence();
+    } else {
+      const st* qp = q + row * D + 8 * half;
+#pragma unroll
+      for (int s = 0; s < KCH; ++s) load_frag_global(qf[s], qp + 16 * s, ok);
+    }
     f32x16 oacc[DM];
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
