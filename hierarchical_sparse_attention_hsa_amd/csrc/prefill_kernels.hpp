@@ -90,6 +90,35 @@ __device__ __forceinline__ void list_insert(float (&s)[K], int (&id)[K], float x
   s[0] = c[0] ? x : s[0];
 }
 
+// Sort K (score, index) pairs in registers into the order (score
+// descending, index ascending) with a bitonic network (K a power of two;
+// padding entries -inf / INT_MAX sort last).
+template <int K>
+__device__ __forceinline__ void sort_pairs(float (&s)[K], int (&id)[K]) {
+  static_assert((K & (K - 1)) == 0, "bitonic network over a power of two");
+#pragma unroll
+  for (int k2 = 2; k2 <= K; k2 <<= 1) {
+#pragma unroll
+    for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const int l = i ^ j2;
+        if (l > i) {
+          // in ascending runs position i takes the element that comes first
+          const bool l_first = s[l] > s[i] || (s[l] == s[i] && id[l] < id[i]);
+          const bool swap = ((i & k2) == 0) ? l_first : !l_first;
+          const float ts = s[i];
+          const int ti = id[i];
+          s[i] = swap ? s[l] : s[i];
+          id[i] = swap ? id[l] : id[i];
+          s[l] = swap ? ts : s[l];
+          id[l] = swap ? ti : id[l];
+        }
+      }
+    }
+  }
+}
+
 // Insert x into a descending list of scores (ties are equal values, so no
 // index is needed): one v_med3 per position.
 template <int K>
@@ -174,10 +203,6 @@ void prefill_select_kernel(
   const int ja = j0 + j;  // absolute query chunk
   const int64_t n = min((int64_t)ja, Nc);
 
-  auto wave_max_i = [&](int v) {
-    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
-    return __builtin_amdgcn_readfirstlane(v);
-  };
 
   int cnt = 0;
   if (n > 0) {
@@ -416,14 +441,26 @@ void prefill_select_kernel(
     os[e] = -__builtin_inff();
     oi[e] = INT_MAX;
   }
-  {
-    // cs/ci hold the kept set in ascending chunk order; list_insert lets the
-    // newest element win score ties, so offer it from the highest index down
-    const int mx = wave_max_i(cnt);
-    for (int e = mx - 1; e >= 0; --e) {
+  // cs/ci hold the kept set (at most KSEL entries, distinct indices, in
+  // ascending chunk order)
+  if constexpr (KSEL <= 16) {
+#pragma unroll
+    for (int e = 0; e < KSEL; ++e) {
       if (e < cnt) {
-        list_insert<KSEL>(os, oi, cs[hh][e][lane], (int)ci[hh][e][lane]);
+        os[e] = cs[hh][e][lane];
+        oi[e] = (int)ci[hh][e][lane];
       }
+    }
+    sort_pairs<KSEL>(os, oi);
+  } else {
+    // (a network over 32 pairs costs more registers than the kernel has)
+    // list_insert lets the newest element win score ties, so the entries are
+    // offered from the highest index down
+    int mx = cnt;
+    for (int off = 32; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+    mx = __builtin_amdgcn_readfirstlane(mx);
+    for (int e = mx - 1; e >= 0; --e) {
+      if (e < cnt) list_insert<KSEL>(os, oi, cs[hh][e][lane], (int)ci[hh][e][lane]);
     }
   }
   // near-tie adaptive budget (value-of-information router abstract, k-th
