@@ -159,8 +159,8 @@ __global__ void bwd_scatter_kernel(const int32_t* __restrict__ sel_idx, const in
 
 // ---------------------------------------------------------------- 2. chunks
 // One workgroup (4 waves) per bucket (b, g, chunk c).  The chunk's K rows, V
-// rows and K^T (tokens in vt_pos order) are staged in LDS once.  The pairs
-// are taken in rounds of four 32-pair tiles, one per wave:
+// rows, K^T (tokens in vt_pos order) and landmark row are staged in LDS
+// once.  The pairs are taken in rounds of four 32-pair tiles, one per wave:
 //   row side (each wave, its own tile): S^T = K Q^T and the softmax, dA^T =
 //     V dO^T (dO as a bf16 head + tail), u, dlogit, ds, then
 //     dq^T = K^T dlogit^T (head + tail) plus ds L_c, written per pair; the
@@ -171,6 +171,15 @@ __global__ void bwd_scatter_kernel(const int32_t* __restrict__ sel_idx, const in
 //     owns a fixed set of 32x32 output blocks, kept in registers.
 // The chunk's dK (times 1/sqrt(D)) and dV are written once at the end
 // (zeros for a chunk nobody kept).
+// Two fp32 values rounded to bf16 (nearest even) by one packed hardware
+// conversion, the first in the low half.
+__device__ __forceinline__ uint32_t bf16_pair_bits(float a, float b) {
+  const bf16x2 t = __builtin_convertvector((f32x2{a, b}), bf16x2);
+  uint32_t u;
+  __builtin_memcpy(&u, &t, 4);
+  return u;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kk, const uint16_t* __restrict__ vv,
@@ -195,6 +204,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
   char* vs = smem + TB;
   char* kts = smem + 2 * TB;
   char* stage = smem + 3 * TB;
+  char* lms = stage + 4 * SLOT;  // the chunk's landmark row
 
   const int64_t bucket = blockIdx.x;
   const int64_t c = bucket % Nc, bg = bucket / Nc;
@@ -224,6 +234,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
       }
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
+    if (tid < D / 8)
+      *reinterpret_cast<u32x4*>(lms + 16 * tid) = *reinterpret_cast<const u32x4*>(lm + bucket * D + 8 * tid);
     wait_loads();
     __syncthreads();
   }
@@ -232,7 +244,6 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
   const int rounds = (ntiles + 3) / 4;
   const int pr = lane & 31;  // this lane's pair column
   char* my = stage + wave * SLOT;
-  const uint16_t* lrow = lm + bucket * D;  // the chunk's landmark
   f32x16 accV[NBW], accK[NBW];
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
@@ -242,31 +253,36 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
 
   // The gathered rows of a round's tile (pair id, weight, delta, q, dOut)
   // are fetched one round ahead, while the previous round's chunk side
-  // runs; the pair ids two steps ahead, while the row side runs.
-  int pid_n = 0;       // pair id of this lane's next tile
-  int pid = 0;         // ... of the tile being fetched or processed
+  // runs; the pair ids two steps ahead, while the row side runs.  Every
+  // load is issued unconditionally (a lane past the bucket's end reads
+  // element 0 of each array) and masked where its value is used, so the
+  // compiler counts each load's completion instead of waiting for all of
+  // them at the first use.
+  int pid_raw = 0;     // pair id loaded for this lane's next tile
+  bool pid_ok = false;
+  int pid = 0;         // pair id of the tile being fetched or processed
   bool ok = false;
-  float w = 0.0f, dlt = 0.0f;
+  float wraw = 0.0f, draw = 0.0f;
   u32x4 qraw[KCH];
   f32x4 graw[2 * KCH];
   auto fetch_id = [&](int t) {
     const int p = begin + 32 * t + pr;
-    pid_n = (t < ntiles && p < end) ? pairs[p] : -1;
+    pid_ok = t < ntiles && p < end;
+    pid_raw = pairs[pid_ok ? p : 0];
   };
   auto fetch_rows = [&]() {
-    pid = pid_n;
-    ok = pid >= 0;
-    const int64_t row = ok ? pid / k : 0;
-    w = ok ? wts[pid] : 0.0f;
-    dlt = ok ? delta[row] : 0.0f;
+    ok = pid_ok;
+    pid = ok ? pid_raw : 0;
+    const int64_t row = pid / k;
+    wraw = wts[pid];
+    draw = delta[row];
     const uint16_t* qp = q + row * D + 8 * half;
     const float* gp = dout + row * D + 8 * half;
-    const f32x4 z{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KCH; ++s) {
-      qraw[s] = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
-      graw[2 * s] = ok ? reinterpret_cast<const f32x4*>(gp + 16 * s)[0] : z;
-      graw[2 * s + 1] = ok ? reinterpret_cast<const f32x4*>(gp + 16 * s)[1] : z;
+      qraw[s] = *reinterpret_cast<const u32x4*>(qp + 16 * s);
+      graw[2 * s] = reinterpret_cast<const f32x4*>(gp + 16 * s)[0];
+      graw[2 * s + 1] = reinterpret_cast<const f32x4*>(gp + 16 * s)[1];
     }
   };
   fetch_id(wave);
@@ -279,11 +295,12 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
       char* Lt = my + SA;
       char* Ot = my + 2 * SA;
       char* Qt = my + 2 * SA + SO;
+      const float w = ok ? wraw : 0.0f, dlt = ok ? draw : 0.0f;
       // q (B operand: pair column, dims 16 s + 8 half + 0..7) and its staging
       Frag<BF16> qf[KCH];
 #pragma unroll
       for (int s = 0; s < KCH; ++s) {
-        const u32x4 raw = qraw[s];
+        const u32x4 raw = ok ? qraw[s] : u32x4{0u, 0u, 0u, 0u};
         qf[s].v = as_bf16x8(raw);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -295,7 +312,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
       Frag<BF16> dh[KCH], dtl[KCH];
 #pragma unroll
       for (int s = 0; s < KCH; ++s) {
-        const f32x4 g0 = graw[2 * s], g1 = graw[2 * s + 1];
+        const f32x4 z{0.f, 0.f, 0.f, 0.f};
+        const f32x4 g0 = ok ? graw[2 * s] : z, g1 = ok ? graw[2 * s + 1] : z;
         float x[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -304,9 +322,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
         }
         split_bf16(x, dh[s], dtl[s]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 8; i += 2) {
+          const uint32_t pb = bf16_pair_bits(x[i], x[i + 1]);
           const int d = 16 * s + 8 * half + i;
-          *reinterpret_cast<uint16_t*>(Ot + (d * 32 + pr) * 2) = (uint16_t)f32_to_bf16_bits(x[i]);
+          *reinterpret_cast<uint16_t*>(Ot + (d * 32 + pr) * 2) = (uint16_t)pb;
+          *reinterpret_cast<uint16_t*>(Ot + ((d + 1) * 32 + pr) * 2) = (uint16_t)(pb >> 16);
         }
       }
       // S^T = K Q^T over the chunk's two 32-token blocks, softmax per pair
@@ -373,10 +393,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int t0 = tile_row(i, half), t1 = 32 + tile_row(i, half);
-        *reinterpret_cast<uint16_t*>(At + (t0 * 32 + pr) * 2) = (uint16_t)f32_to_bf16_bits(s0[i]);
-        *reinterpret_cast<uint16_t*>(At + (t1 * 32 + pr) * 2) = (uint16_t)f32_to_bf16_bits(s1[i]);
-        *reinterpret_cast<uint16_t*>(Lt + (t0 * 32 + pr) * 2) = (uint16_t)f32_to_bf16_bits(d0[i] + dss);
-        *reinterpret_cast<uint16_t*>(Lt + (t1 * 32 + pr) * 2) = (uint16_t)f32_to_bf16_bits(d1[i] + dss);
+        const uint32_t pa = bf16_pair_bits(s0[i], s1[i]), pl = bf16_pair_bits(d0[i] + dss, d1[i] + dss);
+        *reinterpret_cast<uint16_t*>(At + (t0 * 32 + pr) * 2) = (uint16_t)pa;
+        *reinterpret_cast<uint16_t*>(At + (t1 * 32 + pr) * 2) = (uint16_t)(pa >> 16);
+        *reinterpret_cast<uint16_t*>(Lt + (t0 * 32 + pr) * 2) = (uint16_t)pl;
+        *reinterpret_cast<uint16_t*>(Lt + (t1 * 32 + pr) * 2) = (uint16_t)(pl >> 16);
       }
       // dq^T = K^T dlogit^T + ds L_c, scaled, one fp32 row per pair
       f32x16 qa[DM];
@@ -406,7 +427,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const int col = out_col(dm, q4, half);
-            const u32x2 lw = *reinterpret_cast<const u32x2*>(lrow + col);
+            const u32x2 lw = *reinterpret_cast<const u32x2*>(lms + 2 * col);
             const float l0 = bf16_lo(lw[0]), l1 = bf16_hi(lw[0]), l2 = bf16_lo(lw[1]), l3 = bf16_hi(lw[1]);
             *reinterpret_cast<f32x4*>(op + col) =
                 f32x4{fmaf(ds, l0, qa[dm][4 * q4]) * scale, fmaf(ds, l1, qa[dm][4 * q4 + 1]) * scale,
@@ -571,7 +592,7 @@ static hipError_t launch_backward_d(const BackwardArgs& a, const BackwardPlan& p
     mark_launch(st);
     hipLaunchKernelGGL((prefill_vt_kernel<BF16, D>), dim3((unsigned)nb), dim3(256), 0, st, kk, kt, g.T, g.Nc);
     mark_launch(st);
-    constexpr size_t lds = 3 * kChunk * D * 2 + 4 * (2 * kChunk * 32 * 2 + 2 * D * 32 * 2);
+    constexpr size_t lds = 3 * kChunk * D * 2 + 4 * (2 * kChunk * 32 * 2 + 2 * D * 32 * 2) + 2 * D;
     static_assert(lds <= 160 * 1024, "chunk kernel LDS");
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_chunk_kernel<D>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)

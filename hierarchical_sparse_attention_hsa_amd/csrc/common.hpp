@@ -47,13 +47,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) {
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 // fp64 -> bf16 bits with a single rounding to nearest even.  The value is
 // first truncated to fp32 with the sticky bit folded into the last place
 // (round-to-odd), which keeps 24 >= 8 + 2 bits, so the final RNE step to bf16

@@ -365,13 +365,13 @@ void prefill_select_kernel(
 
     // ---- pass 2: collect the k best in ascending chunk order.  Each wave
     // recomputes only the tiles it marked, streaming their landmark
-    // fragments from L2 into registers (double-buffered; no barriers).
+    // fragments from L2 into registers (no barriers).
     const float tau = ls[KSEL - 1];
     int quota = KSEL;  // entries equal to tau that still fit
 #pragma unroll
     for (int e = 0; e < KSEL; ++e) quota -= ls[e] > tau;
     const st* lmr = lm + ((int64_t)b * Hkv + g) * Nc * D + 8 * half;
-    Frag<T> fa[KCH], fb[KCH];
+    Frag<T> fa[KCH];
     auto fetch = [&](Frag<T>(&f)[KCH], int ti) {
       const int64_t c = min((int64_t)ti * 32 + (lane & 31), n - 1);
       const st* p = lmr + c * D;
@@ -385,13 +385,7 @@ void prefill_select_kernel(
       while (ti < ntiles && !marked(ti)) ++ti;
       return ti;
     };
-    auto pass2 = [&](const Frag<T>(&f)[KCH], int ti) {
-      f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-      for (int s2 = 0; s2 < KCH; ++s2) {
-        mfma(acc0, f[s2], qf[0][s2]);
-        mfma(acc1, f[s2], qf[1][s2]);
-      }
+    auto collect = [&](f32x16& acc0, f32x16& acc1, int ti) {
       const bool top = (int64_t)ti * 32 + 32 > n;
       if (!top && !__ballot(row_max(acc0, acc1) >= tau)) return;
       float lo[16], hi[16];
@@ -419,17 +413,28 @@ void prefill_select_kernel(
         }
       }
     };
+    // One register buffer: a tile's fragments are consumed by its MFMAs,
+    // then the next marked tile's loads are issued (unconditionally: past
+    // the last tile they re-read the last landmark) and fly while this
+    // tile's candidates are collected.  (Two buffers do not fit the
+    // register budget of three waves per SIMD: the spill code's reloads
+    // waited for every load in flight.)
     int ti = next_marked(0);
-    if (ti < ntiles) fetch(fa, ti);
-    while (ti < ntiles) {
-      const int t1 = next_marked(ti + 1);
-      if (t1 < ntiles) fetch(fb, t1);
-      pass2(fa, ti);
-      if (t1 >= ntiles) break;
-      const int t2 = next_marked(t1 + 1);
-      if (t2 < ntiles) fetch(fa, t2);
-      pass2(fb, t1);
-      ti = t2;
+    if (ti < ntiles) {
+      fetch(fa, ti);
+      while (true) {
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int s2 = 0; s2 < KCH; ++s2) {
+          mfma(acc0, fa[s2], qf[0][s2]);
+          mfma(acc1, fa[s2], qf[1][s2]);
+        }
+        const int t1 = next_marked(ti + 1);
+        fetch(fa, t1);
+        collect(acc0, acc1, ti);
+        if (t1 >= ntiles) break;
+        ti = t1;
+      }
     }
   }
   const int64_t t_row = (int64_t)j * kChunk + lane;
@@ -913,10 +918,17 @@ __global__ __launch_bounds__(256) void prefill_remote_kernel(const typename T::s
   // MFMA fragments (which touch 32 rows per load)
   constexpr int QROWB = D * T::kBytes, QNSL = QROWB / 16, QRPI = kWave / QNSL;
   constexpr bool kQStage = 32 * QROWB <= 32 * kStageRow * 4 && QNSL >= 8 && kWave % QNSL == 0;
-  for (int blk = wave; begin + 32 * blk < end; blk += 4) {
+  // the pair ids of the wave's next block are loaded one block ahead (a
+  // lane past the bucket's end reads the bucket's first pair, a valid row)
+  auto pair_row = [&](int blk) {
     const int p = begin + 32 * blk + (lane & 31);
-    const bool ok = p < end;
-    const int64_t row = ok ? pairs[p] : 0;
+    return pairs[p < end ? p : begin];
+  };
+  int32_t row_next = pair_row(wave);
+  for (int blk = wave; begin + 32 * blk < end; blk += 4) {
+    const bool ok = begin + 32 * blk + (lane & 31) < end;
+    const int64_t row = row_next;
+    row_next = pair_row(blk + 4);
     Frag<T> qf[KCH];
     if constexpr (kQStage) {
       char* qs = reinterpret_cast<char*>(stg);
