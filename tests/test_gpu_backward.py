@@ -100,3 +100,46 @@ def test_backward_is_linear_in_dout():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.allclose(2 * x, y, rtol=1e-2, atol=1e-5)
+
+
+def test_rows_without_pairs_do_not_leak():
+    """Lanes past the end of a bucket load the first pair's rows and mask
+    the values where they are used.  Rows of the first 64 tokens keep no
+    pair (no complete chunk lies before them); filling their q with +inf and
+    their dOut with NaN must leave every gradient as it is with finite
+    values there (dq bit for bit: its partials do not depend on the order
+    of a bucket's pairs; dK, dV within the order's rounding), and their dq
+    rows zero."""
+    B, Hq, Hkv, T, D, k = 1, 4, 1, 64 * 12 + 30, 128, 4
+    print(f"backward poisoned-row case {(B, Hq, Hkv, T, D, k)}", flush=True)
+    q, kc, vc = small_inputs(B, Hq, Hkv, T, D, "bf16", seed=321)
+    dout = np.random.default_rng(322).standard_normal((B, Hq, T, D)).astype(np.float32)
+    out, sel, score, _ = O.prefill(f64(q), f64(kc), f64(vc), S, k, "bf16")
+    assert (sel[:, :, :S] < 0).all()
+    qd, kd, vd = q.cuda(), kc.cuda(), vc.cuda()
+    L = torch.empty((B, Hkv, T // S, D), dtype=torch.bfloat16, device="cuda")
+    hsa.hsa_build_landmarks(kd, L, S)
+    sel_t = torch.from_numpy(sel.astype(np.int32)).cuda()
+    score_t = torch.from_numpy(score.astype(np.float32)).cuda()
+    out_t = torch.from_numpy(out.astype(np.float32)).cuda()
+
+    def run(qx, gx):
+        grads = [torch.full((B, h, T, D), 7.0, device="cuda") for h in (Hq, Hkv, Hkv)]
+        hsa.hsa_backward_prefill(qx, kd, vd, L, out_t, gx, sel_t, score_t, S, dq=grads[0], dk=grads[1],
+                                 dv=grads[2])
+        torch.cuda.synchronize()
+        return [g.cpu().numpy() for g in grads]
+
+    clean = run(qd, torch.from_numpy(dout).cuda())
+    qp = qd.clone()
+    qp[:, :, :S] = float("inf")
+    gp = torch.from_numpy(dout).cuda()
+    gp[:, :, :S] = float("nan")
+    poisoned = run(qp, gp)
+    for g in poisoned:
+        assert np.isfinite(g).all()
+    assert np.array_equal(poisoned[0], clean[0])
+    assert (poisoned[0][:, :, :S] == 0).all()
+    for name, a, b in (("dk", poisoned[1], clean[1]), ("dv", poisoned[2], clean[2])):
+        scale = np.abs(b).max() + 1e-30
+        assert np.abs(a - b).max() <= 1e-5 * scale, name
