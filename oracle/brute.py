@@ -141,3 +141,99 @@ def prefill(Q, K, V, S: int, k: int, dtype: str):
         sels.append(sb)
         scs.append(cb)
     return outs, sels, scs
+
+
+# ---------------------------------------------------------------------------
+# backward of one query row, term by term
+# ---------------------------------------------------------------------------
+
+def backward_query(q, K, V, S: int, sel, g, dtype: str):
+    """Gradient of one query row's output with respect to q, K and V, written
+    as explicit sums of elementary products (pure Python, no shared helpers).
+
+    Forward of the row (card "Core Technique" / "Implementation"): landmark
+    L_c = mean of chunk c's keys (stored rounded; the rounding is taken as
+    the identity for the gradient, so each of the chunk's keys receives 1/S
+    of the landmark's gradient), s_c = q.L_c/sqrt(D) over the kept chunks
+    sel (fixed: selection is piecewise constant), w = softmax(s), in-chunk
+    probabilities a_ct = softmax_t(q.k_t/sqrt(D)), o_c = sum_t a_ct v_t,
+    out = sum_c w_c o_c.  g is dLoss/dout of the row.
+
+    Each gradient entry is the sum of a list of products; the chain rule
+    gives, with every dot product opened into its D products:
+      dv_te   <- a_ct w_c g_e
+      dlogit_ct = sum_e a_ct w_c g_e v_te - sum_t' sum_e a_ct a_ct' w_c g_e v_t'e
+      ds_c      = sum_t sum_e a_ct w_c g_e v_te - sum_e w_c g_e out_e
+      dq_d    = (sum_c sum_t dlogit_ct k_td + sum_c ds_c L_cd) / sqrt(D)
+      dk_td  <- (dlogit_ct + ds_c / S) q_d / sqrt(D)
+    For every entry this returns three numbers: the sum of the products (the
+    gradient), the sum of their absolute values (the magnitude sum that
+    bounds the error of a lower-precision evaluation of the same products),
+    and the sum of |product / out_e| over the products holding a factor
+    out_e (how much an error in the row's output, as used for the
+    gradient, can move the entry per unit of max-abs output error).
+
+    Returns (dq, dK, dV): dq is a list of D triples (value, magnitude,
+    out_sensitivity); dK and dV map a token index to such a list.
+    """
+    D = len(q)
+    sig = 1.0 / math.sqrt(D)
+    sel = [c for c in sel if c >= 0]
+    zero = [(0.0, 0.0, 0.0)] * D
+    if not sel:
+        return list(zero), {}, {}
+    lms = {c: landmark(K[c * S:(c + 1) * S], dtype) for c in sel}
+    s = [sum(q[d] * lms[c][d] for d in range(D)) * sig for c in sel]
+    w = _softmax(s)
+    a, o = {}, {}
+    for c in sel:
+        logits = [sum(q[d] * K[t][d] for d in range(D)) * sig for t in range(c * S, c * S + S)]
+        pr = _softmax(logits)
+        for i in range(S):
+            a[c, c * S + i] = pr[i]
+        o[c] = [sum(pr[i] * V[c * S + i][e] for i in range(S)) for e in range(D)]
+    out = [sum(w[j] * o[c][e] for j, c in enumerate(sel)) for e in range(D)]
+
+    # the products of dlogit_ct and of ds_c, each as (value, |value|, |value / out_e| if it holds out_e)
+    def dlogit_terms(j, c, t):
+        terms = []
+        for e in range(D):
+            terms.append(a[c, t] * w[j] * g[e] * V[t][e])
+        for t2 in range(c * S, c * S + S):
+            for e in range(D):
+                terms.append(-a[c, t] * a[c, t2] * w[j] * g[e] * V[t2][e])
+        return [(x, abs(x), 0.0) for x in terms]
+
+    def ds_terms(j, c):
+        terms = []
+        for t in range(c * S, c * S + S):
+            for e in range(D):
+                x = a[c, t] * w[j] * g[e] * V[t][e]
+                terms.append((x, abs(x), 0.0))
+        for e in range(D):
+            x = -w[j] * g[e] * out[e]
+            terms.append((x, abs(x), abs(w[j] * g[e])))
+        return terms
+
+    def scaled(terms, f):
+        return [(x * f, m * abs(f), o_ * abs(f)) for x, m, o_ in terms]
+
+    def total(terms):
+        return (sum(x for x, _, _ in terms), sum(m for _, m, _ in terms), sum(o_ for _, _, o_ in terms))
+
+    dq = []
+    for d in range(D):
+        terms = []
+        for j, c in enumerate(sel):
+            for t in range(c * S, c * S + S):
+                terms += scaled(dlogit_terms(j, c, t), K[t][d] * sig)
+            terms += scaled(ds_terms(j, c), lms[c][d] * sig)
+        dq.append(total(terms))
+    dK, dV = {}, {}
+    for j, c in enumerate(sel):
+        ds = ds_terms(j, c)
+        for t in range(c * S, c * S + S):
+            dl = dlogit_terms(j, c, t)
+            dK[t] = [total(scaled(dl, q[d] * sig) + scaled(ds, q[d] * sig / S)) for d in range(D)]
+            dV[t] = [(a[c, t] * w[j] * g[e], abs(a[c, t] * w[j] * g[e]), 0.0) for e in range(D)]
+    return dq, dK, dV

@@ -390,10 +390,16 @@ class BackwardResult:
     abs_dK: np.ndarray
     abs_dV: np.ndarray
     abs_dq: np.ndarray
+    # how far an error in the rows' outputs, as the gradient uses them (in
+    # delta = g.out), can move each entry per unit of max-abs output error
+    out_dK: np.ndarray
+    out_dq: np.ndarray
+    # the rows' outputs under the given selection (the forward, fp64)
+    out: np.ndarray
 
 
 def hsa_rows_backward(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.ndarray, Lg: np.ndarray,
-                      S: int, sel, dout: np.ndarray) -> BackwardResult:
+                      S: int, sel, dout: np.ndarray, delta_out=None) -> BackwardResult:
     """Gradients of the layer's output rows with respect to q, K and V.
 
     The forward (hsa_rows) for a row is: s_c = q.L_c/sqrt(D) over its kept
@@ -414,12 +420,22 @@ def hsa_rows_backward(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.nda
       dk_t += (dlogit_ct q + ds_c q / S) / sqrt(D)    for t in chunk c
 
     q: [R, D] rows at positions pos; Kg, Vg: [T, D]; Lg: landmarks; sel: one
-    index list per row (its kept chunks); dout: [R, D].  Returns dq [R, D] and
+    index list per row (its kept chunks); dout: [R, D]; delta_out: [R, D]
+    output rows to use in delta = g.out in place of the forward's own (the
+    sensitivity pins perturb them).  Returns dq [R, D] and
     the rows' contributions dK, dV [T, D], plus the magnitude sums
     abs_dV = sum a_ct |do_c|,
     abs_dK = sum (a_ct (A_ct + U_c) + (U_c + w_c E) / S) |q| / sqrt(D),
     abs_dq = (sum a_ct (A_ct + U_c) |k_t| + sum (U_c + w_c E) |L_c|) / sqrt(D)
-    with A_ct = |do_c| . |v_t|, U_c = sum_t a_ct A_ct and E = |g| . |out|.
+    with A_ct = |do_c| . |v_t|, U_c = sum_t a_ct A_ct and E = |g| . |out|:
+    the sums of the absolute values of the elementary products each entry
+    adds up once every dot product (da, u, delta) is opened, which bound the
+    error of evaluating those products in lower precision (cancellation
+    inside dlogit and ds included); and the output sensitivities
+    out_dq = sum_c w_c |L_c| (sum_e |g_e|) / sqrt(D),
+    out_dK = sum w_c (sum_e |g_e|) / S |q| / sqrt(D),
+    the bound on how much an output row that is off by at most eps in every
+    element moves dq and dK (through delta = g.out inside ds), per unit eps.
     """
     q = np.asarray(q, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
@@ -432,6 +448,9 @@ def hsa_rows_backward(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.nda
     abs_dK = np.zeros((T, D))
     abs_dV = np.zeros((T, D))
     abs_dq = np.zeros((R, D))
+    out_dK = np.zeros((T, D))
+    out_dq = np.zeros((R, D))
+    out_rows = np.zeros((R, D))
     for r in range(R):
         chunks = np.asarray(sel[r], dtype=np.int64)
         chunks = chunks[chunks >= 0]
@@ -448,6 +467,9 @@ def hsa_rows_backward(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.nda
         a /= a.sum(axis=1, keepdims=True)
         o = np.einsum("mt,mtd->md", a, Vc)                    # [m, D]
         out = w @ o
+        out_rows[r] = out
+        if delta_out is not None:
+            out = np.asarray(delta_out[r], dtype=np.float64)
         do = w[:, None] * g[None, :]                          # [m, D]
         ds = w * (o @ g - out @ g)                            # [m]
         da = np.einsum("mtd,md->mt", Vc, do)                  # do_c . v_t
@@ -464,7 +486,10 @@ def hsa_rows_backward(q: np.ndarray, pos: np.ndarray, Kg: np.ndarray, Vg: np.nda
         abs_dK[ti] += ((mag_l + mag_s[:, None] / S).reshape(-1, 1) * np.abs(q[r])[None, :]) * sig
         abs_dV[ti] += (a[:, :, None] * np.abs(do)[:, None, :]).reshape(-1, D)
         abs_dq[r] = (np.einsum("mt,mtd->d", mag_l, np.abs(Kc)) + mag_s @ np.abs(Lg[chunks])) * sig
-    return BackwardResult(dq, dK, dV, abs_dK, abs_dV, abs_dq)
+        g1 = np.abs(g).sum()                                  # |g . err| <= eps * g1
+        out_dq[r] = (w @ np.abs(Lg[chunks])) * g1 * sig
+        out_dK[ti] += (np.repeat(w, S)[:, None] * np.abs(q[r])[None, :]) * (g1 * sig / S)
+    return BackwardResult(dq, dK, dV, abs_dK, abs_dV, abs_dq, out_dK, out_dq, out_rows)
 
 
 def prefill_backward(Q, K, V, S: int, k: int, dtype: str, dOut, sel_idx=None):

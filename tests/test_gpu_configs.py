@@ -263,9 +263,14 @@ def test_backward_256k_bf16_sampled():
     selection validated against the oracle's rule first (exact, or a valid
     set within the near-tie band), and the oracle then differentiates with
     that same selection.  The GPU backward uses the GPU forward's output for
-    delta = dOut . out, so the forward's own rounding enters ds: the bound is
-    the bf16 one, 9e-3 of the magnitude sums (plus 1e-6), for dq of sampled
-    rows and for dK, dV of two chunks summed over every row that kept them."""
+    delta = dOut . out, so the forward's own error enters ds; the bounds are
+    those of the backward's arithmetic (dq: 2e-4 of the magnitude sums, the
+    head + tail operands; dK, dV: 9e-3, the bf16 operands; plus 1e-6) plus
+    that forward error: the max-abs difference eps between the GPU output
+    row and the oracle's, measured per row (and itself held to the forward
+    tolerance), times the oracle's output sensitivities (out_dq, out_dK),
+    for dq of sampled rows and for dK, dV of two chunks summed over every
+    row that kept them."""
     w = WORKLOADS["backward_256k_bf16"]
     S, D = w.S, w.D
     G = w.Hq // w.Hkv
@@ -287,6 +292,12 @@ def test_backward_256k_bf16_sampled():
         pos_t = torch.as_tensor(pos, device="cuda")
         return host64(q[b, h, pos_t]), sel[b, h, pos_t].cpu().numpy(), host64(dout[b, h, pos_t])
 
+    def forward_error(b, h, pos, ref):
+        """Per-row max-abs error of the GPU forward output the backward used."""
+        eps = np.abs(host64(out[b, h, torch.as_tensor(pos, device="cuda")]) - ref.out).max(axis=1)
+        assert eps.max() <= 2e-3, f"forward output error {eps.max():.3e}"
+        return eps
+
     def validated(qr, pos, Lg, sl):
         for r in range(len(pos)):
             n = int(O.num_candidates(np.array([pos[r]]), S, Nc)[0])
@@ -304,9 +315,12 @@ def test_backward_256k_bf16_sampled():
         qr, sl, gr = rows_of(b, h, pos)
         validated(qr, pos, Lh[g], sl)
         ref = O.hsa_rows_backward(qr, pos, DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lh[g], S, sl, gr)
+        eps = forward_error(b, h, pos, ref)
         got = host64(dq[b, h, torch.as_tensor(pos, device="cuda")])
         err = np.abs(got - ref.dq)
-        assert np.all(err <= 9e-3 * ref.abs_dq + 1e-6), f"dq head {h}: worst {err.max():.3e}"
+        bound = 2e-4 * ref.abs_dq + eps[:, None] * ref.out_dq + 1e-6
+        print(f"dq head {h}: forward error {eps.max():.3e}, worst error / bound {(err / bound).max():.3f}", flush=True)
+        assert np.all(err <= bound), f"dq head {h}: worst {err.max():.3e}"
     # dK, dV of two chunks of KV head 2: every (head, row) that kept them
     g = 2
     for c in (100, 3000):
@@ -314,6 +328,7 @@ def test_backward_256k_bf16_sampled():
         acc_v = np.zeros((S, D))
         abs_k = np.zeros((S, D))
         abs_v = np.zeros((S, D))
+        fwd_k = np.zeros((S, D))
         for h in range(g * G, (g + 1) * G):
             rows = torch.nonzero((sel[b, h] == c).any(dim=-1)).flatten().cpu().numpy()
             if rows.size == 0:
@@ -321,6 +336,7 @@ def test_backward_256k_bf16_sampled():
             qr, sl, gr = rows_of(b, h, rows)
             validated(qr, rows, Lh[g], sl)
             ref = O.hsa_rows_backward(qr, rows, DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lh[g], S, sl, gr)
+            fwd_k += forward_error(b, h, rows, ref).max() * ref.out_dK[c * S:(c + 1) * S]
             acc_k += ref.dK[c * S:(c + 1) * S]
             acc_v += ref.dV[c * S:(c + 1) * S]
             abs_k += ref.abs_dK[c * S:(c + 1) * S]
@@ -328,6 +344,6 @@ def test_backward_256k_bf16_sampled():
         got_k = host64(dk[b, g, c * S:(c + 1) * S])
         got_v = host64(dv[b, g, c * S:(c + 1) * S])
         print(f"chunk {c}: max |dK| {np.abs(acc_k).max():.3e}, |dV| {np.abs(acc_v).max():.3e}", flush=True)
-        assert np.all(np.abs(got_k - acc_k) <= 9e-3 * abs_k + 1e-6), f"dK chunk {c}"
+        assert np.all(np.abs(got_k - acc_k) <= 9e-3 * abs_k + fwd_k + 1e-6), f"dK chunk {c}"
         assert np.all(np.abs(got_v - acc_v) <= 9e-3 * abs_v + 1e-6), f"dV chunk {c}"
     del q, k, v, L, sel, sc, out, dq, dk, dv, dout
