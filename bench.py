@@ -133,6 +133,60 @@ def blas_threads():
         return 1
 
 
+def host_info():
+    """Where the oracle baseline ran: host cores this process may use (its
+    affinity set), the CPU model, and numpy with the BLAS it calls (and that
+    BLAS's thread count, the threads the oracle actually uses)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [f"{p.get('internal_api')} {p.get('version')} ({p.get('num_threads')} threads)"
+                for p in threadpool_info() if p.get("user_api") == "blas"]
+    except Exception:
+        pass
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": model, "numpy": np.__version__,
+            "blas": blas}
+
+
+def near_tie_rows(q_rows, Lg, n, k, rel=1e-5):
+    """Rows whose cut is a near tie under the layer's acceptance rule, counted
+    by rescoring in fp64 on the device: with m = min(k, n) < n, the m-th and
+    (m+1)-th best scores s_m, s_m+1 (q.L/sqrt(D)) differ by less than
+    rel * max(|s_m|, |s_m+1|, A_m, A_m+1), A_c = sum_d |q_d| |L_cd| / sqrt(D).
+    q_rows [R, D] and Lg [Nc, D] are device tensors in the storage dtype,
+    n [R] the rows' candidate counts (a device int64 tensor).  Returns
+    (near-tie rows, rows with a cut)."""
+    import torch
+    D = q_rows.shape[-1]
+    qd = q_rows.double()
+    Ld = Lg.double()
+    s = (qd @ Ld.T) / math.sqrt(D)
+    cols = torch.arange(Ld.shape[0], device=s.device)
+    s.masked_fill_(cols[None, :] >= n[:, None], -math.inf)
+    m = torch.clamp(n, max=k)
+    cut = m < n
+    if not bool(cut.any()):
+        return 0, 0
+    kk = min(k + 1, Ld.shape[0])
+    top, idx = torch.topk(s, kk, dim=1)
+    r = torch.arange(s.shape[0], device=s.device)
+    mi = (m - 1).clamp(min=0, max=kk - 2)
+    a, b = top[r, mi], top[r, mi + 1]
+    ia, ib = idx[r, mi], idx[r, mi + 1]
+    A = lambda i: (qd.abs() * Ld[i].abs()).sum(-1) / math.sqrt(D)  # noqa: E731
+    mu = torch.maximum(torch.maximum(a.abs(), b.abs()), torch.maximum(A(ia), A(ib)))
+    tie = cut & (a - b < rel * mu)
+    return int(tie.sum().item()), int(cut.sum().item())
+
+
 def summarize_profile(workload, prof_dir, command, kernel):
     """Turn the rocprofv3 CSVs of one workload (<workload>_kernel_stats.csv,
     _FETCH_SIZE.csv, _WRITE_SIZE.csv in prof_dir) into profiles/<kernel>.<workload>.md,
@@ -187,9 +241,79 @@ def summarize_profile(workload, prof_dir, command, kernel):
     for n, v in sorted(rows.items(), key=lambda kv: -traffic[kv[0]]):
         lines.append(f"| {n} | {len(v)} | {np.mean([f for f, _ in v]):.0f} | {np.mean([w for _, w in v]):.0f} | "
                      f"{traffic[n] / 2**30:.3f} GiB |")
+    mfma_csv = os.path.join(prof_dir, f"{workload}_MFMA.csv")
+    if os.path.exists(mfma_csv):
+        lines += mfma_summary(workload, mfma_csv, stats, short)
     with open(os.path.join(ROOT, "profiles", f"{kernel}.{workload}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+SIMD_NUM = 1024  # MI355X: 256 CUs x 4 SIMDs
+
+
+def mfma_summary(workload, csv_path, stats, short):
+    """MFMA counters of one --pmc pass (SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE and rocprofv3's derived
+    MfmaUtil = sum of the busy cycles / (max GRBM_GUI_ACTIVE x SIMD_NUM)) per
+    library kernel: the fraction of SIMD-cycles the matrix cores were busy,
+    and the bf16 flops they executed (512 per MOPS count) over the kernel's
+    average duration from the trace.  Written to profiles/<workload>.mfma.json
+    (keyed to the built library, read by the benchmark) and returned as
+    summary lines."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(float))
+    for r in csv.DictReader(open(csv_path)):
+        if "hsa_attn" not in r["Kernel_Name"]:
+            continue
+        vals[(int(r["Dispatch_Id"]), short(r["Kernel_Name"]))][r["Counter_Name"]] += float(r["Counter_Value"])
+    avg_ns = {short(r["Name"]): float(r["AverageNs"]) for r in stats}
+    per = defaultdict(list)
+    for (_, name), c in vals.items():
+        per[name].append(c)
+    out = {}
+    for name, rows in per.items():
+        util = float(np.mean([c.get("MfmaUtil", 0.0) for c in rows])) / 100.0
+        flops = float(np.mean([512.0 * c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for c in rows]))
+        ns = avg_ns.get(name)
+        out[name] = {"mfma_busy_frac": util, "mfma_bf16_flops": flops, "avg_ns": ns,
+                     "counter_tflops": flops / ns / 1e3 if ns else None,
+                     "busy_cycles": float(np.mean([c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for c in rows])),
+                     "grbm_gui_active": float(np.mean([c.get("GRBM_GUI_ACTIVE", 0.0) for c in rows]))}
+    rec = {"workload": workload, "library_sha256_16": library_digest(), "simd_num": SIMD_NUM, "kernels": out}
+    with open(os.path.join(ROOT, "profiles", f"{workload}.mfma.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    lines = ["", "## MFMA counters (--pmc, one dispatch per kernel)", "",
+             "MfmaUtil (rocprofv3's derived counter) = sum of SQ_VALU_MFMA_BUSY_CYCLES / (max GRBM_GUI_ACTIVE x "
+             f"SIMD_NUM); bf16 MFMA flops = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16, over the trace's average duration, "
+             f"against 2.5 PFLOP/s dense bf16.", "",
+             "| kernel | MfmaUtil | bf16 MFMA flops | flops / duration | of 2.5 PFLOP/s |", "|---|---|---|---|---|"]
+    for name, o in sorted(out.items(), key=lambda kv: -(kv[1]["mfma_bf16_flops"])):
+        if o["mfma_bf16_flops"] <= 0:
+            continue
+        tf = o["counter_tflops"]
+        lines.append(f"| {name} | {100 * o['mfma_busy_frac']:.1f}% | {o['mfma_bf16_flops']:.3e} | "
+                     f"{tf:.0f} TFLOP/s | {tf / PEAK_BF16_TFLOPS:.3f} |" if tf else f"| {name} | "
+                     f"{100 * o['mfma_busy_frac']:.1f}% | {o['mfma_bf16_flops']:.3e} | - | - |")
+    return lines
+
+
+def profiled_mfma(workload, kernel_prefix):
+    """Counter-based MFMA figures of a kernel from profiles/<workload>.mfma.json,
+    or None when the built library differs from the profiled one."""
+    path = os.path.join(ROOT, "profiles", f"{workload}.mfma.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("library_sha256_16") != library_digest():
+        return None
+    for name, o in rec["kernels"].items():
+        if kernel_prefix in name:
+            return {"mfma_busy_frac": o["mfma_busy_frac"],
+                    "counter_flops_frac": (o["counter_tflops"] / PEAK_BF16_TFLOPS) if o["counter_tflops"] else None,
+                    "counter_tflops": o["counter_tflops"]}
+    return None
 
 
 # ---------------------------------------------------------------- decode
@@ -267,6 +391,14 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
             hit += len(nd & got)
             tot += len(nd)
     res["needle_recall"] = hit / max(tot, 1)
+    ties = cuts = 0
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            t, c = near_tie_rows(q[b, g * G:(g + 1) * G], L[b, g],
+                                 torch.full((G,), Nc, dtype=torch.int64, device="cuda"), w.k)
+            ties += t
+            cuts += c
+    res["near_tie_rows"] = {"rows": w.B * w.Hq, "with_cut": cuts, "near_tie": ties}
     log(f"[{wname}] {ms_step:.3f} ms/step, kernels {dict(zip(names, np.round(per, 4)))}, "
         f"{dom['kernel']} {dom['achieved']:.0f} GB/s, {other['kernel']} {other['achieved']:.0f} GB/s, "
         f"needle recall {res['needle_recall']:.4f}")
@@ -447,6 +579,7 @@ def decode_cpu_baseline(w, q, k, v, queries=(0, 37), min_seconds=10.0, tau=None)
             total += time.perf_counter() - t0
             del Kg, Vg
     return {"value": len(queries) * reps / total, "unit": "queries/s", "cores": blas_threads(), "kind": "oracle",
+            "host": host_info(),
             "sample": f"queries {list(queries)} of {w.B} (all {w.Hq} heads), each KV group's oracle call repeated "
                       f"{reps} times ({total:.1f} s timed); oracle landmark build and host copies untimed"}
 
@@ -530,6 +663,9 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
         "workload": wname, "value": w.B * Tq / (ms_step / 1e3), "unit": "tokens/s", "ms_per_step": ms_step,
         "kernel_ms": {n: float(x) for n, x in zip(names, per)},
         "scoring_tflops": sel_tf, "scoring_mfma_frac": sel_tf / peak,
+        # rocprofv3 MFMA counters of the scoring and local kernels (profiles/), null once the library changed
+        "scoring_mfma_counters": profiled_mfma(wname, "prefill_select_kernel"),
+        "local_mfma_counters": profiled_mfma(wname, "prefill_local_kernel"),
         "attention_ms": attn_ms, "attention_tflops": att_tf, "attention_mfma_frac": att_tf / peak,
         "remote_pair_frac": n_remote / max(n_pairs, 1),
         "remote_tflops": remote_flops / (per[6] / 1e3) / 1e12,
@@ -542,6 +678,18 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
                      "frac": dom_tf / peak, "traffic": profiled_traffic(wname, dom_name),
                      "alg_flops_per_launch": dom_flops},
     }
+    if tau is None:
+        G = w.Hq // w.Hkv
+        ties = cuts = 0
+        n_all = torch.clamp(torch.arange(off, w.T, device="cuda") // w.S, max=Nc)
+        blk = 16384
+        for b in range(w.B):
+            for h in range(w.Hq):
+                for r0 in range(0, Tq, blk):
+                    t, c = near_tie_rows(q[b, h, r0:r0 + blk], L[b, h // G], n_all[r0:r0 + blk], w.k)
+                    ties += t
+                    cuts += c
+        res["near_tie_rows"] = {"rows": w.B * w.Hq * Tq, "with_cut": cuts, "near_tie": ties}
     log(f"[{wname}] {ms_step:.3f} ms/step, kernels {dict(zip(names, np.round(per, 4)))}, "
         f"scoring {sel_tf:.1f} TFLOP/s, attention {att_tf:.1f} TFLOP/s, remote pairs {n_remote / max(n_pairs, 1):.3f}")
     if tau is not None:
@@ -581,6 +729,7 @@ def prefill_cpu_baseline(w, q, k, v, chunks=tuple(range(250, 4001, 250)), tau=No
             total += time.perf_counter() - t0
     tokens = len(chunks) * w.S
     return {"value": tokens / total, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "host": host_info(),
             "sample": f"query chunks {list(chunks)} ({tokens} tokens, all {w.Hq} heads; {total:.1f} s timed); "
                       f"host copies and oracle landmark build untimed"}
 
@@ -666,6 +815,7 @@ def backward_cpu_baseline(w, q, k, v, dout, sel, chunks=(500, 1500, 2500, 3500))
                 total += time.perf_counter() - t0
     tokens = len(chunks) * w.S
     return {"value": tokens / total, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "host": host_info(),
             "sample": f"query chunks {list(chunks)} ({tokens} tokens, all {w.Hq} heads; {total:.1f} s timed); "
                       f"forward selection from the layer, host copies and oracle landmark build untimed"}
 
@@ -704,7 +854,13 @@ def main():
     if args.calibrate_copy:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
+        # evict the freshly written source from L2 and the 256 MiB MALL, so
+        # that the copy reads all of it from HBM (a partly cached source made
+        # the read scale drift from run to run)
+        flush = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+        flush.fill_(1)
         torch.cuda.synchronize()
+        del flush
         dst.copy_(src)
         torch.cuda.synchronize()
         log("calibration copy: 1 GiB read + 1 GiB written")
@@ -716,6 +872,9 @@ def main():
     if args.workload == "all":
         results["prefill"] = bench_prefill("prefill_256k_bf16", args.steps, args.warmup, cpu)
         main_res = bench_decode("decode_1m_bf16", args.steps, args.warmup, cpu)
+        # the 16M-token decode rides along once the 1M caches are freed (its
+        # oracle baseline would stream 32 GiB caches through the host: none)
+        results["decode_16m"] = bench_decode("decode_16m_bf16", args.steps, args.warmup, False)
     elif "varlen" in args.workload:
         main_res = bench_decode_varlen(args.workload, args.steps, args.warmup)
     elif args.workload.startswith("backward"):
@@ -732,12 +891,13 @@ def main():
     }
     if "cpu_baseline" in main_res:
         line["cpu_baseline"] = main_res["cpu_baseline"]
-    for key in ("roofline_other", "kernel_ms", "step_alg_GBps", "needle_recall", "gap_threshold",
-                "doubled_head_frac", "doubled_row_frac"):
+    for key in ("roofline_other", "kernel_ms", "step_alg_GBps", "needle_recall", "near_tie_rows",
+                "gap_threshold", "doubled_head_frac", "doubled_row_frac", "mfma_counters"):
         if key in main_res:
             line[key] = main_res[key]
-    if "prefill" in results:
-        line["prefill"] = results["prefill"]
+    for key in ("prefill", "decode_16m"):
+        if key in results:
+            line[key] = results[key]
     if ATTAINABLE:
         line["hbm_read_attainable"] = {"GBps": ATTAINABLE["GBps"], "frac_of_peak": ATTAINABLE["GBps"] / PEAK_HBM_GBS,
                                        "probe": ATTAINABLE["probe"]}

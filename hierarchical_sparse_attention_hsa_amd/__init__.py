@@ -154,6 +154,56 @@ def make_dims(batch, num_q_heads, num_kv_heads, head_dim, chunk_size, top_k, seq
     return Dims(batch, num_q_heads, num_kv_heads, head_dim, chunk_size, top_k, seq_len, dtype, 0)
 
 
+def _same_device(device, *tensors):
+    """Every given tensor lives on `device` (the library reads and writes them
+    with kernels launched there)."""
+    for t in tensors:
+        if t is not None and t.device != device:
+            raise ValueError(f"all tensors must be on {device}, got one on {t.device}")
+
+
+def _output(t, shape, dtype, device, name):
+    """Validate a caller-supplied output buffer, or allocate one.  The C ABI
+    cannot see buffer sizes, so a wrong shape or dtype here would become an
+    out-of-bounds device write."""
+    torch = _torch()
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _selection(sel_idx, sel_score, shape, device):
+    """Optional selection outputs: both or neither, int32 / float32 of shape
+    [..., slots]."""
+    torch = _torch()
+    if (sel_idx is None) != (sel_score is None):
+        raise ValueError("give both sel_idx and sel_score or neither")
+    if sel_idx is None:
+        return None, None
+    return (_output(sel_idx, shape, torch.int32, device, "sel_idx"),
+            _output(sel_score, shape, torch.float32, device, "sel_score"))
+
+
+def _workspace(workspace, dims, kind, device):
+    """The caller's workspace (any dtype, contiguous, on the device), or a
+    new one of hsa_attn_workspace_size bytes."""
+    torch = _torch()
+    if workspace is None:
+        need = hsa_attn_workspace_size(dims, kind)
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if workspace.device != device:
+        raise ValueError(f"workspace must be on {device}, got {workspace.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace
+
+
 def landmarks_shape(k_shape, chunk_size):
     B, Hkv, T, D = k_shape
     return (B, Hkv, T // chunk_size, D)
@@ -196,6 +246,7 @@ def hsa_build_landmarks(k, landmarks, chunk_size: int, chunk_begin: int = 0, chu
     if chunk_end is None:
         chunk_end = T // chunk_size
     dims = make_dims(B, Hkv, Hkv, D, chunk_size, 1, T, _dtype_code(k))
+    _same_device(k.device, landmarks)
     _check(load_library().hsa_build_landmarks(ctypes.byref(dims), _ptr(k), _ptr(landmarks), int(chunk_begin),
                                               int(chunk_end), _stream(k.device)), "hsa_build_landmarks")
     return landmarks
@@ -213,13 +264,10 @@ def _forward(is_decode, q, k, v, landmarks, chunk_size, top_k, out, sel_idx, sel
     if tuple(landmarks.shape) != landmarks_shape(k.shape, chunk_size) or landmarks.dtype != k.dtype:
         raise ValueError("landmarks must be [B, Hkv, T // chunk_size, D] with the dtype of k")
     dims = make_dims(B, Hq, Hkv, D, chunk_size, top_k, T, _dtype_code(k))
-    if out is None:
-        out = torch.empty(expect_q, dtype=torch.float32, device=q.device)
-    if (sel_idx is None) != (sel_score is None):
-        raise ValueError("give both sel_idx and sel_score or neither")
-    if workspace is None:
-        need = hsa_attn_workspace_size(dims, is_decode)
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _same_device(q.device, k, v, landmarks, lens)
+    out = _output(out, expect_q, torch.float32, q.device, "out")
+    sel_idx, sel_score = _selection(sel_idx, sel_score, expect_q[:-1] + (top_k,), q.device)
+    workspace = _workspace(workspace, dims, int(is_decode), q.device)
     lib = load_library()
     if lens is not None:
         if lens.dtype != torch.int64 or tuple(lens.shape) != (B,):
@@ -275,13 +323,10 @@ def hsa_forward_decode_adaptive(q, k_cache, v_cache, landmarks, chunk_size: int,
     if cache_lens is not None and (cache_lens.dtype != torch.int64 or tuple(cache_lens.shape) != (B,)):
         raise ValueError("cache_lens must be an int64 tensor of shape [B]")
     dims = make_dims(B, Hq, Hkv, D, chunk_size, top_k, T, _dtype_code(k_cache))
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    if (sel_idx is None) != (sel_score is None):
-        raise ValueError("give both sel_idx and sel_score or neither")
-    if workspace is None:
-        need = hsa_attn_workspace_size(dims, 2)
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _same_device(q.device, k_cache, v_cache, landmarks, cache_lens)
+    out = _output(out, (B, Hq, D), torch.float32, q.device, "out")
+    sel_idx, sel_score = _selection(sel_idx, sel_score, (B, Hq, 2 * top_k), q.device)
+    workspace = _workspace(workspace, dims, 2, q.device)
     st = load_library().hsa_forward_decode_adaptive(
         ctypes.byref(dims), float(gap_threshold), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(landmarks),
         _ptr(cache_lens), _ptr(out), _ptr(sel_idx), _ptr(sel_score), _ptr(workspace),
@@ -306,13 +351,10 @@ def hsa_forward_prefill_adaptive(q, k, v, landmarks, chunk_size: int, top_k: int
     if tuple(landmarks.shape) != landmarks_shape(k.shape, chunk_size) or landmarks.dtype != k.dtype:
         raise ValueError("landmarks must be [B, Hkv, T // chunk_size, D] with the dtype of k")
     dims = make_dims(B, Hq, Hkv, D, chunk_size, top_k, T, _dtype_code(k))
-    if out is None:
-        out = torch.empty((B, Hq, T, D), dtype=torch.float32, device=q.device)
-    if (sel_idx is None) != (sel_score is None):
-        raise ValueError("give both sel_idx and sel_score or neither")
-    if workspace is None:
-        need = hsa_attn_workspace_size(dims, 3)
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _same_device(q.device, k, v, landmarks)
+    out = _output(out, (B, Hq, T, D), torch.float32, q.device, "out")
+    sel_idx, sel_score = _selection(sel_idx, sel_score, (B, Hq, T, 2 * top_k), q.device)
+    workspace = _workspace(workspace, dims, 3, q.device)
     st = load_library().hsa_forward_prefill_adaptive(
         ctypes.byref(dims), float(gap_threshold), _ptr(q), _ptr(k), _ptr(v), _ptr(landmarks), _ptr(out),
         _ptr(sel_idx), _ptr(sel_score), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -344,15 +386,11 @@ def hsa_backward_prefill(q, k, v, landmarks, out, dout, sel_idx, sel_score, chun
     if sel_idx.dtype != torch.int32 or sel_score.dtype != torch.float32:
         raise ValueError("sel_idx must be int32 and sel_score float32")
     dims = make_dims(B, Hq, Hkv, D, chunk_size, top_k, T, _dtype_code(k))
-    if dq is None:
-        dq = torch.empty((B, Hq, T, D), dtype=torch.float32, device=q.device)
-    if dk is None:
-        dk = torch.empty((B, Hkv, T, D), dtype=torch.float32, device=q.device)
-    if dv is None:
-        dv = torch.empty((B, Hkv, T, D), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        need = hsa_attn_workspace_size(dims, 4)
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _same_device(q.device, k, v, landmarks, out, dout, sel_idx, sel_score)
+    dq = _output(dq, (B, Hq, T, D), torch.float32, q.device, "dq")
+    dk = _output(dk, (B, Hkv, T, D), torch.float32, q.device, "dk")
+    dv = _output(dv, (B, Hkv, T, D), torch.float32, q.device, "dv")
+    workspace = _workspace(workspace, dims, 4, q.device)
     st = load_library().hsa_backward_prefill(
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(landmarks), _ptr(out), _ptr(dout), _ptr(sel_idx),
         _ptr(sel_score), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -376,6 +414,7 @@ def hsa_append_kv(k_new, v_new, k_cache, v_cache, landmarks, cache_lens, chunk_s
     if cache_lens.dtype != torch.int64 or tuple(cache_lens.shape) != (B,):
         raise ValueError("cache_lens must be an int64 tensor of shape [B]")
     dims = make_dims(B, Hkv, Hkv, D, chunk_size, 1, T, _dtype_code(k_cache))
+    _same_device(k_cache.device, k_new, v_new, v_cache, landmarks, cache_lens)
     _check(load_library().hsa_append_kv(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                         _ptr(landmarks), _ptr(cache_lens), _stream(k_cache.device)),
            "hsa_append_kv")
@@ -397,13 +436,10 @@ def hsa_forward_prefill_cached(q, k, v, landmarks, q_offset: int, chunk_size: in
     if tuple(landmarks.shape) != landmarks_shape(k.shape, chunk_size) or landmarks.dtype != k.dtype:
         raise ValueError("landmarks must be [B, Hkv, T // chunk_size, D] with the dtype of k")
     dims = make_dims(B, Hq, Hkv, D, chunk_size, top_k, T, _dtype_code(k))
-    if out is None:
-        out = torch.empty((B, Hq, Tq, D), dtype=torch.float32, device=q.device)
-    if (sel_idx is None) != (sel_score is None):
-        raise ValueError("give both sel_idx and sel_score or neither")
-    if workspace is None:
-        need = hsa_attn_workspace_size(dims, False)
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _same_device(q.device, k, v, landmarks)
+    out = _output(out, (B, Hq, Tq, D), torch.float32, q.device, "out")
+    sel_idx, sel_score = _selection(sel_idx, sel_score, (B, Hq, Tq, top_k), q.device)
+    workspace = _workspace(workspace, dims, 0, q.device)
     st = load_library().hsa_forward_prefill_cached(ctypes.byref(dims), int(q_offset), _ptr(q), _ptr(k), _ptr(v),
                                                    _ptr(landmarks), _ptr(out), _ptr(sel_idx), _ptr(sel_score),
                                                    _ptr(workspace), workspace.numel() * workspace.element_size(),

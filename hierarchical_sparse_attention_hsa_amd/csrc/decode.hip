@@ -160,44 +160,59 @@ __device__ __forceinline__ void sort_gathered(const float2* buf, int cnt, float&
   out_i = i0;
 }
 
+// Entries equal to -inf are padding (an empty slot of a split list): they
+// are neither binned nor gathered, so only the nf finite entries compete
+// and lanes nf.. of the result hold padding.
 __device__ __forceinline__ bool split_topk(const float* sc, int n, int idx0, int k, int* hist, float2* buf,
                                            float& out_s, int& out_i) {
   const int lane = __lane_id();
-  const int m = min(k, n);
   float lo = __builtin_inff(), hi = -__builtin_inff();
+  int nf = 0;
   for (int r = lane; r < n; r += kWave) {
     const float x = sc[r];
-    lo = fminf(lo, x);
-    hi = fmaxf(hi, x);
+    if (x > -__builtin_inff()) {
+      lo = fminf(lo, x);
+      hi = fmaxf(hi, x);
+      ++nf;
+    }
   }
   lo = wave_min_f(lo);
   hi = wave_max_f(hi);
+  for (int off = 32; off >= 1; off >>= 1) nf += __shfl_xor(nf, off);
+  const int m = min(k, nf);
+  // finite lo and hi whenever nf > 0, so t is finite and >= 0 for every
+  // finite entry
   float inv = hi > lo ? 256.0f / (hi - lo) : 0.0f;
   if (!(inv < 1e30f)) inv = 0.0f;  // a range too narrow to bin: one bin (then gather or fall back)
   auto tval = [&](float x) { return (x - lo) * inv; };
   auto bin_of = [&](float t) { return min(255, (int)t); };
   int B1 = 0, B2 = 0;
-  if (n > kGather) {
+  if (nf > kGather) {
     // pass 1
 #pragma unroll
     for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
-    for (int r = lane; r < n; r += kWave) atomicAdd(&hist[bin_of(tval(sc[r]))], 1);
+    for (int r = lane; r < n; r += kWave) {
+      const float x = sc[r];
+      if (x > -__builtin_inff()) atomicAdd(&hist[bin_of(tval(x))], 1);
+    }
     int above1;
     hist_select(hist, m, lane, B1, above1);
     // pass 2: inside B1
 #pragma unroll
     for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
     for (int r = lane; r < n; r += kWave) {
-      const float t = tval(sc[r]);
+      const float x = sc[r];
+      if (!(x > -__builtin_inff())) continue;
+      const float t = tval(x);
       if (bin_of(t) == B1) atomicAdd(&hist[min(255, (int)((t - (float)B1) * 256.0f))], 1);
     }
     int above2;
     hist_select(hist, m - above1, lane, B2, above2);
   } else {
     B1 = 0;
-    B2 = 0;  // gather everything
+    B2 = 0;  // gather every finite entry
   }
-  // gather (bin, sub-bin) >= (B1, B2), in index order
+  // gather the finite entries with (bin, sub-bin) >= (B1, B2), in index order
   int cnt = 0;
   for (int r0 = 0; r0 < n; r0 += kWave) {
     const int r = r0 + lane;
@@ -205,9 +220,11 @@ __device__ __forceinline__ bool split_topk(const float* sc, int n, int idx0, int
     float x = 0.0f;
     if (r < n) {
       x = sc[r];
-      const float t = tval(x);
-      const int b1 = bin_of(t);
-      take = b1 > B1 || (b1 == B1 && min(255, (int)((t - (float)B1) * 256.0f)) >= B2);
+      if (x > -__builtin_inff()) {
+        const float t = tval(x);
+        const int b1 = bin_of(t);
+        take = b1 > B1 || (b1 == B1 && min(255, (int)((t - (float)B1) * 256.0f)) >= B2);
+      }
     }
     const uint64_t mk = __ballot(take);
     const int pos = cnt + __popcll(mk & ((1ull << lane) - 1ull));

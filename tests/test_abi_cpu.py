@@ -207,3 +207,75 @@ def test_backward_validation():
     pairs = 32 * (1 << 18) * 16
     need = hsa.hsa_attn_workspace_size(d, 4)
     assert pairs * (4 * 128 + 12) < need < pairs * (4 * 128 + 12) + (1 << 30) + 8 * 4096 * 64 * 128 * 2
+
+
+def test_binding_rejects_wrong_output_buffers_before_any_launch():
+    """The binding checks every caller-supplied output (shape, dtype, device,
+    contiguity) and the workspace before it calls the library: the C ABI
+    cannot see buffer sizes, so a wrong buffer would be written out of
+    bounds.  CPU tensors stand in for device ones: every check here fires
+    before a pointer is taken."""
+    import torch
+    B, Hq, Hkv, T, D, S, k = 1, 4, 2, 256, 64, 64, 4
+    q = torch.zeros((B, Hq, T, D), dtype=torch.bfloat16)
+    kv = torch.zeros((B, Hkv, T, D), dtype=torch.bfloat16)
+    L = torch.zeros((B, Hkv, T // S, D), dtype=torch.bfloat16)
+    f32 = torch.float32
+    good_out = torch.zeros((B, Hq, T, D), dtype=f32)
+    cases = {
+        "out dtype": dict(out=torch.zeros((B, Hq, T, D), dtype=torch.bfloat16)),
+        "out shape": dict(out=torch.zeros((B, Hq, T, D + 1), dtype=f32)),
+        "out strided": dict(out=torch.zeros((B, Hq, D, T), dtype=f32).transpose(2, 3)),
+        "sel_idx int64": dict(out=good_out, sel_idx=torch.zeros((B, Hq, T, k), dtype=torch.int64),
+                              sel_score=torch.zeros((B, Hq, T, k), dtype=f32)),
+        "sel_idx slots": dict(out=good_out, sel_idx=torch.zeros((B, Hq, T, k + 1), dtype=torch.int32),
+                              sel_score=torch.zeros((B, Hq, T, k + 1), dtype=f32)),
+        "sel_score dtype": dict(out=good_out, sel_idx=torch.zeros((B, Hq, T, k), dtype=torch.int32),
+                                sel_score=torch.zeros((B, Hq, T, k), dtype=torch.float64)),
+        "only sel_idx": dict(out=good_out, sel_idx=torch.zeros((B, Hq, T, k), dtype=torch.int32)),
+    }
+    for name, kw in cases.items():
+        with pytest.raises(ValueError):
+            hsa.hsa_forward_prefill(q, kv, kv, L, S, k, **kw)
+        with pytest.raises(ValueError):
+            hsa.hsa_forward_prefill_cached(q[:, :, S:].contiguous(), kv, kv, L, S, S, k,
+                                           **{n: (t[:, :, S:].contiguous() if t is not None else None)
+                                              for n, t in kw.items()})
+    # the adaptive calls write 2k slots per row
+    with pytest.raises(ValueError):
+        hsa.hsa_forward_prefill_adaptive(q, kv, kv, L, S, k, 0.1, out=good_out,
+                                         sel_idx=torch.zeros((B, Hq, T, k), dtype=torch.int32),
+                                         sel_score=torch.zeros((B, Hq, T, k), dtype=f32))
+    qd = torch.zeros((B, Hq, D), dtype=torch.bfloat16)
+    for kw in (dict(out=torch.zeros((B, Hq, D), dtype=torch.bfloat16)),
+               dict(out=torch.zeros((B, Hq + 1, D), dtype=f32)),
+               dict(sel_idx=torch.zeros((B, Hq, k), dtype=torch.int64), sel_score=torch.zeros((B, Hq, k)))):
+        with pytest.raises(ValueError):
+            hsa.hsa_forward_decode(qd, kv, kv, L, S, k, **kw)
+    with pytest.raises(ValueError):
+        hsa.hsa_forward_decode_adaptive(qd, kv, kv, L, S, k, 0.1, out=torch.zeros((B, Hq, D)),
+                                        sel_idx=torch.zeros((B, Hq, k), dtype=torch.int32),
+                                        sel_score=torch.zeros((B, Hq, k)))
+    # backward gradients are float32 [B,Hq,T,D] / [B,Hkv,T,D]
+    sel = torch.zeros((B, Hq, T, k), dtype=torch.int32)
+    sc = torch.zeros((B, Hq, T, k), dtype=f32)
+    for kw in (dict(dq=torch.zeros((B, Hq, T, D), dtype=torch.bfloat16)),
+               dict(dk=torch.zeros((B, Hq, T, D), dtype=f32)),
+               dict(dv=torch.zeros((B, Hkv, T, D - 1), dtype=f32))):
+        with pytest.raises(ValueError):
+            hsa.hsa_backward_prefill(q, kv, kv, L, good_out, good_out, sel, sc, S, **kw)
+
+
+@pytest.mark.gpu
+def test_binding_rejects_tensors_on_another_device():
+    import torch
+    B, Hq, Hkv, T, D, S, k = 1, 4, 2, 256, 64, 64, 4
+    q = torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((B, Hkv, T, D), dtype=torch.bfloat16, device="cuda")
+    L = torch.zeros((B, Hkv, T // S, D), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        hsa.hsa_forward_prefill(q, kv, kv, L, S, k, out=torch.zeros((B, Hq, T, D)))
+    with pytest.raises(ValueError):
+        hsa.hsa_forward_prefill(q, kv, kv, L, S, k, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        hsa.hsa_forward_prefill(q, kv.cpu(), kv, L, S, k)

@@ -53,6 +53,10 @@ CASES = [
     (6, 16, 4, 64 * 80, 128, 16, "bf16", [0, 50, 64, 64 * 37 + 5, 4000, 64 * 80]),
     (3, 8, 8, 64 * 40, 64, 8, "fp32", [64 * 40, 100, 64 * 9]),
     (4, 8, 1, 64 * 3000, 128, 64, "bf16", [64 * 3000, 64 * 1500 + 7, 1, 64 * 700]),
+    # 200 splits of 256 landmarks: the merge samples one entry per split
+    # (more than its 128-entry gather), and the short sequence's 50 splits
+    # past its end hand it -inf padding, which must not enter the binning
+    (2, 2, 1, 64 * 256 * 200, 64, 64, "bf16", [64 * 256 * 200, 64 * 256 * 150 + 1000]),
 ]
 
 
