@@ -17,6 +17,8 @@ import hierarchical_sparse_attention_hsa_amd as hsa
 from hierarchical_sparse_attention_hsa_amd.workloads import WORKLOADS, decode_inputs, prefill_inputs
 from oracle import hsa_oracle as O
 from tests.gpu_util import TOL, check_rows, check_rows_adaptive, new_stats
+from tests.oracle_pool import OraclePool, check_prefill_rows_task, gather_landmarks, merge_stats
+from tests.oracle_pool import oracle_landmarks as pool_landmarks
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -59,6 +61,14 @@ def oracle_landmarks(kg, S, dtype, slab=1 << 20):
         t1 = min(Nc * S, t0 + slab)
         parts.append(O.landmarks(host64(kg[t0:t1]), S, dtype))
     return np.concatenate(parts, axis=0) if parts else np.zeros((0, kg.shape[1]))
+
+
+def host_stored(t):
+    """Host copy of a device tensor as stored: bf16 as its uint16 bit
+    patterns, everything else unchanged."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
 
 
 def check_landmarks(L_gpu, L_ref, dtype):
@@ -127,9 +137,44 @@ def test_prefill_4k_fp32_every_row():
     assert stats["rows"] == 4 * 4096
 
 
-def test_prefill_32k_bf16_sampled():
-    # no candidate, one candidate, exactly k, k + 1, and spread chunks to the last
-    run_prefill_workload("prefill_32k_bf16", [0, 1, 16, 17, 100, 255, 400, 511])
+def test_prefill_32k_bf16_every_row():
+    """Every row of every head of the 32K prefill, the oracle side split over
+    a pool of worker processes (blocks of 1024 rows of one head)."""
+    w = WORKLOADS["prefill_32k_bf16"]
+    print(f"workload {w.name}: every row", flush=True)
+    q, k, v = prefill_inputs(w, "cuda")
+    Nc = w.T // w.S
+    L = torch.empty((w.B, w.Hkv, Nc, w.D), dtype=k.dtype, device="cuda")
+    out = torch.empty((w.B, w.Hq, w.T, w.D), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((w.B, w.Hq, w.T, w.k), dtype=torch.float32, device="cuda")
+    hsa.hsa_build_landmarks(k, L, w.S)
+    hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    stats = new_stats()
+    with OraclePool() as P:
+        for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("sel", sel), ("sc", sc)):
+            a = host_stored(t)
+            m = P.array(name, a.shape, a.dtype)
+            m[:] = a
+            m.flush()
+            del m, a
+        futs = []
+        for b in range(w.B):
+            for h in range(w.Hq):
+                for r0 in range(0, w.T, 1024):
+                    futs.append(P.submit(check_prefill_rows_task, P.dir, b, h, h // G,
+                                         np.arange(r0, min(w.T, r0 + 1024)), w.S, w.k, w.dtype, TOL[w.dtype]))
+        for b in range(w.B):
+            for g in range(w.Hkv):
+                check_landmarks(L[b, g], O.landmarks(host64(k[b, g]), w.S, w.dtype), w.dtype)
+        for i, f in enumerate(futs):
+            merge_stats(stats, f.result())
+            if (i + 1) % 128 == 0:
+                print(f"{i + 1}/{len(futs)} row blocks checked: {stats}", flush=True)
+    print(w.name, stats, flush=True)
+    assert stats["rows"] == w.B * w.Hq * w.T
 
 
 def test_prefill_256k_bf16_sampled():
@@ -197,26 +242,50 @@ def run_decode_workload(name, queries):
     torch.cuda.synchronize()
     G = w.Hq // w.Hkv
     stats = new_stats()
-    for b in queries:
-        for g in range(w.Hkv):
-            Lg = oracle_landmarks(k[b, g], w.S, w.dtype)
-            check_landmarks(L[b, g], Lg, w.dtype)
-            hs = slice(g * G, (g + 1) * G)
-            if tau is None:
-                check_rows(host64(q[b, hs]), np.full(G, w.T), DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lg, w.S,
-                           w.k, host64(out[b, hs]), sel[b, hs].cpu().numpy(), host64(sc[b, hs]), TOL[w.dtype], stats)
-                continue
+
+    def check_group(b, g, Lg):
+        check_landmarks(L[b, g], Lg, w.dtype)
+        hs = slice(g * G, (g + 1) * G)
+        if tau is None:
+            check_rows(host64(q[b, hs]), np.full(G, w.T), DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lg, w.S,
+                       w.k, host64(out[b, hs]), sel[b, hs].cpu().numpy(), host64(sc[b, hs]), TOL[w.dtype], stats)
+        else:
             check_rows_adaptive(host64(q[b, hs]), np.full(G, w.T), DeviceRows(k[b, g]), DeviceRows(v[b, g]), Lg,
                                 w.S, w.k, tau, host64(out[b, hs]), sel[b, hs].cpu().numpy(), host64(sc[b, hs]),
                                 TOL[w.dtype], stats)
-        print(name, "query", b, stats, flush=True)
+        if g == w.Hkv - 1:
+            print(name, "query", b, stats, flush=True)
+
+    # the oracle's landmarks of each (query, KV head) are built by the pool
+    # from a shared-memory copy of the cache's keys, a few caches ahead of
+    # the checks, which run here
+    items = [(b, g) for b in queries for g in range(w.Hkv)]
+    per_item = max(1, (Nc * w.S) // (1 << 20))               # slab tasks per cache
+    depth = max(2, min(16, -(-28 // per_item), (8 << 30) // max(1, w.T * w.D * esz)))
+    pending = []
+    with OraclePool() as P:
+        for i, (b, g) in enumerate(items):
+            tag = f"k_{b}_{g}"
+            m = P.array(tag, (w.T, w.D), np.uint16 if w.dtype == "bf16" else np.float32)
+            m[:] = host_stored(k[b, g])
+            m.flush()
+            del m
+            pending.append((b, g, tag, pool_landmarks(P, P.path(tag), (), w.T, w.S, w.dtype)))
+            while len(pending) >= depth or (i == len(items) - 1 and pending):
+                b0, g0, tag0, futs = pending.pop(0)
+                Lg = gather_landmarks(futs, w.D)
+                P.remove(tag0)
+                check_group(b0, g0, Lg)
+    print(name, stats, flush=True)
     del q, k, v, L, out, sel, sc
     torch.cuda.empty_cache()
     return stats
 
 
 def test_decode_1m_bf16_sampled():
-    run_decode_workload("decode_1m_bf16", [0, 41])
+    # 16 of the 64 queries, spread over the batch
+    stats = run_decode_workload("decode_1m_bf16", list(range(0, 64, 4)))
+    assert stats["rows"] == 16 * 32
 
 
 def test_decode_1m_adaptive_bf16_sampled():
@@ -224,8 +293,9 @@ def test_decode_1m_adaptive_bf16_sampled():
     assert stats.get("doubled", 0) > 0
 
 
-def test_decode_16m_bf16_sampled():
-    run_decode_workload("decode_16m_bf16", [2])
+def test_decode_16m_bf16_every_query():
+    stats = run_decode_workload("decode_16m_bf16", [0, 1, 2, 3])
+    assert stats["rows"] == 4 * 32
 
 
 def test_decode_1m_varlen_bf16_sampled():
