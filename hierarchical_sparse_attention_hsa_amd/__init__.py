@@ -27,7 +27,7 @@ __all__ = [
     "hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
     "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive", "hsa_append_kv",
     "hsa_backward_prefill", "hsa_attn_set_timing_events", "hsa_attn_workspace_size",
-    "hsa_attn_status_string", "hsa_attn_last_error", "landmarks_shape",
+    "hsa_attn_status_string", "hsa_attn_last_error", "landmarks_shape", "hsa_forward_decode_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +36,7 @@ EXPORTED_SYMBOLS = (
     "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive",
     "hsa_append_kv", "hsa_backward_prefill", "hsa_attn_set_timing_events", "hsa_attn_workspace_size",
     "hsa_attn_status_string",
-    "hsa_attn_last_error",
+    "hsa_attn_last_error", "hsa_forward_decode_noalloc",
 )
 
 HSA_ATTN_OK = 0
@@ -86,6 +86,7 @@ def load_library():
     lib.hsa_build_landmarks.argtypes = [dims, P, P, I64, I64, P]
     lib.hsa_forward_prefill.argtypes = [dims, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_decode.argtypes = [dims, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_forward_decode_noalloc.argtypes = [dims, P, P, P, P, P, P, P, P]
     lib.hsa_forward_decode_varlen.argtypes = [dims, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_prefill_cached.argtypes = [dims, I64, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_decode_adaptive.argtypes = [dims, ctypes.c_float, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -99,6 +100,7 @@ def load_library():
     lib.hsa_attn_last_error.argtypes = []
     lib.hsa_attn_last_error.restype = ctypes.c_char_p
     for f in ("hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
+              "hsa_forward_decode_noalloc",
               "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive",
               "hsa_append_kv", "hsa_backward_prefill", "hsa_attn_workspace_size", "hsa_attn_set_timing_events"):
         getattr(lib, f).restype = ctypes.c_int
@@ -294,6 +296,33 @@ def hsa_forward_decode(q, k_cache, v_cache, landmarks, chunk_size: int, top_k: i
                        sel_score=None, workspace=None):
     """HSA for single-token queries q [B,Hq,D] after caches k/v [B,Hkv,T,D] -> out [B,Hq,D] fp32."""
     return _forward(True, q, k_cache, v_cache, landmarks, chunk_size, top_k, out, sel_idx, sel_score, workspace)
+
+
+def hsa_forward_decode_noalloc(q, k_cache, v_cache, landmarks, chunk_size: int, top_k: int, out, sel_idx=None,
+                               sel_score=None):
+    """hsa_forward_decode without a workspace: the library uses its own
+    fixed per-GPU scratch array and allocates nothing (the caller passes the
+    output buffer too).  Calls that overlap on one GPU race."""
+    torch = _torch()
+    B, Hkv, T, D = k_cache.shape
+    Hq = q.shape[1]
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype or q.dtype != k_cache.dtype:
+        raise ValueError("q, k and v must share dtype; v must match k's shape")
+    if tuple(q.shape) != (B, Hq, D):
+        raise ValueError(f"q must be {(B, Hq, D)}, got {tuple(q.shape)}")
+    if tuple(landmarks.shape) != landmarks_shape(k_cache.shape, chunk_size) or landmarks.dtype != k_cache.dtype:
+        raise ValueError("landmarks must be [B, Hkv, T // chunk_size, D] with the dtype of k")
+    if out is None:
+        raise ValueError("out must be given: this entry point allocates nothing")
+    _same_device(q.device, k_cache, v_cache, landmarks)
+    out = _output(out, (B, Hq, D), torch.float32, q.device, "out")
+    sel_idx, sel_score = _selection(sel_idx, sel_score, (B, Hq, top_k), q.device)
+    dims = make_dims(B, Hq, Hkv, D, chunk_size, top_k, T, _dtype_code(k_cache))
+    st = load_library().hsa_forward_decode_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                   _ptr(landmarks), _ptr(out), _ptr(sel_idx), _ptr(sel_score),
+                                                   _stream(q.device))
+    _check(st, "hsa_forward_decode_noalloc")
+    return out
 
 
 def hsa_forward_decode_varlen(q, k_cache, v_cache, landmarks, cache_lens, chunk_size: int, top_k: int, out=None,

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <exception>
+#include <mutex>
 
 #include "../../include/hsa_attn.h"
 #include "kernels.hpp"
@@ -332,6 +333,69 @@ hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, co
                                      float* sel_score, void* workspace, size_t workspace_bytes, void* stream) {
   return forward_decode(d, q, k_cache, v_cache, landmarks, nullptr, out, sel_idx, sel_score, workspace,
                         workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- decode without a workspace
+// Device memory the no-allocation decode uses in place of a caller
+// workspace: a fixed array in the library's code object, one copy per GPU,
+// alive until the process ends.  Host code never passes `scratch` itself
+// (its host-side name is not a device address): the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's copy of `scratch`, looked up on the first call there
+hsa_attn_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HSA_ATTN_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(HSA_ATTN_HIP_ERROR, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HSA_ATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+hsa_attn_status_t hsa_forward_decode_noalloc(const hsa_attn_dims_t* d, const void* q, const void* k_cache,
+                                             const void* v_cache, const void* landmarks, float* out,
+                                             int32_t* sel_idx, float* sel_score, void* stream) {
+  try {
+    // size the work before any HIP call: a call that does not fit is
+    // rejected without touching the device
+    hsa_attn::Geometry g;
+    hsa_attn_status_t st = check_dims(d, Call::kDecode, &g);
+    if (st != HSA_ATTN_OK) return st;
+    const size_t need = hsa_attn::plan_decode(g, sel_idx == nullptr).bytes;
+    if (need > kScratchBytes)
+      return fail(HSA_ATTN_WORKSPACE_TOO_SMALL,
+                  "decode needs %zu bytes of scratch; the no-allocation entry point holds %zu (use "
+                  "hsa_forward_decode with a workspace)",
+                  need, kScratchBytes);
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != HSA_ATTN_OK) return st;
+    return forward_decode(d, q, k_cache, v_cache, landmarks, nullptr, out, sel_idx, sel_score, ws, kScratchBytes,
+                          stream);
+  } catch (const std::exception& e) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error");
+  }
 }
 
 hsa_attn_status_t hsa_forward_decode_varlen(const hsa_attn_dims_t* d, const void* q, const void* k_cache,

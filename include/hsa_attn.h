@@ -24,7 +24,8 @@
  *  - Q, K, V and landmarks are stored as bf16 or fp32 (hsa_attn_dims_t.dtype);
  *    arithmetic accumulates in fp32 (landmark sums in fp64); out is fp32.
  *  - Every pointer is a device pointer, owned by the caller, 16-byte aligned.
- *    The library allocates no memory and keeps no state between calls.
+ *    The library allocates no memory and keeps no state between calls, apart
+ *    from the fixed scratch array of hsa_forward_decode_noalloc.
  *  - Calls are asynchronous: they validate on the host, enqueue kernels on
  *    `stream` (a hipStream_t; NULL means the default stream) and return.
  *    HSA_ATTN_OK means "enqueued".  Validation happens before any HIP call,
@@ -187,6 +188,26 @@ hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, co
                                      const void* v_cache, const void* landmarks, float* out,
                                      int32_t* sel_idx, float* sel_score, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/*
+ * hsa_forward_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and results, bit for bit, without a
+ * workspace argument.  The scratch memory lives in a fixed 64 MiB array of
+ * the library, one copy per GPU, held until the process ends; its device
+ * address is looked up once per device on the first call there (call with
+ * the stream's device current).  Nothing is allocated, by the library or
+ * anything it calls.  A shape whose workspace (hsa_attn_workspace_size(d, 1),
+ * or less when sel_idx/sel_score are given) exceeds 64 MiB returns
+ * HSA_ATTN_WORKSPACE_TOO_SMALL before any HIP call (both benchmark decodes,
+ * 64 x 1M and 4 x 16M tokens, fit).  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (different streams or
+ * threads without ordering) race and give undefined results.  No part of
+ * the array needs to start at zero; it keeps the last call's contents.
+ */
+hsa_attn_status_t hsa_forward_decode_noalloc(const hsa_attn_dims_t* d, const void* q, const void* k_cache,
+                                             const void* v_cache, const void* landmarks, float* out,
+                                             int32_t* sel_idx, float* sel_score, void* stream);
 
 /*
  * Decode over a batch of caches of different lengths (incremental decoding;

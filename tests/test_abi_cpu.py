@@ -279,3 +279,18 @@ def test_binding_rejects_tensors_on_another_device():
         hsa.hsa_forward_prefill(q, kv, kv, L, S, k, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
     with pytest.raises(ValueError):
         hsa.hsa_forward_prefill(q, kv.cpu(), kv, L, S, k)
+
+
+def test_noalloc_decode_rejects_oversized_shapes_on_the_host():
+    """The no-allocation decode sizes its work before any HIP call: a shape
+    whose scratch exceeds the library's fixed array is refused on the host
+    (no GPU needed), as are the usual invalid dimensions."""
+    lib = hsa.load_library()
+    p = ctypes.c_void_p(0x1000)
+    big = dims(batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128, top_k=64, seq_len=1 << 22)
+    st = lib.hsa_forward_decode_noalloc(ctypes.byref(big), p, p, p, p, p, None, None, None)
+    assert st == hsa.HSA_ATTN_WORKSPACE_TOO_SMALL
+    assert "scratch" in hsa.hsa_attn_last_error()
+    bad = dims(num_q_heads=30)
+    assert lib.hsa_forward_decode_noalloc(ctypes.byref(bad), p, p, p, p, p, None, None, None) == \
+        hsa.HSA_ATTN_INVALID_ARGUMENT
