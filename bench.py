@@ -610,6 +610,14 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
     sel = torch.empty((w.B, w.Hq, Tq, kk), dtype=torch.int32, device="cuda")
     sc = torch.empty((w.B, w.Hq, Tq, kk), dtype=torch.float32, device="cuda")
     events = HipEvents()
+    # the default workspace (hsa_attn_workspace_size), allocated once; the
+    # rows run in slabs as large as it holds
+    dims = hsa.make_dims(w.B, w.Hq, w.Hkv, w.D, w.S, w.k, w.T, hsa.HSA_ATTN_BF16 if esz == 2 else hsa.HSA_ATTN_FP32)
+    ws = torch.empty(hsa.hsa_attn_workspace_size(dims, 3 if tau is not None else 0), dtype=torch.uint8,
+                     device="cuda")
+    slab_rows = hsa.hsa_attn_prefill_slab_rows(dims, ws.numel(), tau is not None, True)
+    nslab = -(-Tq // slab_rows)
+    log(f"[{wname}] workspace {ws.numel() / 1e9:.2f} GB: {nslab} slab(s) of {slab_rows} query rows")
 
     def step(ev):
         if ev is not None:
@@ -618,15 +626,22 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
         if ev is not None:
             hsa.hsa_attn_set_timing_events(ev[2:])
         if off:
-            hsa.hsa_forward_prefill_cached(q, k, v, L, off, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
+            hsa.hsa_forward_prefill_cached(q, k, v, L, off, w.S, w.k, out=out, sel_idx=sel, sel_score=sc,
+                                           workspace=ws)
         elif tau is not None:
-            hsa.hsa_forward_prefill_adaptive(q, k, v, L, w.S, w.k, tau, out=out, sel_idx=sel, sel_score=sc)
+            hsa.hsa_forward_prefill_adaptive(q, k, v, L, w.S, w.k, tau, out=out, sel_idx=sel, sel_score=sc,
+                                             workspace=ws)
         else:
-            hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc)
+            hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc, workspace=ws)
 
+    # launches: landmarks; the V transpose; per slab zero, select, scan,
+    # scatter, remote, local.  Per-kernel times are summed over the slabs.
     names = ["landmarks", "prefill_zero", "prefill_select", "prefill_vt", "prefill_scan", "prefill_scatter",
              "prefill_remote", "prefill_local"]
-    secs, per = timed_steps(step, steps, warmup, len(names), events)
+    order = ["landmarks", "prefill_vt"] + ["prefill_zero", "prefill_select", "prefill_scan", "prefill_scatter",
+                                           "prefill_remote", "prefill_local"] * nslab
+    secs, per_launch = timed_steps(step, steps, warmup, len(order), events)
+    per = np.array([sum(t for n, t in zip(order, per_launch) if n == name) for name in names])
     ms_step = 1e3 * secs / steps
     # exact algorithmic work
     p = np.arange(off, w.T)
@@ -671,6 +686,7 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
         "remote_tflops": remote_flops / (per[6] / 1e3) / 1e12,
         "local_tflops": local_flops / (per[7] / 1e3) / 1e12,
         "landmark_GBps": (w.B * w.Hkv * (Nc - off // w.S) * w.S * w.D * esz) / (per[0] / 1e3) / 1e9,
+        "workspace_bytes": int(ws.numel()), "slabs": nslab, "slab_rows": slab_rows,
         "config": {"workload": wname, "batch": w.B, "seq_len": w.T, "query_tokens": Tq, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.D, "chunk": w.S, "top_k": w.k, "lowrank": w.lowrank},
         "dtype": w.dtype,
@@ -698,7 +714,7 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
         res["config"]["gap_threshold"] = tau
     if cpu_baseline:
         res["cpu_baseline"] = prefill_cpu_baseline(w, q, k, v, tau=tau)
-    del q, k, v, L, out, sel, sc
+    del q, k, v, L, out, sel, sc, ws
     torch.cuda.empty_cache()
     return res
 

@@ -28,6 +28,7 @@ __all__ = [
     "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive", "hsa_append_kv",
     "hsa_backward_prefill", "hsa_attn_set_timing_events", "hsa_attn_workspace_size",
     "hsa_attn_status_string", "hsa_attn_last_error", "landmarks_shape", "hsa_forward_decode_noalloc",
+    "hsa_attn_prefill_slab_rows",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive",
     "hsa_append_kv", "hsa_backward_prefill", "hsa_attn_set_timing_events", "hsa_attn_workspace_size",
     "hsa_attn_status_string",
-    "hsa_attn_last_error", "hsa_forward_decode_noalloc",
+    "hsa_attn_last_error", "hsa_forward_decode_noalloc", "hsa_attn_prefill_slab_rows",
 )
 
 HSA_ATTN_OK = 0
@@ -94,6 +95,7 @@ def load_library():
     lib.hsa_backward_prefill.argtypes = [dims, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_append_kv.argtypes = [dims, P, P, P, P, P, P, P]
     lib.hsa_attn_workspace_size.argtypes = [dims, ctypes.c_int, ctypes.POINTER(SZ)]
+    lib.hsa_attn_prefill_slab_rows.argtypes = [dims, ctypes.c_int, ctypes.c_int, SZ, ctypes.POINTER(I64)]
     lib.hsa_attn_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.hsa_attn_status_string.argtypes = [ctypes.c_int]
     lib.hsa_attn_status_string.restype = ctypes.c_char_p
@@ -102,7 +104,8 @@ def load_library():
     for f in ("hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
               "hsa_forward_decode_noalloc",
               "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive",
-              "hsa_append_kv", "hsa_backward_prefill", "hsa_attn_workspace_size", "hsa_attn_set_timing_events"):
+              "hsa_append_kv", "hsa_backward_prefill", "hsa_attn_workspace_size", "hsa_attn_set_timing_events",
+              "hsa_attn_prefill_slab_rows"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -236,6 +239,17 @@ def hsa_attn_workspace_size(dims: Dims, is_decode) -> int:
     n = ctypes.c_size_t(0)
     _check(load_library().hsa_attn_workspace_size(ctypes.byref(dims), int(is_decode), ctypes.byref(n)),
            "hsa_attn_workspace_size")
+    return n.value
+
+
+def hsa_attn_prefill_slab_rows(dims: Dims, workspace_bytes: int, adaptive: bool = False,
+                               selection_given: bool = False) -> int:
+    """Query rows per slab a prefill call uses with a workspace of
+    workspace_bytes (0: too small)."""
+    n = ctypes.c_int64(0)
+    _check(load_library().hsa_attn_prefill_slab_rows(ctypes.byref(dims), int(bool(adaptive)),
+                                                     int(bool(selection_given)), int(workspace_bytes),
+                                                     ctypes.byref(n)), "hsa_attn_prefill_slab_rows")
     return n.value
 
 

@@ -57,10 +57,16 @@ hsa_attn_status_t check_dims(const hsa_attn_dims_t* d, Call call, hsa_attn::Geom
     if (G != 1 && G != 2 && G != 4 && G != 8)
       return fail(HSA_ATTN_UNSUPPORTED, "query heads per KV head %d unsupported (1, 2, 4, 8)", G);
     if (d->chunk_size != 64) return fail(HSA_ATTN_UNSUPPORTED, "chunk_size %d unsupported (64)", d->chunk_size);
-    // decode keeps one list entry per lane of a wave, prefill up to 32 per
-    // row in registers; the adaptive budget doubles k
-    const int kmax = (call == Call::kDecode || call == Call::kDecodeAdaptive ? 64 : 32) / (adaptive ? 2 : 1);
+    // decode keeps one list entry per lane of a wave, prefill up to 64 per
+    // row in registers; the adaptive budget doubles k; the backward's row
+    // preparation spreads a row's slots over 16 lanes, two each
+    const int kmax = call == Call::kBackward ? 32 : 64 / (adaptive ? 2 : 1);
     if (d->top_k > kmax) return fail(HSA_ATTN_UNSUPPORTED, "top_k %d unsupported (<= %d)", d->top_k, kmax);
+    // prefill lists of more than 32 slots: the local attention's per-row
+    // tables of more than four heads per KV head would not fit the LDS
+    const bool prefill = call == Call::kPrefill || call == Call::kPrefillAdaptive || call == Call::kBackward;
+    if (prefill && d->top_k * (adaptive ? 2 : 1) > 32 && G > 4)
+      return fail(HSA_ATTN_UNSUPPORTED, "prefill with more than 32 selection slots needs num_q_heads / num_kv_heads <= 4");
   }
   if (call == Call::kDecodeAdaptive) call = Call::kDecode;
   if (call == Call::kPrefillAdaptive) call = Call::kPrefill;
@@ -159,6 +165,22 @@ hsa_attn_status_t hsa_attn_workspace_size(const hsa_attn_dims_t* d, int is_decod
   }
 }
 
+hsa_attn_status_t hsa_attn_prefill_slab_rows(const hsa_attn_dims_t* d, int adaptive, int selection_given,
+                                             size_t workspace_bytes, int64_t* slab_rows) {
+  try {
+    if (!slab_rows) return fail(HSA_ATTN_INVALID_ARGUMENT, "slab_rows is NULL");
+    hsa_attn::Geometry g;
+    const hsa_attn_status_t st = check_dims(d, adaptive ? Call::kPrefillAdaptive : Call::kPrefill, &g);
+    if (st != HSA_ATTN_OK) return st;
+    *slab_rows = hsa_attn::plan_prefill_for(g, selection_given == 0, workspace_bytes).slab_rows;
+    return ok();
+  } catch (const std::exception& e) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error");
+  }
+}
+
 hsa_attn_status_t hsa_build_landmarks(const hsa_attn_dims_t* d, const void* k, void* landmarks, int64_t chunk_begin,
                                       int64_t chunk_end, void* stream) {
   try {
@@ -204,9 +226,11 @@ static hsa_attn_status_t forward_prefill(const hsa_attn_dims_t* d, int64_t q_off
                           (const void*)workspace})
       if (p && !aligned16(p)) return fail(HSA_ATTN_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
     const bool own = sel_idx == nullptr;
-    const hsa_attn::PrefillPlan plan = hsa_attn::plan_prefill(g, own);
-    if (workspace_bytes < plan.bytes)
-      return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes, workspace_bytes);
+    // the largest slabs of query rows the workspace holds
+    const hsa_attn::PrefillPlan plan = hsa_attn::plan_prefill_for(g, own, workspace_bytes);
+    if (plan.slab_rows == 0)
+      return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs at least %zu bytes (slabs of 64 query rows), got %zu",
+                  plan.bytes, workspace_bytes);
     if (g.Tq == 0) return ok();
     if (!workspace) return fail(HSA_ATTN_INVALID_ARGUMENT, "workspace is NULL");
     char* ws = static_cast<char*>(workspace);
@@ -218,7 +242,7 @@ static hsa_attn_status_t forward_prefill(const hsa_attn_dims_t* d, int64_t q_off
     hsa_attn::PrefillArgs a{g, q, k, v, landmarks, out, sel_idx, sel_score,
                             reinterpret_cast<int32_t*>(ws + plan.off_pair_pos), reinterpret_cast<int*>(ws + plan.off_cnt),
                             reinterpret_cast<int*>(ws + plan.off_off), reinterpret_cast<int32_t*>(ws + plan.off_pairs),
-                            reinterpret_cast<float*>(ws + plan.off_partial), ws + plan.off_vt};
+                            reinterpret_cast<float*>(ws + plan.off_partial), ws + plan.off_vt, plan.slab_rows};
     if (adaptive) {
       a.k_base = d->top_k;
       a.gap_tau = gap_tau;

@@ -71,9 +71,28 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t st);
 
 // ---------------------------------------------------------------- prefill
+// The query rows are processed in slabs of slab_rows rows (a multiple of 64;
+// the last slab may be shorter): the chunk-major pairs of one slab and their
+// outputs are all the workspace has to hold at a time, so the workspace is
+// the per-call part (selection when the library keeps it, pair positions,
+// bucket counts, transposed V) plus one slab's worst case (every pair
+// chunk-major).
 struct PrefillPlan {
   size_t off_sel_idx, off_sel_score, off_pair_pos, off_cnt, off_off, off_pairs, off_partial, off_vt, bytes;
+  int64_t slab_rows;  // 0: the workspace cannot hold one slab of 64 rows
 };
+// Fixed part and per-row part of the workspace (bytes).
+void prefill_workspace_parts(const Geometry& g, bool own_sel, size_t* fixed, size_t* per_row);
+// The plan for slabs of at most `slab_rows` rows (rounded to whole 64-row
+// chunks; at least one chunk, at most the whole call).
+PrefillPlan plan_prefill_slab(const Geometry& g, bool own_sel, int64_t slab_rows);
+// The plan with the largest slabs a workspace of `bytes` holds (slabs of
+// equal numbers of 64-row chunks; slab_rows = 0 when not even one fits).
+PrefillPlan plan_prefill_for(const Geometry& g, bool own_sel, size_t bytes);
+// The default plan (hsa_attn_workspace_size): one slab when its worst case
+// holds at most kPrefillSlabBudget bytes of chunk-major pairs, else equal
+// slabs that each stay within it.
+constexpr size_t kPrefillSlabBudget = size_t(16) << 30;
 PrefillPlan plan_prefill(const Geometry& g, bool own_sel);
 
 struct PrefillArgs {
@@ -83,12 +102,13 @@ struct PrefillArgs {
   int32_t* sel_idx;
   float* sel_score;
   // workspace: remote-pair bucketing and the remote pairs' outputs
-  int32_t* pair_pos;  // [B, Hq, T, k]
+  int32_t* pair_pos;  // [B, Hq, Tq, k]
   int* cnt;           // [B * Hkv * Nc]
   int* off;           // [B * Hkv * Nc + 1]
-  int32_t* pairs;     // [B * Hq * T * k] (worst case)
-  float* partial;     // [B * Hq * T * k, D] (worst case)
+  int32_t* pairs;     // [B * Hq * slab_rows * k] (one slab's worst case)
+  float* partial;     // [B * Hq * slab_rows * k, D]
   void* vt;           // [B, Hkv, Nc, D, 64] transposed V tiles (storage dtype)
+  int64_t slab_rows;  // query rows per slab (multiple of 64)
   // adaptive budget, as in DecodeArgs: g.k == 2 * k_base when k_base > 0
   int k_base = 0;
   float gap_tau = 0.0f;

@@ -1,5 +1,7 @@
 // HSA prefill: host-side planning and dispatch.  The kernels live in
 // prefill_kernels.hpp and are instantiated in prefill_inst_*.hip.
+#include <algorithm>
+
 #include "prefill_kernels.hpp"
 
 namespace hsa_attn {
@@ -17,6 +19,10 @@ HSA_ATTN_PREFILL_EXTERN(FP32, 128, 16)
 HSA_ATTN_PREFILL_EXTERN(FP32, 128, 32)
 HSA_ATTN_PREFILL_EXTERN(FP32, 64, 16)
 HSA_ATTN_PREFILL_EXTERN(FP32, 64, 32)
+HSA_ATTN_PREFILL_EXTERN(BF16, 128, 64)
+HSA_ATTN_PREFILL_EXTERN(BF16, 64, 64)
+HSA_ATTN_PREFILL_EXTERN(FP32, 128, 64)
+HSA_ATTN_PREFILL_EXTERN(FP32, 64, 64)
 
 #define HSA_ATTN_CALL(HAVE, T, D, K)                   \
   do {                                                 \
@@ -59,22 +65,27 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(const int* __restric
   if (tid == 1023) off[n] = part[1023];
 }
 
-// pairs[pos] = row of each remote pair; pair_pos becomes the global position
+// For the remote pairs of the slab's rows [r0, r0 + rn) of every (b, h):
+// pairs[pos] = the pair's query row (b * Hq + h) * T_len + t, and pair_pos
+// becomes the position in the slab's pair list
 __global__ void prefill_scatter_kernel(const int32_t* __restrict__ sel_idx, const int* __restrict__ off,
                                        int32_t* __restrict__ pair_pos, int32_t* __restrict__ pairs, int Hq, int G,
-                                       int64_t T_len, int64_t Nc, int k, int64_t total) {
-  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+                                       int64_t T_len, int64_t Nc, int k, int64_t r0, int64_t rn, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
-  const int32_t inb = pair_pos[i];
+  const int64_t rl = i / k;
+  const int e = (int)(i % k);
+  const int64_t bh = rl / rn, t = r0 + rl % rn;
+  const int64_t row = bh * T_len + t;
+  const int64_t gi = row * k + e;
+  const int32_t inb = pair_pos[gi];
   if (inb < 0) return;
-  const int row = i / k;
-  const int bh = row / (int)T_len;
-  const int h = bh % Hq;
-  const int b = bh / Hq;
-  const int64_t bucket = ((int64_t)b * (Hq / G) + h / G) * Nc + sel_idx[i];
+  const int h = (int)(bh % Hq);
+  const int b = (int)(bh / Hq);
+  const int64_t bucket = ((int64_t)b * (Hq / G) + h / G) * Nc + sel_idx[gi];
   const int32_t pos = off[bucket] + inb;
   pairs[pos] = (int32_t)row;
-  pair_pos[i] = pos;
+  pair_pos[gi] = pos;
 }
 
 
@@ -99,9 +110,9 @@ hipError_t launch_prefill_zero_counts(const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_bucketing(const PrefillArgs& a, hipStream_t st) {
+hipError_t launch_prefill_bucketing(const PrefillArgs& a, int64_t r0, int64_t rn, hipStream_t st) {
   const Geometry& g = a.g;
-  const int64_t total = (int64_t)g.B * g.Hq * g.Tq * g.k;
+  const int64_t total = (int64_t)g.B * g.Hq * rn * g.k;
   const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;
   const unsigned pb = (unsigned)((total + 255) / 256);
   mark_launch(st);
@@ -109,15 +120,40 @@ hipError_t launch_prefill_bucketing(const PrefillArgs& a, hipStream_t st) {
   mark_launch(st);
   mark_launch(st);
   hipLaunchKernelGGL(prefill_scatter_kernel, dim3(pb), dim3(256), 0, st, a.sel_idx, a.off, a.pair_pos, a.pairs, g.Hq,
-                     g.G, g.Tq, g.Nc, g.k, total);
+                     g.G, g.Tq, g.Nc, g.k, r0, rn, total);
   mark_launch(st);
   return hipGetLastError();
 }
 
-PrefillPlan plan_prefill(const Geometry& g, bool own_sel) {
+// Workspace layout: [selection if the library keeps it] pair positions,
+// bucket counts and offsets, transposed V (all per call), then one slab's
+// pair list and pair outputs.
+void prefill_workspace_parts(const Geometry& g, bool own_sel, size_t* fixed, size_t* per_row) {
+  const size_t pairs = (size_t)g.B * g.Hq * (size_t)g.Tq * g.k;
+  const size_t nb = (size_t)g.B * g.Hkv * (size_t)g.Nc;
+  size_t f = 0;
+  if (own_sel) f += align_up_p(pairs * sizeof(int32_t), 256) + align_up_p(pairs * sizeof(float), 256);
+  f += align_up_p(pairs * sizeof(int32_t), 256) + align_up_p(nb * sizeof(int), 256) +
+       align_up_p((nb + 1) * sizeof(int), 256) + align_up_p(nb * kChunk * g.D * (g.bf16 ? 2 : 4), 256);
+  *fixed = f;
+  *per_row = (size_t)g.B * g.Hq * g.k * (sizeof(int32_t) + g.D * sizeof(float));
+}
+
+PrefillPlan plan_prefill_slab(const Geometry& g, bool own_sel, int64_t slab_rows) {
   PrefillPlan p{};
+  const int64_t nqc = (g.Tq + kChunk - 1) / kChunk;
+  // equal slabs of whole 64-row chunks: the fewest slabs of at most
+  // slab_rows rows, then the chunks spread evenly over them
+  int64_t cps = std::max<int64_t>(1, slab_rows / kChunk);
+  if (nqc > 0) {
+    cps = std::min(cps, nqc);
+    const int64_t nslab = (nqc + cps - 1) / cps;
+    cps = (nqc + nslab - 1) / nslab;
+  }
+  p.slab_rows = cps * kChunk;
   size_t off = 0;
   const size_t pairs = (size_t)g.B * g.Hq * (size_t)g.Tq * g.k;
+  const size_t spairs = (size_t)g.B * g.Hq * (size_t)p.slab_rows * g.k;
   const size_t nb = (size_t)g.B * g.Hkv * (size_t)g.Nc;
   if (own_sel) {
     p.off_sel_idx = off;
@@ -131,14 +167,37 @@ PrefillPlan plan_prefill(const Geometry& g, bool own_sel) {
   off = align_up_p(off + nb * sizeof(int), 256);
   p.off_off = off;
   off = align_up_p(off + (nb + 1) * sizeof(int), 256);
-  p.off_pairs = off;
-  off = align_up_p(off + pairs * sizeof(int32_t), 256);
-  p.off_partial = off;
-  off = align_up_p(off + pairs * g.D * sizeof(float), 256);
   p.off_vt = off;
   off = align_up_p(off + nb * kChunk * g.D * (g.bf16 ? 2 : 4), 256);
+  p.off_pairs = off;
+  off = align_up_p(off + spairs * sizeof(int32_t), 256);
+  p.off_partial = off;
+  off = align_up_p(off + spairs * g.D * sizeof(float), 256);
   p.bytes = off;
   return p;
+}
+
+PrefillPlan plan_prefill_for(const Geometry& g, bool own_sel, size_t bytes) {
+  size_t fixed, per_row;
+  prefill_workspace_parts(g, own_sel, &fixed, &per_row);
+  const int64_t nqc = std::max<int64_t>(1, (g.Tq + kChunk - 1) / kChunk);
+  // the most chunks per slab whose plan fits (the plan's size only shrinks
+  // as its slabs do; the estimate ignores the two arrays' alignment)
+  int64_t cps = bytes > fixed ? (int64_t)std::min<size_t>((bytes - fixed) / (per_row * kChunk), (size_t)nqc) : 0;
+  while (cps > 0 && plan_prefill_slab(g, own_sel, cps * kChunk).bytes > bytes) --cps;
+  if (cps == 0) {
+    PrefillPlan p = plan_prefill_slab(g, own_sel, kChunk);  // bytes: the smallest workable workspace
+    p.slab_rows = 0;
+    return p;
+  }
+  return plan_prefill_slab(g, own_sel, cps * kChunk);
+}
+
+PrefillPlan plan_prefill(const Geometry& g, bool own_sel) {
+  size_t fixed, per_row;
+  prefill_workspace_parts(g, own_sel, &fixed, &per_row);
+  const int64_t rows = (int64_t)std::max<size_t>(1, kPrefillSlabBudget / (per_row * kChunk)) * kChunk;
+  return plan_prefill_slab(g, own_sel, rows);
 }
 
 size_t prefill_local_lds_bytes(const Geometry& g, int nbuf) {
@@ -151,22 +210,27 @@ size_t prefill_local_lds_bytes(const Geometry& g, int nbuf) {
 // 32-slot tables)
 int prefill_local_buffers(const Geometry& g) { return 2 * prefill_local_lds_bytes(g, 2) <= 160 * 1024 ? 2 : 1; }
 
-// the register top-k list holds 16 or 32 entries; k <= 16 uses the short list
+// the register top-k list holds 16, 32 or 64 entries: the shortest that
+// holds k (64-entry lists serve query groups of at most 4 heads)
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
-  const bool shortlist = a.g.k <= 16;
+  const bool shortlist = a.g.k <= 16, longlist = a.g.k > 32;
   if (a.g.bf16) {
     if (a.g.D == 128) {
       if (shortlist) HSA_ATTN_CALL(HSA_ATTN_HAVE_BF16_D128_K16, BF16, 128, 16);
+      if (longlist) HSA_ATTN_CALL(HSA_ATTN_HAVE_BF16_D128_K64, BF16, 128, 64);
       HSA_ATTN_CALL(HSA_ATTN_HAVE_BF16_D128_K32, BF16, 128, 32);
     }
     if (shortlist) HSA_ATTN_CALL(HSA_ATTN_HAVE_BF16_D64_K16, BF16, 64, 16);
+    if (longlist) HSA_ATTN_CALL(HSA_ATTN_HAVE_BF16_D64_K64, BF16, 64, 64);
     HSA_ATTN_CALL(HSA_ATTN_HAVE_BF16_D64_K32, BF16, 64, 32);
   }
   if (a.g.D == 128) {
     if (shortlist) HSA_ATTN_CALL(HSA_ATTN_HAVE_FP32_D128_K16, FP32, 128, 16);
+    if (longlist) HSA_ATTN_CALL(HSA_ATTN_HAVE_FP32_D128_K64, FP32, 128, 64);
     HSA_ATTN_CALL(HSA_ATTN_HAVE_FP32_D128_K32, FP32, 128, 32);
   }
   if (shortlist) HSA_ATTN_CALL(HSA_ATTN_HAVE_FP32_D64_K16, FP32, 64, 16);
+  if (longlist) HSA_ATTN_CALL(HSA_ATTN_HAVE_FP32_D64_K64, FP32, 64, 64);
   HSA_ATTN_CALL(HSA_ATTN_HAVE_FP32_D64_K32, FP32, 64, 32);
 }
 

@@ -1,0 +1,7 @@
+// Instantiation of the prefill kernels for storage FP32, head dim 128,
+// top-k register list of 64 entries (query-group sizes up to 4).
+#include "prefill_kernels.hpp"
+
+namespace hsa_attn {
+template hipError_t launch_prefill_g<FP32, 128, 64>(const PrefillArgs&, hipStream_t);
+}  // namespace hsa_attn

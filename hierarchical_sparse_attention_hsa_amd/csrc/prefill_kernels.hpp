@@ -28,6 +28,7 @@
 //   weighted remote outputs and writes the rows.
 #pragma once
 
+#include <algorithm>
 #include <climits>
 
 #include "common.hpp"
@@ -151,8 +152,10 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) __attribute__((amdgpu_waves_
 void prefill_select_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ lm,
     int32_t* __restrict__ sel_idx, float* __restrict__ sel_score, int* __restrict__ rcnt, int32_t* __restrict__ pair_pos,
-    int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int j0, int k, float scale, int k_base, float gap_tau) {
+    int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int jlo, int j0, int k, float scale, int k_base,
+    float gap_tau) {
   // T_len: query rows per (b, h); query row r sits at position 64*j0 + r.
+  // The grid covers the slab of query chunks [jlo, jlo + nqc) of those rows.
   // k_base > 0: adaptive budget, k == 2 * k_base (see the epilogue)
   using st = typename T::storage;
   constexpr int HPW = G < 4 ? G : 4;  // query heads (waves) per workgroup
@@ -197,7 +200,7 @@ void prefill_select_kernel(
   const int hs = rest % HS;
   rest /= HS;
   const int b = rest % B;
-  const int j = nqc - 1 - rest / B;  // heaviest query chunks first
+  const int j = jlo + nqc - 1 - rest / B;  // heaviest query chunks first
   const int tid = threadIdx.x, lane = tid & 63, hh = tid >> 6, half = lane >> 5;
   const int Hq = Hkv * G, h = g * G + hs * HPW + hh;
   const int ja = j0 + j;  // absolute query chunk
@@ -873,7 +876,7 @@ __device__ __forceinline__ int out_col(int dm, int q4, int half) { return 32 * d
 // within its bucket into its position in pairs[] and records its query row
 // there (two launches).
 hipError_t launch_prefill_zero_counts(const PrefillArgs& a, hipStream_t st);
-hipError_t launch_prefill_bucketing(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_prefill_bucketing(const PrefillArgs& a, int64_t r0, int64_t rn, hipStream_t st);
 
 // ---- chunk-major attention of the remote pairs
 template <typename T, int D, int G>
@@ -992,8 +995,9 @@ __global__ __launch_bounds__(kWave* G)
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ kk,
     const typename T::storage* __restrict__ vt_g, const int32_t* __restrict__ sel_idx,
     const float* __restrict__ sel_score, const int32_t* __restrict__ pair_pos, const float* __restrict__ partial,
-    float* __restrict__ out, int B, int Hkv, int64_t T_len, int64_t T_q, int64_t Nc, int nqc, int j0, int k,
-    float scale, int nbuf) {
+    float* __restrict__ out, int B, int Hkv, int64_t T_len, int64_t T_q, int64_t Nc, int nqc, int jlo, int j0,
+    int k, float scale, int nbuf) {
+  // the grid covers the slab of query chunks [jlo, jlo + nqc) of the T_q rows
   using st = typename T::storage;
   using TL = Tile<T, D>;
   constexpr int KCH = D / 16;
@@ -1015,7 +1019,7 @@ __global__ __launch_bounds__(kWave* G)
   const int b = rest % B;
   rest /= B;
   const int hc = rest & 1;
-  const int j = nqc - 1 - (rest >> 1);  // query chunk among the T_q query rows
+  const int j = jlo + nqc - 1 - (rest >> 1);  // query chunk among the T_q query rows
   const int ja = j0 + j;                 // its absolute chunk (keys: T_len rows)
   const int tid = threadIdx.x, lane = tid & 63, hh = tid >> 6, half = lane >> 5;
   const int Hq = Hkv * G, h = g * G + hh;
@@ -1203,48 +1207,60 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   const int nqc = (int)((g.Tq + kChunk - 1) / kChunk);  // query chunks
   const int j0 = (int)g.J0;
   const float scale = 1.0f / sqrtf((float)D);
-  const unsigned blocks = (unsigned)((int64_t)nqc * g.B * g.Hkv);
   const stg* q = static_cast<const stg*>(a.q);
   const stg* k = static_cast<const stg*>(a.k);
   const stg* v = static_cast<const stg*>(a.v);
   constexpr int HPW = G < 4 ? G : 4;
   const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;  // chunks = remote-pair buckets
-  if (nb > 0) {
-    hipError_t e = launch_prefill_zero_counts(a, st);
+  const int cps = (int)(a.slab_rows / kChunk);      // query chunks per slab
+  if (cps < 1) return hipErrorInvalidValue;
+  const int nbuf = prefill_local_buffers(g);
+  const size_t lds = prefill_local_lds_bytes(g, nbuf);
+  auto local = prefill_local_kernel<T, D, G, KSEL>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(local),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  mark_launch(st);
-  hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(blocks * (G / HPW)), dim3(kWave * HPW), 0, st, q,
-                     static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, nb > 0 ? a.cnt : nullptr, a.pair_pos,
-                     g.B, g.Hkv, g.Tq, g.Nc, nqc, j0, g.k, scale, a.k_base, a.gap_tau);
-  mark_launch(st);
+  // Launch order per call: the transposed V tiles once, then per slab of
+  // query chunks [jlo, jlo + ns): bucket counts cleared, selection (which
+  // counts the slab's remote pairs), scan and scatter of the remote pairs,
+  // chunk-major attention, local attention and fusion.
   if (nb > 0) {
     mark_launch(st);
     hipLaunchKernelGGL((prefill_vt_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, st, v, static_cast<stg*>(a.vt),
                        g.T, g.Nc);
     mark_launch(st);
-    hipError_t e = launch_prefill_bucketing(a, st);
+  }
+  for (int jlo = 0; jlo < nqc; jlo += cps) {
+    const int ns = std::min(cps, nqc - jlo);
+    const int64_t r0 = (int64_t)jlo * kChunk, rn = std::min<int64_t>((int64_t)ns * kChunk, g.Tq - r0);
+    const unsigned blocks = (unsigned)((int64_t)ns * g.B * g.Hkv);
+    if (nb > 0) {
+      hipError_t e = launch_prefill_zero_counts(a, st);
+      if (e != hipSuccess) return e;
+    }
+    mark_launch(st);
+    hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(blocks * (G / HPW)), dim3(kWave * HPW), 0, st,
+                       q, static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, nb > 0 ? a.cnt : nullptr,
+                       a.pair_pos, g.B, g.Hkv, g.Tq, g.Nc, ns, jlo, j0, g.k, scale, a.k_base, a.gap_tau);
+    mark_launch(st);
+    if (nb > 0) {
+      hipError_t e = launch_prefill_bucketing(a, r0, rn, st);
+      if (e != hipSuccess) return e;
+      mark_launch(st);
+      hipLaunchKernelGGL((prefill_remote_kernel<T, D, G>), dim3((unsigned)nb), dim3(256), 0, st, q, k,
+                         static_cast<const stg*>(a.vt), a.off, a.pairs, a.partial, g.Hkv, g.T, g.Nc, scale);
+      mark_launch(st);
+    }
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     mark_launch(st);
-    hipLaunchKernelGGL((prefill_remote_kernel<T, D, G>), dim3((unsigned)nb), dim3(256), 0, st, q, k,
-                       static_cast<const stg*>(a.vt), a.off, a.pairs, a.partial, g.Hkv, g.T, g.Nc, scale);
+    hipLaunchKernelGGL(local, dim3(2 * blocks), dim3(kWave * G), lds, st, q, k, static_cast<const stg*>(a.vt),
+                       a.sel_idx, a.sel_score, a.pair_pos, a.partial, a.out, g.B, g.Hkv, g.T, g.Tq, g.Nc, ns, jlo,
+                       j0, g.k, scale, nbuf);
     mark_launch(st);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nbuf = prefill_local_buffers(g);
-  const size_t lds = prefill_local_lds_bytes(g, nbuf);
-  auto kern = prefill_local_kernel<T, D, G, KSEL>;
-  if (lds > 65536) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  mark_launch(st);
-  hipLaunchKernelGGL(kern, dim3(2 * blocks), dim3(kWave * G), lds, st, q, k, static_cast<const stg*>(a.vt),
-                     a.sel_idx, a.sel_score, a.pair_pos, a.partial, a.out, g.B, g.Hkv, g.T, g.Tq, g.Nc, nqc, j0,
-                     g.k, scale, nbuf);
-  mark_launch(st);
   return hipGetLastError();
 }
 
@@ -1256,7 +1272,11 @@ hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t st) {
     case 1: return launch_prefill_t<T, D, 1, KSEL>(a, st);
     case 2: return launch_prefill_t<T, D, 2, KSEL>(a, st);
     case 4: return launch_prefill_t<T, D, 4, KSEL>(a, st);
-    default: return launch_prefill_t<T, D, 8, KSEL>(a, st);
+    default:
+      // 64-entry lists: the local kernel's per-row tables of eight heads
+      // would not fit the LDS next to a chunk image (the host rejects it)
+      if constexpr (KSEL > 32) return hipErrorNotSupported;
+      else return launch_prefill_t<T, D, 8, KSEL>(a, st);
   }
 }
 

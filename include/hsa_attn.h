@@ -34,8 +34,10 @@
  *  - Errors: HSA_ATTN_INVALID_ARGUMENT (null or misaligned pointer, bad
  *    sizes), HSA_ATTN_UNSUPPORTED (sizes outside the supported envelope:
  *    D in {64,128}, S == 64 for the forward calls, Hq/Hkv in {1,2,4,8},
- *    k <= 64 for decode and k <= 32 for prefill; prefill also needs
- *    floor(T/S) <= 65536 and B*Hq*T*k < 2^31), HSA_ATTN_WORKSPACE_TOO_SMALL,
+ *    k <= 64 (the adaptive calls: base k <= 32; the prefill backward:
+ *    k <= 32); prefill with more than 32 selection slots needs Hq/Hkv <= 4,
+ *    and prefill also needs floor(T/S) <= 65536 and B*Hq*T*slots < 2^31),
+ *    HSA_ATTN_WORKSPACE_TOO_SMALL,
  *    HSA_ATTN_HIP_ERROR (a launch failed).  hsa_attn_last_error() returns a
  *    thread-local message about the last failure.
  */
@@ -100,19 +102,36 @@ hsa_attn_status_t hsa_build_landmarks(const hsa_attn_dims_t* d, const void* k, v
  * the fp32 dot products q.L before the 1/sqrt(D) factor is applied; where
  * that factor rounds two different dot products to one stored score, the
  * larger dot product is the one kept at the cut.
- * workspace: device scratch of at least hsa_attn_workspace_size(d, 0) bytes
- * (never NULL when T > 0).  It holds the selection when sel_idx is NULL,
- * the bucketing of the pairs attended chunk-major (selected chunks before
- * the query's aligned window of 64 chunks, and window chunks that few rows
- * of the query's 32-row block selected), one fp32 [D] attention output per
- * such pair, and a transposed copy of V.  The size covers the worst case,
- * every selected pair chunk-major: about B*Hq*T*k*(4*D + 16) bytes plus the size of
- * V (69 GB at B=1, Hq=32, T=2^18, k=16, D=128, bf16).
+ * workspace: device scratch (never NULL when T > 0).  It holds, for the
+ * whole call, the selection when sel_idx is NULL (8 bytes per slot), the
+ * pair positions (4 bytes per slot), per-chunk bucket counts and a
+ * transposed copy of V; and, for one slab of query rows at a time, the pairs
+ * attended chunk-major (selected chunks before the query's aligned window
+ * of 64 chunks, and window chunks that few rows of the query's 32-row block
+ * selected) with one fp32 [D] attention output each, sized for the worst
+ * case (every pair of the slab chunk-major: B*Hq*rows*k*(4*D + 4) bytes).
+ * The call processes its rows in equal slabs of whole 64-row chunks, as
+ * large as workspace_bytes allows (hsa_attn_prefill_slab_rows tells the
+ * size); results do not depend on the slab size.  hsa_attn_workspace_size(d,
+ * 0) returns the size for slabs whose worst case stays within 16 GiB (about
+ * 18 GB at B=1, Hq=32, T=2^18, k=16, D=128, bf16, in 5 slabs); the minimum is
+ * the per-call part plus one slab of 64 rows, and less returns
+ * HSA_ATTN_WORKSPACE_TOO_SMALL.
  */
 hsa_attn_status_t hsa_forward_prefill(const hsa_attn_dims_t* d, const void* q, const void* k,
                                       const void* v, const void* landmarks, float* out,
                                       int32_t* sel_idx, float* sel_score, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/*
+ * Query rows per slab that hsa_forward_prefill (adaptive = 0) or
+ * hsa_forward_prefill_adaptive (adaptive != 0; d->top_k is the base k) uses
+ * with a workspace of workspace_bytes, when the caller passes sel_idx and
+ * sel_score (selection_given != 0) or not: a multiple of 64, or 0 when the
+ * workspace is too small.  A planning query: it touches no device.
+ */
+hsa_attn_status_t hsa_attn_prefill_slab_rows(const hsa_attn_dims_t* d, int adaptive, int selection_given,
+                                             size_t workspace_bytes, int64_t* slab_rows);
 
 /*
  * Chunked prefill over a cached prefix (serving: new tokens appended to a
@@ -140,7 +159,8 @@ hsa_attn_status_t hsa_forward_prefill_cached(const hsa_attn_dims_t* d, int64_t q
  * the 1/sqrt(D) scale, the values written to sel_score), its best k
  * otherwise.  gap_threshold = 0 reproduces hsa_forward_prefill with top_k = k
  * and +inf with top_k = 2k, bit for bit.  gap_threshold must be >= 0 (+inf
- * allowed).  Requires k <= 16.  sel_idx/sel_score [B,Hq,T,2k] optional, -1 /
+ * allowed).  Requires k <= 32 (and Hq/Hkv <= 4 when k > 16).
+ * sel_idx/sel_score [B,Hq,T,2k] optional, -1 /
  * -inf padding.  workspace: at least hsa_attn_workspace_size(d, 3) bytes.
  */
 hsa_attn_status_t hsa_forward_prefill_adaptive(const hsa_attn_dims_t* d, float gap_threshold, const void* q,
@@ -270,9 +290,10 @@ hsa_attn_status_t hsa_append_kv(const hsa_attn_dims_t* d, const void* k_new, con
  * forward, landmark or append call made on the calling thread records events[2*i] (hipEvent_t, created by the caller)
  * on its stream just before its i-th kernel launch and events[2*i+1] just
  * after it, for i < n_pairs; the index restarts at 0 with each call.
- * Launch order: landmarks: 1 kernel; prefill, cached and adaptive prefill (when T >= S): zero, select,
- * V transpose, scan, scatter, remote attention, local attention (for T < S:
- * select, local attention); decode and varlen decode: scan, merge,
+ * Launch order: landmarks: 1 kernel; prefill, cached and adaptive prefill (when T >= S): V transpose,
+ * then per slab of query rows (hsa_attn_prefill_slab_rows) zero, select,
+ * scan, scatter, remote attention, local attention (for T < S: select,
+ * local attention per slab); decode and varlen decode: scan, merge,
  * attention, fusion, for adaptive decode too (scan and attention are skipped when the cache capacity
  * holds no complete chunk); append: 1 kernel; backward: zero counts, row
  * preparation, scan, scatter, K transpose, chunk gradients, dq (scan,

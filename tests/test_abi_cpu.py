@@ -91,22 +91,71 @@ def test_supported_envelope():
     for call in ("prefill", "decode"):
         assert status_of(dims(chunk_size=32), call) == hsa.HSA_ATTN_UNSUPPORTED
         assert status_of(dims(num_q_heads=48, num_kv_heads=3), call) == hsa.HSA_ATTN_UNSUPPORTED  # G = 16
-    assert status_of(dims(top_k=33), "prefill") == hsa.HSA_ATTN_UNSUPPORTED
+    assert status_of(dims(top_k=65), "prefill") == hsa.HSA_ATTN_UNSUPPORTED
     assert status_of(dims(top_k=65), "decode") == hsa.HSA_ATTN_UNSUPPORTED
+    # more than 32 prefill slots: up to four query heads per KV head
+    assert status_of(dims(top_k=33, num_q_heads=64), "prefill") == hsa.HSA_ATTN_UNSUPPORTED
+    for kk, hq in ((33, 32), (64, 32), (64, 8), (32, 64)):
+        assert status_of(dims(top_k=kk, num_q_heads=hq), "prefill") not in (
+            hsa.HSA_ATTN_INVALID_ARGUMENT, hsa.HSA_ATTN_UNSUPPORTED, hsa.HSA_ATTN_WORKSPACE_TOO_SMALL), (kk, hq)
     # landmarks accept any chunk size and group size
     assert status_of(dims(chunk_size=1, num_q_heads=3, num_kv_heads=3), "landmarks", c0=0, c1=0) == 0
 
 
-@pytest.mark.parametrize("is_decode", [0, 1])
-def test_workspace_size_and_too_small_workspace(is_decode):
+def test_decode_workspace_size_and_too_small_workspace():
     d = dims(batch=2, seq_len=64 * 100 + 7)
-    n = hsa.hsa_attn_workspace_size(d, is_decode)
+    n = hsa.hsa_attn_workspace_size(d, 1)
     assert n > 0 and n % 256 == 0
-    call = "decode" if is_decode else "prefill"
-    assert status_of(d, call, ws=n - 1) == hsa.HSA_ATTN_WORKSPACE_TOO_SMALL
+    assert status_of(d, "decode", ws=n - 1) == hsa.HSA_ATTN_WORKSPACE_TOO_SMALL
     assert "workspace" in hsa.hsa_attn_last_error()
-    if not is_decode:
-        assert n >= 2 * 32 * (64 * 100 + 7) * 16 * 4  # selection of every row
+
+
+def min_prefill_workspace(d, adaptive=False, given=False):
+    lo, hi = 0, 1 << 50
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if hsa.hsa_attn_prefill_slab_rows(d, mid, adaptive, given) > 0:
+            hi = mid
+        else:
+            lo = mid + 1
+    return lo
+
+
+def test_prefill_workspace_slabs():
+    """The prefill runs its query rows in slabs as large as the workspace
+    holds: the default size takes the whole call in one slab when its worst
+    case stays within 16 GiB, a smaller workspace gives smaller slabs (whole
+    64-row chunks, spread evenly), and below one 64-row slab the call is
+    refused before anything is launched."""
+    d = dims(batch=2, seq_len=64 * 100 + 7)
+    n = hsa.hsa_attn_workspace_size(d, 0)
+    assert n > 0 and n % 256 == 0
+    assert n >= 2 * 32 * (64 * 100 + 7) * 16 * 4  # selection of every row
+    assert hsa.hsa_attn_prefill_slab_rows(d, n) == 64 * 101
+    m = min_prefill_workspace(d)
+    assert hsa.hsa_attn_prefill_slab_rows(d, m) == 64
+    assert status_of(d, "prefill", ws=m - 1) == hsa.HSA_ATTN_WORKSPACE_TOO_SMALL
+    assert "workspace" in hsa.hsa_attn_last_error()
+    # a slab of 64 rows holds every pair of its rows chunk-major: 4 + 4 D bytes each
+    per_row = 2 * 32 * 16 * (4 + 4 * 128)
+    m2 = min_prefill_workspace(d, given=True)
+    assert m - m2 == 2 * 32 * (64 * 100 + 7) * 16 * 8 // 256 * 256 or abs(m - m2 - 2 * 32 * 6407 * 16 * 8) < 1024
+    # slabs are equal numbers of whole chunks
+    for ws in (m + per_row * 64 * 3, m + per_row * 64 * 50, m + per_row * 64 * 60):
+        rows = hsa.hsa_attn_prefill_slab_rows(d, ws)
+        assert rows % 64 == 0 and 64 <= rows
+        nslab = -(-101 // (rows // 64))
+        assert (rows // 64) == -(-101 // nslab)
+        assert rows <= 64 + (ws - m) // per_row
+    # the long prefill: the default workspace stays far below the one-slab worst case
+    big = dims(seq_len=1 << 18)
+    nb = hsa.hsa_attn_workspace_size(big, 0)
+    worst_one_slab = 32 * (1 << 18) * 16 * (4 + 4 * 128)
+    assert nb < 20e9 and nb < worst_one_slab / 3
+    assert hsa.hsa_attn_prefill_slab_rows(big, nb) < (1 << 18)
+    # a 1M-token prefill fits the 288 GB card with the default size
+    huge = dims(seq_len=1 << 20)
+    assert hsa.hsa_attn_workspace_size(huge, 0) < 40e9
 
 
 def test_status_strings():
@@ -179,7 +228,8 @@ def test_adaptive_prefill_validation():
 
     for bad in (float("nan"), -0.5):
         assert call(dims(), bad) == hsa.HSA_ATTN_INVALID_ARGUMENT
-    assert call(dims(top_k=17), 0.1) == hsa.HSA_ATTN_UNSUPPORTED  # 2k must stay <= 32
+    assert call(dims(top_k=33), 0.1) == hsa.HSA_ATTN_UNSUPPORTED  # 2k must stay <= 64
+    assert call(dims(top_k=17, num_q_heads=64), 0.1) == hsa.HSA_ATTN_UNSUPPORTED  # 2k > 32 needs G <= 4
     assert call(dims(), 0.1, ws=16) == hsa.HSA_ATTN_WORKSPACE_TOO_SMALL
     d = dims(top_k=16, seq_len=1 << 15)
     assert hsa.hsa_attn_workspace_size(d, 3) == hsa.hsa_attn_workspace_size(dims(top_k=32, seq_len=1 << 15), 0)

@@ -123,6 +123,8 @@ PREFILL_CASES = [
     (1, 8, 2, 64 * 70 + 13, 128, 8, "bf16"),  # 2k = 16
     (1, 4, 4, 64 * 80, 64, 16, "fp32"),       # 2k = 32, past one 64-chunk window
     (2, 4, 1, 64 * 140, 128, 16, "bf16"),     # two windows: remote pairs
+    (1, 4, 1, 64 * 90 + 3, 128, 32, "bf16"),  # 2k = 64 (64-entry lists), past one window
+    (1, 2, 2, 64 * 70, 64, 24, "fp32"),       # 2k = 48, G = 1
 ]
 
 

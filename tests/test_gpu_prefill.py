@@ -60,6 +60,11 @@ CASES = [
     (1, 2, 2, 64 * 75 + 5, 64, 8, "fp32"),       # G = 1
     (1, 8, 1, 64 * 66, 64, 32, "bf16"),          # G = 8, k = 32
     (2, 4, 2, 64 * 129 + 33, 128, 4, "fp32"),    # G = 2, three windows
+    # 64-entry lists (k > 32; up to four query heads per KV head)
+    (1, 4, 1, 64 * 140 + 7, 128, 64, "bf16"),    # G = 4, k = 64, past one window
+    (1, 4, 4, 64 * 70 + 13, 64, 48, "fp32"),     # G = 1, k = 48
+    (1, 2, 1, 64 * 90, 128, 40, "bf16"),         # G = 2, k = 40
+    (2, 4, 2, 64 * 66 + 5, 64, 64, "fp32"),      # B = 2, G = 2, k = 64
 ]
 
 
@@ -99,7 +104,7 @@ def test_prefill_is_deterministic():
         assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("topk", [4, 16, 32])
+@pytest.mark.parametrize("topk", [4, 16, 32, 64])
 def test_prefill_duplicate_chunks_keep_index_order(topk):
     """Chunks with bit-equal keys score bit-equal: when both are kept the
     lower index takes the earlier slot, and a cut between them keeps the
@@ -119,7 +124,7 @@ def test_prefill_duplicate_chunks_keep_index_order(topk):
                     assert lo in s and s.index(lo) < s.index(hi), (lo, hi, h, p, s)
 
 
-@pytest.mark.parametrize("topk", [8, 32])
+@pytest.mark.parametrize("topk", [8, 32, 64])
 def test_prefill_all_scores_equal_keep_lowest_indices(topk):
     """Every chunk identical: each row keeps its topk lowest chunk indices in
     index order."""
@@ -133,3 +138,50 @@ def test_prefill_all_scores_equal_keep_lowest_indices(topk):
         assert np.array_equal(sel[0, :, p, :n], np.tile(np.arange(n), (Hq, 1))), p
         assert np.all(sel[0, :, p, n:] == -1)
     compare(q, k, v, 64, topk, "bf16", out, sel, score, rows=np.arange(0, T, 37))
+
+
+def min_workspace(dims):
+    """Smallest prefill workspace (slabs of 64 query rows)."""
+    lo, hi = 0, 1 << 44
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if hsa.hsa_attn_prefill_slab_rows(dims, mid, False, True) > 0:
+            hi = mid
+        else:
+            lo = mid + 1
+    return lo
+
+
+@pytest.mark.parametrize("case", [(1, 8, 2, 64 * 140 + 7, 128, 16, "bf16"), (1, 4, 1, 64 * 75 + 30, 64, 64, "fp32")])
+def test_prefill_results_do_not_depend_on_slab_size(case):
+    """The rows run in slabs as large as the workspace holds; slabs of one
+    chunk, of a few chunks and the default give the same results bit for
+    bit (every pair's arithmetic is the same, only what is in flight at a
+    time changes), and they match the oracle."""
+    B, Hq, Hkv, T, D, topk, dtype = case
+    print(f"prefill slab case {case}", flush=True)
+    q, k, v = small_inputs(B, Hq, Hkv, T, D, dtype, seed=case_seed(case))
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    L = torch.empty((B, Hkv, T // 64, D), dtype=k.dtype, device="cuda")
+    hsa.hsa_build_landmarks(kd, L, 64)
+    dims = hsa.make_dims(B, Hq, Hkv, D, 64, topk, T, hsa.HSA_ATTN_BF16 if dtype == "bf16" else hsa.HSA_ATTN_FP32)
+    m = min_workspace(dims)
+    per_chunk = B * Hq * topk * (4 + 4 * D) * 64
+    results = []
+    for ws_bytes in (m, m + 2 * per_chunk, hsa.hsa_attn_workspace_size(dims, 0)):
+        rows = hsa.hsa_attn_prefill_slab_rows(dims, ws_bytes, False, True)
+        print(f"workspace {ws_bytes} bytes: slabs of {rows} rows", flush=True)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        sel = torch.full((B, Hq, T, topk), -7, dtype=torch.int32, device="cuda")
+        score = torch.full((B, Hq, T, topk), 7.0, dtype=torch.float32, device="cuda")
+        out = torch.full((B, Hq, T, D), 3.0, dtype=torch.float32, device="cuda")
+        hsa.hsa_forward_prefill(qd, kd, vd, L, 64, topk, out=out, sel_idx=sel, sel_score=score, workspace=ws)
+        torch.cuda.synchronize()
+        results.append((rows, out.cpu(), sel.cpu(), score.cpu()))
+        del ws
+    assert results[0][0] == 64 and results[1][0] == 192 and results[2][0] >= 64 * (T // 64)
+    for r in results[1:]:
+        for a, b in zip(results[0][1:], r[1:]):
+            assert torch.equal(a, b)
+    _, out, sel, score = results[0]
+    compare(q, k, v, 64, topk, dtype, out.double().numpy(), sel.numpy(), score.double().numpy())
