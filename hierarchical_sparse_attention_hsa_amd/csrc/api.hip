@@ -242,7 +242,8 @@ static hsa_attn_status_t forward_prefill(const hsa_attn_dims_t* d, int64_t q_off
     hsa_attn::PrefillArgs a{g, q, k, v, landmarks, out, sel_idx, sel_score,
                             reinterpret_cast<int32_t*>(ws + plan.off_pair_pos), reinterpret_cast<int*>(ws + plan.off_cnt),
                             reinterpret_cast<int*>(ws + plan.off_off), reinterpret_cast<int32_t*>(ws + plan.off_pairs),
-                            reinterpret_cast<float*>(ws + plan.off_partial), ws + plan.off_vt, plan.slab_rows};
+                            reinterpret_cast<float*>(ws + plan.off_partial), ws + plan.off_vt, plan.slab_rows,
+                            plan.slab_group};
     if (adaptive) {
       a.k_base = d->top_k;
       a.gap_tau = gap_tau;

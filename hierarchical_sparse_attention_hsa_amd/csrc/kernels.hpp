@@ -80,7 +80,10 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s
 struct PrefillPlan {
   size_t off_sel_idx, off_sel_score, off_pair_pos, off_cnt, off_off, off_pairs, off_partial, off_vt, bytes;
   int64_t slab_rows;  // 0: the workspace cannot hold one slab of 64 rows
+  int slab_group;     // slabs whose pairs one selection launch counts (their bucket counts side by side)
 };
+// at most this many slabs' bucket counts are kept at once
+constexpr int kPrefillCountSlabs = 64;
 // Fixed part and per-row part of the workspace (bytes).
 void prefill_workspace_parts(const Geometry& g, bool own_sel, size_t* fixed, size_t* per_row);
 // The plan for slabs of at most `slab_rows` rows (rounded to whole 64-row
@@ -103,12 +106,13 @@ struct PrefillArgs {
   float* sel_score;
   // workspace: remote-pair bucketing and the remote pairs' outputs
   int32_t* pair_pos;  // [B, Hq, Tq, k]
-  int* cnt;           // [B * Hkv * Nc]
+  int* cnt;           // [slab_group][B * Hkv * Nc]
   int* off;           // [B * Hkv * Nc + 1]
   int32_t* pairs;     // [B * Hq * slab_rows * k] (one slab's worst case)
   float* partial;     // [B * Hq * slab_rows * k, D]
   void* vt;           // [B, Hkv, Nc, D, 64] transposed V tiles (storage dtype)
   int64_t slab_rows;  // query rows per slab (multiple of 64)
+  int slab_group;     // slabs per selection launch
   // adaptive budget, as in DecodeArgs: g.k == 2 * k_base when k_base > 0
   int k_base = 0;
   float gap_tau = 0.0f;

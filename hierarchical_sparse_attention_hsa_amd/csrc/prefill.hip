@@ -102,7 +102,7 @@ hipError_t launch_exclusive_scan(const int* cnt, int* off, int64_t n, hipStream_
 
 hipError_t launch_prefill_zero_counts(const PrefillArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
-  const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;
+  const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc * a.slab_group;
   mark_launch(st);
   hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)std::min<int64_t>((nb + 255) / 256, 4096)), dim3(256), 0,
                      st, a.cnt, nb);
@@ -110,13 +110,13 @@ hipError_t launch_prefill_zero_counts(const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_bucketing(const PrefillArgs& a, int64_t r0, int64_t rn, hipStream_t st) {
+hipError_t launch_prefill_bucketing(const PrefillArgs& a, const int* cnt, int64_t r0, int64_t rn, hipStream_t st) {
   const Geometry& g = a.g;
   const int64_t total = (int64_t)g.B * g.Hq * rn * g.k;
   const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;
   const unsigned pb = (unsigned)((total + 255) / 256);
   mark_launch(st);
-  hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, a.cnt, a.off, nb);
+  hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, cnt, a.off, nb);
   mark_launch(st);
   mark_launch(st);
   hipLaunchKernelGGL(prefill_scatter_kernel, dim3(pb), dim3(256), 0, st, a.sel_idx, a.off, a.pair_pos, a.pairs, g.Hq,
@@ -151,6 +151,8 @@ PrefillPlan plan_prefill_slab(const Geometry& g, bool own_sel, int64_t slab_rows
     cps = (nqc + nslab - 1) / nslab;
   }
   p.slab_rows = cps * kChunk;
+  const int64_t nslab = nqc > 0 ? (nqc + cps - 1) / cps : 1;
+  p.slab_group = (int)std::min<int64_t>(nslab, kPrefillCountSlabs);
   size_t off = 0;
   const size_t pairs = (size_t)g.B * g.Hq * (size_t)g.Tq * g.k;
   const size_t spairs = (size_t)g.B * g.Hq * (size_t)p.slab_rows * g.k;
@@ -164,7 +166,7 @@ PrefillPlan plan_prefill_slab(const Geometry& g, bool own_sel, int64_t slab_rows
   p.off_pair_pos = off;
   off = align_up_p(off + pairs * sizeof(int32_t), 256);
   p.off_cnt = off;
-  off = align_up_p(off + nb * sizeof(int), 256);
+  off = align_up_p(off + nb * p.slab_group * sizeof(int), 256);
   p.off_off = off;
   off = align_up_p(off + (nb + 1) * sizeof(int), 256);
   p.off_vt = off;

@@ -152,10 +152,12 @@ __global__ __launch_bounds__(kWave*(G < 4 ? G : 4)) __attribute__((amdgpu_waves_
 void prefill_select_kernel(
     const typename T::storage* __restrict__ q, const typename T::storage* __restrict__ lm,
     int32_t* __restrict__ sel_idx, float* __restrict__ sel_score, int* __restrict__ rcnt, int32_t* __restrict__ pair_pos,
-    int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int jlo, int j0, int k, float scale, int k_base,
-    float gap_tau) {
+    int B, int Hkv, int64_t T_len, int64_t Nc, int nqc, int jlo, int slab_chunks, int j0, int k, float scale,
+    int k_base, float gap_tau) {
   // T_len: query rows per (b, h); query row r sits at position 64*j0 + r.
-  // The grid covers the slab of query chunks [jlo, jlo + nqc) of those rows.
+  // The grid covers the query chunks [jlo, jlo + nqc) of those rows, which
+  // fall in slabs of slab_chunks chunks starting at jlo; the remote pairs of
+  // each slab are counted in its own block of B * Hkv * Nc bucket counts.
   // k_base > 0: adaptive budget, k == 2 * k_base (see the epilogue)
   using st = typename T::storage;
   constexpr int HPW = G < 4 ? G : 4;  // query heads (waves) per workgroup
@@ -591,7 +593,7 @@ void prefill_select_kernel(
     }
   }
   __syncthreads();
-  int* bucket0 = rcnt + ((int64_t)b * Hkv + g) * Nc;
+  int* bucket0 = rcnt + ((int64_t)((j - jlo) / slab_chunks) * B * Hkv + (int64_t)b * Hkv + g) * Nc;
   for (int i = tid; i < HASH; i += kWave * HPW) {
     const uint32_t w = hw[i];
     if (w != kEmpty) hw[i] = (uint32_t)atomicAdd(&bucket0[w >> 16], (int)(w & 0xffffu));  // -> first position
@@ -876,7 +878,7 @@ __device__ __forceinline__ int out_col(int dm, int q4, int half) { return 32 * d
 // within its bucket into its position in pairs[] and records its query row
 // there (two launches).
 hipError_t launch_prefill_zero_counts(const PrefillArgs& a, hipStream_t st);
-hipError_t launch_prefill_bucketing(const PrefillArgs& a, int64_t r0, int64_t rn, hipStream_t st);
+hipError_t launch_prefill_bucketing(const PrefillArgs& a, const int* cnt, int64_t r0, int64_t rn, hipStream_t st);
 
 // ---- chunk-major attention of the remote pairs
 template <typename T, int D, int G>
@@ -1222,44 +1224,51 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  // Launch order per call: the transposed V tiles once, then per slab of
-  // query chunks [jlo, jlo + ns): bucket counts cleared, selection (which
-  // counts the slab's remote pairs), scan and scatter of the remote pairs,
-  // chunk-major attention, local attention and fusion.
+  // Launch order per call: the transposed V tiles once; then per group of
+  // up to kPrefillCountSlabs slabs of query chunks: the group's bucket
+  // counts cleared and one selection over its rows (which counts each
+  // slab's remote pairs apart), and per slab [jlo, jlo + ns): scan and
+  // scatter of its remote pairs, chunk-major attention, local attention and
+  // fusion.
   if (nb > 0) {
     mark_launch(st);
     hipLaunchKernelGGL((prefill_vt_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, st, v, static_cast<stg*>(a.vt),
                        g.T, g.Nc);
     mark_launch(st);
   }
-  for (int jlo = 0; jlo < nqc; jlo += cps) {
-    const int ns = std::min(cps, nqc - jlo);
-    const int64_t r0 = (int64_t)jlo * kChunk, rn = std::min<int64_t>((int64_t)ns * kChunk, g.Tq - r0);
-    const unsigned blocks = (unsigned)((int64_t)ns * g.B * g.Hkv);
+  const int sgc = cps * a.slab_group;  // query chunks per selection launch
+  for (int jg = 0; jg < nqc; jg += sgc) {
+    const int ng = std::min(sgc, nqc - jg);
     if (nb > 0) {
       hipError_t e = launch_prefill_zero_counts(a, st);
       if (e != hipSuccess) return e;
     }
+    const unsigned gblocks = (unsigned)((int64_t)ng * g.B * g.Hkv);
     mark_launch(st);
-    hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(blocks * (G / HPW)), dim3(kWave * HPW), 0, st,
+    hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(gblocks * (G / HPW)), dim3(kWave * HPW), 0, st,
                        q, static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, nb > 0 ? a.cnt : nullptr,
-                       a.pair_pos, g.B, g.Hkv, g.Tq, g.Nc, ns, jlo, j0, g.k, scale, a.k_base, a.gap_tau);
+                       a.pair_pos, g.B, g.Hkv, g.Tq, g.Nc, ng, jg, cps, j0, g.k, scale, a.k_base, a.gap_tau);
     mark_launch(st);
-    if (nb > 0) {
-      hipError_t e = launch_prefill_bucketing(a, r0, rn, st);
+    for (int jlo = jg; jlo < jg + ng; jlo += cps) {
+      const int ns = std::min(cps, jg + ng - jlo);
+      const int64_t r0 = (int64_t)jlo * kChunk, rn = std::min<int64_t>((int64_t)ns * kChunk, g.Tq - r0);
+      const unsigned blocks = (unsigned)((int64_t)ns * g.B * g.Hkv);
+      if (nb > 0) {
+        hipError_t e = launch_prefill_bucketing(a, a.cnt + (int64_t)((jlo - jg) / cps) * nb, r0, rn, st);
+        if (e != hipSuccess) return e;
+        mark_launch(st);
+        hipLaunchKernelGGL((prefill_remote_kernel<T, D, G>), dim3((unsigned)nb), dim3(256), 0, st, q, k,
+                           static_cast<const stg*>(a.vt), a.off, a.pairs, a.partial, g.Hkv, g.T, g.Nc, scale);
+        mark_launch(st);
+      }
+      hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       mark_launch(st);
-      hipLaunchKernelGGL((prefill_remote_kernel<T, D, G>), dim3((unsigned)nb), dim3(256), 0, st, q, k,
-                         static_cast<const stg*>(a.vt), a.off, a.pairs, a.partial, g.Hkv, g.T, g.Nc, scale);
+      hipLaunchKernelGGL(local, dim3(2 * blocks), dim3(kWave * G), lds, st, q, k, static_cast<const stg*>(a.vt),
+                         a.sel_idx, a.sel_score, a.pair_pos, a.partial, a.out, g.B, g.Hkv, g.T, g.Tq, g.Nc, ns, jlo,
+                         j0, g.k, scale, nbuf);
       mark_launch(st);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    mark_launch(st);
-    hipLaunchKernelGGL(local, dim3(2 * blocks), dim3(kWave * G), lds, st, q, k, static_cast<const stg*>(a.vt),
-                       a.sel_idx, a.sel_score, a.pair_pos, a.partial, a.out, g.B, g.Hkv, g.T, g.Tq, g.Nc, ns, jlo,
-                       j0, g.k, scale, nbuf);
-    mark_launch(st);
   }
   return hipGetLastError();
 }
