@@ -635,14 +635,14 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
             hsa.hsa_forward_prefill(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc, workspace=ws)
 
     # launches: landmarks; the V transpose; per group of up to 64 slabs
-    # zero and select, then per slab scan, scatter, remote, local.  Per-kernel
-    # times are summed over the slabs.
+    # zero, select, scan and scatter, then per slab remote and local.
+    # Per-kernel times are summed over the slabs.
     names = ["landmarks", "prefill_zero", "prefill_select", "prefill_vt", "prefill_scan", "prefill_scatter",
              "prefill_remote", "prefill_local"]
     order = ["landmarks", "prefill_vt"]
     for s0 in range(0, nslab, 64):
-        order += ["prefill_zero", "prefill_select"]
-        order += ["prefill_scan", "prefill_scatter", "prefill_remote", "prefill_local"] * min(64, nslab - s0)
+        order += ["prefill_zero", "prefill_select", "prefill_scan", "prefill_scatter"]
+        order += ["prefill_remote", "prefill_local"] * min(64, nslab - s0)
     secs, per_launch = timed_steps(step, steps, warmup, len(order), events)
     per = np.array([sum(t for n, t in zip(order, per_launch) if n == name) for name in names])
     ms_step = 1e3 * secs / steps

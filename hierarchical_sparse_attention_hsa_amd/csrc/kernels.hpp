@@ -75,8 +75,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s
 // the last slab may be shorter): the chunk-major pairs of one slab and their
 // outputs are all the workspace has to hold at a time, so the workspace is
 // the per-call part (selection when the library keeps it, pair positions,
-// bucket counts, transposed V) plus one slab's worst case (every pair
-// chunk-major).
+// bucket counts and pair lists, transposed V) plus one slab's worst case of
+// chunk-major pair outputs (every pair chunk-major).
 struct PrefillPlan {
   size_t off_sel_idx, off_sel_score, off_pair_pos, off_cnt, off_off, off_pairs, off_partial, off_vt, bytes;
   int64_t slab_rows;  // 0: the workspace cannot hold one slab of 64 rows
@@ -107,9 +107,9 @@ struct PrefillArgs {
   // workspace: remote-pair bucketing and the remote pairs' outputs
   int32_t* pair_pos;  // [B, Hq, Tq, k]
   int* cnt;           // [slab_group][B * Hkv * Nc]
-  int* off;           // [B * Hkv * Nc + 1]
-  int32_t* pairs;     // [B * Hq * slab_rows * k] (one slab's worst case)
-  float* partial;     // [B * Hq * slab_rows * k, D]
+  int* off;           // [slab_group][B * Hkv * Nc + 1]
+  int32_t* pairs;     // [slab_group][B * Hq * slab_rows * k] (each slab's worst case)
+  float* partial;     // [B * Hq * slab_rows * k, D] (one slab's worst case)
   void* vt;           // [B, Hkv, Nc, D, 64] transposed V tiles (storage dtype)
   int64_t slab_rows;  // query rows per slab (multiple of 64)
   int slab_group;     // slabs per selection launch

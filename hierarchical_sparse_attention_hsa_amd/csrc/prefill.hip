@@ -39,55 +39,95 @@ __global__ void prefill_zero_kernel(int* __restrict__ p, int64_t n) {
     p[i] = 0;
 }
 
-// exclusive prefix sum of n counts into off[0..n] (off[n] = total), one
-// workgroup of 1024 threads
+// exclusive prefix sums of blockIdx.x's n counts cnt[x * n ..] into
+// off[x * (n + 1) ..] (off[.. n] = the total); one workgroup of 1024
+// threads per array: each thread sums a contiguous run, the runs' sums are
+// scanned by the waves (shuffles) and across the waves, then each thread
+// writes its run's offsets
 __global__ __launch_bounds__(1024) void prefill_scan_kernel(const int* __restrict__ cnt, int* __restrict__ off,
                                                             int64_t n) {
-  __shared__ int part[1024];
-  const int tid = threadIdx.x;
+  __shared__ int wsum[1024 / kWave];
+  cnt += (int64_t)blockIdx.x * n;
+  off += (int64_t)blockIdx.x * (n + 1);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int64_t per = (n + 1023) / 1024;
-  const int64_t lo = tid * per, hi = min(n, lo + per);
+  const int64_t lo = min(n, tid * per), hi = min(n, lo + per);
   int s = 0;
   for (int64_t i = lo; i < hi; ++i) s += cnt[i];
-  part[tid] = s;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int v = tid >= d ? part[tid - d] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  int x = s;  // inclusive scan over the wave
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
   }
-  int run = tid > 0 ? part[tid - 1] : 0;
+  if (lane == kWave - 1) wsum[w] = x;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += wsum[i];
+  int run = base + x - s;
   for (int64_t i = lo; i < hi; ++i) {
     off[i] = run;
     run += cnt[i];
   }
-  if (tid == 1023) off[n] = part[1023];
+  if (tid == 1023) off[n] = base + x;
 }
 
-// For the remote pairs of the slab's rows [r0, r0 + rn) of every (b, h):
-// pairs[pos] = the pair's query row (b * Hq + h) * T_len + t, and pair_pos
-// becomes the position in the slab's pair list
-__global__ void prefill_scatter_kernel(const int32_t* __restrict__ sel_idx, const int* __restrict__ off,
-                                       int32_t* __restrict__ pair_pos, int32_t* __restrict__ pairs, int Hq, int G,
-                                       int64_t T_len, int64_t Nc, int k, int64_t r0, int64_t rn, int64_t total) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  const int64_t rl = i / k;
-  const int e = (int)(i % k);
-  const int64_t bh = rl / rn, t = r0 + rl % rn;
-  const int64_t row = bh * T_len + t;
-  const int64_t gi = row * k + e;
-  const int32_t inb = pair_pos[gi];
-  if (inb < 0) return;
+// For the remote pairs of the rows [r0, r0 + rn) of every (b, h), one
+// thread per row: the row's slab is sl = (t - r0) / slab_rows, whose
+// bucket offsets are off[sl * (nb + 1) ..]; pairs[sl * slab_cap + pos] =
+// the pair's query row (b * Hq + h) * T_len + t, and pair_pos becomes pos,
+// the position in the slab's pair list.  K4 > 0: k = 4 * K4, the row's
+// slots as 16-byte loads.
+template <int K4>
+__global__ __launch_bounds__(256) void prefill_scatter_kernel(const int32_t* __restrict__ sel_idx,
+                                                              const int* __restrict__ off,
+                                                              int32_t* __restrict__ pair_pos,
+                                                              int32_t* __restrict__ pairs, int Hq, int G,
+                                                              int64_t T_len, int64_t Nc, int k, int64_t r0,
+                                                              int64_t rn, int64_t slab_rows, int64_t slab_cap,
+                                                              int64_t nb, int64_t nrows) {
+  const int64_t rl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (rl >= nrows) return;
+  const int64_t bh = rl / rn, tr = rl % rn;
+  const int64_t row = bh * T_len + r0 + tr;
   const int h = (int)(bh % Hq);
   const int b = (int)(bh / Hq);
-  const int64_t bucket = ((int64_t)b * (Hq / G) + h / G) * Nc + sel_idx[gi];
-  const int32_t pos = off[bucket] + inb;
-  pairs[pos] = (int32_t)row;
-  pair_pos[gi] = pos;
+  const int64_t sl = tr / slab_rows;
+  const int* o = off + sl * (nb + 1) + ((int64_t)b * (Hq / G) + h / G) * Nc;
+  int32_t* pp = pair_pos + row * k;
+  const int32_t* si = sel_idx + row * k;
+  int32_t* pr = pairs + sl * slab_cap;
+  if constexpr (K4 > 0) {
+    u32x4 p4[K4], c4[K4];
+#pragma unroll
+    for (int e4 = 0; e4 < K4; ++e4) {
+      p4[e4] = *reinterpret_cast<const u32x4*>(pp + 4 * e4);
+      c4[e4] = *reinterpret_cast<const u32x4*>(si + 4 * e4);
+    }
+#pragma unroll
+    for (int e4 = 0; e4 < K4; ++e4) {
+      bool any = false;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int inb = (int)p4[e4][u];
+        if (inb >= 0) {
+          const int pos = o[(int)c4[e4][u]] + inb;
+          pr[pos] = (int32_t)row;
+          p4[e4][u] = (uint32_t)pos;
+          any = true;
+        }
+      }
+      if (any) *reinterpret_cast<u32x4*>(pp + 4 * e4) = p4[e4];
+    }
+  } else {
+    for (int e = 0; e < k; ++e) {
+      const int inb = pp[e];
+      if (inb < 0) continue;
+      const int pos = o[si[e]] + inb;
+      pr[pos] = (int32_t)row;
+      pp[e] = pos;
+    }
+  }
 }
-
 
 hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t st) {
   hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
@@ -110,17 +150,26 @@ hipError_t launch_prefill_zero_counts(const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_bucketing(const PrefillArgs& a, const int* cnt, int64_t r0, int64_t rn, hipStream_t st) {
+hipError_t launch_prefill_bucketing(const PrefillArgs& a, int nslab, int64_t r0, int64_t rn, hipStream_t st) {
   const Geometry& g = a.g;
-  const int64_t total = (int64_t)g.B * g.Hq * rn * g.k;
+  const int64_t nrows = (int64_t)g.B * g.Hq * rn;
   const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;
-  const unsigned pb = (unsigned)((total + 255) / 256);
+  const int64_t cap = (int64_t)g.B * g.Hq * a.slab_rows * g.k;  // one slab's pair list
+  const unsigned pb = (unsigned)((nrows + 255) / 256);
   mark_launch(st);
-  hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, cnt, a.off, nb);
+  hipLaunchKernelGGL(prefill_scan_kernel, dim3((unsigned)nslab), dim3(1024), 0, st, a.cnt, a.off, nb);
   mark_launch(st);
   mark_launch(st);
-  hipLaunchKernelGGL(prefill_scatter_kernel, dim3(pb), dim3(256), 0, st, a.sel_idx, a.off, a.pair_pos, a.pairs, g.Hq,
-                     g.G, g.Tq, g.Nc, g.k, r0, rn, total);
+#define HSA_SCATTER(K4)                                                                                              \
+  hipLaunchKernelGGL(prefill_scatter_kernel<K4>, dim3(pb), dim3(256), 0, st, a.sel_idx, a.off, a.pair_pos, a.pairs, \
+                     g.Hq, g.G, g.Tq, g.Nc, g.k, r0, rn, a.slab_rows, cap, nb, nrows)
+  switch (g.k) {
+    case 16: HSA_SCATTER(4); break;
+    case 32: HSA_SCATTER(8); break;
+    case 64: HSA_SCATTER(16); break;
+    default: HSA_SCATTER(0); break;
+  }
+#undef HSA_SCATTER
   mark_launch(st);
   return hipGetLastError();
 }
@@ -133,10 +182,12 @@ void prefill_workspace_parts(const Geometry& g, bool own_sel, size_t* fixed, siz
   const size_t nb = (size_t)g.B * g.Hkv * (size_t)g.Nc;
   size_t f = 0;
   if (own_sel) f += align_up_p(pairs * sizeof(int32_t), 256) + align_up_p(pairs * sizeof(float), 256);
-  f += align_up_p(pairs * sizeof(int32_t), 256) + align_up_p(nb * sizeof(int), 256) +
+  // (an estimate for planning: the counts, offsets and pair lists of a
+  // group of slabs are taken as those of one slab and of every row)
+  f += 2 * align_up_p(pairs * sizeof(int32_t), 256) + align_up_p(nb * sizeof(int), 256) +
        align_up_p((nb + 1) * sizeof(int), 256) + align_up_p(nb * kChunk * g.D * (g.bf16 ? 2 : 4), 256);
   *fixed = f;
-  *per_row = (size_t)g.B * g.Hq * g.k * (sizeof(int32_t) + g.D * sizeof(float));
+  *per_row = (size_t)g.B * g.Hq * g.k * g.D * sizeof(float);
 }
 
 PrefillPlan plan_prefill_slab(const Geometry& g, bool own_sel, int64_t slab_rows) {
@@ -168,11 +219,11 @@ PrefillPlan plan_prefill_slab(const Geometry& g, bool own_sel, int64_t slab_rows
   p.off_cnt = off;
   off = align_up_p(off + nb * p.slab_group * sizeof(int), 256);
   p.off_off = off;
-  off = align_up_p(off + (nb + 1) * sizeof(int), 256);
+  off = align_up_p(off + (nb + 1) * p.slab_group * sizeof(int), 256);
   p.off_vt = off;
   off = align_up_p(off + nb * kChunk * g.D * (g.bf16 ? 2 : 4), 256);
   p.off_pairs = off;
-  off = align_up_p(off + spairs * sizeof(int32_t), 256);
+  off = align_up_p(off + spairs * p.slab_group * sizeof(int32_t), 256);
   p.off_partial = off;
   off = align_up_p(off + spairs * g.D * sizeof(float), 256);
   p.bytes = off;

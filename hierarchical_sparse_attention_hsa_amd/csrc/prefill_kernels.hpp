@@ -873,12 +873,13 @@ __device__ __forceinline__ void attend_block(const Frag<T> (&qf)[D / 16], const 
 __device__ __forceinline__ int out_col(int dm, int q4, int half) { return 32 * dm + 8 * q4 + 4 * half; }
 
 // Remote-pair bucketing around the select kernel (prefill.hip): the bucket
-// counts are cleared before it (one launch); after it, their exclusive scan
-// gives the bucket offsets off[], and the scatter turns each pair's position
-// within its bucket into its position in pairs[] and records its query row
-// there (two launches).
+// counts of a group of slabs are cleared before it (one launch); after it,
+// the exclusive scans of every slab's counts give its bucket offsets (one
+// launch, a workgroup per slab), and the scatter turns each pair's position
+// within its bucket into its position in its slab's pair list and records
+// its query row there (one launch for the group, a thread per row).
 hipError_t launch_prefill_zero_counts(const PrefillArgs& a, hipStream_t st);
-hipError_t launch_prefill_bucketing(const PrefillArgs& a, const int* cnt, int64_t r0, int64_t rn, hipStream_t st);
+hipError_t launch_prefill_bucketing(const PrefillArgs& a, int nslab, int64_t r0, int64_t rn, hipStream_t st);
 
 // ---- chunk-major attention of the remote pairs
 template <typename T, int D, int G>
@@ -1225,10 +1226,11 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   // Launch order per call: the transposed V tiles once; then per group of
-  // up to kPrefillCountSlabs slabs of query chunks: the group's bucket
-  // counts cleared and one selection over its rows (which counts each
-  // slab's remote pairs apart), and per slab [jlo, jlo + ns): scan and
-  // scatter of its remote pairs, chunk-major attention, local attention and
+  // up to kPrefillCountSlabs slabs of query chunks [jg, jg + ng): the
+  // group's bucket counts cleared, one selection over its rows (which
+  // counts each slab's remote pairs apart), one scan of every slab's counts
+  // and one scatter of the group's remote pairs into each slab's list; then
+  // per slab [jlo, jlo + ns): chunk-major attention, local attention and
   // fusion.
   if (nb > 0) {
     mark_launch(st);
@@ -1237,6 +1239,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     mark_launch(st);
   }
   const int sgc = cps * a.slab_group;  // query chunks per selection launch
+  const int64_t cap = (int64_t)g.B * g.Hq * a.slab_rows * g.k;
   for (int jg = 0; jg < nqc; jg += sgc) {
     const int ng = std::min(sgc, nqc - jg);
     if (nb > 0) {
@@ -1249,16 +1252,20 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
                        q, static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, nb > 0 ? a.cnt : nullptr,
                        a.pair_pos, g.B, g.Hkv, g.Tq, g.Nc, ng, jg, cps, j0, g.k, scale, a.k_base, a.gap_tau);
     mark_launch(st);
+    if (nb > 0) {
+      const int64_t r0 = (int64_t)jg * kChunk, rn = std::min<int64_t>((int64_t)ng * kChunk, g.Tq - r0);
+      hipError_t e = launch_prefill_bucketing(a, (ng + cps - 1) / cps, r0, rn, st);
+      if (e != hipSuccess) return e;
+    }
     for (int jlo = jg; jlo < jg + ng; jlo += cps) {
       const int ns = std::min(cps, jg + ng - jlo);
-      const int64_t r0 = (int64_t)jlo * kChunk, rn = std::min<int64_t>((int64_t)ns * kChunk, g.Tq - r0);
+      const int sl = (jlo - jg) / cps;
       const unsigned blocks = (unsigned)((int64_t)ns * g.B * g.Hkv);
       if (nb > 0) {
-        hipError_t e = launch_prefill_bucketing(a, a.cnt + (int64_t)((jlo - jg) / cps) * nb, r0, rn, st);
-        if (e != hipSuccess) return e;
         mark_launch(st);
         hipLaunchKernelGGL((prefill_remote_kernel<T, D, G>), dim3((unsigned)nb), dim3(256), 0, st, q, k,
-                           static_cast<const stg*>(a.vt), a.off, a.pairs, a.partial, g.Hkv, g.T, g.Nc, scale);
+                           static_cast<const stg*>(a.vt), a.off + (int64_t)sl * (nb + 1), a.pairs + sl * cap,
+                           a.partial, g.Hkv, g.T, g.Nc, scale);
         mark_launch(st);
       }
       hipError_t e = hipGetLastError();

@@ -292,9 +292,9 @@ hsa_attn_status_t hsa_append_kv(const hsa_attn_dims_t* d, const void* k_new, con
  * after it, for i < n_pairs; the index restarts at 0 with each call.
  * Launch order: landmarks: 1 kernel; prefill, cached and adaptive prefill (when T >= S): V transpose,
  * then per group of up to 64 slabs of query rows (hsa_attn_prefill_slab_rows)
- * zero and select, then per slab of the group scan, scatter, remote
- * attention, local attention (for T < S: select, then local attention per
- * slab); decode and varlen decode: scan, merge,
+ * zero, select, scan, scatter, then per slab of the group remote attention,
+ * local attention (for T < S: select, then local attention per slab);
+ * decode and varlen decode: scan, merge,
  * attention, fusion, for adaptive decode too (scan and attention are skipped when the cache capacity
  * holds no complete chunk); append: 1 kernel; backward: zero counts, row
  * preparation, scan, scatter, K transpose, chunk gradients, dq (scan,

@@ -168,7 +168,7 @@ def test_prefill_results_do_not_depend_on_slab_size(case):
     m = min_workspace(dims)
     per_chunk = B * Hq * topk * (4 + 4 * D) * 64
     results = []
-    for ws_bytes in (m, m + 2 * per_chunk, hsa.hsa_attn_workspace_size(dims, 0)):
+    for ws_bytes in (m, m + 4 * per_chunk, hsa.hsa_attn_workspace_size(dims, 0)):
         rows = hsa.hsa_attn_prefill_slab_rows(dims, ws_bytes, False, True)
         print(f"workspace {ws_bytes} bytes: slabs of {rows} rows", flush=True)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
@@ -179,7 +179,7 @@ def test_prefill_results_do_not_depend_on_slab_size(case):
         torch.cuda.synchronize()
         results.append((rows, out.cpu(), sel.cpu(), score.cpu()))
         del ws
-    assert results[0][0] == 64 and results[1][0] == 192 and results[2][0] >= 64 * (T // 64)
+    assert results[0][0] == 64 and 64 < results[1][0] < results[2][0] and results[2][0] >= 64 * (T // 64)
     for r in results[1:]:
         for a, b in zip(results[0][1:], r[1:]):
             assert torch.equal(a, b)
