@@ -248,9 +248,9 @@ hsa_attn_status_t hsa_forward_decode_varlen(const hsa_attn_dims_t* d, const void
 
 /*
  * Decode with the near-tie adaptive budget (value-of-information router
- * abstract on the automata-index page: the gap between a query's k-th and
- * (k+1)-th best block scores measures how decisively its top-k cut was made,
- * and the queries with the smallest gaps get twice the budget).  Each query
+ * abstract on the automata-index page: a doubled budget for the queries
+ * whose k-th and (k+1)-th best scores are closest; read as a per-head
+ * threshold on that gap).  Each query
  * head ranks its candidates as hsa_forward_decode does (k = d->top_k) and
  * computes gap = s_k - s_(k+1) from its fp32 scores (1/sqrt(D) included);
  * when it has more than k candidates and gap < gap_threshold it keeps its

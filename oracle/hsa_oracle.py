@@ -314,11 +314,10 @@ def decode(q, Kc, Vc, L, S: int, k: int):
 def adaptive_keep_count(s_sorted: np.ndarray, k: int, tau: float):
     """Kept count of one row under the near-tie adaptive budget, and its gap.
 
-    Value-of-information router abstract (automata-index page): the selector
-    measures how decisively its top-k cut was made -- the gap between the
-    k-th and (k+1)-th best block scores -- and doubles the kept set of the
-    queries whose gap is smallest.  Read here as a per-row threshold tau on
-    that gap (in score units, the 1/sqrt(D) scale included): s_sorted holds a
+    Value-of-information router abstract (automata-index page): a row whose
+    k-th and (k+1)-th best scores lie close together gets a doubled budget.
+    Read here as a per-row threshold tau on that gap (in score units, the
+    1/sqrt(D) scale included): s_sorted holds a
     row's candidate scores in selection order (score descending, index
     ascending), n = len(s_sorted).  With n > k the row keeps min(2k, n)
     chunks when s_sorted[k-1] - s_sorted[k] < tau and k otherwise; with
