@@ -110,8 +110,8 @@ def library_digest():
 
 def profiled_traffic(workload, kernel_prefix):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter
-    record (profiles/<workload>.traffic.json: FETCH_SIZE and WRITE_SIZE scaled
-    by a 1 GiB copy), or None when the kernel sources changed since."""
+    record (profiles/<workload>.traffic.json: 128-byte read requests and
+    WRITE_SIZE), or None when the kernel sources changed since."""
     path = os.path.join(ROOT, "profiles", f"{workload}.traffic.json")
     if not os.path.exists(path):
         return None
@@ -187,14 +187,21 @@ def near_tie_rows(q_rows, Lg, n, k, rel=1e-5):
     return int(tie.sum().item()), int(cut.sum().item())
 
 
-def summarize_profile(workload, prof_dir, command, kernel):
+def summarize_profile(workload, prof_dir, command, kernel, out_dir=None):
     """Turn the rocprofv3 CSVs of one workload (<workload>_kernel_stats.csv,
-    _FETCH_SIZE.csv, _WRITE_SIZE.csv in prof_dir) into profiles/<kernel>.<workload>.md,
-    named for the dominant kernel (kernel times and HBM bytes) and
-    profiles/<workload>.traffic.json (bytes
-    per launch, read by the benchmark).  Counter values are KiB per dispatch;
-    they are scaled so that the calibration copy (1 GiB read, 1 GiB written)
-    reads as exactly that."""
+    _RDREQ.csv, _WRITE_SIZE.csv and _MFMA.csv in prof_dir) into
+    profiles/<kernel>.<workload>.md, named for the dominant kernel (kernel
+    times, HBM bytes, MFMA counters), and profiles/<workload>.traffic.json
+    (bytes per launch, read by the benchmark).
+
+    Bytes follow from the counters' definitions.  Reads: the L2 of gfx950
+    sends 128-byte read requests to memory (TCC_EA0_RDREQ) and 32-byte ones
+    (TCC_EA0_RDREQ_32B, counted among the former), so read bytes =
+    128 (RDREQ - RDREQ_32B) + 32 RDREQ_32B.  (FETCH_SIZE prices every request
+    that TCC_BUBBLE does not flag at 64 bytes, and TCC_BUBBLE flags only a few
+    of the 128-byte requests on this chip, so FETCH_SIZE reads about half.)
+    Writes: WRITE_SIZE (KiB).  A device copy of exactly 1 GiB run in the same
+    process is the check: it must read and write 1 GiB."""
     import csv
     from collections import defaultdict
 
@@ -203,28 +210,37 @@ def summarize_profile(workload, prof_dir, command, kernel):
 
     stats = [r for r in csv.DictReader(open(os.path.join(prof_dir, f"{workload}_kernel_stats.csv")))
              if "hsa_attn" in r["Name"]]
-    counters = {}
-    for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        per = defaultdict(list)
+    per = {"RDREQ": defaultdict(lambda: defaultdict(float)), "WRITE_SIZE": defaultdict(lambda: defaultdict(float))}
+    for c in per:
         for r in csv.DictReader(open(os.path.join(prof_dir, f"{workload}_{c}.csv"))):
-            per[(int(r["Dispatch_Id"]), r["Kernel_Name"])].append(float(r["Counter_Value"]))
-        counters[c] = {k: sum(v) for k, v in per.items()}
-    gib_kib = float(1 << 20)
-    # the copy: of the non-library dispatches that write 1 GiB (the fill of
-    # its source does too), the one that also reads
-    cands = [k for k, w in counters["WRITE_SIZE"].items()
-             if "hsa_attn" not in k[1] and abs(w - gib_kib) < 0.05 * gib_kib and k in counters["FETCH_SIZE"]]
-    copy_w = max(cands, key=lambda k: counters["FETCH_SIZE"][k])
-    read_scale = gib_kib / counters["FETCH_SIZE"][copy_w]
-    write_scale = gib_kib / counters["WRITE_SIZE"][copy_w]
-    rows = defaultdict(list)
-    for k, f in counters["FETCH_SIZE"].items():
-        if "hsa_attn" in k[1] and k in counters["WRITE_SIZE"]:
-            rows[short(k[1])].append((f, counters["WRITE_SIZE"][k]))
-    traffic = {n: 1024.0 * float(np.mean([f * read_scale + w * write_scale for f, w in v])) for n, v in rows.items()}
-    rec = {"workload": workload, "library_sha256_16": library_digest(), "read_scale": read_scale,
-           "write_scale": write_scale, "traffic_bytes_per_launch": traffic}
-    with open(os.path.join(ROOT, "profiles", f"{workload}.traffic.json"), "w") as fh:
+            per[c][(int(r["Dispatch_Id"]), r["Kernel_Name"])][r["Counter_Name"]] += float(r["Counter_Value"])
+    reads = {k: 128.0 * (v["TCC_EA0_RDREQ_sum"] - v["TCC_EA0_RDREQ_32B_sum"]) + 32.0 * v["TCC_EA0_RDREQ_32B_sum"]
+             for k, v in per["RDREQ"].items()}
+    writes = {k: 1024.0 * v["WRITE_SIZE"] for k, v in per["WRITE_SIZE"].items()}
+    gib = float(1 << 30)
+
+    def copy_of(counts):
+        # the calibration copy: the non-library dispatch whose count is nearest 1 GiB
+        cands = [k for k in counts if "hsa_attn" not in k[1] and "copy" in k[1].lower()]
+        return min(cands, key=lambda k: abs(counts[k] - gib)) if cands else None
+
+    cr, cw = copy_of(reads), copy_of(writes)
+    check = {"copy_read_GiB": reads[cr] / gib if cr else None, "copy_written_GiB": writes[cw] / gib if cw else None}
+    rd_per, wr_per = defaultdict(list), defaultdict(list)  # per library kernel, one entry per dispatch
+    for k, rb in reads.items():
+        if "hsa_attn" in k[1]:
+            rd_per[short(k[1])].append(rb)
+    for k, wb in writes.items():
+        if "hsa_attn" in k[1]:
+            wr_per[short(k[1])].append(wb)
+    rd_avg = {n: float(np.mean(v)) for n, v in rd_per.items()}
+    wr_avg = {n: float(np.mean(v)) for n, v in wr_per.items()}
+    traffic = {n: rd_avg.get(n, 0.0) + wr_avg.get(n, 0.0) for n in set(rd_avg) | set(wr_avg)}
+    rec = {"workload": workload, "library_sha256_16": library_digest(),
+           "bytes": "reads 128 x (TCC_EA0_RDREQ - TCC_EA0_RDREQ_32B) + 32 x TCC_EA0_RDREQ_32B; writes 1024 x WRITE_SIZE",
+           "check_copy_1GiB": check, "traffic_bytes_per_launch": traffic}
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    with open(os.path.join(out_dir, f"{workload}.traffic.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
     lines = [f"# {kernel} and the other library kernels: {workload}", "",
              "Commands (repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`; REPO = the root):", ""]
@@ -233,18 +249,20 @@ def summarize_profile(workload, prof_dir, command, kernel):
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                      f"{float(r['TotalDurationNs']):.0f} |")
-    lines += ["", "## HBM bytes per dispatch (--pmc, KiB per dispatch, averaged)", "",
-              f"Calibration: the 1 GiB device copy reads FETCH_SIZE = {counters['FETCH_SIZE'][copy_w]:.0f} KiB and "
-              f"WRITE_SIZE = {counters['WRITE_SIZE'][copy_w]:.0f} KiB, so reads are scaled by {read_scale:.3f} "
-              f"and writes by {write_scale:.3f}.", "",
-              "| kernel | dispatches | FETCH_SIZE | WRITE_SIZE | scaled HBM bytes |", "|---|---|---|---|---|"]
-    for n, v in sorted(rows.items(), key=lambda kv: -traffic[kv[0]]):
-        lines.append(f"| {n} | {len(v)} | {np.mean([f for f, _ in v]):.0f} | {np.mean([w for _, w in v]):.0f} | "
-                     f"{traffic[n] / 2**30:.3f} GiB |")
+    fmt = lambda x: f"{x:.3f}" if x is not None else "-"  # noqa: E731
+    lines += ["", "## HBM bytes per dispatch (--pmc, averaged)", "",
+              "Reads = 128 B x (TCC_EA0_RDREQ_sum - TCC_EA0_RDREQ_32B_sum) + 32 B x TCC_EA0_RDREQ_32B_sum (the L2 "
+              "of gfx950 reads memory in 128-byte requests); writes = WRITE_SIZE. Check: the 1 GiB device copy "
+              f"run in the same process reads {fmt(check['copy_read_GiB'])} GiB and writes "
+              f"{fmt(check['copy_written_GiB'])} GiB by these definitions.", "",
+              "| kernel | dispatches | read GiB | written GiB | HBM bytes |", "|---|---|---|---|---|"]
+    for n in sorted(traffic, key=lambda n: -traffic[n]):
+        lines.append(f"| {n} | {len(rd_per.get(n, []))} | {rd_avg.get(n, 0.0) / gib:.3f} | "
+                     f"{wr_avg.get(n, 0.0) / gib:.3f} | {traffic[n] / gib:.3f} GiB |")
     mfma_csv = os.path.join(prof_dir, f"{workload}_MFMA.csv")
     if os.path.exists(mfma_csv):
-        lines += mfma_summary(workload, mfma_csv, stats, short)
-    with open(os.path.join(ROOT, "profiles", f"{kernel}.{workload}.md"), "w") as fh:
+        lines += mfma_summary(workload, mfma_csv, stats, short, out_dir)
+    with open(os.path.join(out_dir, f"{kernel}.{workload}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -252,7 +270,7 @@ def summarize_profile(workload, prof_dir, command, kernel):
 SIMD_NUM = 1024  # MI355X: 256 CUs x 4 SIMDs
 
 
-def mfma_summary(workload, csv_path, stats, short):
+def mfma_summary(workload, csv_path, stats, short, out_dir):
     """MFMA counters of one --pmc pass (SQ_VALU_MFMA_BUSY_CYCLES,
     SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE and rocprofv3's derived
     MfmaUtil = sum of the busy cycles / (max GRBM_GUI_ACTIVE x SIMD_NUM)) per
@@ -282,7 +300,7 @@ def mfma_summary(workload, csv_path, stats, short):
                      "busy_cycles": float(np.mean([c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for c in rows])),
                      "grbm_gui_active": float(np.mean([c.get("GRBM_GUI_ACTIVE", 0.0) for c in rows]))}
     rec = {"workload": workload, "library_sha256_16": library_digest(), "simd_num": SIMD_NUM, "kernels": out}
-    with open(os.path.join(ROOT, "profiles", f"{workload}.mfma.json"), "w") as fh:
+    with open(os.path.join(out_dir, f"{workload}.mfma.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
     lines = ["", "## MFMA counters (--pmc, one dispatch per kernel)", "",
              "MfmaUtil (rocprofv3's derived counter) = sum of SQ_VALU_MFMA_BUSY_CYCLES / (max GRBM_GUI_ACTIVE x "

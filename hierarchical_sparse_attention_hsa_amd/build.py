@@ -4,7 +4,9 @@
 
 Compiles every csrc/*.hip with hipcc for gfx950 and links one shared
 library; the benchmark's read-bandwidth probe (measure/stream_read.hip) is
-built into a library of its own, libhsa_attn_stream.so.  No fast-math and no denormal flushing; packed fp32 VALU ops are
+built into a library of its own, libhsa_attn_stream.so, and the MFMA/VALU
+overlap probe (measure/mfma_valu_overlap.hip) into an executable next to
+its source.  No fast-math and no denormal flushing; packed fp32 VALU ops are
 disabled for device code.
 """
 from __future__ import annotations
@@ -22,6 +24,9 @@ LIB = os.path.join(HERE, "libhsa_attn.so")
 # the benchmark's read-bandwidth probe, a library of its own (measure/)
 STREAM_SRC = os.path.join(HERE, "measure", "stream_read.hip")
 STREAM_LIB = os.path.join(HERE, "libhsa_attn_stream.so")
+# a standalone probe of MFMA / VALU overlap (measure/; an executable)
+OVERLAP_SRC = os.path.join(HERE, "measure", "mfma_valu_overlap.hip")
+OVERLAP_EXE = os.path.join(HERE, "measure", "mfma_valu_overlap")
 ARCH = "gfx950"
 
 CXXFLAGS = [
@@ -100,8 +105,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, STREAM_LIB)
+    tmp = OVERLAP_EXE + ".tmp"
+    cmd = [hipcc(), *CXXFLAGS, "-o", tmp, OVERLAP_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, OVERLAP_EXE)
     if verbose:
-        print(f"built {LIB} and {STREAM_LIB}")
+        print(f"built {LIB}, {STREAM_LIB} and {OVERLAP_EXE}")
     return LIB
 
 

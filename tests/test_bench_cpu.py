@@ -30,3 +30,30 @@ def test_stream_probe_library_exports_and_validates():
     assert f(None, 1 << 20, 64, 4, None, None) != 0
     assert f(16, 1 << 20, 64, 3, 16, None) != 0   # unroll must be 4 or 8
     assert f(16, 17, 64, 4, 16, None) != 0        # not a whole number of 16-byte words
+
+
+def test_profile_bytes_follow_the_request_counters(tmp_path):
+    # read bytes = 128 per read request, 32 per 32-byte one (counted among
+    # them); write bytes = WRITE_SIZE KiB; the 1 GiB copy is the check
+    import csv
+    import json
+
+    def write(name, header, rows):
+        with open(tmp_path / name, "w", newline="") as fh:
+            w = csv.writer(fh)
+            w.writerow(header)
+            w.writerows(rows)
+
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    copy = "__amd_rocclr_copyBuffer"
+    kern = "void hsa_attn::decode_scan_kernel<hsa_attn::BF16, 128, 4>(int)"
+    gib = 1 << 30
+    write("w_kernel_stats.csv", ["Name", "Calls", "AverageNs", "TotalDurationNs"], [[kern, 1, 1000.0, 1000.0]])
+    write("w_RDREQ.csv", hdr, [[1, copy, "TCC_EA0_RDREQ_sum", gib // 128], [1, copy, "TCC_EA0_RDREQ_32B_sum", 0],
+                               [2, kern, "TCC_EA0_RDREQ_sum", 1000], [2, kern, "TCC_EA0_RDREQ_32B_sum", 100]])
+    write("w_WRITE_SIZE.csv", hdr, [[1, copy, "WRITE_SIZE", gib // 1024], [2, kern, "WRITE_SIZE", 3]])
+    bench.summarize_profile("w", str(tmp_path), ["cmd"], "decode_scan_kernel", out_dir=str(tmp_path))
+    rec = json.load(open(tmp_path / "w.traffic.json"))
+    assert rec["check_copy_1GiB"] == {"copy_read_GiB": 1.0, "copy_written_GiB": 1.0}
+    (name, b), = rec["traffic_bytes_per_launch"].items()
+    assert "decode_scan_kernel" in name and b == 900 * 128 + 100 * 32 + 3 * 1024
