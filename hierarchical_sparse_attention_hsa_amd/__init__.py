@@ -19,6 +19,7 @@ Functions carry the C names:
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -28,7 +29,7 @@ __all__ = [
     "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive", "hsa_append_kv",
     "hsa_backward_prefill", "hsa_attn_set_timing_events", "hsa_attn_workspace_size",
     "hsa_attn_status_string", "hsa_attn_last_error", "landmarks_shape", "hsa_forward_decode_noalloc",
-    "hsa_attn_prefill_slab_rows",
+    "hsa_attn_prefill_slab_rows", "hsa_attn_debug_flags", "debug_library",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive",
     "hsa_append_kv", "hsa_backward_prefill", "hsa_attn_set_timing_events", "hsa_attn_workspace_size",
     "hsa_attn_status_string",
-    "hsa_attn_last_error", "hsa_forward_decode_noalloc", "hsa_attn_prefill_slab_rows",
+    "hsa_attn_last_error", "hsa_forward_decode_noalloc", "hsa_attn_prefill_slab_rows", "hsa_attn_debug_flags",
 )
 
 HSA_ATTN_OK = 0
@@ -66,16 +67,40 @@ class HSAError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libhsa_attn.so")
+    return os.path.join(_HERE, "libhsa_attn_debug.so" if _ACTIVE == "debug" else "libhsa_attn.so")
 
 
-_LIB = None
+_LIB = None          # the library the calls go to
+_LOADED = {}         # "release" / "debug" -> loaded library
+_ACTIVE = "release"
+
+
+@contextlib.contextmanager
+def debug_library():
+    """Within the block, every call goes to libhsa_attn_debug.so: the same
+    kernels built with HSA_ATTN_DEBUG=1, which poison each call's workspace
+    and outputs before its kernels and check the indices the kernels read
+    back from the workspace (hsa_attn_debug_flags reads the result).  Its
+    workspaces are 256 bytes larger (hsa_attn_workspace_size inside the
+    block gives the size)."""
+    global _LIB, _ACTIVE
+    prev_lib, prev_active = _LIB, _ACTIVE
+    _ACTIVE, _LIB = "debug", _LOADED.get("debug")
+    try:
+        load_library()
+        yield
+    finally:
+        _LIB, _ACTIVE = prev_lib, prev_active
 
 
 def load_library():
-    """Load libhsa_attn.so (built in-tree); raises if it has not been built."""
+    """Load libhsa_attn.so (built in-tree; libhsa_attn_debug.so inside
+    debug_library()); raises if it has not been built."""
     global _LIB
     if _LIB is not None:
+        return _LIB
+    if _ACTIVE in _LOADED:
+        _LIB = _LOADED[_ACTIVE]
         return _LIB
     path = library_path()
     if not os.path.exists(path):
@@ -101,14 +126,27 @@ def load_library():
     lib.hsa_attn_status_string.restype = ctypes.c_char_p
     lib.hsa_attn_last_error.argtypes = []
     lib.hsa_attn_last_error.restype = ctypes.c_char_p
+    lib.hsa_attn_debug_flags.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
     for f in ("hsa_build_landmarks", "hsa_forward_prefill", "hsa_forward_prefill_cached", "hsa_forward_decode",
               "hsa_forward_decode_noalloc",
               "hsa_forward_decode_varlen", "hsa_forward_decode_adaptive", "hsa_forward_prefill_adaptive",
               "hsa_append_kv", "hsa_backward_prefill", "hsa_attn_workspace_size", "hsa_attn_set_timing_events",
-              "hsa_attn_prefill_slab_rows"):
+              "hsa_attn_prefill_slab_rows", "hsa_attn_debug_flags"):
         getattr(lib, f).restype = ctypes.c_int
+    _LOADED[_ACTIVE] = lib
     _LIB = lib
     return lib
+
+
+def hsa_attn_debug_flags(workspace=None) -> int:
+    """Flag word of the last debug-library call that used `workspace` (a
+    device tensor; None: the no-allocation decode's scratch): 0 when every
+    check passed, else HSA_ATTN_DEBUG_* bits (include/hsa_attn.h).  Waits
+    for the device.  The release library raises HSAError (unsupported)."""
+    flags = ctypes.c_uint32(0)
+    ptr = None if workspace is None else workspace.data_ptr()
+    _check(load_library().hsa_attn_debug_flags(ptr, ctypes.byref(flags)), "hsa_attn_debug_flags")
+    return int(flags.value)
 
 
 def hsa_attn_status_string(status: int) -> str:

@@ -3,7 +3,8 @@
     python -m hierarchical_sparse_attention_hsa_amd.build
 
 Compiles every csrc/*.hip with hipcc for gfx950 and links one shared
-library; the benchmark's read-bandwidth probe (measure/stream_read.hip) is
+library, and the same sources with HSA_ATTN_DEBUG=1 into
+libhsa_attn_debug.so (poisoned workspaces and index checks); the benchmark's read-bandwidth probe (measure/stream_read.hip) is
 built into a library of its own, libhsa_attn_stream.so, and the MFMA/VALU
 overlap probe (measure/mfma_valu_overlap.hip) into an executable next to
 its source.  No fast-math and no denormal flushing; packed fp32 VALU ops are
@@ -21,6 +22,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhsa_attn.so")
+# the same sources with HSA_ATTN_DEBUG=1: poisoned workspaces, index checks
+DEBUG_BUILD = os.path.join(HERE, "_build_debug")
+DEBUG_LIB = os.path.join(HERE, "libhsa_attn_debug.so")
 # the benchmark's read-bandwidth probe, a library of its own (measure/)
 STREAM_SRC = os.path.join(HERE, "measure", "stream_read.hip")
 STREAM_LIB = os.path.join(HERE, "libhsa_attn_stream.so")
@@ -75,8 +79,8 @@ def _variant_defines(srcs):
     return defs
 
 
-def _compile(src: str, defines=()) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+def _compile(src: str, defines=(), build_dir=BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
     cmd = [hipcc(), *CXXFLAGS, *defines, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -84,21 +88,33 @@ def _compile(src: str, defines=()) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Builds libhsa_attn.so, and (debug=True) libhsa_attn_debug.so from the
+    same sources with HSA_ATTN_DEBUG=1, plus the measurement probes."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
     defines = _variant_defines(srcs)
     # slowest units first so the pool stays busy
     order = sorted(srcs, key=lambda s: not os.path.basename(s).startswith("prefill_inst_"))
+    tasks = [(s, tuple(defines), BUILD) for s in order]
+    if debug:
+        os.makedirs(DEBUG_BUILD, exist_ok=True)
+        tasks += [(s, tuple(defines) + ("-DHSA_ATTN_DEBUG=1",), DEBUG_BUILD) for s in order]
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, defines), order))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        objs = list(ex.map(lambda t: _compile(*t), tasks))
+    _link(objs[:len(order)], LIB)
+    if debug:
+        _link(objs[len(order):], DEBUG_LIB)
     tmp = STREAM_LIB + ".tmp"
     cmd = [hipcc(), *CXXFLAGS, "-shared", "-o", tmp, STREAM_SRC]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -112,7 +128,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OVERLAP_EXE)
     if verbose:
-        print(f"built {LIB}, {STREAM_LIB} and {OVERLAP_EXE}")
+        print(f"built {LIB}{', ' + DEBUG_LIB if debug else ''}, {STREAM_LIB} and {OVERLAP_EXE}")
     return LIB
 
 

@@ -1,9 +1,11 @@
 // C ABI of libhsa_attn: host-side validation, workspace sizing and dispatch.
 // Every check runs before the first HIP call, so a rejected call enqueues
 // nothing.  No C++ exception crosses the ABI.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <exception>
+#include <initializer_list>
 #include <mutex>
 
 #include "../../include/hsa_attn.h"
@@ -106,6 +108,47 @@ hsa_attn_status_t hip_status(hipError_t e, const char* what) {
   return fail(HSA_ATTN_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
 }
 
+// ---- debug build (HSA_ATTN_DEBUG=1): the first 256 bytes of every workspace
+// hold the call's flag word; before its kernels a call clears the word and
+// fills the rest of the workspace it uses and its outputs with kPoison
+#ifndef HSA_ATTN_DEBUG
+#define HSA_ATTN_DEBUG 0
+#endif
+constexpr size_t kDebugHeader = HSA_ATTN_DEBUG ? 256 : 0;
+constexpr uint32_t kPoison = 0x7FC00001u;  // a quiet NaN as fp32; 2143289345 as int32
+
+__global__ void debug_fill_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+struct Region {
+  void* p;
+  size_t bytes;  // a multiple of 4
+};
+
+// Debug builds: clear the flag word at `workspace` (the start of the
+// caller's workspace) and poison `regions`; the flag word's device address
+// for the kernels.  Release builds: nothing, and no flag word.
+hsa_attn_status_t debug_prepare(void* workspace, std::initializer_list<Region> regions, hipStream_t st,
+                                uint32_t** dbg) {
+  *dbg = nullptr;
+  if constexpr (HSA_ATTN_DEBUG) {
+    hipLaunchKernelGGL(debug_fill_kernel, dim3(1), dim3(64), 0, st, static_cast<uint32_t*>(workspace),
+                       (int64_t)(kDebugHeader / 4), 0u);
+    for (const Region& r : regions) {
+      if (!r.p || r.bytes < 4) continue;
+      const int64_t n = (int64_t)(r.bytes / 4);
+      hipLaunchKernelGGL(debug_fill_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 16384)), dim3(256), 0,
+                         st, static_cast<uint32_t*>(r.p), n, kPoison);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "debug workspace fill");
+    *dbg = static_cast<uint32_t*>(workspace);
+  }
+  return HSA_ATTN_OK;
+}
+
 }  // namespace
 
 void hsa_attn::mark_launch(hipStream_t st) {
@@ -151,12 +194,12 @@ hsa_attn_status_t hsa_attn_workspace_size(const hsa_attn_dims_t* d, int is_decod
     const hsa_attn_status_t st = check_dims(d, call, &g);
     if (st != HSA_ATTN_OK) return st;
     if (is_decode == 4) {
-      *bytes = hsa_attn::plan_backward(g).bytes;
+      *bytes = hsa_attn::plan_backward(g).bytes + kDebugHeader;
       return ok();
     }
     // the size assumes the library keeps the selection itself (sel outputs NULL)
     const bool dec = is_decode == 1 || is_decode == 2;
-    *bytes = dec ? hsa_attn::plan_decode(g, true).bytes : hsa_attn::plan_prefill(g, true).bytes;
+    *bytes = (dec ? hsa_attn::plan_decode(g, true).bytes : hsa_attn::plan_prefill(g, true).bytes) + kDebugHeader;
     return ok();
   } catch (const std::exception& e) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
@@ -172,7 +215,8 @@ hsa_attn_status_t hsa_attn_prefill_slab_rows(const hsa_attn_dims_t* d, int adapt
     hsa_attn::Geometry g;
     const hsa_attn_status_t st = check_dims(d, adaptive ? Call::kPrefillAdaptive : Call::kPrefill, &g);
     if (st != HSA_ATTN_OK) return st;
-    *slab_rows = hsa_attn::plan_prefill_for(g, selection_given == 0, workspace_bytes).slab_rows;
+    const size_t usable = workspace_bytes > kDebugHeader ? workspace_bytes - kDebugHeader : 0;
+    *slab_rows = hsa_attn::plan_prefill_for(g, selection_given == 0, usable).slab_rows;
     return ok();
   } catch (const std::exception& e) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
@@ -227,13 +271,23 @@ static hsa_attn_status_t forward_prefill(const hsa_attn_dims_t* d, int64_t q_off
       if (p && !aligned16(p)) return fail(HSA_ATTN_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
     const bool own = sel_idx == nullptr;
     // the largest slabs of query rows the workspace holds
-    const hsa_attn::PrefillPlan plan = hsa_attn::plan_prefill_for(g, own, workspace_bytes);
+    const size_t usable = workspace_bytes > kDebugHeader ? workspace_bytes - kDebugHeader : 0;
+    const hsa_attn::PrefillPlan plan = hsa_attn::plan_prefill_for(g, own, usable);
     if (plan.slab_rows == 0)
       return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs at least %zu bytes (slabs of 64 query rows), got %zu",
-                  plan.bytes, workspace_bytes);
+                  plan.bytes + kDebugHeader, workspace_bytes);
     if (g.Tq == 0) return ok();
     if (!workspace) return fail(HSA_ATTN_INVALID_ARGUMENT, "workspace is NULL");
-    char* ws = static_cast<char*>(workspace);
+    char* ws = static_cast<char*>(workspace) + kDebugHeader;
+    const size_t rows_q = (size_t)g.B * g.Hq * (size_t)g.Tq;
+    uint32_t* dbg = nullptr;
+    st = debug_prepare(workspace,
+                       {{ws, plan.bytes},
+                        {out, rows_q * g.D * sizeof(float)},
+                        {own ? nullptr : sel_idx, rows_q * g.k * sizeof(int32_t)},
+                        {own ? nullptr : sel_score, rows_q * g.k * sizeof(float)}},
+                       static_cast<hipStream_t>(stream), &dbg);
+    if (st != HSA_ATTN_OK) return st;
     if (own) {
       sel_idx = reinterpret_cast<int32_t*>(ws + plan.off_sel_idx);
       sel_score = reinterpret_cast<float*>(ws + plan.off_sel_score);
@@ -248,6 +302,7 @@ static hsa_attn_status_t forward_prefill(const hsa_attn_dims_t* d, int64_t q_off
       a.k_base = d->top_k;
       a.gap_tau = gap_tau;
     }
+    a.dbg = dbg;
     return hip_status(hsa_attn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
   } catch (const std::exception& e) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
@@ -297,13 +352,22 @@ hsa_attn_status_t hsa_backward_prefill(const hsa_attn_dims_t* d, const void* q, 
                           (const void*)workspace})
       if (p && !aligned16(p)) return fail(HSA_ATTN_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
     const hsa_attn::BackwardPlan plan = hsa_attn::plan_backward(g);
-    if (workspace_bytes < plan.bytes)
-      return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes, workspace_bytes);
+    if (workspace_bytes < plan.bytes + kDebugHeader)
+      return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes + kDebugHeader,
+                  workspace_bytes);
     if (g.T == 0) return ok();
     if (!workspace) return fail(HSA_ATTN_INVALID_ARGUMENT, "workspace is NULL");
+    char* ws = static_cast<char*>(workspace) + kDebugHeader;
+    const size_t qe = (size_t)g.B * g.Hq * (size_t)g.T * g.D, ke = (size_t)g.B * g.Hkv * (size_t)g.T * g.D;
+    uint32_t* dbg = nullptr;
+    st = debug_prepare(workspace,
+                       {{ws, plan.bytes}, {dq, qe * sizeof(float)}, {dk, ke * sizeof(float)}, {dv, ke * sizeof(float)}},
+                       static_cast<hipStream_t>(stream), &dbg);
+    if (st != HSA_ATTN_OK) return st;
     restart_timing();
     hsa_attn::BackwardArgs a{g,  q,  k,  v,  landmarks, out, dout, sel_idx, sel_score,
-                             dq, dk, dv, workspace};
+                             dq, dk, dv, ws};
+    a.dbg = dbg;
     return hip_status(hsa_attn::launch_backward(a, plan, static_cast<hipStream_t>(stream)), "backward launch");
   } catch (const std::exception& e) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
@@ -332,19 +396,31 @@ static hsa_attn_status_t forward_decode(const hsa_attn_dims_t* d, const void* q,
       return fail(HSA_ATTN_INVALID_ARGUMENT, "cache_lens must be 8-byte aligned");
     const bool own = sel_idx == nullptr;
     const hsa_attn::DecodePlan plan = hsa_attn::plan_decode(g, own);
-    if (workspace_bytes < plan.bytes)
-      return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes, workspace_bytes);
+    if (workspace_bytes < plan.bytes + kDebugHeader)
+      return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes + kDebugHeader,
+                  workspace_bytes);
     if (!workspace) return fail(HSA_ATTN_INVALID_ARGUMENT, "workspace is NULL");
+    char* ws = static_cast<char*>(workspace) + kDebugHeader;
+    const size_t rows_q = (size_t)g.B * g.Hq;
+    uint32_t* dbg = nullptr;
+    st = debug_prepare(workspace,
+                       {{ws, plan.bytes},
+                        {out, rows_q * g.D * sizeof(float)},
+                        {own ? nullptr : sel_idx, rows_q * g.k * sizeof(int32_t)},
+                        {own ? nullptr : sel_score, rows_q * g.k * sizeof(float)}},
+                       static_cast<hipStream_t>(stream), &dbg);
+    if (st != HSA_ATTN_OK) return st;
     if (own) {
-      sel_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.off_sel_idx);
-      sel_score = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.off_sel_score);
+      sel_idx = reinterpret_cast<int32_t*>(ws + plan.off_sel_idx);
+      sel_score = reinterpret_cast<float*>(ws + plan.off_sel_score);
     }
     restart_timing();
-    hsa_attn::DecodeArgs a{g, q, k_cache, v_cache, landmarks, out, sel_idx, sel_score, workspace, lens};
+    hsa_attn::DecodeArgs a{g, q, k_cache, v_cache, landmarks, out, sel_idx, sel_score, ws, lens};
     if (adaptive) {
       a.k_base = d->top_k;
       a.gap_tau = gap_tau;
     }
+    a.dbg = dbg;
     return hip_status(hsa_attn::launch_decode(a, plan, static_cast<hipStream_t>(stream)), "decode launch");
   } catch (const std::exception& e) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
@@ -405,7 +481,7 @@ hsa_attn_status_t hsa_forward_decode_noalloc(const hsa_attn_dims_t* d, const voi
     hsa_attn::Geometry g;
     hsa_attn_status_t st = check_dims(d, Call::kDecode, &g);
     if (st != HSA_ATTN_OK) return st;
-    const size_t need = hsa_attn::plan_decode(g, sel_idx == nullptr).bytes;
+    const size_t need = hsa_attn::plan_decode(g, sel_idx == nullptr).bytes + kDebugHeader;
     if (need > kScratchBytes)
       return fail(HSA_ATTN_WORKSPACE_TOO_SMALL,
                   "decode needs %zu bytes of scratch; the no-allocation entry point holds %zu (use "
@@ -416,6 +492,31 @@ hsa_attn_status_t hsa_forward_decode_noalloc(const hsa_attn_dims_t* d, const voi
     if (st != HSA_ATTN_OK) return st;
     return forward_decode(d, q, k_cache, v_cache, landmarks, nullptr, out, sel_idx, sel_score, ws, kScratchBytes,
                           stream);
+  } catch (const std::exception& e) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(HSA_ATTN_HIP_ERROR, "internal error");
+  }
+}
+
+hsa_attn_status_t hsa_attn_debug_flags(const void* workspace, uint32_t* flags) {
+  try {
+    if constexpr (!HSA_ATTN_DEBUG) {
+      (void)workspace;
+      (void)flags;
+      return fail(HSA_ATTN_UNSUPPORTED, "this library is built without HSA_ATTN_DEBUG (libhsa_attn_debug.so has it)");
+    } else {
+      if (!flags) return fail(HSA_ATTN_INVALID_ARGUMENT, "flags is NULL");
+      void* p = const_cast<void*>(workspace);
+      if (!p) {
+        const hsa_attn_status_t st = scratch_address(&p);
+        if (st != HSA_ATTN_OK) return st;
+      }
+      hipError_t e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_status(e, "hipDeviceSynchronize");
+      e = hipMemcpy(flags, p, sizeof(uint32_t), hipMemcpyDeviceToHost);
+      return hip_status(e, "flag word copy");
+    }
   } catch (const std::exception& e) {
     return fail(HSA_ATTN_HIP_ERROR, "internal error: %s", e.what());
   } catch (...) {

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
 // pairs[off[bucket] + pair_pos[i]] = i (the pair id: row * k + slot)
 __global__ void bwd_scatter_kernel(const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ pair_pos,
                                    const int* __restrict__ off, int32_t* __restrict__ pairs, int64_t total, int Hq,
-                                   int G, int64_t T_len, int64_t Nc, int k) {
+                                   int G, int64_t T_len, int64_t Nc, int k, uint32_t* __restrict__ dbg) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const int32_t pp = pair_pos[i];
@@ -153,8 +153,12 @@ __global__ void bwd_scatter_kernel(const int32_t* __restrict__ sel_idx, const in
   const int64_t bh = row / T_len;
   const int h = (int)(bh % Hq);
   const int64_t b = bh / Hq;
-  const int64_t bucket = (b * (Hq / G) + h / G) * Nc + sel_idx[i];
-  pairs[off[bucket] + pp] = (int32_t)i;
+  const int32_t c = sel_idx[i];
+  if (!dbg_ok(dbg, c >= 0 && c < Nc, HSA_ATTN_DEBUG_BWD_SCATTER)) return;
+  const int64_t bucket = (b * (Hq / G) + h / G) * Nc + c;
+  const int64_t dst = (int64_t)off[bucket] + pp;
+  if (!dbg_ok(dbg, dst >= 0 && dst < total, HSA_ATTN_DEBUG_BWD_SCATTER)) return;
+  pairs[dst] = (int32_t)i;
 }
 
 // ---------------------------------------------------------------- 2. chunks
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     const uint16_t* __restrict__ kt_g, const uint16_t* __restrict__ lm, const float* __restrict__ dout,
     const float* __restrict__ wts, const float* __restrict__ delta, const int* __restrict__ off,
     const int32_t* __restrict__ pairs, float* __restrict__ dqp, float* __restrict__ dk, float* __restrict__ dv, int k,
-    int64_t T_len, int64_t Nc, float scale) {
+    int64_t T_len, int64_t Nc, float scale, int64_t total, uint32_t* __restrict__ dbg) {
   constexpr int KCH = D / 16;            // 16-dim contraction steps
   constexpr int DM = D / 32;             // 32-dim output blocks
   constexpr int ROWB = D * 2;            // bytes of one K or V row
@@ -209,7 +213,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
   const int64_t bucket = blockIdx.x;
   const int64_t c = bucket % Nc, bg = bucket / Nc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-  const int begin = off[bucket], end = off[bucket + 1];
+  int begin = off[bucket], end = off[bucket + 1];
+  if (!dbg_ok(dbg, begin >= 0 && begin <= end && end <= total, HSA_ATTN_DEBUG_BWD_PAIR)) begin = end = 0;
   {
     const char* kb = reinterpret_cast<const char*>(kk + (bg * T_len + c * kChunk) * D);
     const char* vb = reinterpret_cast<const char*>(vv + (bg * T_len + c * kChunk) * D);
@@ -271,7 +276,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     pid_raw = pairs[pid_ok ? p : 0];
   };
   auto fetch_rows = [&]() {
-    ok = pid_ok;
+    ok = pid_ok && dbg_ok(dbg, pid_raw >= 0 && pid_raw < total, HSA_ATTN_DEBUG_BWD_PAIR);
     pid = ok ? pid_raw : 0;
     const int64_t row = pid / k;
     wraw = wts[pid];
@@ -587,7 +592,7 @@ static hipError_t launch_backward_d(const BackwardArgs& a, const BackwardPlan& p
     mark_launch(st);
     mark_launch(st);
     hipLaunchKernelGGL(bwd_scatter_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a.sel_idx,
-                       pair_pos, offs, pairs, total, g.Hq, g.G, g.T, g.Nc, g.k);
+                       pair_pos, offs, pairs, total, g.Hq, g.G, g.T, g.Nc, g.k, a.dbg);
     mark_launch(st);
     mark_launch(st);
     hipLaunchKernelGGL((prefill_vt_kernel<BF16, D>), dim3((unsigned)nb), dim3(256), 0, st, kk, kt, g.T, g.Nc);
@@ -600,7 +605,7 @@ static hipError_t launch_backward_d(const BackwardArgs& a, const BackwardPlan& p
     mark_launch(st);
     hipLaunchKernelGGL(bwd_chunk_kernel<D>, dim3((unsigned)nb), dim3(256), lds, st, q, kk, vv, kt,
                        static_cast<const uint16_t*>(a.lm), a.dout, wts, delta, offs, pairs, dqp, a.dk, a.dv, g.k, g.T,
-                       g.Nc, scale);
+                       g.Nc, scale, total, a.dbg);
     mark_launch(st);
   }
   mark_launch(st);

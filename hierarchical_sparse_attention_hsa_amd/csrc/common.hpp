@@ -4,9 +4,34 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "hsa_attn.h"  // HSA_ATTN_DEBUG_* flag bits
+
 namespace hsa_attn {
 
 constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- debug build
+// Compiled with HSA_ATTN_DEBUG=1 (libhsa_attn_debug.so), a kernel checks each
+// index it reads back from the workspace before using it: a failed check
+// sets its HSA_ATTN_DEBUG_* bit in the call's flag word `dbg` and the caller
+// skips the access.  In the release library the check is the constant true.
+#ifndef HSA_ATTN_DEBUG
+#define HSA_ATTN_DEBUG 0
+#endif
+__device__ __forceinline__ bool dbg_ok(uint32_t* dbg, bool cond, uint32_t bit) {
+#if HSA_ATTN_DEBUG
+  if (!cond) {
+    if (dbg) atomicOr(dbg, bit);
+    return false;
+  }
+  return true;
+#else
+  (void)dbg;
+  (void)cond;
+  (void)bit;
+  return true;
+#endif
+}
 
 // ---------------------------------------------------------------- storage types
 // Storage dtypes of Q/K/V/landmarks.  Every kernel reads 16-byte vectors; a

@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void decode_attn_kernel(const t
                                                           const int4* __restrict__ ulist,
                                                           const int* __restrict__ ucount,
                                                           float* __restrict__ partial, int Hkv, int64_t T_len,
-                                                          int k, float scale) {
+                                                          int k, float scale, uint32_t* __restrict__ dbg) {
   using st = typename T::storage;
   constexpr int S = 64;
   constexpr int KCH = D / 16;
@@ -510,10 +510,23 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void decode_attn_kernel(const t
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
   const int e = blockIdx.x * kAttnWaves + wave;
   const int64_t grp = (int64_t)b * Hkv + g;
-  if (e >= ucount[grp]) return;
+  const int uc = ucount[grp];
+  if (e >= uc) return;
+  if (!dbg_ok(dbg, uc <= G * k, HSA_ATTN_DEBUG_DECODE_ENTRIES)) return;
   const int4 ent = ulist[grp * (G * k) + e];
   const int c = ent.x;
-  const uint32_t slots[2] = {(uint32_t)ent.y, (uint32_t)ent.z};
+  if (!dbg_ok(dbg, c >= 0 && (int64_t)c * S + S <= T_len, HSA_ATTN_DEBUG_DECODE_CHUNK)) return;
+  uint32_t slots[2] = {(uint32_t)ent.y, (uint32_t)ent.z};
+  if constexpr (HSA_ATTN_DEBUG) {
+    // a slot number beyond k (other than 0xff, "not selected") would index
+    // past the head's partial outputs: flagged and treated as not selected
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const uint32_t sl = (slots[hh / 4] >> (8 * (hh % 4))) & 0xffu;
+      if (!dbg_ok(dbg, sl == 0xffu || (int)sl < k, HSA_ATTN_DEBUG_DECODE_SLOT))
+        slots[hh / 4] |= 0xffu << (8 * (hh % 4));
+    }
+  }
   const int half = lane >> 5;
   const st* ktile = kc + (grp * T_len + (int64_t)c * S) * D;
   const st* vtile = vc + (grp * T_len + (int64_t)c * S) * D;
@@ -752,7 +765,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipS
     hipLaunchKernelGGL((decode_attn_kernel<T, D, G>), dim3((G * g.k + kAttnWaves - 1) / kAttnWaves, g.Hkv, g.B),
                        dim3(kAttnWaves * kWave), 0, st,
                        static_cast<const stg*>(a.q), static_cast<const stg*>(a.k), static_cast<const stg*>(a.v),
-                       ulist, ucount, partial, g.Hkv, g.T, g.k, scale);
+                       ulist, ucount, partial, g.Hkv, g.T, g.k, scale, a.dbg);
     mark_launch(st);
   }
   mark_launch(st);

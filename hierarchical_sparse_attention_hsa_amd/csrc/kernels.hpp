@@ -67,6 +67,7 @@ struct DecodeArgs {
   // gap is below gap_tau
   int k_base = 0;
   float gap_tau = 0.0f;
+  uint32_t* dbg = nullptr;  // debug builds: the call's flag word
 };
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t st);
 
@@ -116,6 +117,7 @@ struct PrefillArgs {
   // adaptive budget, as in DecodeArgs: g.k == 2 * k_base when k_base > 0
   int k_base = 0;
   float gap_tau = 0.0f;
+  uint32_t* dbg = nullptr;  // debug builds: the call's flag word
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 
@@ -138,6 +140,7 @@ struct BackwardArgs {
   const float* sel_score;
   float *dq, *dk, *dv;
   void* ws;
+  uint32_t* dbg = nullptr;  // debug builds: the call's flag word
 };
 hipError_t launch_backward(const BackwardArgs& a, const BackwardPlan& p, hipStream_t st);
 

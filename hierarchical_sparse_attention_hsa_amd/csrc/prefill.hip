@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void prefill_scatter_kernel(const int32_t* __r
                                                               int32_t* __restrict__ pairs, int Hq, int G,
                                                               int64_t T_len, int64_t Nc, int k, int64_t r0,
                                                               int64_t rn, int64_t slab_rows, int64_t slab_cap,
-                                                              int64_t nb, int64_t nrows) {
+                                                              int64_t nb, int64_t nrows, uint32_t* __restrict__ dbg) {
   const int64_t rl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (rl >= nrows) return;
   const int64_t bh = rl / rn, tr = rl % rn;
@@ -110,7 +110,10 @@ __global__ __launch_bounds__(256) void prefill_scatter_kernel(const int32_t* __r
       for (int u = 0; u < 4; ++u) {
         const int inb = (int)p4[e4][u];
         if (inb >= 0) {
-          const int pos = o[(int)c4[e4][u]] + inb;
+          const int c = (int)c4[e4][u];
+          if (!dbg_ok(dbg, c >= 0 && c < Nc, HSA_ATTN_DEBUG_SCATTER_CHUNK)) continue;
+          const int pos = o[c] + inb;
+          if (!dbg_ok(dbg, pos >= 0 && pos < slab_cap, HSA_ATTN_DEBUG_SCATTER_POS)) continue;
           pr[pos] = (int32_t)row;
           p4[e4][u] = (uint32_t)pos;
           any = true;
@@ -122,7 +125,10 @@ __global__ __launch_bounds__(256) void prefill_scatter_kernel(const int32_t* __r
     for (int e = 0; e < k; ++e) {
       const int inb = pp[e];
       if (inb < 0) continue;
-      const int pos = o[si[e]] + inb;
+      const int c = si[e];
+      if (!dbg_ok(dbg, c >= 0 && c < Nc, HSA_ATTN_DEBUG_SCATTER_CHUNK)) continue;
+      const int pos = o[c] + inb;
+      if (!dbg_ok(dbg, pos >= 0 && pos < slab_cap, HSA_ATTN_DEBUG_SCATTER_POS)) continue;
       pr[pos] = (int32_t)row;
       pp[e] = pos;
     }
@@ -162,7 +168,7 @@ hipError_t launch_prefill_bucketing(const PrefillArgs& a, int nslab, int64_t r0,
   mark_launch(st);
 #define HSA_SCATTER(K4)                                                                                              \
   hipLaunchKernelGGL(prefill_scatter_kernel<K4>, dim3(pb), dim3(256), 0, st, a.sel_idx, a.off, a.pair_pos, a.pairs, \
-                     g.Hq, g.G, g.Tq, g.Nc, g.k, r0, rn, a.slab_rows, cap, nb, nrows)
+                     g.Hq, g.G, g.Tq, g.Nc, g.k, r0, rn, a.slab_rows, cap, nb, nrows, a.dbg)
   switch (g.k) {
     case 16: HSA_SCATTER(4); break;
     case 32: HSA_SCATTER(8); break;

@@ -889,7 +889,8 @@ __global__ __launch_bounds__(256) void prefill_remote_kernel(const typename T::s
                                                              const int* __restrict__ off,
                                                              const int32_t* __restrict__ pairs,
                                                              float* __restrict__ partial, int Hkv, int64_t T_len,
-                                                             int64_t Nc, float scale) {
+                                                             int64_t Nc, float scale, int64_t cap, int64_t qrows,
+                                                             uint32_t* __restrict__ dbg) {
   using st = typename T::storage;
   using TL = Tile<T, D>;
   constexpr int KCH = D / 16;
@@ -909,6 +910,7 @@ __global__ __launch_bounds__(256) void prefill_remote_kernel(const typename T::s
   const int64_t bucket = blockIdx.x;
   const int begin = off[bucket], end = off[bucket + 1];
   if (begin == end) return;
+  if (!dbg_ok(dbg, begin >= 0 && begin <= end && end <= cap, HSA_ATTN_DEBUG_REMOTE_RANGE)) return;
   const int64_t c = bucket % Nc;
   const int64_t bg = bucket / Nc;  // b * Hkv + g
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
@@ -928,7 +930,8 @@ __global__ __launch_bounds__(256) void prefill_remote_kernel(const typename T::s
   // lane past the bucket's end reads the bucket's first pair, a valid row)
   auto pair_row = [&](int blk) {
     const int p = begin + 32 * blk + (lane & 31);
-    return pairs[p < end ? p : begin];
+    const int32_t r = pairs[p < end ? p : begin];
+    return dbg_ok(dbg, r >= 0 && r < qrows, HSA_ATTN_DEBUG_REMOTE_ROW) ? r : 0;
   };
   int32_t row_next = pair_row(wave);
   for (int blk = wave; begin + 32 * blk < end; blk += 4) {
@@ -999,7 +1002,7 @@ __global__ __launch_bounds__(kWave* G)
     const typename T::storage* __restrict__ vt_g, const int32_t* __restrict__ sel_idx,
     const float* __restrict__ sel_score, const int32_t* __restrict__ pair_pos, const float* __restrict__ partial,
     float* __restrict__ out, int B, int Hkv, int64_t T_len, int64_t T_q, int64_t Nc, int nqc, int jlo, int j0,
-    int k, float scale, int nbuf) {
+    int k, float scale, int nbuf, int64_t cap, uint32_t* __restrict__ dbg) {
   // the grid covers the slab of query chunks [jlo, jlo + nqc) of the T_q rows
   using st = typename T::storage;
   using TL = Tile<T, D>;
@@ -1086,6 +1089,19 @@ __global__ __launch_bounds__(kWave* G)
     } else {
 #pragma unroll
       for (int e = 0; e < KSEL; ++e) pp[e] = ci[e] >= 0 ? pair_pos[base + e] : 0;
+    }
+    if constexpr (HSA_ATTN_DEBUG) {
+      // a local chunk must lie in the query's window and among its
+      // candidates; a chunk-major pair's position inside the slab's list:
+      // a pair that fails is flagged and dropped
+#pragma unroll
+      for (int e = 0; e < KSEL; ++e) {
+        if (ci[e] < 0) continue;
+        const bool good = pp[e] < 0 ? dbg_ok(dbg, ci[e] >= ws && ci[e] < ws + kLocalWindow && ci[e] < n,
+                                             HSA_ATTN_DEBUG_LOCAL_CHUNK)
+                                    : dbg_ok(dbg, pp[e] < cap, HSA_ATTN_DEBUG_LOCAL_POS);
+        if (!good) ci[e] = -1;
+      }
     }
 #pragma unroll
     for (int e = 0; e < KSEL; ++e) {
@@ -1265,7 +1281,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
         mark_launch(st);
         hipLaunchKernelGGL((prefill_remote_kernel<T, D, G>), dim3((unsigned)nb), dim3(256), 0, st, q, k,
                            static_cast<const stg*>(a.vt), a.off + (int64_t)sl * (nb + 1), a.pairs + sl * cap,
-                           a.partial, g.Hkv, g.T, g.Nc, scale);
+                           a.partial, g.Hkv, g.T, g.Nc, scale, cap, (int64_t)g.B * g.Hq * g.Tq, a.dbg);
         mark_launch(st);
       }
       hipError_t e = hipGetLastError();
@@ -1273,7 +1289,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
       mark_launch(st);
       hipLaunchKernelGGL(local, dim3(2 * blocks), dim3(kWave * G), lds, st, q, k, static_cast<const stg*>(a.vt),
                          a.sel_idx, a.sel_score, a.pair_pos, a.partial, a.out, g.B, g.Hkv, g.T, g.Tq, g.Nc, ns, jlo,
-                         j0, g.k, scale, nbuf);
+                         j0, g.k, scale, nbuf, cap, a.dbg);
       mark_launch(st);
     }
   }

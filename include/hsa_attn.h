@@ -316,6 +316,41 @@ const char* hsa_attn_status_string(hsa_attn_status_t status);
 /* Thread-local detail about the last failed call on this thread ("" if none). */
 const char* hsa_attn_last_error(void);
 
+/* ---------------------------------------------------------------------------
+ * Debug build (libhsa_attn_debug.so: the same sources compiled with
+ * HSA_ATTN_DEBUG=1).  Every call of the debug library first fills its
+ * workspace and its outputs with the word 0x7FC00001 (a quiet NaN as fp32,
+ * 2143289345 as int32), so a result that depends on memory the call did not
+ * write shows up as NaN or as a failed check; and its kernels check every
+ * index they read back from the workspace (chunk indices, pair positions,
+ * bucket ranges, pair and row ids) before using it.  A failed check sets
+ * its bit below in the call's flag word and the access is skipped (the
+ * kernel does not trap).  The flag word is the first 256-byte block of the
+ * workspace, which the debug library reserves: its hsa_attn_workspace_size
+ * is 256 bytes larger than the release library's, and the calls use the
+ * rest of the workspace as the release library uses all of it.  The
+ * no-allocation decode keeps the flag word at the start of its scratch.
+ * The fills and checks cost time; the release library has neither. */
+#define HSA_ATTN_DEBUG_DECODE_ENTRIES   0x001u /* decode: a group's chunk count exceeds its slots */
+#define HSA_ATTN_DEBUG_DECODE_CHUNK     0x002u /* decode: a listed chunk outside the cache */
+#define HSA_ATTN_DEBUG_DECODE_SLOT      0x004u /* decode: a head's slot number beyond k */
+#define HSA_ATTN_DEBUG_SCATTER_CHUNK    0x008u /* prefill bucketing: a selected chunk outside [0, Nc) */
+#define HSA_ATTN_DEBUG_SCATTER_POS      0x010u /* prefill bucketing: a pair position beyond its slab's list */
+#define HSA_ATTN_DEBUG_REMOTE_RANGE     0x020u /* prefill chunk-major: a bucket range outside its slab's list */
+#define HSA_ATTN_DEBUG_REMOTE_ROW       0x040u /* prefill chunk-major: a listed query row out of range */
+#define HSA_ATTN_DEBUG_LOCAL_CHUNK      0x080u /* prefill local: a window chunk outside the query's candidates */
+#define HSA_ATTN_DEBUG_LOCAL_POS        0x100u /* prefill local: a chunk-major pair position beyond the list */
+#define HSA_ATTN_DEBUG_BWD_SCATTER      0x200u /* backward bucketing: a pair position out of range */
+#define HSA_ATTN_DEBUG_BWD_PAIR         0x400u /* backward chunks: a bucket range or pair id out of range */
+
+/* Debug library: waits for the device to finish its work, then copies the
+ * flag word of the calls that used `workspace` (NULL: the current device's
+ * no-allocation decode scratch) into *flags (0: every check passed).  Each
+ * call clears the word before its kernels run, so it reports the last call
+ * that used the workspace.  The release library returns
+ * HSA_ATTN_UNSUPPORTED and leaves *flags unchanged. */
+hsa_attn_status_t hsa_attn_debug_flags(const void* workspace, uint32_t* flags);
+
 #ifdef __cplusplus
 }
 #endif

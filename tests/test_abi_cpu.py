@@ -344,3 +344,32 @@ def test_noalloc_decode_rejects_oversized_shapes_on_the_host():
     bad = dims(num_q_heads=30)
     assert lib.hsa_forward_decode_noalloc(ctypes.byref(bad), p, p, p, p, p, None, None, None) == \
         hsa.HSA_ATTN_INVALID_ARGUMENT
+
+
+DEBUG_LIB = os.path.join(ROOT, "hierarchical_sparse_attention_hsa_amd", "libhsa_attn_debug.so")
+
+
+@pytest.mark.skipif(not os.path.exists(DEBUG_LIB), reason="libhsa_attn_debug.so not built")
+def test_debug_library_exports_the_same_calls_and_reserves_its_flag_block():
+    # the debug build (HSA_ATTN_DEBUG=1) exports every declared call; its
+    # workspaces carry a 256-byte flag block in front of the release layout
+    out = os.popen(f"nm -D --defined-only {DEBUG_LIB}").read()
+    for name in header_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+    shapes = [(dims(batch=2, seq_len=64 * 100 + 7), 1), (dims(seq_len=64 * 40), 0), (dims(seq_len=64 * 40), 4)]
+    release = [hsa.hsa_attn_workspace_size(d, kind) for d, kind in shapes]
+    with hsa.debug_library():
+        assert hsa.library_path() == DEBUG_LIB
+        debug = [hsa.hsa_attn_workspace_size(d, kind) for d, kind in shapes]
+        # a NULL flags pointer is rejected before any HIP call
+        st = hsa.load_library().hsa_attn_debug_flags(None, None)
+        assert st == hsa.HSA_ATTN_INVALID_ARGUMENT
+    assert [x - y for x, y in zip(debug, release)] == [256] * len(shapes)
+    assert hsa.library_path().endswith("libhsa_attn.so")
+
+
+def test_release_library_has_no_debug_flags():
+    flags = ctypes.c_uint32(7)
+    st = hsa.load_library().hsa_attn_debug_flags(None, ctypes.byref(flags))
+    assert st == hsa.HSA_ATTN_UNSUPPORTED and flags.value == 7
+    assert "HSA_ATTN_DEBUG" in hsa.hsa_attn_last_error()
