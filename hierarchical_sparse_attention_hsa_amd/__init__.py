@@ -72,7 +72,9 @@ def library_path() -> str:
 
 _LIB = None          # the library the calls go to
 _LOADED = {}         # "release" / "debug" -> loaded library
-_ACTIVE = "release"
+# HSA_ATTN_DEBUG=1 in the environment sends every call of the process to the
+# debug library
+_ACTIVE = "debug" if os.environ.get("HSA_ATTN_DEBUG", "") == "1" else "release"
 
 
 @contextlib.contextmanager

@@ -3,6 +3,8 @@ header declares, and rejects bad arguments on the host before any HIP call."""
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -373,3 +375,16 @@ def test_release_library_has_no_debug_flags():
     st = hsa.load_library().hsa_attn_debug_flags(None, ctypes.byref(flags))
     assert st == hsa.HSA_ATTN_UNSUPPORTED and flags.value == 7
     assert "HSA_ATTN_DEBUG" in hsa.hsa_attn_last_error()
+
+
+def test_debug_environment_variable_selects_the_debug_library():
+    code = ("import hierarchical_sparse_attention_hsa_amd as h, ctypes; "
+            "print(h.library_path()); "
+            "print(h.load_library().hsa_attn_debug_flags(None, None))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root,
+                       env=dict(os.environ, HSA_ATTN_DEBUG="1"), timeout=300)
+    assert r.returncode == 0, r.stderr
+    path, status = r.stdout.split()
+    assert path.endswith("libhsa_attn_debug.so")
+    assert int(status) == hsa.HSA_ATTN_INVALID_ARGUMENT  # the debug build's answer to a NULL flags pointer
