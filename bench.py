@@ -14,8 +14,9 @@ The default (`all`) times prefill_256k_bf16 and then decode_1m_bf16 and prints
 ONE JSON line: `value` is the 1M decode throughput (queries/s); the prefill
 result rides along under "prefill".  Each timed region: W warm-up steps, then
 K steps bracketed by torch.cuda.synchronize(); inputs are resident in HBM.
-Per-kernel durations come from HIP events the library records around each of
-its launches on the same stream (hsa_attn_set_timing_events).
+Per-kernel durations come from HIP events that each of the library's launches
+carries (hsa_attn_set_timing_events): the runtime stamps them with the
+kernel's own start and end, so the timed steps hold no extra packets.
 """
 from __future__ import annotations
 
@@ -78,26 +79,35 @@ class HipEvents:
 
 
 def timed_steps(step, steps, warmup, n_launch, events):
-    """Run warm-up, then `steps` timed steps; returns (total seconds,
-    per-launch mean durations in ms)."""
+    """Run `warmup` untimed steps, then `steps` timed steps without timing
+    events, then `steps` more in which every launch carries an event pair.
+    Returns (seconds of the plain steps, per-launch mean durations in ms,
+    seconds of the instrumented steps).  The step rate comes from the plain
+    steps: an event pair on a launch costs a few microseconds of the step
+    (about 3% of a 1M decode step), which the kernels themselves do not see."""
     import torch
     import hierarchical_sparse_attention_hsa_amd as hsa
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(None)
+    torch.cuda.synchronize()
+    t_plain = time.perf_counter() - t0
     evs = [events.create(2 * n_launch) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    t_events = time.perf_counter() - t0
     hsa.hsa_attn_set_timing_events(None)
     per = np.zeros(n_launch)
     for i in range(steps):
         for j in range(n_launch):
             per[j] += events.ms(evs[i][2 * j], evs[i][2 * j + 1])
-    return t1 - t0, per / steps
+    return t_plain, per / steps, t_events
 
 
 def library_digest():
@@ -377,7 +387,7 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
         else:
             hsa.hsa_forward_decode(q, k, v, L, w.S, w.k, out=out, sel_idx=sel, sel_score=sc, workspace=ws)
 
-    secs, per = timed_steps(step, steps, warmup, 4, HipEvents())
+    secs, per, secs_ev = timed_steps(step, steps, warmup, 4, HipEvents())
     ms_step = 1e3 * secs / steps
     # distinct selected (b, g, chunk) tiles
     attn_bytes = distinct_tile_bytes(sel, w)
@@ -386,6 +396,7 @@ def bench_decode(wname, steps, warmup, cpu_baseline):
     dom, other = decode_roofline(wname, per[0], lm_bytes, per[2], attn_bytes)
     res = {
         "workload": wname, "value": w.B / (ms_step / 1e3), "unit": "queries/s", "ms_per_step": ms_step,
+        "ms_per_step_timed_kernels": 1e3 * secs_ev / steps,
         "kernel_ms": {n: float(x) for n, x in zip(names, per)},
         "step_alg_bytes": alg_bytes, "step_alg_GBps": alg_bytes / (ms_step / 1e3) / 1e9,
         "config": {"workload": wname, "batch_queries": w.B, "cache_tokens": w.T, "q_heads": w.Hq,
@@ -467,7 +478,7 @@ def bench_decode_varlen(wname, steps, warmup):
             hsa.hsa_attn_set_timing_events(ev[8:])
         hsa.hsa_append_kv(k_new, v_new, k, v, L, lens, w.S)
 
-    secs, per = timed_steps(step, steps, warmup, 5, HipEvents())
+    secs, per, secs_ev = timed_steps(step, steps, warmup, 5, HipEvents())
     ms_step = 1e3 * secs / steps
     # landmark bytes the scan reads in the timed steps (lengths grow by one per step)
     ln = lens.cpu().numpy()
@@ -477,6 +488,7 @@ def bench_decode_varlen(wname, steps, warmup):
     dom, other = decode_roofline(wname, per[0], lm_bytes, per[2], distinct_tile_bytes(sel, w))
     res = {
         "workload": wname, "value": w.B / (ms_step / 1e3), "unit": "queries/s", "ms_per_step": ms_step,
+        "ms_per_step_timed_kernels": 1e3 * secs_ev / steps,
         "kernel_ms": {n: float(x) for n, x in zip(names, per)},
         "config": {"workload": wname, "batch_queries": w.B, "cache_capacity": w.T,
                    "cache_tokens": [int(lens0.min()), int(lens0.max())], "q_heads": w.Hq, "kv_heads": w.Hkv,
@@ -661,7 +673,7 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
     for s0 in range(0, nslab, 64):
         order += ["prefill_zero", "prefill_select", "prefill_scan", "prefill_scatter"]
         order += ["prefill_remote", "prefill_local"] * min(64, nslab - s0)
-    secs, per_launch = timed_steps(step, steps, warmup, len(order), events)
+    secs, per_launch, secs_ev = timed_steps(step, steps, warmup, len(order), events)
     per = np.array([sum(t for n, t in zip(order, per_launch) if n == name) for name in names])
     ms_step = 1e3 * secs / steps
     # exact algorithmic work
@@ -697,6 +709,7 @@ def bench_prefill(wname, steps, warmup, cpu_baseline):
     dom_tf = dom_flops / (per[dom] / 1e3) / 1e12
     res = {
         "workload": wname, "value": w.B * Tq / (ms_step / 1e3), "unit": "tokens/s", "ms_per_step": ms_step,
+        "ms_per_step_timed_kernels": 1e3 * secs_ev / steps,
         "kernel_ms": {n: float(x) for n, x in zip(names, per)},
         "scoring_tflops": sel_tf, "scoring_mfma_frac": sel_tf / peak,
         # rocprofv3 MFMA counters of the scoring and local kernels (profiles/), null once the library changed
@@ -805,7 +818,7 @@ def bench_backward(wname, steps, warmup, cpu_baseline):
     names = ["bwd_zero", "bwd_prep", "bwd_scan", "bwd_scatter", "bwd_kt", "bwd_chunk", "bwd_dq"]
     if w.T % w.S:
         names.append("bwd_tail")
-    secs, per = timed_steps(step, steps, warmup, len(names), HipEvents())
+    secs, per, secs_ev = timed_steps(step, steps, warmup, len(names), HipEvents())
     ms_step = 1e3 * secs / steps
     n_pairs = int((sel >= 0).sum().item())
     # per kept pair: S = K q, dA = V do, dq = K^T dlogit, dV += a do, dK += dlogit q
@@ -814,6 +827,7 @@ def bench_backward(wname, steps, warmup, cpu_baseline):
     tf = flops / (per[ci] / 1e3) / 1e12
     res = {
         "workload": wname, "value": w.B * w.T / (ms_step / 1e3), "unit": "tokens/s", "ms_per_step": ms_step,
+        "ms_per_step_timed_kernels": 1e3 * secs_ev / steps,
         "kernel_ms": {n: float(x) for n, x in zip(names, per)},
         "config": {"workload": wname, "batch": w.B, "seq_len": w.T, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "chunk": w.S, "top_k": w.k, "lowrank": w.lowrank},

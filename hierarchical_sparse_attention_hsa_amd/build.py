@@ -90,7 +90,9 @@ def _compile(src: str, defines=(), build_dir=BUILD) -> str:
 
 def _link(objs, lib):
     tmp = lib + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # every symbol resolved at link time: a kernel whose host stub the host
+    # pass left out would otherwise surface only when the library is loaded
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -151,11 +151,12 @@ hsa_attn_status_t debug_prepare(void* workspace, std::initializer_list<Region> r
 
 }  // namespace
 
-void hsa_attn::mark_launch(hipStream_t st) {
-  if (g_events && g_event_next < 2 * g_event_pairs) {
-    (void)hipEventRecord(static_cast<hipEvent_t>(g_events[g_event_next]), st);
-    ++g_event_next;
-  }
+bool hsa_attn::next_timing_pair(hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_events || g_event_next + 2 > 2 * g_event_pairs) return false;
+  *start = static_cast<hipEvent_t>(g_events[g_event_next]);
+  *stop = static_cast<hipEvent_t>(g_events[g_event_next + 1]);
+  g_event_next += 2;
+  return true;
 }
 
 extern "C" {

@@ -578,46 +578,30 @@ static hipError_t launch_backward_d(const BackwardArgs& a, const BackwardPlan& p
   const uint16_t* kk = static_cast<const uint16_t*>(a.k);
   const uint16_t* vv = static_cast<const uint16_t*>(a.v);
   hipError_t e;
-  mark_launch(st);
   if (nb > 0 && (e = launch_zero_ints(cnt, nb, st)) != hipSuccess) return e;
-  mark_launch(st);
-  mark_launch(st);
-  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + kPrepRows - 1) / kPrepRows)), dim3(256), 0, st,
-                     a.out, a.dout,
-                     a.sel_idx, a.sel_score, wts, delta, cnt, pair_pos, rows, g.Hq, g.G, g.T, g.Nc, g.k);
-  mark_launch(st);
+  launch_kernel(bwd_prep_kernel<D>, dim3((unsigned)((rows + kPrepRows - 1) / kPrepRows)), dim3(256), 0, st,
+                a.out, a.dout,
+                a.sel_idx, a.sel_score, wts, delta, cnt, pair_pos, rows, g.Hq, g.G, g.T, g.Nc, g.k);
   if (nb > 0) {
-    mark_launch(st);
     if ((e = launch_exclusive_scan(cnt, offs, nb, st)) != hipSuccess) return e;
-    mark_launch(st);
-    mark_launch(st);
-    hipLaunchKernelGGL(bwd_scatter_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a.sel_idx,
-                       pair_pos, offs, pairs, total, g.Hq, g.G, g.T, g.Nc, g.k, a.dbg);
-    mark_launch(st);
-    mark_launch(st);
-    hipLaunchKernelGGL((prefill_vt_kernel<BF16, D>), dim3((unsigned)nb), dim3(256), 0, st, kk, kt, g.T, g.Nc);
-    mark_launch(st);
+    launch_kernel(bwd_scatter_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a.sel_idx,
+                  pair_pos, offs, pairs, total, g.Hq, g.G, g.T, g.Nc, g.k, a.dbg);
+    launch_kernel((prefill_vt_kernel<BF16, D>), dim3((unsigned)nb), dim3(256), 0, st, kk, kt, g.T, g.Nc);
     constexpr size_t lds = 3 * kChunk * D * 2 + 4 * (2 * kChunk * 32 * 2 + 2 * D * 32 * 2) + 2 * D;
     static_assert(lds <= 160 * 1024, "chunk kernel LDS");
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_chunk_kernel<D>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
       return e;
-    mark_launch(st);
-    hipLaunchKernelGGL(bwd_chunk_kernel<D>, dim3((unsigned)nb), dim3(256), lds, st, q, kk, vv, kt,
-                       static_cast<const uint16_t*>(a.lm), a.dout, wts, delta, offs, pairs, dqp, a.dk, a.dv, g.k, g.T,
-                       g.Nc, scale, total, a.dbg);
-    mark_launch(st);
+    launch_kernel(bwd_chunk_kernel<D>, dim3((unsigned)nb), dim3(256), lds, st, q, kk, vv, kt,
+                  static_cast<const uint16_t*>(a.lm), a.dout, wts, delta, offs, pairs, dqp, a.dk, a.dv, g.k, g.T,
+                  g.Nc, scale, total, a.dbg);
   }
-  mark_launch(st);
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)((rows * (D / 4) + 255) / 256)), dim3(256), 0, st, dqp,
-                     pair_pos, a.dq, rows, g.k);
-  mark_launch(st);
+  launch_kernel(bwd_dq_kernel<D>, dim3((unsigned)((rows * (D / 4) + 255) / 256)), dim3(256), 0, st, dqp,
+                pair_pos, a.dq, rows, g.k);
   const int64_t tail = (g.T - g.Nc * kChunk) * D * (int64_t)g.B * g.Hkv;
   if (tail > 0) {
-    mark_launch(st);
-    hipLaunchKernelGGL(bwd_tail_kernel, dim3((unsigned)((tail + 255) / 256)), dim3(256), 0, st, a.dk, a.dv,
-                       (int64_t)g.B * g.Hkv, g.T, g.Nc, D);
-    mark_launch(st);
+    launch_kernel(bwd_tail_kernel, dim3((unsigned)((tail + 255) / 256)), dim3(256), 0, st, a.dk, a.dv,
+                  (int64_t)g.B * g.Hkv, g.T, g.Nc, D);
   }
   return hipGetLastError();
 }

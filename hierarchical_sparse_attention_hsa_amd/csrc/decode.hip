@@ -366,9 +366,10 @@ __global__ __launch_bounds__(kWave* G) void decode_merge_kernel(const float2* __
 
   // Fast path: the k-th best of the first r entries of every split's sorted
   // list (at least 2k values) is a lower bound tau of the head's k-th best
-  // score; every entry at or above tau is gathered (each list is walked
-  // until it drops below tau) and sorted.  Too many gathered entries fall
-  // back to merging every candidate.
+  // score; every entry at or above tau is gathered and sorted: the first r
+  // of each list by one parallel read, deeper entries only from the lists
+  // whose r-th entry reached tau (walked until they drop below it).  Too
+  // many gathered entries fall back to merging every candidate.
   bool done = false;
   {
     const int r = min(k, max(1, (2 * k + splits - 1) / splits));
@@ -384,8 +385,17 @@ __global__ __launch_bounds__(kWave* G) void decode_merge_kernel(const float2* __
       if (split_topk(tvals[hh], nv, 0, k, hist[hh], gbuf[hh], ts, ti)) {
         const float tau = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ts), min(k, nv) - 1));
         if (tau > -__builtin_inff()) {
+          // an entry at or above the finite tau is a valid one
+          for (int v = lane; v < nv; v += kWave) {
+            if (tvals[hh][v] >= tau) {
+              const float2 c = cb[(int64_t)(v / r) * G * k + v % r];
+              const int pos = atomicAdd(&gcnt[hh], 1);
+              if (pos < kGather) gbuf[hh][pos] = c;
+            }
+          }
           for (int sp = lane; sp < splits; sp += kWave) {
-            for (int e = 0; e < k; ++e) {
+            if (!(tvals[hh][sp * r + r - 1] >= tau)) continue;
+            for (int e = r; e < k; ++e) {
               const float2 c = cb[(int64_t)sp * G * k + e];
               if (__float_as_int(c.y) == INT_MAX || c.x < tau) break;
               const int pos = atomicAdd(&gcnt[hh], 1);
@@ -440,22 +450,38 @@ __global__ __launch_bounds__(kWave* G) void decode_merge_kernel(const float2* __
     sel_score[bh * k + lane] = ok ? list.s : -__builtin_inff();
     ls[hh * k + lane] = ok ? list.i : -1;
   }
+  // the entries padded to a multiple of 8 with a value no entry holds
+  const int nent = G * k, nent8 = (nent + 7) & ~7;
+  if ((int)threadIdx.x < nent8 - nent) ls[nent + threadIdx.x] = -2;
   __syncthreads();
   // entry e = hh * k + lane owns its chunk when no earlier entry names it;
-  // every entry of the group is compared through uniform LDS reads
+  // every entry of the group is compared through uniform LDS reads, eight
+  // issued together
   const int e = hh * k + lane;
   const int c = lane < k ? ls[e] : -1;
   bool owner = c >= 0;
-  uint32_t slots[2] = {0xffffffffu, 0xffffffffu};
-  for (int h2 = 0; h2 < G; ++h2) {
-    for (int s2 = 0; s2 < k; ++s2) {
-      const int f = h2 * k + s2;
-      if (ls[f] == c) {
-        if (f < e) owner = false;
-        slots[h2 / 4] = (slots[h2 / 4] & ~(0xffu << (8 * (h2 % 4)))) | ((uint32_t)s2 << (8 * (h2 % 4)));
+  uint32_t slots0 = 0xffffffffu, slots1 = 0xffffffffu;  // heads 0..3, 4..7
+  int h2 = 0, s2 = 0;  // head and slot of entry f
+  for (int f0 = 0; f0 < nent8; f0 += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = ls[f0 + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (v[u] == c) {
+        if (f0 + u < e) owner = false;
+        const int sh = 8 * (h2 & 3);
+        const uint32_t put = (uint32_t)s2 << sh, keep = ~(0xffu << sh);
+        if (h2 < 4) slots0 = (slots0 & keep) | put;
+        else slots1 = (slots1 & keep) | put;
+      }
+      if (++s2 == k) {
+        s2 = 0;
+        ++h2;
       }
     }
   }
+  const uint32_t slots[2] = {slots0, slots1};
   const uint64_t om = __ballot(owner);
   if (lane == 0) wave_cnt[hh] = __popcll(om);
   __syncthreads();
@@ -587,6 +613,19 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void decode_attn_kernel(const t
       mfma(sacc[tb], a, qf[s]);
     }
   }
+  // With two value passes, the second pass's slices go into the key tile's
+  // LDS (direct global->LDS loads, lane l's 16 bytes of load i at i * 1 KiB
+  // + 16 l) as soon as the key fragments are read, so they fly during the
+  // softmax and the first pass instead of after it.
+  if constexpr (VPASS == 2) {
+    static_assert(VLP * kWave * 16 <= KTB, "the second value pass fits the key tile's LDS");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the key fragments are in registers
+#pragma unroll
+    for (int i = 0; i < VLP; ++i)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const char*>(vtile + (int64_t)(RPI * (VLP + i) + vrow0) * D + vcol),
+          (__attribute__((address_space(3))) void*)(ktl[wave] + i * kWave * 16), 16, 0, 0);
+  }
 
   // softmax per head column: lane l (l%32 = head) holds tokens
   // 32*tb + tile_row(r, half); its partner l^32 holds the rest
@@ -629,9 +668,10 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void decode_attn_kernel(const t
 #pragma unroll
   for (int ps = 0; ps < VPASS; ++ps) {
     if (ps > 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the second pass's slices are in LDS
 #pragma unroll
       for (int i = 0; i < VLP; ++i)
-        vr[i] = *reinterpret_cast<const u32x4*>(vtile + (int64_t)(RPI * (ps * VLP + i) + vrow0) * D + vcol);
+        vr[i] = *reinterpret_cast<const u32x4*>(ktl[wave] + i * kWave * 16 + 16 * lane);
     }
 #pragma unroll
     for (int i = 0; i < VLP; ++i) {
@@ -750,28 +790,20 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipS
     // scores, then per wave a 256-bin histogram and the gather buffer
     const size_t lds = (size_t)G * p.rows_per_split * sizeof(float) +
                        (size_t)(kScanThreads / kWave) * (256 * sizeof(int) + kGather * sizeof(float2));
-    mark_launch(st);
-    hipLaunchKernelGGL((decode_scan_kernel<T, D, G>), dim3(p.splits, g.Hkv, g.B), dim3(kScanThreads), lds, st,
-                       static_cast<const stg*>(a.q), static_cast<const stg*>(a.lm), cand, g.Hkv, g.Nc,
-                       p.rows_per_split, p.splits, g.k, scale, a.lens, g.T);
-    mark_launch(st);
+    launch_kernel((decode_scan_kernel<T, D, G>), dim3(p.splits, g.Hkv, g.B), dim3(kScanThreads), lds, st,
+                  static_cast<const stg*>(a.q), static_cast<const stg*>(a.lm), cand, g.Hkv, g.Nc,
+                  p.rows_per_split, p.splits, g.k, scale, a.lens, g.T);
   }
-  mark_launch(st);
-  hipLaunchKernelGGL((decode_merge_kernel<G>), dim3(g.Hkv, g.B), dim3(kWave * G), 0, st, cand, a.sel_idx,
-                     a.sel_score, ulist, ucount, g.Hkv, p.splits, g.k, a.k_base, a.gap_tau);
-  mark_launch(st);
+  launch_kernel((decode_merge_kernel<G>), dim3(g.Hkv, g.B), dim3(kWave * G), 0, st, cand, a.sel_idx,
+                a.sel_score, ulist, ucount, g.Hkv, p.splits, g.k, a.k_base, a.gap_tau);
   if (p.splits > 0) {
-    mark_launch(st);
-    hipLaunchKernelGGL((decode_attn_kernel<T, D, G>), dim3((G * g.k + kAttnWaves - 1) / kAttnWaves, g.Hkv, g.B),
-                       dim3(kAttnWaves * kWave), 0, st,
-                       static_cast<const stg*>(a.q), static_cast<const stg*>(a.k), static_cast<const stg*>(a.v),
-                       ulist, ucount, partial, g.Hkv, g.T, g.k, scale, a.dbg);
-    mark_launch(st);
+    launch_kernel((decode_attn_kernel<T, D, G>), dim3((G * g.k + kAttnWaves - 1) / kAttnWaves, g.Hkv, g.B),
+                  dim3(kAttnWaves * kWave), 0, st,
+                  static_cast<const stg*>(a.q), static_cast<const stg*>(a.k), static_cast<const stg*>(a.v),
+                  ulist, ucount, partial, g.Hkv, g.T, g.k, scale, a.dbg);
   }
-  mark_launch(st);
-  hipLaunchKernelGGL(decode_fuse_kernel, dim3(g.B * g.Hq), dim3(D), 0, st, partial, a.sel_idx, a.sel_score, a.out,
-                     g.k, D);
-  mark_launch(st);
+  launch_kernel(decode_fuse_kernel, dim3(g.B * g.Hq), dim3(D), 0, st, partial, a.sel_idx, a.sel_score, a.out,
+                g.k, D);
   return hipGetLastError();
 }
 

@@ -1,15 +1,29 @@
 // Host-side launch interfaces of the HSA kernels (internal to libhsa_attn).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace hsa_attn {
 
-// Records the next caller-provided timing event on `st` when per-launch
-// timing is enabled on this thread (hsa_attn_set_timing_events); no-op otherwise.
-void mark_launch(hipStream_t st);
+// The next caller-provided pair of timing events when per-launch timing is
+// enabled on this thread (hsa_attn_set_timing_events); false otherwise.
+bool next_timing_pair(hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel of the library is launched through this: with timing on, the
+// launch carries the next event pair, which the runtime stamps with the
+// kernel's own start and end (no extra packets between the kernels, so the
+// timed sequence runs as it does untimed); otherwise a plain launch.
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (next_timing_pair(&e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, e0, e1, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+}
 
 struct LandmarkArgs {
   const void* k;

@@ -102,11 +102,9 @@ static hipError_t launch_landmarks_t(const LandmarkArgs& a, hipStream_t st) {
   if (total <= 0) return hipSuccess;
   constexpr int kWavesPerBlock = 4;
   const int64_t blocks = (total + kWavesPerBlock - 1) / kWavesPerBlock;
-  mark_launch(st);
-  hipLaunchKernelGGL((landmarks_kernel<T, D>), dim3((unsigned)blocks), dim3(kWave * kWavesPerBlock), 0, st,
-                     static_cast<const typename T::storage*>(a.k), static_cast<typename T::storage*>(a.lm),
-                     a.T, a.S, a.Nc, a.c0, a.c1 - a.c0, total);
-  mark_launch(st);
+  launch_kernel((landmarks_kernel<T, D>), dim3((unsigned)blocks), dim3(kWave * kWavesPerBlock), 0, st,
+                static_cast<const typename T::storage*>(a.k), static_cast<typename T::storage*>(a.lm),
+                a.T, a.S, a.Nc, a.c0, a.c1 - a.c0, total);
   return hipGetLastError();
 }
 
@@ -202,11 +200,9 @@ static hipError_t launch_append_t(const AppendArgs& a, hipStream_t st) {
   if (a.B <= 0) return hipSuccess;
   using stg = typename T::storage;
   const int waves = a.Hkv < 4 ? a.Hkv : 4;
-  mark_launch(st);
-  hipLaunchKernelGGL((append_kv_kernel<T, D>), dim3(a.B), dim3(kWave * waves), 0, st,
-                     static_cast<const stg*>(a.k_new), static_cast<const stg*>(a.v_new), static_cast<stg*>(a.k),
-                     static_cast<stg*>(a.v), static_cast<stg*>(a.lm), a.lens, a.Hkv, a.T, a.S, a.Nc);
-  mark_launch(st);
+  launch_kernel((append_kv_kernel<T, D>), dim3(a.B), dim3(kWave * waves), 0, st,
+                static_cast<const stg*>(a.k_new), static_cast<const stg*>(a.v_new), static_cast<stg*>(a.k),
+                static_cast<stg*>(a.v), static_cast<stg*>(a.lm), a.lens, a.Hkv, a.T, a.S, a.Nc);
   return hipGetLastError();
 }
 

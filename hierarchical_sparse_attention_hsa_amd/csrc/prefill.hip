@@ -136,23 +136,21 @@ __global__ __launch_bounds__(256) void prefill_scatter_kernel(const int32_t* __r
 }
 
 hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t st) {
-  hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
-                     st, p, n);
+  launch_kernel(prefill_zero_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0, st, p,
+                n);
   return hipGetLastError();
 }
 
 hipError_t launch_exclusive_scan(const int* cnt, int* off, int64_t n, hipStream_t st) {
-  hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, cnt, off, n);
+  launch_kernel(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, cnt, off, n);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_zero_counts(const PrefillArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
   const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc * a.slab_group;
-  mark_launch(st);
-  hipLaunchKernelGGL(prefill_zero_kernel, dim3((unsigned)std::min<int64_t>((nb + 255) / 256, 4096)), dim3(256), 0,
+  launch_kernel(prefill_zero_kernel, dim3((unsigned)std::min<int64_t>((nb + 255) / 256, 4096)), dim3(256), 0,
                      st, a.cnt, nb);
-  mark_launch(st);
   return hipGetLastError();
 }
 
@@ -162,13 +160,10 @@ hipError_t launch_prefill_bucketing(const PrefillArgs& a, int nslab, int64_t r0,
   const int64_t nb = (int64_t)g.B * g.Hkv * g.Nc;
   const int64_t cap = (int64_t)g.B * g.Hq * a.slab_rows * g.k;  // one slab's pair list
   const unsigned pb = (unsigned)((nrows + 255) / 256);
-  mark_launch(st);
-  hipLaunchKernelGGL(prefill_scan_kernel, dim3((unsigned)nslab), dim3(1024), 0, st, a.cnt, a.off, nb);
-  mark_launch(st);
-  mark_launch(st);
-#define HSA_SCATTER(K4)                                                                                              \
-  hipLaunchKernelGGL(prefill_scatter_kernel<K4>, dim3(pb), dim3(256), 0, st, a.sel_idx, a.off, a.pair_pos, a.pairs, \
-                     g.Hq, g.G, g.Tq, g.Nc, g.k, r0, rn, a.slab_rows, cap, nb, nrows, a.dbg)
+  launch_kernel(prefill_scan_kernel, dim3((unsigned)nslab), dim3(1024), 0, st, a.cnt, a.off, nb);
+#define HSA_SCATTER(K4)                                                                                         \
+  launch_kernel(prefill_scatter_kernel<K4>, dim3(pb), dim3(256), 0, st, a.sel_idx, a.off, a.pair_pos, a.pairs, \
+                g.Hq, g.G, g.Tq, g.Nc, g.k, r0, rn, a.slab_rows, cap, nb, nrows, a.dbg)
   switch (g.k) {
     case 16: HSA_SCATTER(4); break;
     case 32: HSA_SCATTER(8); break;
@@ -176,7 +171,6 @@ hipError_t launch_prefill_bucketing(const PrefillArgs& a, int nslab, int64_t r0,
     default: HSA_SCATTER(0); break;
   }
 #undef HSA_SCATTER
-  mark_launch(st);
   return hipGetLastError();
 }
 

@@ -1249,10 +1249,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   // per slab [jlo, jlo + ns): chunk-major attention, local attention and
   // fusion.
   if (nb > 0) {
-    mark_launch(st);
-    hipLaunchKernelGGL((prefill_vt_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, st, v, static_cast<stg*>(a.vt),
-                       g.T, g.Nc);
-    mark_launch(st);
+    launch_kernel((prefill_vt_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, st, v, static_cast<stg*>(a.vt),
+                  g.T, g.Nc);
   }
   const int sgc = cps * a.slab_group;  // query chunks per selection launch
   const int64_t cap = (int64_t)g.B * g.Hq * a.slab_rows * g.k;
@@ -1263,11 +1261,9 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
       if (e != hipSuccess) return e;
     }
     const unsigned gblocks = (unsigned)((int64_t)ng * g.B * g.Hkv);
-    mark_launch(st);
-    hipLaunchKernelGGL((prefill_select_kernel<T, D, G, KSEL>), dim3(gblocks * (G / HPW)), dim3(kWave * HPW), 0, st,
-                       q, static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, nb > 0 ? a.cnt : nullptr,
-                       a.pair_pos, g.B, g.Hkv, g.Tq, g.Nc, ng, jg, cps, j0, g.k, scale, a.k_base, a.gap_tau);
-    mark_launch(st);
+    launch_kernel((prefill_select_kernel<T, D, G, KSEL>), dim3(gblocks * (G / HPW)), dim3(kWave * HPW), 0, st,
+                  q, static_cast<const stg*>(a.lm), a.sel_idx, a.sel_score, nb > 0 ? a.cnt : nullptr,
+                  a.pair_pos, g.B, g.Hkv, g.Tq, g.Nc, ng, jg, cps, j0, g.k, scale, a.k_base, a.gap_tau);
     if (nb > 0) {
       const int64_t r0 = (int64_t)jg * kChunk, rn = std::min<int64_t>((int64_t)ng * kChunk, g.Tq - r0);
       hipError_t e = launch_prefill_bucketing(a, (ng + cps - 1) / cps, r0, rn, st);
@@ -1278,19 +1274,15 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
       const int sl = (jlo - jg) / cps;
       const unsigned blocks = (unsigned)((int64_t)ns * g.B * g.Hkv);
       if (nb > 0) {
-        mark_launch(st);
-        hipLaunchKernelGGL((prefill_remote_kernel<T, D, G>), dim3((unsigned)nb), dim3(256), 0, st, q, k,
-                           static_cast<const stg*>(a.vt), a.off + (int64_t)sl * (nb + 1), a.pairs + sl * cap,
-                           a.partial, g.Hkv, g.T, g.Nc, scale, cap, (int64_t)g.B * g.Hq * g.Tq, a.dbg);
-        mark_launch(st);
+        launch_kernel((prefill_remote_kernel<T, D, G>), dim3((unsigned)nb), dim3(256), 0, st, q, k,
+                      static_cast<const stg*>(a.vt), a.off + (int64_t)sl * (nb + 1), a.pairs + sl * cap,
+                      a.partial, g.Hkv, g.T, g.Nc, scale, cap, (int64_t)g.B * g.Hq * g.Tq, a.dbg);
       }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      mark_launch(st);
-      hipLaunchKernelGGL(local, dim3(2 * blocks), dim3(kWave * G), lds, st, q, k, static_cast<const stg*>(a.vt),
-                         a.sel_idx, a.sel_score, a.pair_pos, a.partial, a.out, g.B, g.Hkv, g.T, g.Tq, g.Nc, ns, jlo,
-                         j0, g.k, scale, nbuf, cap, a.dbg);
-      mark_launch(st);
+      launch_kernel(local, dim3(2 * blocks), dim3(kWave * G), lds, st, q, k, static_cast<const stg*>(a.vt),
+                    a.sel_idx, a.sel_score, a.pair_pos, a.partial, a.out, g.B, g.Hkv, g.T, g.Tq, g.Nc, ns, jlo,
+                    j0, g.k, scale, nbuf, cap, a.dbg);
     }
   }
   return hipGetLastError();

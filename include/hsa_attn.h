@@ -287,9 +287,12 @@ hsa_attn_status_t hsa_append_kv(const hsa_attn_dims_t* d, const void* k_new, con
 
 /*
  * Diagnostics: per-launch timing.  After this call, every subsequent
- * forward, landmark or append call made on the calling thread records events[2*i] (hipEvent_t, created by the caller)
- * on its stream just before its i-th kernel launch and events[2*i+1] just
- * after it, for i < n_pairs; the index restarts at 0 with each call.
+ * forward, landmark or append call made on the calling thread hands its i-th
+ * kernel launch the pair events[2*i], events[2*i+1] (hipEvent_t, created by
+ * the caller), for i < n_pairs, which the runtime stamps with that kernel's
+ * start and end (the launch itself carries them: no extra packet enters the
+ * stream, so timed calls run like untimed ones); the index restarts at 0
+ * with each call.
  * Launch order: landmarks: 1 kernel; prefill, cached and adaptive prefill (when T >= S): V transpose,
  * then per group of up to 64 slabs of query rows (hsa_attn_prefill_slab_rows)
  * zero, select, scan, scatter, then per slab of the group remote attention,
@@ -297,8 +300,8 @@ hsa_attn_status_t hsa_append_kv(const hsa_attn_dims_t* d, const void* k_new, con
  * decode and varlen decode: scan, merge,
  * attention, fusion, for adaptive decode too (scan and attention are skipped when the cache capacity
  * holds no complete chunk); append: 1 kernel; backward: zero counts, row
- * preparation, scan, scatter, K transpose, chunk gradients, dq (scan,
- * scatter, K transpose and chunk gradients only when T >= S), then zeros
+ * preparation, scan, scatter, K transpose, chunk gradients, dq (zero counts,
+ * scan, scatter, K transpose and chunk gradients only when T >= S), then zeros
  * for the tokens after the last complete chunk when T is not a multiple of S.  events == NULL or
  * n_pairs == 0 turns recording off.  The setting is thread-local; the events stay owned by the
  * caller and must outlive the calls that record them.
