@@ -14,9 +14,9 @@ The default (`all`) times prefill_256k_bf16 and then decode_1m_bf16 and prints
 ONE JSON line: `value` is the 1M decode throughput (queries/s); the prefill
 result rides along under "prefill".  Each timed region: W warm-up steps, then
 K steps bracketed by torch.cuda.synchronize(); inputs are resident in HBM.
-Per-kernel durations come from HIP events that each of the library's launches
-carries (hsa_attn_set_timing_events): the runtime stamps them with the
-kernel's own start and end, so the timed steps hold no extra packets.
+The step rate comes from K steps without timing events; per-kernel durations
+come from K more steps in which the library records HIP events around each
+of its launches on the same stream (hsa_attn_set_timing_events).
 """
 from __future__ import annotations
 

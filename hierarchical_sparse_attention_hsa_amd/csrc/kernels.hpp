@@ -1,7 +1,6 @@
 // Host-side launch interfaces of the HSA kernels (internal to libhsa_attn).
 #pragma once
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -13,16 +12,17 @@ namespace hsa_attn {
 bool next_timing_pair(hipEvent_t* start, hipEvent_t* stop);
 
 // Every kernel of the library is launched through this: with timing on, the
-// launch carries the next event pair, which the runtime stamps with the
-// kernel's own start and end (no extra packets between the kernels, so the
-// timed sequence runs as it does untimed); otherwise a plain launch.
+// next event pair is recorded on the stream just before and just after the
+// launch.  (Handing the pair to the launch itself, hipExtLaunchKernelGGL,
+// costs fewer microseconds per launch, but the runtime then holds on to the
+// device memory the timed kernels touched for as long as the events live.)
 template <typename F, typename... Args>
 inline void launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, Args... args) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (next_timing_pair(&e0, &e1))
-    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, e0, e1, 0u, args...);
-  else
-    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  const bool timed = next_timing_pair(&e0, &e1);
+  if (timed) (void)hipEventRecord(e0, st);
+  hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  if (timed) (void)hipEventRecord(e1, st);
 }
 
 struct LandmarkArgs {

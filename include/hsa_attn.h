@@ -287,12 +287,11 @@ hsa_attn_status_t hsa_append_kv(const hsa_attn_dims_t* d, const void* k_new, con
 
 /*
  * Diagnostics: per-launch timing.  After this call, every subsequent
- * forward, landmark or append call made on the calling thread hands its i-th
- * kernel launch the pair events[2*i], events[2*i+1] (hipEvent_t, created by
- * the caller), for i < n_pairs, which the runtime stamps with that kernel's
- * start and end (the launch itself carries them: no extra packet enters the
- * stream, so timed calls run like untimed ones); the index restarts at 0
- * with each call.
+ * forward, landmark or append call made on the calling thread records
+ * events[2*i] (hipEvent_t, created by the caller) on its stream just before
+ * its i-th kernel launch and events[2*i+1] just after it, for i < n_pairs;
+ * the index restarts at 0 with each call.  Each recorded event adds a few
+ * microseconds to the call's run on the device.
  * Launch order: landmarks: 1 kernel; prefill, cached and adaptive prefill (when T >= S): V transpose,
  * then per group of up to 64 slabs of query rows (hsa_attn_prefill_slab_rows)
  * zero, select, scan, scatter, then per slab of the group remote attention,
