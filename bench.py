@@ -79,22 +79,20 @@ class HipEvents:
 
 
 def timed_steps(step, steps, warmup, n_launch, events):
-    """Run `warmup` untimed steps, then `steps` timed steps without timing
-    events, then `steps` more in which every launch carries an event pair.
-    Returns (seconds of the plain steps, per-launch mean durations in ms,
-    seconds of the instrumented steps).  The step rate comes from the plain
-    steps: an event pair on a launch costs a few microseconds of the step
-    (about 3% of a 1M decode step), which the kernels themselves do not see."""
+    """Run `warmup` untimed steps, then `steps` steps with timing events
+    recorded around every launch, then the `steps` timed steps without them.
+    Returns (seconds of the plain timed steps, per-launch mean durations in
+    ms, seconds of the instrumented steps).  The step rate comes from the
+    plain steps: the events add a few microseconds per launch (about 4% of a
+    1M decode step), which the kernels themselves do not see; running the
+    instrumented steps first also lets the GPU reach its steady clocks
+    before the timed region (the first 20 decode steps after 5 warm-up steps
+    run about 3% slower than the following ones)."""
     import torch
     import hierarchical_sparse_attention_hsa_amd as hsa
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step(None)
-    torch.cuda.synchronize()
-    t_plain = time.perf_counter() - t0
     evs = [events.create(2 * n_launch) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -103,6 +101,12 @@ def timed_steps(step, steps, warmup, n_launch, events):
     torch.cuda.synchronize()
     t_events = time.perf_counter() - t0
     hsa.hsa_attn_set_timing_events(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(None)
+    torch.cuda.synchronize()
+    t_plain = time.perf_counter() - t0
     per = np.zeros(n_launch)
     for i in range(steps):
         for j in range(n_launch):
@@ -480,9 +484,10 @@ def bench_decode_varlen(wname, steps, warmup):
 
     secs, per, secs_ev = timed_steps(step, steps, warmup, 5, HipEvents())
     ms_step = 1e3 * secs / steps
-    # landmark bytes the scan reads in the timed steps (lengths grow by one per step)
+    # landmark bytes the scan reads in the instrumented steps, the second to
+    # last run of `steps` (lengths grow by one per step)
     ln = lens.cpu().numpy()
-    mid = ln - steps // 2
+    mid = ln - steps - steps // 2
     lm_bytes = float(np.sum(mid // w.S)) * w.Hkv * w.D * esz
     names = ["decode_scan", "decode_merge", "decode_attn", "decode_fuse", "append_kv"]
     dom, other = decode_roofline(wname, per[0], lm_bytes, per[2], distinct_tile_bytes(sel, w))
