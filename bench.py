@@ -947,10 +947,11 @@ def main():
     }
     if "cpu_baseline" in main_res:
         line["cpu_baseline"] = main_res["cpu_baseline"]
-    for key in ("roofline_other", "kernel_ms", "step_alg_GBps", "needle_recall", "near_tie_rows",
-                "gap_threshold", "doubled_head_frac", "doubled_row_frac", "mfma_counters"):
-        if key in main_res:
-            line[key] = main_res[key]
+    # the rest of the workload's record (kernel times, the other roofline,
+    # MFMA counters, near-tie counts, ...)
+    for key, val in main_res.items():
+        if key not in line and key != "workload":
+            line[key] = val
     for key in ("prefill", "decode_16m"):
         if key in results:
             line[key] = results[key]
