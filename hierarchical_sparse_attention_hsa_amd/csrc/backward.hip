@@ -141,24 +141,49 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
     }
 }
 
-// pairs[off[bucket] + pair_pos[i]] = i (the pair id: row * k + slot)
+// pairs[off[bucket] + pair_pos[i]] = i (the pair id: row * k + slot).  A
+// thread takes V consecutive slots of one row (V divides k): their loads as
+// one 16-byte load each (V = 4), the row's bucket base computed once, and
+// every slot's bucket offset read at once (a slot without a pair reads the
+// base's first entry).
+template <int V>
 __global__ void bwd_scatter_kernel(const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ pair_pos,
                                    const int* __restrict__ off, int32_t* __restrict__ pairs, int64_t total, int Hq,
                                    int G, int64_t T_len, int64_t Nc, int k, uint32_t* __restrict__ dbg) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  const int32_t pp = pair_pos[i];
-  if (pp < 0) return;
-  const int64_t row = i / k;
+  const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
+  if (i0 >= total) return;
+  const int64_t row = i0 / k;
   const int64_t bh = row / T_len;
   const int h = (int)(bh % Hq);
   const int64_t b = bh / Hq;
-  const int32_t c = sel_idx[i];
-  if (!dbg_ok(dbg, c >= 0 && c < Nc, HSA_ATTN_DEBUG_BWD_SCATTER)) return;
-  const int64_t bucket = (b * (Hq / G) + h / G) * Nc + c;
-  const int64_t dst = (int64_t)off[bucket] + pp;
-  if (!dbg_ok(dbg, dst >= 0 && dst < total, HSA_ATTN_DEBUG_BWD_SCATTER)) return;
-  pairs[dst] = (int32_t)i;
+  const int* ob = off + (b * (Hq / G) + h / G) * Nc;
+  int32_t pp[V], c[V];
+  if constexpr (V == 4) {
+    const u32x4 p4 = *reinterpret_cast<const u32x4*>(pair_pos + i0);
+    const u32x4 c4 = *reinterpret_cast<const u32x4*>(sel_idx + i0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      pp[u] = (int32_t)p4[u];
+      c[u] = (int32_t)c4[u];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      pp[u] = pair_pos[i0 + u];
+      c[u] = sel_idx[i0 + u];
+    }
+  }
+  int o[V];
+#pragma unroll
+  for (int u = 0; u < V; ++u) o[u] = ob[pp[u] >= 0 && c[u] >= 0 && c[u] < Nc ? c[u] : 0];
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    if (pp[u] < 0) continue;
+    if (!dbg_ok(dbg, c[u] >= 0 && c[u] < Nc, HSA_ATTN_DEBUG_BWD_SCATTER)) continue;
+    const int64_t dst = (int64_t)o[u] + pp[u];
+    if (!dbg_ok(dbg, dst >= 0 && dst < total, HSA_ATTN_DEBUG_BWD_SCATTER)) continue;
+    pairs[dst] = (int32_t)(i0 + u);
+  }
 }
 
 // ---------------------------------------------------------------- 2. chunks
@@ -584,8 +609,12 @@ static hipError_t launch_backward_d(const BackwardArgs& a, const BackwardPlan& p
                 a.sel_idx, a.sel_score, wts, delta, cnt, pair_pos, rows, g.Hq, g.G, g.T, g.Nc, g.k);
   if (nb > 0) {
     if ((e = launch_exclusive_scan(cnt, offs, nb, st)) != hipSuccess) return e;
-    launch_kernel(bwd_scatter_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a.sel_idx,
-                  pair_pos, offs, pairs, total, g.Hq, g.G, g.T, g.Nc, g.k, a.dbg);
+    if (g.k % 4 == 0)
+      launch_kernel(bwd_scatter_kernel<4>, dim3((unsigned)((total / 4 + 255) / 256)), dim3(256), 0, st, a.sel_idx,
+                    pair_pos, offs, pairs, total, g.Hq, g.G, g.T, g.Nc, g.k, a.dbg);
+    else
+      launch_kernel(bwd_scatter_kernel<1>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a.sel_idx,
+                    pair_pos, offs, pairs, total, g.Hq, g.G, g.T, g.Nc, g.k, a.dbg);
     launch_kernel((prefill_vt_kernel<BF16, D>), dim3((unsigned)nb), dim3(256), 0, st, kk, kt, g.T, g.Nc);
     constexpr size_t lds = 3 * kChunk * D * 2 + 4 * (2 * kChunk * 32 * 2 + 2 * D * 32 * 2) + 2 * D;
     static_assert(lds <= 160 * 1024, "chunk kernel LDS");

@@ -103,6 +103,17 @@ __global__ __launch_bounds__(256) void prefill_scatter_kernel(const int32_t* __r
       p4[e4] = *reinterpret_cast<const u32x4*>(pp + 4 * e4);
       c4[e4] = *reinterpret_cast<const u32x4*>(si + 4 * e4);
     }
+    // every slot's bucket offset is read at once (a slot that is not a
+    // chunk-major pair reads bucket 0), so the row's offsets arrive in one
+    // round trip instead of one per pair
+    int ob[K4][4];
+#pragma unroll
+    for (int e4 = 0; e4 < K4; ++e4)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = (int)c4[e4][u];
+        ob[e4][u] = o[(int)p4[e4][u] >= 0 && c >= 0 && c < Nc ? c : 0];
+      }
 #pragma unroll
     for (int e4 = 0; e4 < K4; ++e4) {
       bool any = false;
@@ -112,7 +123,7 @@ __global__ __launch_bounds__(256) void prefill_scatter_kernel(const int32_t* __r
         if (inb >= 0) {
           const int c = (int)c4[e4][u];
           if (!dbg_ok(dbg, c >= 0 && c < Nc, HSA_ATTN_DEBUG_SCATTER_CHUNK)) continue;
-          const int pos = o[c] + inb;
+          const int pos = ob[e4][u] + inb;
           if (!dbg_ok(dbg, pos >= 0 && pos < slab_cap, HSA_ATTN_DEBUG_SCATTER_POS)) continue;
           pr[pos] = (int32_t)row;
           p4[e4][u] = (uint32_t)pos;
