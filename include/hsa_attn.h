@@ -113,8 +113,8 @@ hsa_attn_status_t hsa_build_landmarks(const hsa_attn_dims_t* d, const void* k, v
  * The call processes its rows in equal slabs of whole 64-row chunks, as
  * large as workspace_bytes allows (hsa_attn_prefill_slab_rows tells the
  * size); results do not depend on the slab size.  hsa_attn_workspace_size(d,
- * 0) returns the size for slabs whose worst case stays within 16 GiB (about
- * 18 GB at B=1, Hq=32, T=2^18, k=16, D=128, bf16, in 5 slabs); the minimum is
+ * 0) returns the size for slabs whose worst case stays within about 16 GiB
+ * (19.9 GB at B=1, Hq=32, T=2^18, k=16, D=128, bf16, in 4 slabs); the minimum is
  * the per-call part plus one slab of 64 rows, and less returns
  * HSA_ATTN_WORKSPACE_TOO_SMALL.
  */
