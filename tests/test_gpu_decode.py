@@ -49,6 +49,7 @@ CASES = [
     (3, 32, 8, 64 * 300, 128, 32, "bf16"),
     (2, 4, 4, 64 * 75 + 63, 64, 8, "fp32"),
     (1, 8, 1, 64 * 100, 64, 16, "bf16"),      # G = 8
+    (1, 8, 1, 64 * 200 + 9, 128, 64, "bf16"),  # G = 8, k = 64: 512 group entries in the merge
     (2, 4, 2, 64 * 129, 128, 64, "fp32"),     # G = 2, k = 64
     (1, 4, 4, 64 * 5, 128, 16, "bf16"),       # fewer chunks than k
     (2, 8, 2, 63, 128, 4, "bf16"),            # no complete chunk: zeros
