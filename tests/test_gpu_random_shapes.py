@@ -47,3 +47,29 @@ def test_random_decode_matches_oracle(case):
     print(dec.compare(q, k, v, 64, topk, dtype, out, sel, score))
     if T < 64:
         assert np.all(out == 0) and np.all(sel == -1)
+
+
+def _backward_cases(n, seed):
+    # bf16 storage, k up to 32 (the backward's envelope), shorter sequences:
+    # the oracle's backward is the slow part
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2]))
+        D = int(rng.choice([64, 128]))
+        k = int(rng.integers(1, 33))
+        T = int(rng.integers(10, 64 * 16 + 64))
+        B = int(rng.choice([1, 2]))
+        out.append((B, G * Hkv, Hkv, T, D, k))
+    return out
+
+
+@pytest.mark.parametrize("case", _backward_cases(8, 2028))
+def test_random_backward_within_bounds(case):
+    from tests import test_gpu_backward as bwd
+    print(f"backward case {case}", flush=True)
+    (gq, gk, gv), (rq, rk, rv), (aq, ak, av) = bwd.run_case(case)
+    bwd.check_bound("dq", gq, rq, aq, bwd.TOL_Q)
+    bwd.check_bound("dk", gk, rk, ak, bwd.TOL_KV)
+    bwd.check_bound("dv", gv, rv, av, bwd.TOL_KV)
