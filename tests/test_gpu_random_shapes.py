@@ -2,7 +2,8 @@
 query-group size, head dim, dtype, k (1 .. 64 within the supported
 envelope), ragged sequence lengths (including fewer tokens than one chunk)
 and batch drawn from a fixed generator, so that combinations the hand-picked
-cases leave out are checked too."""
+cases leave out are checked too.  The backward and the adaptive-budget
+decode and prefill get the same treatment within their own envelopes."""
 import numpy as np
 import pytest
 
@@ -73,3 +74,41 @@ def test_random_backward_within_bounds(case):
     bwd.check_bound("dq", gq, rq, aq, bwd.TOL_Q)
     bwd.check_bound("dk", gk, rk, ak, bwd.TOL_KV)
     bwd.check_bound("dv", gv, rv, av, bwd.TOL_KV)
+
+
+def _adaptive_cases(kind, n, seed):
+    # base k with 2k <= 64 (2k <= 32 for prefill groups above four heads);
+    # sequences long enough that rows have a k-th/(k+1)-th cut; for decode,
+    # ragged cache lengths (some below one chunk) in about half the cases
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2]))
+        D = int(rng.choice([64, 128]))
+        dtype = str(rng.choice(["bf16", "fp32"]))
+        kmax = 16 if (kind == "prefill" and G > 4) else 32
+        k = int(rng.integers(1, kmax + 1))
+        B = int(rng.choice([1, 2])) if kind == "prefill" else int(rng.integers(2, 5))
+        hi = 64 * 60 if kind == "prefill" else 64 * 2000
+        T = int(rng.integers(64 * (2 * k + 3), hi))
+        if kind == "prefill":
+            out.append((B, G * Hkv, Hkv, T, D, k, dtype))
+            continue
+        lens = None
+        if rng.random() < 0.5:
+            lens = [T] + [int(x) for x in rng.integers(1, T + 1, size=B - 1)]
+        out.append((B, G * Hkv, Hkv, T, D, k, dtype, lens))
+    return out
+
+
+@pytest.mark.parametrize("case", _adaptive_cases("decode", 6, 2029))
+def test_random_adaptive_decode(case):
+    from tests import test_gpu_adaptive as ada
+    ada.test_adaptive_decode(case)
+
+
+@pytest.mark.parametrize("case", _adaptive_cases("prefill", 4, 2030))
+def test_random_adaptive_prefill(case):
+    from tests import test_gpu_adaptive as ada
+    ada.test_adaptive_prefill(case)
