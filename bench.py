@@ -115,22 +115,55 @@ def timed_steps(step, steps, warmup, n_launch, events):
 
 
 def library_digest():
-    """Digest of the built library (the code the profile measured; the build
-    is deterministic, and comments do not change it)."""
+    """Digest of the built library (the build is deterministic for a given
+    checkout path, and comments do not change it)."""
     import hashlib
     path = os.path.join(ROOT, "hierarchical_sparse_attention_hsa_amd", "libhsa_attn.so")
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
+def device_code_digest():
+    """Digest of the library's device code: its .hip_fatbin section, every
+    kernel as compiled.  Host-side changes (argument checks, workspace
+    planning) leave it unchanged, so counters taken for the kernels stay
+    valid across them; any kernel change alters it.  (hipcc embeds
+    compilation-unit ids derived from the source paths, so a build from
+    another checkout path differs and reads as changed.)"""
+    import hashlib
+    import struct
+    path = os.path.join(ROOT, "hierarchical_sparse_attention_hsa_amd", "libhsa_attn.so")
+    data = open(path, "rb").read()
+    shoff, = struct.unpack_from("<Q", data, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+
+    def header(i):  # name, type, flags, addr, offset, size, ...
+        return struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize)
+
+    names = header(shstrndx)[4]
+    for i in range(shnum):
+        h = header(i)
+        if data[names + h[0]: data.index(b"\0", names + h[0])] == b".hip_fatbin":
+            return hashlib.sha256(data[h[4]: h[4] + h[5]]).hexdigest()[:16]
+    return None
+
+
+def profile_is_current(rec):
+    """A committed counter record applies to the built kernels: same device
+    code (or, for a record without that key, the same library)."""
+    if "device_code_sha256_16" in rec:
+        return rec["device_code_sha256_16"] == device_code_digest()
+    return rec.get("library_sha256_16") == library_digest()
+
+
 def profiled_traffic(workload, kernel_prefix):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter
     record (profiles/<workload>.traffic.json: 128-byte read requests and
-    WRITE_SIZE), or None when the kernel sources changed since."""
+    WRITE_SIZE), or None when the built kernels differ from the profiled ones."""
     path = os.path.join(ROOT, "profiles", f"{workload}.traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("library_sha256_16") != library_digest():
+    if not profile_is_current(rec):
         return None
     for name, b in rec["traffic_bytes_per_launch"].items():
         if kernel_prefix in name:
@@ -250,7 +283,7 @@ def summarize_profile(workload, prof_dir, command, kernel, out_dir=None):
     rd_avg = {n: float(np.mean(v)) for n, v in rd_per.items()}
     wr_avg = {n: float(np.mean(v)) for n, v in wr_per.items()}
     traffic = {n: rd_avg.get(n, 0.0) + wr_avg.get(n, 0.0) for n in set(rd_avg) | set(wr_avg)}
-    rec = {"workload": workload, "library_sha256_16": library_digest(),
+    rec = {"workload": workload, "library_sha256_16": library_digest(), "device_code_sha256_16": device_code_digest(),
            "bytes": "reads 128 x (TCC_EA0_RDREQ - TCC_EA0_RDREQ_32B) + 32 x TCC_EA0_RDREQ_32B; writes 1024 x WRITE_SIZE",
            "check_copy_1GiB": check, "traffic_bytes_per_launch": traffic}
     out_dir = out_dir or os.path.join(ROOT, "profiles")
@@ -313,7 +346,7 @@ def mfma_summary(workload, csv_path, stats, short, out_dir):
                      "counter_tflops": flops / ns / 1e3 if ns else None,
                      "busy_cycles": float(np.mean([c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for c in rows])),
                      "grbm_gui_active": float(np.mean([c.get("GRBM_GUI_ACTIVE", 0.0) for c in rows]))}
-    rec = {"workload": workload, "library_sha256_16": library_digest(), "simd_num": SIMD_NUM, "kernels": out}
+    rec = {"workload": workload, "library_sha256_16": library_digest(), "device_code_sha256_16": device_code_digest(), "simd_num": SIMD_NUM, "kernels": out}
     with open(os.path.join(out_dir, f"{workload}.mfma.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
     lines = ["", "## MFMA counters (--pmc, one dispatch per kernel)", "",
@@ -333,12 +366,12 @@ def mfma_summary(workload, csv_path, stats, short, out_dir):
 
 def profiled_mfma(workload, kernel_prefix):
     """Counter-based MFMA figures of a kernel from profiles/<workload>.mfma.json,
-    or None when the built library differs from the profiled one."""
+    or None when the built kernels differ from the profiled ones."""
     path = os.path.join(ROOT, "profiles", f"{workload}.mfma.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("library_sha256_16") != library_digest():
+    if not profile_is_current(rec):
         return None
     for name, o in rec["kernels"].items():
         if kernel_prefix in name:

@@ -263,6 +263,9 @@ static hsa_attn_status_t forward_prefill(const hsa_attn_dims_t* d, int64_t q_off
                   (long long)q_offset);
     g.Tq = g.T - q_offset;
     g.J0 = q_offset / g.S;
+    // no query rows (an empty sequence, or no new tokens after the prefix):
+    // nothing is read or written, so empty buffers may be NULL
+    if (g.Tq == 0) return ok();
     if (!q || !k || !v || !out || (!landmarks && g.Nc > 0))
       return fail(HSA_ATTN_INVALID_ARGUMENT, "q, k, v, landmarks and out must be non-NULL");
     if ((sel_idx == nullptr) != (sel_score == nullptr))
@@ -277,7 +280,6 @@ static hsa_attn_status_t forward_prefill(const hsa_attn_dims_t* d, int64_t q_off
     if (plan.slab_rows == 0)
       return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs at least %zu bytes (slabs of 64 query rows), got %zu",
                   plan.bytes + kDebugHeader, workspace_bytes);
-    if (g.Tq == 0) return ok();
     if (!workspace) return fail(HSA_ATTN_INVALID_ARGUMENT, "workspace is NULL");
     char* ws = static_cast<char*>(workspace) + kDebugHeader;
     const size_t rows_q = (size_t)g.B * g.Hq * (size_t)g.Tq;
@@ -345,6 +347,7 @@ hsa_attn_status_t hsa_backward_prefill(const hsa_attn_dims_t* d, const void* q, 
     hsa_attn::Geometry g;
     hsa_attn_status_t st = check_dims(d, Call::kBackward, &g);
     if (st != HSA_ATTN_OK) return st;
+    if (g.T == 0) return ok();  // an empty sequence: nothing is read or written (empty buffers may be NULL)
     if (!q || !k || !v || !out || !dout || !sel_idx || !sel_score || !dq || !dk || !dv || (!landmarks && g.Nc > 0))
       return fail(HSA_ATTN_INVALID_ARGUMENT,
                   "q, k, v, landmarks, out, dout, sel_idx, sel_score, dq, dk and dv must be non-NULL");
@@ -356,7 +359,6 @@ hsa_attn_status_t hsa_backward_prefill(const hsa_attn_dims_t* d, const void* q, 
     if (workspace_bytes < plan.bytes + kDebugHeader)
       return fail(HSA_ATTN_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes + kDebugHeader,
                   workspace_bytes);
-    if (g.T == 0) return ok();
     if (!workspace) return fail(HSA_ATTN_INVALID_ARGUMENT, "workspace is NULL");
     char* ws = static_cast<char*>(workspace) + kDebugHeader;
     const size_t qe = (size_t)g.B * g.Hq * (size_t)g.T * g.D, ke = (size_t)g.B * g.Hkv * (size_t)g.T * g.D;

@@ -755,7 +755,9 @@ DecodePlan plan_decode(const Geometry& g, bool own_sel) {
   rows = (rows + 63) / 64 * 64;
   rows = rows < 256 ? 256 : (rows > HSA_ATTN_SCAN_MAX_ROWS ? HSA_ATTN_SCAN_MAX_ROWS : rows);
   p.rows_per_split = (int)rows;
-  p.splits = g.Nc > 0 ? (int)((g.Nc + rows - 1) / rows) : 0;
+  // caches without a complete chunk still get one split: its scan writes
+  // empty candidate lists, so the merge always reads at least one list
+  p.splits = g.Nc > 0 ? (int)((g.Nc + rows - 1) / rows) : 1;
   size_t off = 0;
   p.off_cand = off;
   off = align_up(off + (size_t)bh * p.splits * g.G * g.k * sizeof(float2), 256);
@@ -796,7 +798,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipS
   }
   launch_kernel((decode_merge_kernel<G>), dim3(g.Hkv, g.B), dim3(kWave * G), 0, st, cand, a.sel_idx,
                 a.sel_score, ulist, ucount, g.Hkv, p.splits, g.k, a.k_base, a.gap_tau);
-  if (p.splits > 0) {
+  if (g.Nc > 0) {  // no complete chunk: nothing selected, nothing to attend
     launch_kernel((decode_attn_kernel<T, D, G>), dim3((G * g.k + kAttnWaves - 1) / kAttnWaves, g.Hkv, g.B),
                   dim3(kAttnWaves * kWave), 0, st,
                   static_cast<const stg*>(a.q), static_cast<const stg*>(a.k), static_cast<const stg*>(a.v),

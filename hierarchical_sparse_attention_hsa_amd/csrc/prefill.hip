@@ -211,6 +211,8 @@ PrefillPlan plan_prefill_slab(const Geometry& g, bool own_sel, int64_t slab_rows
     cps = std::min(cps, nqc);
     const int64_t nslab = (nqc + cps - 1) / cps;
     cps = (nqc + nslab - 1) / nslab;
+  } else {
+    cps = 1;  // no query rows: the smallest plan (the call returns before using it)
   }
   p.slab_rows = cps * kChunk;
   const int64_t nslab = nqc > 0 ? (nqc + cps - 1) / cps : 1;

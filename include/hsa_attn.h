@@ -102,6 +102,8 @@ hsa_attn_status_t hsa_build_landmarks(const hsa_attn_dims_t* d, const void* k, v
  * the fp32 dot products q.L before the 1/sqrt(D) factor is applied; where
  * that factor rounds two different dot products to one stored score, the
  * larger dot product is the one kept at the cut.
+ * T = 0 (no query rows) enqueues nothing and returns HSA_ATTN_OK without
+ * looking at any pointer, so empty buffers may be NULL.
  * workspace: device scratch (never NULL when T > 0).  It holds, for the
  * whole call, the selection when sel_idx is NULL (8 bytes per slot), the
  * pair positions (4 bytes per slot), per-chunk bucket counts and a
@@ -144,6 +146,8 @@ hsa_attn_status_t hsa_attn_prefill_slab_rows(const hsa_attn_dims_t* d, int adapt
  * in hsa_forward_prefill; its results equal that call's row q_offset + r.
  * q_offset must be a multiple of S (the prefix is whole chunks).  The
  * workspace of hsa_forward_prefill for the same dims is sufficient.
+ * q_offset = T (no new rows) enqueues nothing and returns HSA_ATTN_OK
+ * without looking at any pointer.
  */
 hsa_attn_status_t hsa_forward_prefill_cached(const hsa_attn_dims_t* d, int64_t q_offset, const void* q,
                                              const void* k, const void* v, const void* landmarks, float* out,
@@ -186,6 +190,8 @@ hsa_attn_status_t hsa_forward_prefill_adaptive(const hsa_attn_dims_t* d, float g
  * probabilities and gradients that feed dk and dv are rounded to bf16
  * (2^-8).  dk and dv accumulate over pairs in an order that depends
  * on scheduling, so they are not bit-reproducible.
+ * T = 0 enqueues nothing and returns HSA_ATTN_OK without looking at any
+ * pointer.
  * workspace: at least hsa_attn_workspace_size(d, 4) bytes (about
  * B*Hq*T*k*(4*D + 12) bytes plus a transposed copy of K: 69 GB at B=1,
  * Hq=32, T=2^18, k=16, D=128).
@@ -202,6 +208,9 @@ hsa_attn_status_t hsa_backward_prefill(const hsa_attn_dims_t* d, const void* q, 
  * all floor(T/S) complete chunks of its cache.
  * q [B,Hq,D], k_cache/v_cache [B,Hkv,T,D], landmarks [B,Hkv,floor(T/S),D],
  * out [B,Hq,D] fp32, sel_idx/sel_score [B,Hq,k] optional (NULL allowed).
+ * Caches without a complete chunk (T < S, T = 0 included) are never read,
+ * so k_cache, v_cache and landmarks may then be NULL; every query has no
+ * candidate and its output is zero.
  * workspace: at least hsa_attn_workspace_size(d, 1) bytes.
  */
 hsa_attn_status_t hsa_forward_decode(const hsa_attn_dims_t* d, const void* q, const void* k_cache,

@@ -388,3 +388,30 @@ def test_debug_environment_variable_selects_the_debug_library():
     path, status = r.stdout.split()
     assert path.endswith("libhsa_attn_debug.so")
     assert int(status) == hsa.HSA_ATTN_INVALID_ARGUMENT  # the debug build's answer to a NULL flags pointer
+
+
+def test_empty_calls_return_ok_without_looking_at_pointers():
+    """No query rows means nothing to read or write: the call returns OK
+    before any pointer check, so the NULL data pointers of empty tensors are
+    accepted (no HIP call is made, so this runs without a GPU)."""
+    lib = hsa.load_library()
+    d0 = dims(seq_len=0)
+    n11 = [None] * 11
+    assert lib.hsa_forward_prefill(ctypes.byref(d0), None, None, None, None, None, None, None, None, 0,
+                                   None) == hsa.HSA_ATTN_OK
+    assert lib.hsa_forward_prefill_adaptive(ctypes.byref(d0), ctypes.c_float(0.5), None, None, None, None, None,
+                                            None, None, None, 0, None) == hsa.HSA_ATTN_OK
+    assert lib.hsa_backward_prefill(ctypes.byref(d0), *n11, None, 0, None) == hsa.HSA_ATTN_OK
+    # a cached prefix covering the whole sequence: q and out are empty
+    p = ctypes.c_void_p(0x1000)
+    d = dims(seq_len=64 * 10)
+    assert lib.hsa_forward_prefill_cached(ctypes.byref(d), 64 * 10, None, p, p, p, None, None, None, None, 0,
+                                          None) == hsa.HSA_ATTN_OK
+    # empty calls still reject malformed dims
+    assert lib.hsa_forward_prefill(ctypes.byref(dims(seq_len=0, top_k=0)), None, None, None, None, None, None,
+                                   None, None, 0, None) == hsa.HSA_ATTN_INVALID_ARGUMENT
+    assert lib.hsa_backward_prefill(ctypes.byref(dims(seq_len=0, dtype=hsa.HSA_ATTN_FP32)), *n11, None, 0,
+                                    None) == hsa.HSA_ATTN_UNSUPPORTED
+    # a non-empty prefill still needs its pointers
+    assert lib.hsa_forward_prefill(ctypes.byref(dims(seq_len=64)), None, p, p, p, p, None, None, p, 1 << 30,
+                                   None) == hsa.HSA_ATTN_INVALID_ARGUMENT

@@ -57,3 +57,24 @@ def test_profile_bytes_follow_the_request_counters(tmp_path):
     assert rec["check_copy_1GiB"] == {"copy_read_GiB": 1.0, "copy_written_GiB": 1.0}
     (name, b), = rec["traffic_bytes_per_launch"].items()
     assert "decode_scan_kernel" in name and b == 900 * 128 + 100 * 32 + 3 * 1024
+
+
+def test_device_code_digest_hashes_the_fatbin_section():
+    # committed counter records are matched to the built kernels by a digest
+    # of the library's .hip_fatbin section; the section located by the
+    # benchmark's own ELF reader must be the one readelf reports
+    import hashlib
+    import shutil
+    import subprocess
+
+    import pytest
+
+    lib = os.path.join(ROOT, "hierarchical_sparse_attention_hsa_amd", "libhsa_attn.so")
+    if not os.path.exists(lib) or shutil.which("readelf") is None:
+        pytest.skip("library not built or readelf missing")
+    out = subprocess.run(["readelf", "-S", "-W", lib], capture_output=True, text=True, check=True).stdout
+    m = re.search(r"\.hip_fatbin\s+\S+\s+[0-9a-f]+\s+([0-9a-f]+)\s+([0-9a-f]+)", out)
+    assert m, "no .hip_fatbin section"
+    off, size = int(m.group(1), 16), int(m.group(2), 16)
+    data = open(lib, "rb").read()[off:off + size]
+    assert size > 0 and bench.device_code_digest() == hashlib.sha256(data).hexdigest()[:16]
