@@ -97,6 +97,25 @@ int main(void) {
   expect(hsa_build_landmarks(&d, p, p, 3, 2, NULL), HSA_ATTN_INVALID_ARGUMENT, "reversed chunk range");
   expect(hsa_build_landmarks(&d, p, p, 0, 4097, NULL), HSA_ATTN_INVALID_ARGUMENT, "chunk range past Nc");
   expect(hsa_build_landmarks(&d, NULL, NULL, 5, 5, NULL), HSA_ATTN_OK, "empty chunk range");
+  {
+    /* empty work: OK before any pointer is looked at */
+    hsa_attn_dims_t e = d;
+    e.seq_len = 0;
+    expect(hsa_forward_prefill(&e, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL), HSA_ATTN_OK,
+           "prefill over no tokens");
+    expect(hsa_forward_prefill_adaptive(&e, 0.5f, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL),
+           HSA_ATTN_OK, "adaptive prefill over no tokens");
+    expect(hsa_backward_prefill(&e, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL),
+           HSA_ATTN_OK, "backward over no tokens");
+    expect(hsa_forward_prefill_cached(&d, d.seq_len, NULL, p, p, p, NULL, NULL, NULL, NULL, 0, NULL), HSA_ATTN_OK,
+           "cached prefill with no new rows");
+    size_t eb = 0;
+    expect(hsa_attn_workspace_size(&e, 0, &eb), HSA_ATTN_OK, "workspace size, no tokens");
+    if (eb > ((size_t)1 << 30)) {
+      fprintf(stderr, "empty prefill plans %zu workspace bytes\n", eb);
+      ++failures;
+    }
+  }
   expect(hsa_forward_decode_varlen(&d, p, p, p, p, NULL, pf, NULL, NULL, p, (size_t)1 << 40, NULL),
          HSA_ATTN_INVALID_ARGUMENT, "NULL cache_lens");
   expect(hsa_append_kv(&d, p, p, p, p, p, (int64_t*)(uintptr_t)0x1004, NULL), HSA_ATTN_INVALID_ARGUMENT,
